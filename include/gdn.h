@@ -1,0 +1,170 @@
+/*
+ * gdn.h: C ABI of the MI355X (gfx950) Gated DeltaNet chunked prefill library.
+ *
+ * The operation (per head h of every packed sequence n), as stated on the page "How to Speed Up
+ * GDN Kernels for Qwen Models", section "What GDN actually computes", and on "Musings on
+ * long-context fine-tuning", section "Isolating the recurrent layers":
+ *
+ *     S_t = exp(g_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,    o_t = scale * S_t^T q_t
+ *
+ * with the d_k x d_v state S reset at every sequence start to that sequence's initial state
+ * (or zero).  The library evaluates it in 64-token chunks (the chunked form of the same page:
+ * gate cumsum, one 64x64 unit-lower-triangular solve per chunk and head, WY-form w/u, the
+ * inter-chunk state chain and the output), on the stream the caller passes.
+ *
+ * Layouts (row-major, token-major, contiguous; T = total_tokens, N = num_seqs, H = num_heads):
+ *   q, k        [T, H, d_k]      dtype (bf16 or fp32)
+ *   v, o        [T, H, d_v]      dtype
+ *   g           [T, H]           fp32: the log-gate, alpha_t = exp(g_t)
+ *   beta        [T, H]           dtype: the write strength
+ *   cu_seqlens  [N + 1]          int32, device; cu_seqlens[0] = 0, cu_seqlens[N] = T, ascending
+ *   h0          sequence n's state at h0 + n * h0_seq_stride, each [H, d_k, d_v] fp32;
+ *               h0_seq_stride = 0 broadcasts one state to every sequence (a shared prefix, as in
+ *               "Musings on long-context fine-tuning", section "Isolating the recurrent layers")
+ *   ht          [N, H, d_k, d_v] fp32, the state after each sequence's last token
+ *
+ * Conventions.
+ *   Ownership: every tensor pointer is a device pointer owned by the caller; the library never
+ *     allocates or frees device memory.  Scratch space is the caller's `workspace`, sized by the
+ *     matching *_workspace_size call; tensors must be 16-byte aligned.
+ *   Asynchrony: calls enqueue work on `stream` and return without a host synchronisation.
+ *   Errors: arguments are validated before anything is enqueued; on an error nothing is written.
+ *     A launch failure returns GDN_ERR_HIP.  gdn_last_error() gives a thread-local detail string.
+ *     The contents of cu_seqlens are read on the device only: sequences must be as described
+ *     above (not checked on the host).
+ *   Architecture: only gfx950 is supported; other devices return GDN_ERR_UNSUPPORTED_ARCH (the
+ *     page's library likewise refuses hardware it was not built for, section "Using it, and the
+ *     fine print").
+ *   Threading: calls are re-entrant; the only global state is a per-device properties cache.
+ */
+#ifndef GDN_H_
+#define GDN_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gdn_status {
+  GDN_OK = 0,
+  GDN_ERR_NULL_ARG = 1,            /* a required pointer is NULL */
+  GDN_ERR_BAD_SHAPE = 2,           /* sizes out of range or unsupported (d, chunk) */
+  GDN_ERR_BAD_DTYPE = 3,           /* dtype not one of GDN_DTYPE_* */
+  GDN_ERR_BAD_MODE = 4,            /* mode / algo / threshold not supported */
+  GDN_ERR_UNSUPPORTED_ARCH = 5,    /* the current device is not gfx950 */
+  GDN_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size figure */
+  GDN_ERR_BAD_ALIGNMENT = 7,       /* a tensor pointer is not 16-byte aligned */
+  GDN_ERR_HIP = 8                  /* a HIP runtime call or kernel launch failed */
+} gdn_status;
+
+/* Element type of q, k, v, beta, o (and of dout, dq, dk, dv, dbeta in the backward). */
+enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
+
+/* Forward mode.
+ *   GDN_MODE_EXACT: the recurrence as defined; every sequence is one chain of chunks.
+ *   GDN_MODE_TRUNCATE: history truncation of "How to Speed Up GDN Kernels for Qwen Models",
+ *     section "Lever 1: the gate is also a license to parallelize".  When num_seqs * num_heads
+ *     is below the CU count, each sequence is split into segments of L chunks,
+ *     L = max(4, nearest power of two of 3 * sqrt(H * Nc / P)) with Nc the number of chunks and
+ *     P the CU count (or L = seg_chunks if positive).  Every (segment, head) starts from zero at
+ *     a warmup window: the shortest run of whole preceding chunks whose summed g is below
+ *     trunc_log_threshold (-10 on the page), or from the true initial state when the window
+ *     reaches the sequence start.  The error this introduces is bounded per token by
+ *     ||q_t|| * exp(threshold) * ||S_exact(window start)||_2 when 0 <= beta ||k||^2 <= 2. */
+enum { GDN_MODE_EXACT = 0, GDN_MODE_TRUNCATE = 1 };
+
+typedef struct gdn_problem {
+  int64_t total_tokens;      /* T = cu_seqlens[N] (>= 0) */
+  int32_t num_seqs;          /* N >= 1 */
+  int32_t num_heads;         /* H >= 1 (q, k and v heads are equal) */
+  int32_t d_k;               /* 64 or 128 */
+  int32_t d_v;               /* equal to d_k */
+  int32_t chunk;             /* 64 */
+  int32_t dtype;             /* GDN_DTYPE_* */
+  int32_t mode;              /* GDN_MODE_* */
+  int32_t seg_chunks;        /* truncate mode: 0 = latency model, > 0 = forced segment length */
+  int32_t num_cus;           /* P of the latency model; 0 = the device's CU count */
+  float trunc_log_threshold; /* truncate mode: -10 */
+  float scale;               /* o_t = scale * S_t^T q_t (1 in the pages' formulation) */
+  int32_t reserved;          /* must be 0 */
+  int64_t h0_seq_stride;     /* elements between consecutive sequences' h0; 0 = broadcast */
+} gdn_problem;
+
+/* Fills *p with defaults: chunk 64, dtype bf16, exact mode, threshold -10, scale 1, and the
+ * given sizes. */
+gdn_status gdn_problem_init(gdn_problem *p, int64_t total_tokens, int32_t num_seqs,
+                            int32_t num_heads, int32_t head_dim);
+
+/* Bytes of device workspace gdn_chunk_fwd needs for *p.  cu_seqlens_host (optional, N + 1
+ * host int32) lets the truncate mode size its segment plan exactly; pass the same pointer (or
+ * NULL) to gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
+                                        size_t *bytes);
+
+/* Forward of the chunked gated delta rule.  h0 may be NULL (zero initial states) and ht may be
+ * NULL (final states not written).  o must not alias an input. */
+gdn_status gdn_chunk_fwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+                         const float *g, const void *beta, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, const float *h0, void *o, float *ht,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The forward's segment plan, for inspection.  Runs the planning step of gdn_chunk_fwd on the
+ * device and writes to plan_out (device int32, capacity plan_capacity entries):
+ *   plan_out[0] = number of units U, plan_out[1] = segment length L (0 = unsplit),
+ *   then for each unit u: seq, first chunk, end chunk (chunk numbers counted from the sequence's
+ *   first chunk), then H warmup-window first chunks (same numbering).
+ * Needs plan_capacity >= 2 + U * (3 + H).  Uses the same workspace as gdn_chunk_fwd. */
+gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t *plan_out,
+                              int64_t plan_capacity, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream);
+
+/* The forward with every per-chunk intermediate of the chunked form written out (fp32), for
+ * checking each step separately; exact mode only.  Chunk c counts the chunks of all sequences
+ * in order.  Any output may be NULL.
+ *   gamma [T, H]            within-chunk cumulative sum of g
+ *   tmat  [Nc, H, 64, 64]   (I + A)^{-1}, A_ri = beta_r exp(gamma_r - gamma_i) k_r.k_i (i < r)
+ *   w     [Nc, H, 64, d_k]  W = Tm diag(beta exp(gamma)) K
+ *   u     [Nc, H, 64, d_v]  U = Tm diag(beta) V
+ *   hc    [Nc, H, d_k, d_v] the state at the start of each chunk
+ *   delta [T, H, d_v]       Delta = U - W hc
+ * Nc = sum over sequences of ceil(len / 64).  Rows past a partial chunk's length are zero. */
+gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, const void *k,
+                                       const void *v, const float *g, const void *beta,
+                                       const int32_t *cu_seqlens, const float *h0, void *o,
+                                       float *ht, float *gamma, float *tmat, float *w, float *u,
+                                       float *hc, float *delta, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of device workspace gdn_chunk_bwd needs for *p. */
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes);
+
+/* Backward of the exact forward (mode must be GDN_MODE_EXACT): given dout (dtype, [T, H, d_v])
+ * and optionally dht ([N, H, d_k, d_v] fp32, NULL = zero), writes dq, dk (dtype, [T, H, d_k]),
+ * dv (dtype, [T, H, d_v]), dg (fp32, [T, H]) and dbeta (dtype, [T, H]).  dh0 (optional, fp32)
+ * receives the gradient of the initial states: [N, H, d_k, d_v] per sequence, or [H, d_k, d_v]
+ * summed over all sequences when h0_seq_stride is 0 (a state shared by every sequence collects
+ * the sum of their gradients, "Musings on long-context fine-tuning", section "Backward
+ * through P").  Hidden states are recomputed, not stored ("How to Speed Up GDN Kernels for
+ * Qwen Models", section "Lever 2"). */
+gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+                         const float *g, const void *beta, const int32_t *cu_seqlens,
+                         const float *h0, const void *dout, const float *dht, void *dq, void *dk,
+                         void *dv, float *dg, void *dbeta, float *dh0, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream);
+
+/* Static description of a status code. */
+const char *gdn_status_string(gdn_status s);
+
+/* Detail of the last error on the calling thread (empty string if none). */
+const char *gdn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H_ */

@@ -1,0 +1,10 @@
+"""MI355X (gfx950) Gated DeltaNet chunked prefill.
+
+``gdn`` holds the Python binding of the HIP library (``libgdn_mi355x.so``, built by
+``python -m linear_attention_recurrence_prefill_amd.build``); the C ABI is ``include/gdn.h``.
+"""
+from .gdn import (GdnError, chunk_bwd, chunk_fwd, chunk_fwd_intermediates, chunk_fwd_plan,
+                  load_library)
+
+__all__ = ["GdnError", "chunk_fwd", "chunk_bwd", "chunk_fwd_plan", "chunk_fwd_intermediates",
+           "load_library"]

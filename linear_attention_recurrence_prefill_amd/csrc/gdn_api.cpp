@@ -1,0 +1,344 @@
+// C ABI of the gated delta rule library: argument validation, workspace sizing, the segment
+// plan's host-side parameters and kernel dispatch.  Declarations and conventions: include/gdn.h.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/gdn.h"
+#include "gdn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gdn_status fail(gdn_status s, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+gdn_status hip_fail(hipError_t e, const char *what) {
+  return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Per-device properties cache: is the device gfx950, and its CU count.
+struct DevInfo {
+  int checked = 0;
+  int is_gfx950 = 0;
+  int cus = 0;
+};
+constexpr int kMaxDevices = 64;
+DevInfo g_dev[kMaxDevices];
+std::mutex g_dev_mu;
+
+gdn_status device_info(int *cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(GDN_ERR_UNSUPPORTED_ARCH, "device %d", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DevInfo &d = g_dev[dev];
+  if (!d.checked) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    d.is_gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    d.checked = 1;
+  }
+  if (!d.is_gfx950) return fail(GDN_ERR_UNSUPPORTED_ARCH, "device %d is not gfx950", dev);
+  if (cus) *cus = d.cus;
+  return GDN_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+gdn_status check_problem(const gdn_problem *p) {
+  if (!p) return fail(GDN_ERR_NULL_ARG, "problem is NULL");
+  if (p->total_tokens < 0 || p->total_tokens > INT32_MAX)
+    return fail(GDN_ERR_BAD_SHAPE, "total_tokens %lld out of range", (long long)p->total_tokens);
+  if (p->num_seqs < 1) return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be >= 1");
+  if (p->num_heads < 1 || p->num_heads > 65535)
+    return fail(GDN_ERR_BAD_SHAPE, "num_heads must be in [1, 65535]");
+  if (!((p->d_k == 64 || p->d_k == 128) && p->d_v == p->d_k))
+    return fail(GDN_ERR_BAD_SHAPE, "head dims must be d_k = d_v in {64, 128}");
+  if (p->chunk != gdn::kChunk) return fail(GDN_ERR_BAD_SHAPE, "chunk must be 64");
+  if (p->dtype != GDN_DTYPE_F32 && p->dtype != GDN_DTYPE_BF16)
+    return fail(GDN_ERR_BAD_DTYPE, "dtype %d", p->dtype);
+  if (p->mode != GDN_MODE_EXACT && p->mode != GDN_MODE_TRUNCATE)
+    return fail(GDN_ERR_BAD_MODE, "mode %d", p->mode);
+  if (p->mode == GDN_MODE_TRUNCATE && !(p->trunc_log_threshold < 0.f))
+    return fail(GDN_ERR_BAD_MODE, "trunc_log_threshold must be negative");
+  if (p->seg_chunks < 0 || p->num_cus < 0 || p->reserved != 0)
+    return fail(GDN_ERR_BAD_SHAPE, "seg_chunks / num_cus / reserved out of range");
+  if (p->h0_seq_stride < 0) return fail(GDN_ERR_BAD_SHAPE, "h0_seq_stride must be >= 0");
+  if (!std::isfinite(p->scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
+  return GDN_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Number of chunks: exact from the host copy of cu_seqlens, else ceil(T / 64).
+int64_t count_chunks(const gdn_problem *p, const int32_t *cu_host) {
+  if (!cu_host) return ceil_div(p->total_tokens, gdn::kChunk);
+  int64_t nc = 0;
+  for (int32_t n = 0; n < p->num_seqs; ++n) nc += ceil_div(cu_host[n + 1] - cu_host[n], gdn::kChunk);
+  return nc;
+}
+
+// Segment length of the truncate mode ("How to Speed Up GDN Kernels for Qwen Models", section
+// "Lever 1"): the latency-optimal length is proportional to sqrt(H * Nc / P); it is scaled by 3,
+// rounded to the nearest power of two in log2 and floored at 4 chunks, and the split is used
+// only when num_seqs * H does not fill the P compute units.  Returns 0 for no split.
+int32_t segment_chunks(const gdn_problem *p, int64_t nchunks, int32_t P) {
+  if (p->mode != GDN_MODE_TRUNCATE) return 0;
+  if (p->seg_chunks > 0) return p->seg_chunks;
+  if ((int64_t)p->num_seqs * p->num_heads >= P) return 0;
+  const double lstar = 3.0 * std::sqrt((double)p->num_heads * (double)nchunks / (double)P);
+  const int e = (int)std::floor(std::log2(lstar) + 0.5);
+  int32_t L = (int32_t)std::ldexp(1.0, e);
+  return L < 4 ? 4 : L;
+}
+
+// Units (workgroups per head) the plan can produce: exact when the host copy is given.
+int64_t max_units(const gdn_problem *p, const int32_t *cu_host, int32_t L) {
+  if (L <= 0) return p->num_seqs;
+  if (cu_host) {
+    int64_t u = 0;
+    for (int32_t n = 0; n < p->num_seqs; ++n)
+      u += ceil_div(ceil_div(cu_host[n + 1] - cu_host[n], gdn::kChunk), L);
+    return u > 0 ? u : 1;
+  }
+  return ceil_div(ceil_div(p->total_tokens, gdn::kChunk) + p->num_seqs, L) + p->num_seqs;
+}
+
+gdn_status check_cu_host(const gdn_problem *p, const int32_t *cu_host) {
+  if (!cu_host) return GDN_OK;
+  if (cu_host[0] != 0 || cu_host[p->num_seqs] != p->total_tokens)
+    return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens_host must start at 0 and end at total_tokens");
+  for (int32_t n = 0; n < p->num_seqs; ++n)
+    if (cu_host[n + 1] < cu_host[n]) return fail(GDN_ERR_BAD_SHAPE, "cu_seqlens_host descends");
+  return GDN_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct FwdLayout {
+  int32_t L = 0;
+  int64_t units = 0;
+  size_t plan_off = 0, chunk0_off = 0, total = 0;
+};
+
+gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, FwdLayout *lay) {
+  int cus = p->num_cus;
+  if (cus == 0 && p->mode == GDN_MODE_TRUNCATE && p->seg_chunks == 0) {
+    gdn_status s = device_info(&cus);
+    if (s != GDN_OK) return s;
+  }
+  const int64_t nc = count_chunks(p, cu_host);
+  lay->L = segment_chunks(p, nc, cus > 0 ? cus : 1);
+  lay->units = max_units(p, cu_host, lay->L);
+  size_t off = 0;
+  lay->plan_off = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)(gdn::kPlanHeader + 3 * lay->units));
+  lay->chunk0_off = off;
+  off = align_up(off + sizeof(int32_t) * (size_t)(p->num_seqs + 1));
+  lay->total = off;
+  return GDN_OK;
+}
+
+struct Tensors {
+  const void *q, *k, *v;
+  const float *g;
+  const void *beta;
+  const int32_t *cu;
+  const float *h0;
+  void *o;
+  float *ht;
+};
+
+gdn_status check_tensors(const Tensors &t) {
+  if (!t.q || !t.k || !t.v || !t.g || !t.beta || !t.cu || !t.o)
+    return fail(GDN_ERR_NULL_ARG, "q, k, v, g, beta, cu_seqlens and o are required");
+  const void *ptrs[] = {t.q, t.k, t.v, t.g, t.beta, t.o};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return fail(GDN_ERR_BAD_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if ((t.h0 && !aligned16(t.h0)) || (t.ht && !aligned16(t.ht)))
+    return fail(GDN_ERR_BAD_ALIGNMENT, "h0 / ht must be 16-byte aligned");
+  return GDN_OK;
+}
+
+gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_host, bool dump,
+                   float *dbg[6], void *ws, size_t ws_bytes, hipStream_t stream) {
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  s = check_tensors(t);
+  if (s != GDN_OK) return s;
+  s = check_cu_host(p, cu_host);
+  if (s != GDN_OK) return s;
+  s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  FwdLayout lay;
+  s = fwd_layout(p, cu_host, &lay);
+  if (s != GDN_OK) return s;
+  if (!ws && lay.total > 0) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
+  if (ws_bytes < lay.total)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
+  char *base = static_cast<char *>(ws);
+  int32_t *plan = reinterpret_cast<int32_t *>(base + lay.plan_off);
+  int32_t *chunk0 = reinterpret_cast<int32_t *>(base + lay.chunk0_off);
+
+  hipError_t e = gdn::launch_plan(t.cu, p->num_seqs, p->total_tokens, lay.L, plan, chunk0,
+                                  lay.units, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  if (t.ht) {
+    e = gdn::launch_empty_states(t.cu, p->num_seqs, p->num_heads, p->d_k, t.h0,
+                                 p->h0_seq_stride, t.ht, stream);
+    if (e != hipSuccess) return hip_fail(e, "empty-state launch");
+  }
+  gdn::FwdArgs a{};
+  a.q = t.q;
+  a.k = t.k;
+  a.v = t.v;
+  a.g = t.g;
+  a.beta = t.beta;
+  a.cu = t.cu;
+  a.h0 = t.h0;
+  a.h0_stride = p->h0_seq_stride;
+  a.o = t.o;
+  a.ht = t.ht;
+  a.plan = plan;
+  a.chunk0 = chunk0;
+  if (dump) {
+    a.dbg_gamma = dbg[0];
+    a.dbg_tmat = dbg[1];
+    a.dbg_w = dbg[2];
+    a.dbg_u = dbg[3];
+    a.dbg_hc = dbg[4];
+    a.dbg_delta = dbg[5];
+  }
+  a.T = p->total_tokens;
+  a.N = p->num_seqs;
+  a.H = p->num_heads;
+  a.scale = p->scale;
+  a.log_thr = p->trunc_log_threshold;
+  a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
+  if (p->total_tokens > 0) {
+    e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
+    if (e != hipSuccess) return hip_fail(e, "forward launch");
+  }
+  return GDN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_problem_init(gdn_problem *p, int64_t total_tokens, int32_t num_seqs,
+                            int32_t num_heads, int32_t head_dim) {
+  if (!p) return fail(GDN_ERR_NULL_ARG, "problem is NULL");
+  std::memset(p, 0, sizeof(*p));
+  p->total_tokens = total_tokens;
+  p->num_seqs = num_seqs;
+  p->num_heads = num_heads;
+  p->d_k = head_dim;
+  p->d_v = head_dim;
+  p->chunk = gdn::kChunk;
+  p->dtype = GDN_DTYPE_BF16;
+  p->mode = GDN_MODE_EXACT;
+  p->trunc_log_threshold = -10.0f;
+  p->scale = 1.0f;
+  p->h0_seq_stride = (int64_t)num_heads * head_dim * head_dim;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
+                                        size_t *bytes) {
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+  s = check_cu_host(p, cu_seqlens_host);
+  if (s != GDN_OK) return s;
+  FwdLayout lay;
+  s = fwd_layout(p, cu_seqlens_host, &lay);
+  if (s != GDN_OK) return s;
+  *bytes = lay.total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_fwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+                         const float *g, const void *beta, const int32_t *cu_seqlens,
+                         const int32_t *cu_seqlens_host, const float *h0, void *o, float *ht,
+                         void *workspace, size_t workspace_bytes, hipStream_t stream) {
+  Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
+  return run_fwd(p, t, cu_seqlens_host, false, nullptr, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, const void *k,
+                                       const void *v, const float *g, const void *beta,
+                                       const int32_t *cu_seqlens, const float *h0, void *o,
+                                       float *ht, float *gamma, float *tmat, float *w, float *u,
+                                       float *hc, float *delta, void *workspace,
+                                       size_t workspace_bytes, hipStream_t stream) {
+  if (p && p->mode != GDN_MODE_EXACT)
+    return fail(GDN_ERR_BAD_MODE, "intermediates are defined for the exact mode only");
+  Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
+  float *dbg[6] = {gamma, tmat, w, u, hc, delta};
+  return run_fwd(p, t, nullptr, true, dbg, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_t *cu_seqlens,
+                              const int32_t *cu_seqlens_host, int32_t *plan_out,
+                              int64_t plan_capacity, void *workspace, size_t workspace_bytes,
+                              hipStream_t stream) {
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  if (!g || !cu_seqlens || !plan_out) return fail(GDN_ERR_NULL_ARG, "g, cu_seqlens, plan_out");
+  s = check_cu_host(p, cu_seqlens_host);
+  if (s != GDN_OK) return s;
+  s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  FwdLayout lay;
+  s = fwd_layout(p, cu_seqlens_host, &lay);
+  if (s != GDN_OK) return s;
+  if (!workspace || workspace_bytes < lay.total)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
+  if (plan_capacity < 2) return fail(GDN_ERR_BAD_SHAPE, "plan_capacity must be >= 2");
+  char *base = static_cast<char *>(workspace);
+  int32_t *plan = reinterpret_cast<int32_t *>(base + lay.plan_off);
+  int32_t *chunk0 = reinterpret_cast<int32_t *>(base + lay.chunk0_off);
+  hipError_t e = gdn::launch_plan(cu_seqlens, p->num_seqs, p->total_tokens, lay.L, plan, chunk0,
+                                  lay.units, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  const int truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
+  e = gdn::launch_plan_export(plan, cu_seqlens, g, p->num_heads, p->trunc_log_threshold,
+                              truncate, lay.units, plan_out, plan_capacity, stream);
+  if (e != hipSuccess) return hip_fail(e, "plan export launch");
+  return GDN_OK;
+}
+
+const char *gdn_status_string(gdn_status s) {
+  switch (s) {
+    case GDN_OK: return "ok";
+    case GDN_ERR_NULL_ARG: return "a required pointer is NULL";
+    case GDN_ERR_BAD_SHAPE: return "unsupported or inconsistent sizes";
+    case GDN_ERR_BAD_DTYPE: return "unsupported dtype";
+    case GDN_ERR_BAD_MODE: return "unsupported mode";
+    case GDN_ERR_UNSUPPORTED_ARCH: return "device is not gfx950";
+    case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case GDN_ERR_BAD_ALIGNMENT: return "tensor pointer not 16-byte aligned";
+    case GDN_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char *gdn_last_error(void) { return g_err; }
+
+}  // extern "C"

@@ -1,0 +1,100 @@
+// Device-side building blocks for the gfx950 gated delta rule kernels: vector types, MFMA
+// wrappers, bf16 conversion and LDS fragment loads.
+//
+// MFMA lane layouts used throughout (wave64, lane l, group gq = l / 16, column c = l % 16):
+//   v_mfma_f32_16x16x32_bf16  A[m][k]: lane m + 16 * (k / 8), item k % 8
+//                             B[k][n]: lane n + 16 * (k / 8), item k % 8
+//                             D[m][n]: lane n + 16 * (m / 4), item m % 4
+//   v_mfma_f32_16x16x4_f32    A[m][k]: lane m + 16 * k;  B[k][n]: lane n + 16 * k;  D as above
+// ds_read_b64_tr_b16 (16-lane groups): lane i of a group receives element i % 4 of the 8-byte
+// words addressed by lanes i / 4, 4 + i / 4, 8 + i / 4, 12 + i / 4 of that group, in that
+// order.  When lane j = 4 r + q of the group addresses row (base + r), column (n0 + 4 q) of a
+// row-major bf16 matrix, lane i receives rows base..base+3 of column n0 + i: a column-major
+// MFMA operand read from row-major storage.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdn {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+#define GDN_LDS __attribute__((address_space(3)))
+
+__device__ __forceinline__ f32x4 mma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+  return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {
+  return cat8(to_bf16x4(a), to_bf16x4(b));
+}
+
+// 4 consecutive bf16 (8 bytes, 8-byte aligned) from LDS.
+__device__ __forceinline__ bf16x4 lds_bf16x4(const bf16 *p) {
+  return *reinterpret_cast<const bf16x4 *>(p);
+}
+// 8 consecutive bf16 (16 bytes, 16-byte aligned) from LDS.
+__device__ __forceinline__ bf16x8 lds_bf16x8(const bf16 *p) {
+  return *reinterpret_cast<const bf16x8 *>(p);
+}
+// 4 consecutive fp32 (16 bytes, 16-byte aligned) from LDS.
+__device__ __forceinline__ f32x4 lds_f32x4(const float *p) {
+  return *reinterpret_cast<const f32x4 *>(p);
+}
+
+// Transposing 8-byte LDS read (see the layout note above).  p must be 8-byte aligned.
+__device__ __forceinline__ bf16x4 lds_tr16(const bf16 *p) {
+  i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((GDN_LDS i16x4 *)((GDN_LDS char *)p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return (float)x; }
+
+template <class E>
+__device__ __forceinline__ E from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) {
+  return x;
+}
+template <>
+__device__ __forceinline__ bf16 from_f32<bf16>(float x) {
+  return (bf16)x;
+}
+
+// Wave-wide inclusive prefix sum (64 lanes).
+__device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    float y = __shfl_up(x, off, 64);
+    if (lane >= off) x += y;
+  }
+  return x;
+}
+
+// Wave-wide sum in fp64 (64 lanes); every lane receives the total.
+__device__ __forceinline__ double wave_sum_f64(double x) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,272 @@
+"""Python binding of the gfx950 gated delta rule library (argument marshalling only).
+
+Every step of the computation runs in the HIP kernels of ``libgdn_mi355x.so``; this module
+checks tensor shapes, takes device pointers from torch tensors, allocates outputs and workspace
+with torch (memory plumbing) and calls the C ABI declared in ``include/gdn.h`` on torch's
+current stream.  There is no fallback: if the library is missing or the device is not gfx950,
+the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libgdn_mi355x.so")
+
+GDN_DTYPE_F32, GDN_DTYPE_BF16 = 0, 1
+GDN_MODE_EXACT, GDN_MODE_TRUNCATE = 0, 1
+_MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
+
+# Every exported entry point of include/gdn.h.
+EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
+           "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
+           "gdn_chunk_bwd", "gdn_status_string", "gdn_last_error")
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+class GdnProblem(ctypes.Structure):
+    _fields_ = [("total_tokens", ctypes.c_int64), ("num_seqs", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("mode", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
+                ("num_cus", ctypes.c_int32), ("trunc_log_threshold", ctypes.c_float),
+                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("h0_seq_stride", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libgdn_mi355x.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m linear_attention_recurrence_prefill_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.POINTER(ctypes.c_int32)
+    P = ctypes.POINTER(GdnProblem)
+    st = ctypes.c_int
+    lib.gdn_problem_init.argtypes = [P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                     ctypes.c_int32]
+    lib.gdn_problem_init.restype = st
+    lib.gdn_chunk_fwd_workspace_size.argtypes = [P, i32p, ctypes.POINTER(sz)]
+    lib.gdn_chunk_fwd_workspace_size.restype = st
+    lib.gdn_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd.restype = st
+    lib.gdn_chunk_fwd_plan.argtypes = [P, vp, vp, i32p, vp, ctypes.c_int64, vp, sz, vp]
+    lib.gdn_chunk_fwd_plan.restype = st
+    lib.gdn_chunk_fwd_intermediates.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, vp, vp, vp, sz, vp]
+    lib.gdn_chunk_fwd_intermediates.restype = st
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.gdn_chunk_bwd_workspace_size.restype = st
+    lib.gdn_chunk_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, vp, sz, vp]
+    lib.gdn_chunk_bwd.restype = st
+    lib.gdn_status_string.argtypes = [st]
+    lib.gdn_status_string.restype = ctypes.c_char_p
+    lib.gdn_last_error.argtypes = []
+    lib.gdn_last_error.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        lib = load_library()
+        raise GdnError(status, f"{lib.gdn_status_string(status).decode()}: "
+                               f"{lib.gdn_last_error().decode()}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact", scale=1.0,
+                 seg_chunks=0, num_cus=0, trunc_log_threshold=-10.0, h0_seq_stride=None):
+    lib = load_library()
+    p = GdnProblem()
+    _check(lib.gdn_problem_init(ctypes.byref(p), int(total_tokens), int(num_seqs),
+                                int(num_heads), int(head_dim)))
+    p.dtype = GDN_DTYPE_BF16 if dtype == torch.bfloat16 else GDN_DTYPE_F32
+    p.mode = _MODES[mode]
+    p.scale = float(scale)
+    p.seg_chunks = int(seg_chunks)
+    p.num_cus = int(num_cus)
+    p.trunc_log_threshold = float(trunc_log_threshold)
+    if h0_seq_stride is not None:
+        p.h0_seq_stride = int(h0_seq_stride)
+    return p
+
+
+def _validate(q, k, v, g, beta, cu_seqlens, h0):
+    T, H, D = q.shape
+    if k.shape != (T, H, D) or v.shape != (T, H, D):
+        raise ValueError("q, k, v must all be [T, H, D]")
+    if g.shape != (T, H) or beta.shape != (T, H):
+        raise ValueError("g and beta must be [T, H]")
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError("q must be bfloat16 or float32")
+    if k.dtype != q.dtype or v.dtype != q.dtype or beta.dtype != q.dtype:
+        raise ValueError("k, v and beta must have q's dtype")
+    if g.dtype != torch.float32:
+        raise ValueError("g must be float32")
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+    for t in (q, k, v, g, beta, cu_seqlens):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("inputs must be contiguous device tensors")
+    N = cu_seqlens.numel() - 1
+    stride = None
+    if h0 is not None:
+        if h0.dtype != torch.float32 or not h0.is_cuda or not h0.is_contiguous():
+            raise ValueError("h0 must be a contiguous float32 device tensor")
+        if h0.shape == (H, D, D):
+            stride = 0
+        elif h0.shape == (N, H, D, D):
+            stride = H * D * D
+        else:
+            raise ValueError("h0 must be [N, H, D, D] or [H, D, D] (shared by all sequences)")
+    return T, H, D, N, stride
+
+
+def _host_cu(cu_seqlens, cu_seqlens_host):
+    if cu_seqlens_host is None:
+        return None
+    arr = (ctypes.c_int32 * len(cu_seqlens_host))(*[int(x) for x in cu_seqlens_host])
+    return arr
+
+
+def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
+              seg_chunks=0, num_cus=0, trunc_log_threshold=-10.0, output_final_state=True,
+              cu_seqlens_host=None, out=None, final_state=None, workspace=None):
+    """Forward of the chunked gated delta rule.  Returns (o, ht or None)."""
+    lib = load_library()
+    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_cus,
+                     trunc_log_threshold, stride)
+    cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(v)
+    ht = None
+    if output_final_state:
+        ht = final_state if final_state is not None else torch.empty(
+            (N, H, D, D), dtype=torch.float32, device=q.device)
+    _check(lib.gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), cu_h, _ptr(h0), _ptr(o), _ptr(ht),
+                             _ptr(workspace), workspace.numel(), _stream()))
+    return o, ht
+
+
+def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, num_cus=0,
+                        cu_seqlens_host=None):
+    lib = load_library()
+    T, Hq, D = q.shape
+    p = make_problem(T, cu_seqlens.numel() - 1, Hq, D, q.dtype, mode, 1.0, seg_chunks, num_cus)
+    n = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), _host_cu(cu_seqlens,
+                                                                      cu_seqlens_host),
+                                            ctypes.byref(n)))
+    return n.value
+
+
+def chunk_fwd_plan(g, cu_seqlens, num_heads, head_dim, dtype, *, mode="truncate", seg_chunks=0,
+                   num_cus=0, trunc_log_threshold=-10.0, cu_seqlens_host=None):
+    """The segment plan the forward uses.  Returns dict(L, seq, c0, c1, warm [U, H])."""
+    lib = load_library()
+    T = g.shape[0]
+    N = cu_seqlens.numel() - 1
+    p = make_problem(T, N, num_heads, head_dim, dtype, mode, 1.0, seg_chunks, num_cus,
+                     trunc_log_threshold)
+    cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
+    ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=g.device)
+    cap = 2 + (T // 64 + N + 1) * (3 + num_heads)
+    out = torch.full((cap,), -1, dtype=torch.int32, device=g.device)
+    _check(lib.gdn_chunk_fwd_plan(ctypes.byref(p), _ptr(g), _ptr(cu_seqlens), cu_h, _ptr(out),
+                                  cap, _ptr(ws), ws.numel(), _stream()))
+    host = out.cpu()
+    U, L = int(host[0]), int(host[1])
+    body = host[2:2 + U * (3 + num_heads)].reshape(U, 3 + num_heads)
+    return dict(L=L, seq=body[:, 0].numpy(), c0=body[:, 1].numpy(), c1=body[:, 2].numpy(),
+                warm=body[:, 3:].numpy())
+
+
+def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
+                            num_chunks=None):
+    """Exact forward that also returns the per-chunk intermediates (fp32):
+    o, ht, dict(gamma [T,H], tmat [Nc,H,64,64], w [Nc,H,64,D], u [Nc,H,64,D],
+    hc [Nc,H,D,D], delta [T,H,D])."""
+    lib = load_library()
+    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    if num_chunks is None:
+        cu = cu_seqlens.cpu().tolist()
+        num_chunks = sum((cu[i + 1] - cu[i] + 63) // 64 for i in range(N))
+    p = make_problem(T, N, H, D, q.dtype, "exact", scale, h0_seq_stride=stride)
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(ws_bytes)))
+    ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    dev = q.device
+    f32 = torch.float32
+    inter = dict(gamma=torch.zeros((T, H), dtype=f32, device=dev),
+                 tmat=torch.zeros((num_chunks, H, 64, 64), dtype=f32, device=dev),
+                 w=torch.zeros((num_chunks, H, 64, D), dtype=f32, device=dev),
+                 u=torch.zeros((num_chunks, H, 64, D), dtype=f32, device=dev),
+                 hc=torch.zeros((num_chunks, H, D, D), dtype=f32, device=dev),
+                 delta=torch.zeros((T, H, D), dtype=f32, device=dev))
+    o = torch.empty_like(v)
+    ht = torch.empty((N, H, D, D), dtype=f32, device=dev)
+    _check(lib.gdn_chunk_fwd_intermediates(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+        _ptr(h0), _ptr(o), _ptr(ht), _ptr(inter["gamma"]), _ptr(inter["tmat"]),
+        _ptr(inter["w"]), _ptr(inter["u"]), _ptr(inter["hc"]), _ptr(inter["delta"]), _ptr(ws),
+        ws.numel(), _stream()))
+    return o, ht, inter
+
+
+def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.0,
+              need_dh0=True, workspace=None):
+    """Backward of the exact forward.  Returns dict(dq, dk, dv, dg, dbeta, dh0).  dh0 is
+    [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D])."""
+    lib = load_library()
+    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must be contiguous with v's shape and q's dtype")
+    if dht is not None and (dht.shape != (N, H, D, D) or dht.dtype != torch.float32):
+        raise ValueError("dht must be float32 [N, H, D, D]")
+    p = make_problem(T, N, H, D, q.dtype, "exact", scale,
+                     h0_seq_stride=stride if stride is not None else H * D * D)
+    ws_bytes = ctypes.c_size_t(0)
+    _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    if workspace is None or workspace.numel() < ws_bytes.value:
+        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dg=torch.empty_like(g), dbeta=torch.empty_like(beta), dh0=None)
+    if need_dh0:
+        shape = (H, D, D) if stride == 0 else (N, H, D, D)
+        out["dh0"] = torch.empty(shape, dtype=torch.float32, device=q.device)
+    _check(lib.gdn_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                             _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(out["dq"]),
+                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
+                             workspace.numel(), _stream()))
+    return out

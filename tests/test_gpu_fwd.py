@@ -1,0 +1,207 @@
+"""GPU parity of the forward against the fp64 oracle (gfx950 only; marked ``gpu``).
+
+Tolerances: relative L2 <= 1e-4 for fp32 inputs, <= 5e-3 for bf16 inputs (fp32 state), on the
+outputs and on the final states.
+"""
+import numpy as np
+import pytest
+
+from gdn_inputs import make_inputs, workload
+from gpu_util import args_of, np64, rel_l2, report, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_recurrence_prefill_amd as m
+
+    m.load_library()
+    return m
+
+
+def _oracle_args(inp):
+    return [inp[x] for x in ("q", "k", "v", "g", "beta")]
+
+
+def _check_fwd(gdn, oracle_mod, inp, label, **kw):
+    d = to_dev(inp)
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], d["h0"], **kw)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle_mod.fwd_recurrent(*_oracle_args(inp), inp["cu_seqlens"], h0=inp["h0"],
+                                             scale=kw.get("scale", 1.0))
+    tol = tol_for(inp["dtype"])
+    print(f"[{label}]", flush=True)
+    report("o", np64(o), o_ref, tol)
+    report("ht", np64(ht), ht_ref, tol)
+    return o, ht
+
+
+def test_tiny_fp32(gdn, oracle_mod):
+    """1 x 256 tokens, H=2, d=64, fp32."""
+    _check_fwd(gdn, oracle_mod, workload("tiny"), "tiny fp32")
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 64), ("f32", 128), ("bf16", 128)])
+def test_ragged_documents_with_h0(gdn, oracle_mod, dtype, d):
+    """Documents of 1, 63, 64, 65, 127, 0 and 200 tokens, nonzero initial states."""
+    inp = make_inputs([1, 63, 64, 65, 127, 0, 200], H=3, dk=d, dv=d, dtype=dtype, seed=77,
+                      h0_scale=0.5)
+    _check_fwd(gdn, oracle_mod, inp, f"ragged {dtype} d={d}")
+
+
+def test_scale(gdn, oracle_mod):
+    inp = make_inputs([300], H=2, dk=128, dv=128, dtype="bf16", seed=78)
+    _check_fwd(gdn, oracle_mod, inp, "scale", scale=0.0883883)
+
+
+def test_packed_8k(gdn, oracle_mod):
+    """8192 tokens packed from documents of U{256..2048} tokens, H=8, d=128, bf16."""
+    _check_fwd(gdn, oracle_mod, workload("packed"), "packed 8K bf16")
+
+
+def test_long_32k_exact(gdn, oracle_mod):
+    """One 32768-token sequence, H=8, d=128, bf16, exact mode."""
+    _check_fwd(gdn, oracle_mod, workload("long"), "long 32K exact")
+
+
+def test_long_32k_truncate(gdn, oracle_mod):
+    """The same sequence in truncate mode: the plan equals the oracle's, and the result is within
+    tolerance of both the oracle's truncated and exact results."""
+    inp = workload("long")
+    d = to_dev(inp)
+    H = 8
+    plan = gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], H, 128, torch.bfloat16, mode="truncate",
+                              num_cus=256, cu_seqlens_host=inp["cu_seqlens"])
+    ref_plan = oracle_mod.plan(inp["g"], inp["cu_seqlens"], H, P=256)
+    assert plan["L"] == 16
+    for key in ("seq", "c0", "c1", "warm"):
+        assert np.array_equal(plan[key], ref_plan[key]), key
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None, mode="truncate", num_cus=256,
+                          cu_seqlens_host=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    o_t, ht_t = oracle_mod.fwd_truncated(*_oracle_args(inp), inp["cu_seqlens"], ref_plan)
+    o_e, ht_e = oracle_mod.fwd_recurrent(*_oracle_args(inp), inp["cu_seqlens"])
+    print("[long 32K truncate]", flush=True)
+    print(f"  oracle truncated vs exact: o {rel_l2(o_t, o_e):.2e}  ht {rel_l2(ht_t, ht_e):.2e}")
+    report("o vs oracle-trunc", np64(o), o_t, 5e-3)
+    report("ht vs oracle-trunc", np64(ht), ht_t, 5e-3)
+    report("o vs oracle-exact", np64(o), o_e, 5e-3)
+    report("ht vs oracle-exact", np64(ht), ht_e, 5e-3)
+
+
+def test_truncate_forced_segments_fp32(gdn, oracle_mod):
+    """fp32, forced 4-chunk segments over several documents: GPU follows the oracle's plan."""
+    inp = make_inputs([64 * 30 + 7, 64 * 9, 100], H=2, dk=64, dv=64, dtype="f32", seed=79,
+                      h0_scale=0.3)
+    d = to_dev(inp)
+    plan = gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], 2, 64, torch.float32, mode="truncate",
+                              seg_chunks=4, cu_seqlens_host=inp["cu_seqlens"])
+    ref_plan = oracle_mod.plan(inp["g"], inp["cu_seqlens"], 2, P=256, seg_chunks=4)
+    for key in ("seq", "c0", "c1", "warm"):
+        assert np.array_equal(plan[key], ref_plan[key]), key
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], d["h0"], mode="truncate",
+                          seg_chunks=4, cu_seqlens_host=inp["cu_seqlens"])
+    o_t, ht_t = oracle_mod.fwd_truncated(*_oracle_args(inp), inp["cu_seqlens"], ref_plan,
+                                         h0=inp["h0"])
+    report("o vs oracle-trunc", np64(o), o_t, 1e-4)
+    report("ht vs oracle-trunc", np64(ht), ht_t, 1e-4)
+
+
+def test_fork_shared_prefix(gdn, oracle_mod):
+    """A 65536-token prefix, then 80 branches of U{1024..4096} tokens whose initial state is the
+    prefix's final state broadcast (stride 0); H=16, d=128, bf16.  The oracle checks heads
+    0, 7 and 15 (heads are independent)."""
+    w = workload("fork")
+    pre, br = w["prefix"], w["branches"]
+    dp, db = to_dev(pre), to_dev(br)
+    _, ht_p = gdn.chunk_fwd(*args_of(dp), dp["cu_seqlens"], None)
+    o_b, ht_b = gdn.chunk_fwd(*args_of(db), db["cu_seqlens"], ht_p[0].contiguous())
+    torch.cuda.synchronize()
+    heads = [0, 7, 15]
+
+    def sub(inp):
+        return [np.ascontiguousarray(inp[x][:, heads]) for x in ("q", "k", "v", "g", "beta")]
+
+    _, ht_pr = oracle_mod.fwd_recurrent(*sub(pre), pre["cu_seqlens"])
+    o_br, ht_br = oracle_mod.fwd_recurrent(*sub(br), br["cu_seqlens"], h0=ht_pr[0])
+    print("[fork]", flush=True)
+    report("prefix ht", np64(ht_p)[:, heads], ht_pr, 5e-3)
+    report("branch o", np64(o_b)[:, heads], o_br, 5e-3)
+    report("branch ht", np64(ht_b)[:, heads], ht_br, 5e-3)
+
+
+def test_broadcast_h0_equals_explicit_copies(gdn):
+    inp = make_inputs([100, 64, 300], H=2, dk=128, dv=128, dtype="bf16", seed=80, h0_scale=1.0,
+                      n_h0=1)
+    d = to_dev(inp)
+    shared = d["h0"][0].contiguous()
+    o1, ht1 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], shared)
+    o2, ht2 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], shared.expand(3, -1, -1, -1).contiguous())
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+
+
+def test_boundary_isolation(gdn):
+    """Perturbing document A leaves document B bitwise unchanged."""
+    inp = make_inputs([200, 150], H=2, dk=128, dv=128, dtype="bf16", seed=81)
+    d = to_dev(inp)
+    o1, ht1 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"])
+    for name in ("q", "k", "v", "beta"):
+        d[name][:200] = d[name][:200].flip(0)
+    d["g"][:200] *= 3.0
+    o2, ht2 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"])
+    assert torch.equal(o1[200:], o2[200:]) and torch.equal(ht1[1], ht2[1])
+    assert not torch.equal(o1[:200], o2[:200])
+
+
+def test_resume_equals_single_call(gdn):
+    inp = make_inputs([640], H=2, dk=128, dv=128, dtype="bf16", seed=82, h0_scale=0.2)
+    d = to_dev(inp)
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], d["h0"])
+    T1 = 384
+    a = [x[:T1].contiguous() for x in args_of(d)]
+    b = [x[T1:].contiguous() for x in args_of(d)]
+    cu1 = torch.tensor([0, T1], dtype=torch.int32, device="cuda")
+    cu2 = torch.tensor([0, 640 - T1], dtype=torch.int32, device="cuda")
+    oa, ha = gdn.chunk_fwd(*a, cu1, d["h0"])
+    ob, hb = gdn.chunk_fwd(*b, cu2, ha)
+    assert torch.equal(torch.cat([oa, ob]), o) and torch.equal(hb, ht)
+
+
+def test_empty_sequences_keep_h0(gdn):
+    inp = make_inputs([0, 70, 0], H=2, dk=64, dv=64, dtype="f32", seed=83, h0_scale=1.0)
+    d = to_dev(inp)
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], d["h0"])
+    assert torch.equal(ht[0], d["h0"][0]) and torch.equal(ht[2], d["h0"][2])
+
+
+def test_deterministic_repeat(gdn):
+    """Repeated launches give bitwise identical results (no races in the LDS pipeline)."""
+    inp = workload("packed")
+    d = to_dev(inp)
+    o1, ht1 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"])
+    for _ in range(20):
+        o2, ht2 = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"])
+        assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("bf16", 128)])
+def test_intermediates_per_step(gdn, oracle_mod, dtype, d):
+    """Each step of the chunked form against the oracle's intermediates: gate cumsum (a1),
+    the triangular inverse (a2, a3), W and U (a4), chunk-start states and Delta (a5)."""
+    inp = make_inputs([130, 64, 1], H=2, dk=d, dv=d, dtype=dtype, seed=84, h0_scale=0.5)
+    dd = to_dev(inp)
+    o, ht, it = gdn.chunk_fwd_intermediates(*args_of(dd), dd["cu_seqlens"], dd["h0"])
+    torch.cuda.synchronize()
+    _, _, ref = oracle_mod.fwd_chunked(*_oracle_args(inp), inp["cu_seqlens"], h0=inp["h0"],
+                                       intermediates=True)
+    tol = tol_for(dtype)
+    print(f"[intermediates {dtype} d={d}]", flush=True)
+    report("gamma", np64(it["gamma"]), ref["gamma"], 1e-5)
+    report("tmat", np64(it["tmat"]), ref["tm"], 1e-5)
+    for name, key in (("w", "w"), ("u", "u"), ("hc", "hc"), ("delta", "delta")):
+        report(name, np64(it[name]), ref[key], tol)
