@@ -112,12 +112,14 @@ gdn_status gdn_chunk_fwd(const gdn_problem *p, const void *q, const void *k, con
                          const int32_t *cu_seqlens_host, const float *h0, void *o, float *ht,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* The forward's segment plan, for inspection.  Runs the planning step of gdn_chunk_fwd on the
- * device and writes to plan_out (device int32, capacity plan_capacity entries):
+/* The forward's segment plan, for inspection.  Runs the forward's own unit lookup and warmup
+ * scan on the device and writes to plan_out (device int32, capacity plan_capacity entries):
  *   plan_out[0] = number of units U, plan_out[1] = segment length L (0 = unsplit),
  *   then for each unit u: seq, first chunk, end chunk (chunk numbers counted from the sequence's
- *   first chunk), then H warmup-window first chunks (same numbering).
- * Needs plan_capacity >= 2 + U * (3 + H).  Uses the same workspace as gdn_chunk_fwd. */
+ *   first chunk), then H warmup-window first chunks (same numbering).  A sequence with no
+ *   tokens has one unit with an empty chunk range (it only writes the final state).
+ * Needs plan_capacity >= 2 + U * (3 + H); entries past the capacity are not written.  The
+ * workspace arguments are those of gdn_chunk_fwd. */
 gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_t *cu_seqlens,
                               const int32_t *cu_seqlens_host, int32_t *plan_out,
                               int64_t plan_capacity, void *workspace, size_t workspace_bytes,

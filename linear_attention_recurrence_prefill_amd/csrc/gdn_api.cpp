@@ -106,14 +106,17 @@ int32_t segment_chunks(const gdn_problem *p, int64_t nchunks, int32_t P) {
   return L < 4 ? 4 : L;
 }
 
-// Units (workgroups per head) the plan can produce: exact when the host copy is given.
+// Units (workgroups per head) of the plan: a sequence of c chunks gives max(1, ceil(c / L))
+// units (one when L == 0).  Exact with the host copy of cu_seqlens, else an upper bound.
 int64_t max_units(const gdn_problem *p, const int32_t *cu_host, int32_t L) {
   if (L <= 0) return p->num_seqs;
   if (cu_host) {
     int64_t u = 0;
-    for (int32_t n = 0; n < p->num_seqs; ++n)
-      u += ceil_div(ceil_div(cu_host[n + 1] - cu_host[n], gdn::kChunk), L);
-    return u > 0 ? u : 1;
+    for (int32_t n = 0; n < p->num_seqs; ++n) {
+      const int64_t c = ceil_div(cu_host[n + 1] - cu_host[n], gdn::kChunk);
+      u += c > 0 ? ceil_div(c, L) : 1;
+    }
+    return u;
   }
   return ceil_div(ceil_div(p->total_tokens, gdn::kChunk) + p->num_seqs, L) + p->num_seqs;
 }
@@ -133,7 +136,7 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct FwdLayout {
   int32_t L = 0;
   int64_t units = 0;
-  size_t plan_off = 0, chunk0_off = 0, total = 0;
+  size_t total = 0;  // workspace bytes (the forward needs none)
 };
 
 gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, FwdLayout *lay) {
@@ -145,12 +148,8 @@ gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, FwdLayout *l
   const int64_t nc = count_chunks(p, cu_host);
   lay->L = segment_chunks(p, nc, cus > 0 ? cus : 1);
   lay->units = max_units(p, cu_host, lay->L);
-  size_t off = 0;
-  lay->plan_off = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)(gdn::kPlanHeader + 3 * lay->units));
-  lay->chunk0_off = off;
-  off = align_up(off + sizeof(int32_t) * (size_t)(p->num_seqs + 1));
-  lay->total = off;
+  if (lay->units > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "too many work units");
+  lay->total = 0;
   return GDN_OK;
 }
 
@@ -188,21 +187,9 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   FwdLayout lay;
   s = fwd_layout(p, cu_host, &lay);
   if (s != GDN_OK) return s;
-  if (!ws && lay.total > 0) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
   if (ws_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
-  char *base = static_cast<char *>(ws);
-  int32_t *plan = reinterpret_cast<int32_t *>(base + lay.plan_off);
-  int32_t *chunk0 = reinterpret_cast<int32_t *>(base + lay.chunk0_off);
-
-  hipError_t e = gdn::launch_plan(t.cu, p->num_seqs, p->total_tokens, lay.L, plan, chunk0,
-                                  lay.units, stream);
-  if (e != hipSuccess) return hip_fail(e, "plan launch");
-  if (t.ht) {
-    e = gdn::launch_empty_states(t.cu, p->num_seqs, p->num_heads, p->d_k, t.h0,
-                                 p->h0_seq_stride, t.ht, stream);
-    if (e != hipSuccess) return hip_fail(e, "empty-state launch");
-  }
+  (void)ws;
   gdn::FwdArgs a{};
   a.q = t.q;
   a.k = t.k;
@@ -214,8 +201,6 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.h0_stride = p->h0_seq_stride;
   a.o = t.o;
   a.ht = t.ht;
-  a.plan = plan;
-  a.chunk0 = chunk0;
   if (dump) {
     a.dbg_gamma = dbg[0];
     a.dbg_tmat = dbg[1];
@@ -227,13 +212,12 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.T = p->total_tokens;
   a.N = p->num_seqs;
   a.H = p->num_heads;
+  a.L = lay.L;
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
-  if (p->total_tokens > 0) {
-    e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
-    if (e != hipSuccess) return hip_fail(e, "forward launch");
-  }
+  hipError_t e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
+  if (e != hipSuccess) return hip_fail(e, "forward launch");
   return GDN_OK;
 }
 
@@ -308,21 +292,139 @@ gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_
   FwdLayout lay;
   s = fwd_layout(p, cu_seqlens_host, &lay);
   if (s != GDN_OK) return s;
-  if (!workspace || workspace_bytes < lay.total)
+  if (workspace_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
+  (void)workspace;
   if (plan_capacity < 2) return fail(GDN_ERR_BAD_SHAPE, "plan_capacity must be >= 2");
-  char *base = static_cast<char *>(workspace);
-  int32_t *plan = reinterpret_cast<int32_t *>(base + lay.plan_off);
-  int32_t *chunk0 = reinterpret_cast<int32_t *>(base + lay.chunk0_off);
-  hipError_t e = gdn::launch_plan(cu_seqlens, p->num_seqs, p->total_tokens, lay.L, plan, chunk0,
-                                  lay.units, stream);
-  if (e != hipSuccess) return hip_fail(e, "plan launch");
   const int truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
-  e = gdn::launch_plan_export(plan, cu_seqlens, g, p->num_heads, p->trunc_log_threshold,
-                              truncate, lay.units, plan_out, plan_capacity, stream);
+  hipError_t e = gdn::launch_plan_export(cu_seqlens, p->num_seqs, g, p->num_heads, lay.L,
+                                         p->trunc_log_threshold, truncate, lay.units, plan_out,
+                                         plan_capacity, stream);
   if (e != hipSuccess) return hip_fail(e, "plan export launch");
   return GDN_OK;
 }
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------- backward
+namespace {
+
+struct BwdLayout {
+  int64_t nc = 0;  // chunk-count bound: ceil(T / 64) + N
+  size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
+  size_t total = 0;
+};
+
+BwdLayout bwd_layout(const gdn_problem *p) {
+  BwdLayout L;
+  const int64_t T = p->total_tokens, H = p->num_heads, D = p->d_k;
+  L.nc = ceil_div(T, gdn::kChunk) + p->num_seqs;
+  const size_t esz = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.gamma = take(sizeof(float) * T * H);
+  L.tmat = take(sizeof(float) * L.nc * H * 64 * 64);
+  L.w = take(sizeof(float) * L.nc * H * 64 * D);
+  L.hc = take(sizeof(float) * L.nc * H * D * D);
+  L.delta = take(sizeof(float) * T * H * D);
+  L.o = take(esz * T * H * D);
+  L.dhn = take(sizeof(float) * L.nc * H * D * D);
+  L.ddelta = take(sizeof(float) * T * H * D);
+  L.dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes) {
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+  *bytes = bwd_layout(p).total;
+  return GDN_OK;
+}
+
+gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
+                         const float *g, const void *beta, const int32_t *cu_seqlens,
+                         const float *h0, const void *dout, const float *dht, void *dq, void *dk,
+                         void *dv, float *dg, void *dbeta, float *dh0, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
+  if (!dout || !dq || !dk || !dv || !dg || !dbeta)
+    return fail(GDN_ERR_NULL_ARG, "dout, dq, dk, dv, dg and dbeta are required");
+  const void *ptrs[] = {dout, dq, dk, dv, dg, dbeta};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return fail(GDN_ERR_BAD_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  if ((dht && !aligned16(dht)) || (dh0 && !aligned16(dh0)))
+    return fail(GDN_ERR_BAD_ALIGNMENT, "dht / dh0 must be 16-byte aligned");
+  const BwdLayout L = bwd_layout(p);
+  if (!workspace) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", L.total);
+  char *base = static_cast<char *>(workspace);
+  float *gamma = reinterpret_cast<float *>(base + L.gamma);
+  float *tmat = reinterpret_cast<float *>(base + L.tmat);
+  float *w = reinterpret_cast<float *>(base + L.w);
+  float *hc = reinterpret_cast<float *>(base + L.hc);
+  float *delta = reinterpret_cast<float *>(base + L.delta);
+  // forward recompute with the per-chunk intermediates (o goes to scratch)
+  Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
+  float *dbg[6] = {gamma, tmat, w, nullptr, hc, delta};
+  gdn_problem pe = *p;
+  s = run_fwd(&pe, t, nullptr, true, dbg, nullptr, 0, stream);
+  if (s != GDN_OK) return s;
+  gdn::BwdArgs b{};
+  b.q = q;
+  b.k = k;
+  b.v = v;
+  b.beta = beta;
+  b.dout = dout;
+  b.g = g;
+  b.dht = dht;
+  b.cu = cu_seqlens;
+  b.dq = dq;
+  b.dk = dk;
+  b.dv = dv;
+  b.dbeta = dbeta;
+  b.dg = dg;
+  const bool shared_h0 = (h0 != nullptr && p->h0_seq_stride == 0);
+  // dh0 per sequence goes straight to the output, or to scratch when one state is shared
+  b.dh0_seq = !dh0 ? nullptr : (shared_h0 ? reinterpret_cast<float *>(base + L.dh0) : dh0);
+  b.gamma = gamma;
+  b.tmat = tmat;
+  b.w = w;
+  b.hc = hc;
+  b.delta = delta;
+  b.dhn = reinterpret_cast<float *>(base + L.dhn);
+  b.ddelta = reinterpret_cast<float *>(base + L.ddelta);
+  b.T = p->total_tokens;
+  b.N = p->num_seqs;
+  b.H = p->num_heads;
+  b.scale = p->scale;
+  const bool bf16 = p->dtype == GDN_DTYPE_BF16;
+  hipError_t e = gdn::launch_bwd_chain(b, p->d_k, bf16, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward chain launch");
+  e = gdn::launch_bwd_grad(b, p->d_k, bf16, L.nc, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
+  if (dh0 && shared_h0) {
+    e = gdn::launch_sum_dh0(b.dh0_seq, p->num_seqs, p->num_heads, p->d_k, dh0, stream);
+    if (e != hipSuccess) return hip_fail(e, "dh0 reduction launch");
+  }
+  return GDN_OK;
+}
+
+}  // extern "C"
+
+extern "C" {
 
 const char *gdn_status_string(gdn_status s) {
   switch (s) {

@@ -28,113 +28,15 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_unit.h"
 
 namespace gdn {
 
 // ------------------------------------------------------------------------------ planning
-__global__ __launch_bounds__(1024) void plan_kernel(const int32_t *__restrict__ cu, int32_t N,
-                                                    int64_t T, int32_t L,
-                                                    int32_t *__restrict__ plan,
-                                                    int32_t *__restrict__ chunk0,
-                                                    int64_t max_units) {
-  __shared__ int32_t s_units[1024];
-  __shared__ int32_t s_chunks[1024];
-  __shared__ int s_bad;
-  __shared__ int64_t s_run_units, s_run_chunks;
-  const int tid = threadIdx.x;
-  if (tid == 0) {
-    s_bad = (cu[0] != 0 || (int64_t)cu[N] != T) ? 1 : 0;
-    s_run_units = 0;
-    s_run_chunks = 0;
-  }
-  __syncthreads();
-  for (int n = tid; n < N; n += 1024)
-    if (cu[n + 1] < cu[n]) s_bad = 1;
-  __syncthreads();
-  if (s_bad) {
-    if (tid == 0) {
-      plan[0] = 0;
-      plan[1] = L;
-    }
-    return;
-  }
-  for (int base = 0; base < N; base += 1024) {
-    const int n = base + tid;
-    int32_t chunks = 0, units = 0;
-    if (n < N) {
-      const int32_t len = cu[n + 1] - cu[n];
-      chunks = (len + kChunk - 1) / kChunk;
-      units = chunks == 0 ? 0 : (L > 0 ? (chunks + L - 1) / L : 1);
-    }
-    s_units[tid] = units;
-    s_chunks[tid] = chunks;
-    __syncthreads();
-    // inclusive Hillis-Steele scan of both counts
-    for (int off = 1; off < 1024; off <<= 1) {
-      int32_t a = tid >= off ? s_units[tid - off] : 0;
-      int32_t b = tid >= off ? s_chunks[tid - off] : 0;
-      __syncthreads();
-      s_units[tid] += a;
-      s_chunks[tid] += b;
-      __syncthreads();
-    }
-    const int64_t u0 = s_run_units + s_units[tid] - units;
-    const int64_t c0 = s_run_chunks + s_chunks[tid] - chunks;
-    if (n < N) {
-      if (chunk0) chunk0[n] = (int32_t)c0;
-      for (int32_t s = 0; s < units; ++s) {
-        const int64_t u = u0 + s;
-        if (u < max_units) {
-          const int32_t a = L > 0 ? s * L : 0;
-          const int32_t b = L > 0 ? min(chunks, (s + 1) * L) : chunks;
-          plan[kPlanHeader + 3 * u + 0] = n;
-          plan[kPlanHeader + 3 * u + 1] = a;
-          plan[kPlanHeader + 3 * u + 2] = b;
-        }
-      }
-    }
-    __syncthreads();
-    if (tid == 1023) {
-      s_run_units += s_units[1023];
-      s_run_chunks += s_chunks[1023];
-    }
-    __syncthreads();
-  }
-  if (tid == 0) {
-    plan[0] = (int32_t)min<int64_t>(s_run_units, max_units);
-    plan[1] = L;
-    if (chunk0) chunk0[N] = (int32_t)s_run_chunks;
-  }
-}
-
-hipError_t launch_plan(const int32_t *cu, int32_t N, int64_t T, int32_t L, int32_t *plan,
-                       int32_t *chunk0, int64_t max_units, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, cu, N, T, L, plan, chunk0,
-                     max_units);
-  return hipGetLastError();
-}
-
-__global__ __launch_bounds__(256) void empty_states_kernel(const int32_t *__restrict__ cu,
-                                                           int32_t H, int32_t D,
-                                                           const float *__restrict__ h0,
-                                                           int64_t h0_stride,
-                                                           float *__restrict__ ht) {
-  const int n = blockIdx.x, h = blockIdx.y;
-  if (cu[n + 1] != cu[n]) return;
-  const int64_t dd = (int64_t)D * D;
-  float *dst = ht + ((int64_t)n * H + h) * dd;
-  const float *src = h0 ? h0 + (int64_t)n * h0_stride + (int64_t)h * dd : nullptr;
-  for (int64_t i = threadIdx.x; i < dd; i += 256) dst[i] = src ? src[i] : 0.f;
-}
-
-hipError_t launch_empty_states(const int32_t *cu, int32_t N, int32_t H, int32_t D,
-                               const float *h0, int64_t h0_stride, float *ht,
-                               hipStream_t stream) {
-  if (N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(empty_states_kernel, dim3(N, H), dim3(256), 0, stream, cu, H, D, h0,
-                     h0_stride, ht);
-  return hipGetLastError();
-}
+// A unit is one (sequence, chunk range) pair; the forward runs one workgroup per (unit, head).
+// With L == 0 every sequence is one unit; with L > 0 a sequence of c chunks is split into
+// max(1, ceil(c / L)) units of L chunks (the last one shorter).  A sequence with no tokens
+// still gets one (empty) unit so that its final state is written.
 
 // Warmup window of a segment starting at chunk c0 > 0 of its sequence ("Lever 1"): whole
 // preceding chunks are added one at a time (c0-1, c0-2, ...) until their summed g is below
@@ -152,39 +54,41 @@ __device__ int warm_window(const float *__restrict__ g, int64_t ts0, int c0, int
   return w;
 }
 
-__global__ __launch_bounds__(64) void plan_export_kernel(const int32_t *__restrict__ plan,
-                                                         const int32_t *__restrict__ cu,
+__global__ __launch_bounds__(64) void plan_export_kernel(const int32_t *__restrict__ cu, int N,
                                                          const float *__restrict__ g, int H,
-                                                         float thr, int truncate,
+                                                         int L, float thr, int truncate,
                                                          int32_t *__restrict__ out,
                                                          int64_t capacity) {
   const int u = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
-  const int U = plan[0];
-  if (u == 0 && h == 0 && lane == 0 && capacity >= 2) {
-    out[0] = U;
-    out[1] = plan[1];
+  Unit un;
+  const bool ok = find_unit(cu, N, L, u, false, lane, un);
+  // the last workgroup that finds a unit also writes the header
+  Unit nx;
+  const bool next = find_unit(cu, N, L, u + 1, false, lane, nx);
+  if (ok && !next && h == 0 && lane == 0 && capacity >= 2) {
+    out[0] = u + 1;
+    out[1] = L;
   }
-  if (u >= U) return;
-  const int seq = plan[kPlanHeader + 3 * u], c0 = plan[kPlanHeader + 3 * u + 1];
+  if (!ok) return;
   const int64_t base = 2 + (int64_t)u * (3 + H);
   if (base + 3 + H > capacity) return;
-  int w = c0;
-  if (truncate && c0 > 0) w = warm_window(g, cu[seq], c0, h, H, thr, lane);
+  int w = un.c0;
+  if (truncate && un.c0 > 0) w = warm_window(g, cu[un.seq], un.c0, h, H, thr, lane);
   if (lane == 0) {
     if (h == 0) {
-      out[base + 0] = seq;
-      out[base + 1] = c0;
-      out[base + 2] = plan[kPlanHeader + 3 * u + 2];
+      out[base + 0] = un.seq;
+      out[base + 1] = un.c0;
+      out[base + 2] = un.c1;
     }
     out[base + 3 + h] = w;
   }
 }
 
-hipError_t launch_plan_export(const int32_t *plan, const int32_t *cu, const float *g, int32_t H,
-                              float log_thr, int32_t truncate, int64_t max_units, int32_t *out,
-                              int64_t capacity, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_export_kernel, dim3((unsigned)max_units, H), dim3(64), 0, stream,
-                     plan, cu, g, H, log_thr, truncate, out, capacity);
+hipError_t launch_plan_export(const int32_t *cu, int32_t N, const float *g, int32_t H,
+                              int32_t L, float log_thr, int32_t truncate, int64_t max_units,
+                              int32_t *out, int64_t capacity, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_export_kernel, dim3((unsigned)max_units, H), dim3(64), 0, stream, cu,
+                     N, g, H, L, log_thr, truncate, out, capacity);
   return hipGetLastError();
 }
 
@@ -277,11 +181,23 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   const int unit = blockIdx.x, h = blockIdx.y, H = a.H;
-  if (unit >= a.plan[0]) return;
-  const int seq = a.plan[kPlanHeader + 3 * unit];
-  const int c0 = a.plan[kPlanHeader + 3 * unit + 1];
-  const int c1 = a.plan[kPlanHeader + 3 * unit + 2];
+  if (wave == 0) {
+    Unit un;
+    const bool ok = find_unit(a.cu, a.N, a.L, unit, DUMP, lane, un);
+    if (lane == 0) {
+      sm.imisc[0] = ok ? un.seq : -1;
+      sm.imisc[1] = un.c0;
+      sm.imisc[2] = un.c1;
+      sm.imisc[3] = (int)un.chunk_base;
+    }
+  }
+  __syncthreads();
+  const int seq = sm.imisc[0];
+  if (seq < 0) return;
+  const int c0 = sm.imisc[1], c1 = sm.imisc[2];
+  const int64_t chunk_base = sm.imisc[3];
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
+  if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
   const E *__restrict__ gq_ = static_cast<const E *>(a.q);
   const E *__restrict__ gk_ = static_cast<const E *>(a.k);
@@ -300,6 +216,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
   int cw = c0;
   if (a.truncate && c0 > 0) {
+    __syncthreads();  // every wave has read the unit from imisc
     if (wave == 0) {
       const int w = warm_window(a.g, ts0, c0, h, H, a.log_thr, lane);
       if (lane == 0) sm.imisc[0] = w;
@@ -330,7 +247,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     const bool emit = (c >= c0);
     const int64_t t0 = ts0 + (int64_t)c * kChunk;
     const int n = (int)min<int64_t>(kChunk, ts1 - t0);
-    const int64_t cglob = DUMP ? (int64_t)a.chunk0[seq] + c : 0;
+    const int64_t cglob = chunk_base + c;
     __syncthreads();  // the previous chunk is done with LDS
 
     // ---- stage K, V (and Q) token-major in LDS

@@ -7,10 +7,10 @@
 namespace gdn {
 
 constexpr int kChunk = 64;
-constexpr int kPlanHeader = 2;  // plan[0] = number of units, plan[1] = segment length (chunks)
 
-// Arguments of the fused forward kernel.  A "unit" is one (sequence, chunk range) pair from the
-// plan; the kernel runs one workgroup per (unit, head).
+// Arguments of the fused forward kernel.  A "unit" is one (sequence, chunk range) pair: each
+// sequence is one unit (L == 0) or is split into units of L chunks; the kernel runs one
+// workgroup per (unit, head) and finds its unit from cu_seqlens itself.
 struct FwdArgs {
   const void *q, *k, *v;
   const float *g;
@@ -20,34 +20,53 @@ struct FwdArgs {
   int64_t h0_stride;
   void *o;
   float *ht;
-  const int32_t *plan;    // [kPlanHeader + 3 * max_units]: seq, first chunk, end chunk
-  const int32_t *chunk0;  // [N + 1]: index of each sequence's first chunk among all chunks
   float *dbg_gamma, *dbg_tmat, *dbg_w, *dbg_u, *dbg_hc, *dbg_delta;  // intermediates (or null)
   int64_t T;
   int32_t N, H;
+  int32_t L;  // segment length in chunks, 0 = whole sequences
   float scale;
   float log_thr;
   int32_t truncate;
 };
 
-// One workgroup: validates cu_seqlens on the device and writes the unit list (every sequence
-// split into segments of L chunks, or whole when L == 0) and each sequence's first chunk index.
-// An invalid cu_seqlens yields zero units (nothing is computed).
-hipError_t launch_plan(const int32_t *cu, int32_t N, int64_t T, int32_t L, int32_t *plan,
-                       int32_t *chunk0, int64_t max_units, hipStream_t stream);
+// Arguments of the backward kernels (see gdn_bwd.hip).  Workspace arrays (fp32):
+//   gamma [T, H], tmat [Nc, H, 64, 64], w [Nc, H, 64, D], hc [Nc, H, D, D], delta [T, H, D]
+//   from the forward recompute; dhn [Nc, H, D, D] (state gradient after each chunk) and
+//   ddelta [T, H, D] from the reverse chain.
+struct BwdArgs {
+  const void *q, *k, *v, *beta, *dout;
+  const float *g, *dht;
+  const int32_t *cu;
+  void *dq, *dk, *dv, *dbeta;
+  float *dg, *dh0_seq;
+  const float *gamma, *tmat, *w, *hc, *delta;
+  float *dhn, *ddelta;
+  int64_t T;
+  int32_t N, H;
+  float scale;
+};
 
-// Final states of sequences with no tokens: ht = h0 (or zero).
-hipError_t launch_empty_states(const int32_t *cu, int32_t N, int32_t H, int32_t D,
-                               const float *h0, int64_t h0_stride, float *ht,
-                               hipStream_t stream);
-
+// A work unit: one sequence, or a segment of it (see gdn_unit.h).
+struct Unit {
+  int seq, c0, c1;      // chunk range [c0, c1) counted from the sequence's first chunk
+  int64_t chunk_base;   // index of the sequence's first chunk among all chunks (if asked)
+};
 // The fused chunked forward over all (unit, head) pairs.
 hipError_t launch_fwd(const FwdArgs &a, int D, bool bf16, bool dump, int64_t max_units,
                       hipStream_t stream);
 
 // Writes the plan with warmup windows to out (see gdn_chunk_fwd_plan).
-hipError_t launch_plan_export(const int32_t *plan, const int32_t *cu, const float *g, int32_t H,
-                              float log_thr, int32_t truncate, int64_t max_units, int32_t *out,
-                              int64_t capacity, hipStream_t stream);
+hipError_t launch_plan_export(const int32_t *cu, int32_t N, const float *g, int32_t H,
+                              int32_t L, float log_thr, int32_t truncate, int64_t max_units,
+                              int32_t *out, int64_t capacity, hipStream_t stream);
+
+// Backward: reverse state-gradient chain (one workgroup per (sequence, head)), per-chunk
+// gradients (one workgroup per (chunk, head)) and the sum of dh0 over sequences that share one
+// initial state.
+hipError_t launch_bwd_chain(const BwdArgs &b, int D, bool bf16, hipStream_t stream);
+hipError_t launch_bwd_grad(const BwdArgs &b, int D, bool bf16, int64_t max_chunks,
+                           hipStream_t stream);
+hipError_t launch_sum_dh0(const float *dh0_seq, int32_t N, int32_t H, int32_t D, float *dh0,
+                          hipStream_t stream);
 
 }  // namespace gdn

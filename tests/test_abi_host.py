@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/gdn.h declares, and rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from linear_attention_recurrence_prefill_amd import gdn
+
+    if not os.path.exists(gdn.LIB_PATH):
+        pytest.fail("libgdn_mi355x.so is not built (run __graft_entry__.build())")
+    return gdn.load_library()
+
+
+def test_header_declares_the_boundary():
+    names = _declared_functions()
+    for required in ("gdn_chunk_fwd", "gdn_chunk_bwd", "gdn_chunk_fwd_workspace_size",
+                     "gdn_chunk_bwd_workspace_size", "gdn_status_string", "gdn_last_error"):
+        assert required in names
+
+
+def test_library_exports_every_declared_function(lib):
+    from linear_attention_recurrence_prefill_amd import gdn
+
+    names = _declared_functions()
+    assert set(names) == set(gdn.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def _problem(**kw):
+    from linear_attention_recurrence_prefill_amd.gdn import GdnProblem
+
+    lib = _lib()
+    p = GdnProblem()
+    assert lib.gdn_problem_init(ctypes.byref(p), 1024, 2, 8, 128) == 0
+    for k, v in kw.items():
+        setattr(p, k, v)
+    return p
+
+
+def _lib():
+    from linear_attention_recurrence_prefill_amd import gdn
+
+    return gdn.load_library()
+
+
+def test_problem_defaults(lib):
+    p = _problem()
+    assert (p.chunk, p.dtype, p.mode, p.scale, p.trunc_log_threshold) == (64, 1, 0, 1.0, -10.0)
+    assert p.h0_seq_stride == 8 * 128 * 128
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("chunk", 32, 2), ("d_k", 96, 2), ("d_v", 64, 2), ("num_heads", 0, 2), ("num_seqs", 0, 2),
+    ("total_tokens", -1, 2), ("dtype", 7, 3), ("mode", 5, 4), ("reserved", 1, 2),
+    ("h0_seq_stride", -1, 2)])
+def test_bad_problem_rejected_on_host(lib, field, value, status):
+    p = _problem(**{field: value})
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == status
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.gdn_last_error()
+
+
+def test_truncate_threshold_must_be_negative(lib):
+    p = _problem(mode=1, trunc_log_threshold=0.5, seg_chunks=4)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 4
+
+
+def test_null_pointers_rejected_before_launch(lib):
+    p = _problem()
+    buf = (ctypes.c_char * 64)()
+    ptr = ctypes.cast(buf, ctypes.c_void_p)
+    # q missing
+    st = lib.gdn_chunk_fwd(ctypes.byref(p), None, ptr, ptr, ptr, ptr, ptr, None, None, ptr, None,
+                           None, 0, None)
+    assert st == 1
+    st = lib.gdn_chunk_bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, ptr,
+                           ptr, ptr, ptr, ptr, None, None, 0, None)
+    assert st == 1
+
+
+def test_misaligned_pointer_rejected(lib):
+    p = _problem()
+    buf = (ctypes.c_char * 256)()
+    base = ctypes.addressof(buf)
+    al = ctypes.c_void_p((base + 15) & ~15)
+    mis = ctypes.c_void_p(((base + 15) & ~15) + 4)
+    st = lib.gdn_chunk_fwd(ctypes.byref(p), mis, al, al, al, al, al, None, None, al, None, None,
+                           0, None)
+    assert st == 7
+
+
+def test_host_cu_seqlens_checked(lib):
+    p = _problem(mode=1, seg_chunks=4)
+    cu = (ctypes.c_int32 * 3)(0, 700, 900)  # does not end at total_tokens = 1024
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu, ctypes.byref(n)) == 2
+
+
+def test_workspace_sizes(lib):
+    p = _problem()
+    n = ctypes.c_size_t(123)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert n.value == 0  # the forward needs no scratch
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert n.value > 1024 * 8 * 128 * 4
+
+
+def test_status_strings(lib):
+    for s in range(9):
+        assert lib.gdn_status_string(s)

@@ -1,0 +1,123 @@
+"""GPU parity of the backward against the fp64 oracle's hand-derived token backward
+(gfx950 only; marked ``gpu``).  Tolerances as for the forward: relative L2 <= 1e-4 for fp32
+inputs and <= 5e-3 for bf16 inputs, per gradient."""
+import numpy as np
+import pytest
+
+from gdn_inputs import make_inputs, workload
+from gpu_util import args_of, np64, report, to_dev, tol_for
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+NAMES = ("dq", "dk", "dv", "dg", "dbeta")
+
+
+@pytest.fixture(scope="module")
+def gdn():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import linear_attention_recurrence_prefill_amd as m
+
+    m.load_library()
+    return m
+
+
+def _oargs(inp, heads=None):
+    out = []
+    for x in ("q", "k", "v", "g", "beta"):
+        a = inp[x]
+        out.append(np.ascontiguousarray(a[:, heads]) if heads is not None else a)
+    return out
+
+
+def _check_bwd(gdn, oracle_mod, inp, label, dht_scale=0.0, scale=1.0, heads=None):
+    d = to_dev(inp)
+    rng = np.random.default_rng(123)
+    dout = inp.get("dout")
+    if dout is None:
+        dout = rng.standard_normal(inp["v"].shape).astype(np.float32)
+        if inp["dtype"] == "bf16":
+            from gdn_inputs import bf16_round
+            dout = bf16_round(dout)
+    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    dout_d = torch.from_numpy(np.ascontiguousarray(dout)).cuda().to(tdt)
+    N = len(inp["cu_seqlens"]) - 1
+    T, H, D = inp["q"].shape
+    dht = None
+    dht_d = None
+    if dht_scale:
+        dht = (dht_scale * rng.standard_normal((N, H, D, D))).astype(np.float32)
+        dht_d = torch.from_numpy(dht).cuda()
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], dout_d, d["h0"], dht_d, scale=scale)
+    torch.cuda.synchronize()
+    sel = heads if heads is not None else slice(None)
+    h0 = inp["h0"]
+    ref = oracle_mod.bwd(*_oargs(inp, heads), inp["cu_seqlens"],
+                         np.ascontiguousarray(dout[:, sel]),
+                         h0=None if h0 is None else np.ascontiguousarray(h0[:, sel]),
+                         dht=None if dht is None else np.ascontiguousarray(dht[:, sel]),
+                         scale=scale)
+    tol = tol_for(inp["dtype"])
+    print(f"[{label}]", flush=True)
+    for name in NAMES:
+        report(name, np64(gr[name])[:, sel], ref[name], tol)
+    if gr["dh0"] is not None:
+        report("dh0", np64(gr["dh0"])[:, sel], ref["dh0"], tol)
+    return gr, ref
+
+
+@pytest.mark.parametrize("dtype,d", [("f32", 64), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_bwd_ragged_with_h0_and_dht(gdn, oracle_mod, dtype, d):
+    inp = make_inputs([1, 63, 64, 65, 130, 0, 200], H=2, dk=d, dv=d, dtype=dtype, seed=91,
+                      h0_scale=0.5)
+    _check_bwd(gdn, oracle_mod, inp, f"bwd ragged {dtype} d={d}", dht_scale=0.3)
+
+
+def test_bwd_tiny_fp32(gdn, oracle_mod):
+    inp = workload("tiny")
+    _check_bwd(gdn, oracle_mod, inp, "bwd tiny fp32")
+
+
+def test_bwd_scale(gdn, oracle_mod):
+    inp = make_inputs([257], H=2, dk=128, dv=128, dtype="bf16", seed=92)
+    _check_bwd(gdn, oracle_mod, inp, "bwd scale", scale=0.0883883)
+
+
+def test_bwd_train_65k(gdn, oracle_mod):
+    """65536 tokens packed from documents of U{4096..16384} tokens, H=8, d=128, bf16,
+    dO ~ N(0, 1).  The oracle checks heads 0 and 5 (heads are independent)."""
+    inp = workload("train")
+    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K", heads=[0, 5])
+
+
+def test_bwd_shared_initial_state_sums_branches(gdn, oracle_mod):
+    """One initial state shared by every sequence (stride 0): dh0 is the sum over sequences of
+    their per-sequence gradients ("Backward through P")."""
+    inp = make_inputs([300, 77, 129], H=2, dk=128, dv=128, dtype="bf16", seed=93, h0_scale=0.5,
+                      n_h0=1)
+    d = to_dev(inp)
+    rng = np.random.default_rng(7)
+    from gdn_inputs import bf16_round
+    dout = bf16_round(rng.standard_normal(inp["v"].shape).astype(np.float32))
+    dout_d = torch.from_numpy(dout).cuda().to(torch.bfloat16)
+    shared = d["h0"][0].contiguous()
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], dout_d, shared)
+    torch.cuda.synchronize()
+    assert tuple(gr["dh0"].shape) == (2, 128, 128)
+    ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], dout, h0=inp["h0"][0])
+    report("dh0 (summed)", np64(gr["dh0"]), ref["dh0"].sum(axis=0), 5e-3)
+    for name in NAMES:
+        report(name, np64(gr[name]), ref[name], 5e-3)
+
+
+def test_bwd_deterministic(gdn):
+    inp = make_inputs([500, 200], H=2, dk=128, dv=128, dtype="bf16", seed=94, h0_scale=0.3,
+                      with_dout=True)
+    d = to_dev(inp)
+    g1 = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], d["h0"])
+    for _ in range(5):
+        g2 = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], d["h0"])
+        for name in NAMES + ("dh0",):
+            assert torch.equal(g1[name], g2[name]), name
