@@ -68,9 +68,9 @@ enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
  *   GDN_MODE_EXACT: the recurrence as defined; every sequence is one chain of chunks.
  *   GDN_MODE_TRUNCATE: history truncation of "How to Speed Up GDN Kernels for Qwen Models",
  *     section "Lever 1: the gate is also a license to parallelize".  When num_seqs * num_heads
- *     is below the CU count, each sequence is split into segments of L chunks,
- *     L = max(4, nearest power of two of 3 * sqrt(H * Nc / P)) with Nc the number of chunks and
- *     P the CU count (or L = seg_chunks if positive).  Every (segment, head) starts from zero at
+ *     is below P, the number of workgroups that run at once, each sequence is split into
+ *     segments of L chunks, L = max(4, nearest power of two of 3 * sqrt(H * Nc / P)) with Nc the
+ *     number of chunks (or L = seg_chunks if positive).  Every (segment, head) starts from zero at
  *     a warmup window: the shortest run of whole preceding chunks whose summed g is below
  *     trunc_log_threshold (-10 on the page), or from the true initial state when the window
  *     reaches the sequence start.  The error this introduces is bounded per token by
@@ -87,7 +87,8 @@ typedef struct gdn_problem {
   int32_t dtype;             /* GDN_DTYPE_* */
   int32_t mode;              /* GDN_MODE_* */
   int32_t seg_chunks;        /* truncate mode: 0 = latency model, > 0 = forced segment length */
-  int32_t num_cus;           /* P of the latency model; 0 = the device's CU count */
+  int32_t num_slots;         /* P of the latency model: workgroups that run at once; 0 = the
+                              * device's CUs x resident workgroups per CU of the forward kernel */
   float trunc_log_threshold; /* truncate mode: -10 */
   float scale;               /* o_t = scale * S_t^T q_t (1 in the pages' formulation) */
   int32_t reserved;          /* must be 0 */

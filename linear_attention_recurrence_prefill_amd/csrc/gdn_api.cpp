@@ -37,6 +37,27 @@ constexpr int kMaxDevices = 64;
 DevInfo g_dev[kMaxDevices];
 std::mutex g_dev_mu;
 
+gdn_status device_info(int *cus);
+
+// The forward kernel a problem runs on: the bf16 kernel sized for two workgroups per CU, or the
+// general kernel (fp32 inputs, and the variant that writes intermediates).
+bool use_fast_fwd(const gdn_problem *p, bool dump) { return p->dtype == GDN_DTYPE_BF16 && !dump; }
+
+// P of the latency model: workgroups that run at once = CUs x resident workgroups per CU.
+gdn_status parallel_slots(const gdn_problem *p, bool dump, int *slots) {
+  if (p->num_slots > 0) {
+    *slots = p->num_slots;
+    return GDN_OK;
+  }
+  int cus = 0;
+  gdn_status s = device_info(&cus);
+  if (s != GDN_OK) return s;
+  const int per_cu = use_fast_fwd(p, dump) ? gdn::fwd_fast_blocks_per_cu(p->d_k)
+                                           : gdn::fwd_blocks_per_cu(p->d_k, p->dtype == GDN_DTYPE_BF16);
+  *slots = cus * per_cu;
+  return GDN_OK;
+}
+
 gdn_status device_info(int *cus) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -75,8 +96,8 @@ gdn_status check_problem(const gdn_problem *p) {
     return fail(GDN_ERR_BAD_MODE, "mode %d", p->mode);
   if (p->mode == GDN_MODE_TRUNCATE && !(p->trunc_log_threshold < 0.f))
     return fail(GDN_ERR_BAD_MODE, "trunc_log_threshold must be negative");
-  if (p->seg_chunks < 0 || p->num_cus < 0 || p->reserved != 0)
-    return fail(GDN_ERR_BAD_SHAPE, "seg_chunks / num_cus / reserved out of range");
+  if (p->seg_chunks < 0 || p->num_slots < 0 || p->reserved != 0)
+    return fail(GDN_ERR_BAD_SHAPE, "seg_chunks / num_slots / reserved out of range");
   if (p->h0_seq_stride < 0) return fail(GDN_ERR_BAD_SHAPE, "h0_seq_stride must be >= 0");
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
   return GDN_OK;
@@ -95,7 +116,7 @@ int64_t count_chunks(const gdn_problem *p, const int32_t *cu_host) {
 // Segment length of the truncate mode ("How to Speed Up GDN Kernels for Qwen Models", section
 // "Lever 1"): the latency-optimal length is proportional to sqrt(H * Nc / P); it is scaled by 3,
 // rounded to the nearest power of two in log2 and floored at 4 chunks, and the split is used
-// only when num_seqs * H does not fill the P compute units.  Returns 0 for no split.
+// only when num_seqs * H does not fill the P workgroup slots.  Returns 0 for no split.
 int32_t segment_chunks(const gdn_problem *p, int64_t nchunks, int32_t P) {
   if (p->mode != GDN_MODE_TRUNCATE) return 0;
   if (p->seg_chunks > 0) return p->seg_chunks;
@@ -139,14 +160,14 @@ struct FwdLayout {
   size_t total = 0;  // workspace bytes (the forward needs none)
 };
 
-gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, FwdLayout *lay) {
-  int cus = p->num_cus;
-  if (cus == 0 && p->mode == GDN_MODE_TRUNCATE && p->seg_chunks == 0) {
-    gdn_status s = device_info(&cus);
+gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, bool dump, FwdLayout *lay) {
+  int slots = 1;
+  if (p->mode == GDN_MODE_TRUNCATE && p->seg_chunks == 0) {
+    gdn_status s = parallel_slots(p, dump, &slots);
     if (s != GDN_OK) return s;
   }
   const int64_t nc = count_chunks(p, cu_host);
-  lay->L = segment_chunks(p, nc, cus > 0 ? cus : 1);
+  lay->L = segment_chunks(p, nc, slots);
   lay->units = max_units(p, cu_host, lay->L);
   if (lay->units > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "too many work units");
   lay->total = 0;
@@ -185,7 +206,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   s = device_info(nullptr);
   if (s != GDN_OK) return s;
   FwdLayout lay;
-  s = fwd_layout(p, cu_host, &lay);
+  s = fwd_layout(p, cu_host, dump, &lay);
   if (s != GDN_OK) return s;
   if (ws_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
@@ -216,7 +237,9 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
-  hipError_t e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
+  hipError_t e = use_fast_fwd(p, dump)
+                     ? gdn::launch_fwd_fast(a, p->d_k, lay.units, stream)
+                     : gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return GDN_OK;
 }
@@ -251,7 +274,7 @@ gdn_status gdn_chunk_fwd_workspace_size(const gdn_problem *p, const int32_t *cu_
   s = check_cu_host(p, cu_seqlens_host);
   if (s != GDN_OK) return s;
   FwdLayout lay;
-  s = fwd_layout(p, cu_seqlens_host, &lay);
+  s = fwd_layout(p, cu_seqlens_host, false, &lay);
   if (s != GDN_OK) return s;
   *bytes = lay.total;
   return GDN_OK;
@@ -290,7 +313,7 @@ gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_
   s = device_info(nullptr);
   if (s != GDN_OK) return s;
   FwdLayout lay;
-  s = fwd_layout(p, cu_seqlens_host, &lay);
+  s = fwd_layout(p, cu_seqlens_host, false, &lay);
   if (s != GDN_OK) return s;
   if (workspace_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);

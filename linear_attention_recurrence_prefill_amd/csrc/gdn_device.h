@@ -33,6 +33,10 @@ __device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Keeps the instruction scheduler from moving work across this point (bounds how far ahead
+// loads are issued, and with it register pressure).
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+
 __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {

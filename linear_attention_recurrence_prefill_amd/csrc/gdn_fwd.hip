@@ -28,6 +28,7 @@
 
 #include "gdn_device.h"
 #include "gdn_internal.h"
+#include "gdn_tiles.h"
 #include "gdn_unit.h"
 
 namespace gdn {
@@ -37,22 +38,6 @@ namespace gdn {
 // With L == 0 every sequence is one unit; with L > 0 a sequence of c chunks is split into
 // max(1, ceil(c / L)) units of L chunks (the last one shorter).  A sequence with no tokens
 // still gets one (empty) unit so that its final state is written.
-
-// Warmup window of a segment starting at chunk c0 > 0 of its sequence ("Lever 1"): whole
-// preceding chunks are added one at a time (c0-1, c0-2, ...) until their summed g is below
-// thr; returns the window's first chunk (0 when it reaches the sequence start).  One full
-// wave calls it; sums are formed in fp64 and are identical on every lane.
-__device__ int warm_window(const float *__restrict__ g, int64_t ts0, int c0, int h, int H,
-                           float thr, int lane) {
-  double acc = 0.0;
-  int w = c0;
-  while (w > 0 && !(acc < (double)thr)) {
-    --w;
-    const int64_t t = ts0 + (int64_t)w * kChunk + lane;
-    acc += wave_sum_f64((double)g[t * H + h]);
-  }
-  return w;
-}
 
 __global__ __launch_bounds__(64) void plan_export_kernel(const int32_t *__restrict__ cu, int N,
                                                          const float *__restrict__ g, int H,
@@ -112,38 +97,6 @@ struct FwdSmem {
   alignas(16) float misc[4];
   alignas(16) int imisc[4];
 };
-
-// Lower-triangular 16x16 tiles (bi, bj), bj <= bi, of a 64x64 matrix, in a fixed order.
-__constant__ int8_t c_tile_bi[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t c_tile_bj[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
-
-template <class E, int D, int LDE>
-__device__ __forceinline__ void load_tile(E *__restrict__ dst, const E *__restrict__ src,
-                                          int64_t t0, int n, int h, int H, int tid) {
-  constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
-  constexpr int UPR = D / EPU;              // units per row
-#pragma unroll
-  for (int u = tid; u < 64 * UPR; u += 256) {
-    const int r = u / UPR, cu16 = u % UPR;
-    uint4 val = {0u, 0u, 0u, 0u};
-    if (r < n) val = *reinterpret_cast<const uint4 *>(src + ((t0 + r) * H + h) * D + cu16 * EPU);
-    *reinterpret_cast<uint4 *>(dst + r * LDE + cu16 * EPU) = val;
-  }
-}
-
-template <class E, int D, int LDE>
-__device__ __forceinline__ void store_tile(E *__restrict__ dst, const E *__restrict__ src,
-                                           int64_t t0, int n, int h, int H, int tid) {
-  constexpr int EPU = 16 / (int)sizeof(E);
-  constexpr int UPR = D / EPU;
-#pragma unroll
-  for (int u = tid; u < 64 * UPR; u += 256) {
-    const int r = u / UPR, cu16 = u % UPR;
-    if (r < n)
-      *reinterpret_cast<uint4 *>(dst + ((t0 + r) * H + h) * D + cu16 * EPU) =
-          *reinterpret_cast<const uint4 *>(src + r * LDE + cu16 * EPU);
-  }
-}
 
 // Tm_bc = -Tm_bb * sum_{j=c}^{b-1} A_bj Tm_jc for one 16x16 block below the diagonal (the
 // blocked inverse of a unit lower-triangular matrix), fp32 MFMA.  One wave.
@@ -277,7 +230,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       const int tau = wave + 4 * s;
       qk[s] = zero4();
       if (tau >= 10) continue;
-      const int bi = c_tile_bi[tau], bj = c_tile_bj[tau];
+      const int bi = tile_bi(tau), bj = tile_bj(tau);
       f32x4 acck = zero4(), accq = zero4();
       if constexpr (BF16) {
 #pragma unroll
@@ -346,7 +299,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       for (int s = 0; s < 3; ++s) {
         const int tau = wave + 4 * s;
         if (tau >= 10) continue;
-        const int bi = c_tile_bi[tau], bj = c_tile_bj[tau];
+        const int bi = tile_bi(tau), bj = tile_bj(tau);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * bi + 4 * gq + i, j = 16 * bj + cl;
@@ -600,6 +553,18 @@ static hipError_t launch_fwd_t(const FwdArgs &a, int64_t max_units, hipStream_t 
   hipLaunchKernelGGL((fwd_kernel<D, BF16, DUMP>), dim3((unsigned)max_units, a.H), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+int fwd_blocks_per_cu(int D, bool bf16) {
+  int blocks = 0;
+  hipError_t e;
+  if (D == 128)
+    e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_kernel<128, true, false>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_kernel<128, false, false>, 256, 0);
+  else
+    e = bf16 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_kernel<64, true, false>, 256, 0)
+             : hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_kernel<64, false, false>, 256, 0);
+  return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 hipError_t launch_fwd(const FwdArgs &a, int D, bool bf16, bool dump, int64_t max_units,

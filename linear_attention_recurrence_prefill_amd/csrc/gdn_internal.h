@@ -55,6 +55,13 @@ struct Unit {
 hipError_t launch_fwd(const FwdArgs &a, int D, bool bf16, bool dump, int64_t max_units,
                       hipStream_t stream);
 
+// bf16 forward sized for two workgroups per CU (gdn_fwd_fast.hip); no intermediates.
+hipError_t launch_fwd_fast(const FwdArgs &a, int D, int64_t max_units, hipStream_t stream);
+
+// Workgroups of a forward kernel that fit on one CU at once (from the runtime's occupancy query).
+int fwd_blocks_per_cu(int D, bool bf16);
+int fwd_fast_blocks_per_cu(int D);
+
 // Writes the plan with warmup windows to out (see gdn_chunk_fwd_plan).
 hipError_t launch_plan_export(const int32_t *cu, int32_t N, const float *g, int32_t H,
                               int32_t L, float log_thr, int32_t truncate, int64_t max_units,

@@ -1,0 +1,63 @@
+// Tile movement and scheduling helpers shared by the forward kernels.
+#pragma once
+
+#include "gdn_device.h"
+#include "gdn_internal.h"
+
+namespace gdn {
+
+// Warmup window of a segment starting at chunk c0 > 0 of its sequence ("Lever 1"): whole
+// preceding chunks are added one at a time (c0-1, c0-2, ...) until their summed g is below
+// thr; returns the window's first chunk (0 when it reaches the sequence start).  One full
+// wave calls it; sums are formed in fp64 and are identical on every lane.
+__device__ inline int warm_window(const float *__restrict__ g, int64_t ts0, int c0, int h, int H,
+                           float thr, int lane) {
+  double acc = 0.0;
+  int w = c0;
+  while (w > 0 && !(acc < (double)thr)) {
+    --w;
+    const int64_t t = ts0 + (int64_t)w * kChunk + lane;
+    acc += wave_sum_f64((double)g[t * H + h]);
+  }
+  return w;
+}
+
+// Lower-triangular 16x16 tiles (bi, bj), bj <= bi, of a 64x64 matrix, numbered row by row:
+// tau = bi (bi + 1) / 2 + bj, 0 <= tau < 10.
+__device__ __forceinline__ int tile_bi(int tau) {
+  return tau >= 6 ? 3 : (tau >= 3 ? 2 : (tau >= 1 ? 1 : 0));
+}
+__device__ __forceinline__ int tile_bj(int tau) {
+  const int bi = tile_bi(tau);
+  return tau - bi * (bi + 1) / 2;
+}
+
+template <class E, int D, int LDE>
+__device__ __forceinline__ void load_tile(E *__restrict__ dst, const E *__restrict__ src,
+                                          int64_t t0, int n, int h, int H, int tid) {
+  constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
+  constexpr int UPR = D / EPU;              // units per row
+#pragma unroll
+  for (int u = tid; u < 64 * UPR; u += 256) {
+    const int r = u / UPR, cu16 = u % UPR;
+    uint4 val = {0u, 0u, 0u, 0u};
+    if (r < n) val = *reinterpret_cast<const uint4 *>(src + ((t0 + r) * H + h) * D + cu16 * EPU);
+    *reinterpret_cast<uint4 *>(dst + r * LDE + cu16 * EPU) = val;
+  }
+}
+
+template <class E, int D, int LDE>
+__device__ __forceinline__ void store_tile(E *__restrict__ dst, const E *__restrict__ src,
+                                           int64_t t0, int n, int h, int H, int tid) {
+  constexpr int EPU = 16 / (int)sizeof(E);
+  constexpr int UPR = D / EPU;
+#pragma unroll
+  for (int u = tid; u < 64 * UPR; u += 256) {
+    const int r = u / UPR, cu16 = u % UPR;
+    if (r < n)
+      *reinterpret_cast<uint4 *>(dst + ((t0 + r) * H + h) * D + cu16 * EPU) =
+          *reinterpret_cast<const uint4 *>(src + r * LDE + cu16 * EPU);
+  }
+}
+
+}  // namespace gdn

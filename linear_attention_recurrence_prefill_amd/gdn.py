@@ -37,7 +37,7 @@ class GdnProblem(ctypes.Structure):
                 ("num_heads", ctypes.c_int32), ("d_k", ctypes.c_int32),
                 ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
-                ("num_cus", ctypes.c_int32), ("trunc_log_threshold", ctypes.c_float),
+                ("num_slots", ctypes.c_int32), ("trunc_log_threshold", ctypes.c_float),
                 ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
                 ("h0_seq_stride", ctypes.c_int64)]
 
@@ -98,7 +98,7 @@ def _stream():
 
 
 def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact", scale=1.0,
-                 seg_chunks=0, num_cus=0, trunc_log_threshold=-10.0, h0_seq_stride=None):
+                 seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, h0_seq_stride=None):
     lib = load_library()
     p = GdnProblem()
     _check(lib.gdn_problem_init(ctypes.byref(p), int(total_tokens), int(num_seqs),
@@ -107,7 +107,7 @@ def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact
     p.mode = _MODES[mode]
     p.scale = float(scale)
     p.seg_chunks = int(seg_chunks)
-    p.num_cus = int(num_cus)
+    p.num_slots = int(num_slots)
     p.trunc_log_threshold = float(trunc_log_threshold)
     if h0_seq_stride is not None:
         p.h0_seq_stride = int(h0_seq_stride)
@@ -153,12 +153,12 @@ def _host_cu(cu_seqlens, cu_seqlens_host):
 
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
-              seg_chunks=0, num_cus=0, trunc_log_threshold=-10.0, output_final_state=True,
+              seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, output_final_state=True,
               cu_seqlens_host=None, out=None, final_state=None, workspace=None):
     """Forward of the chunked gated delta rule.  Returns (o, ht or None)."""
     lib = load_library()
     T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
-    p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_cus,
+    p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_slots,
                      trunc_log_threshold, stride)
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)
@@ -176,11 +176,11 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
     return o, ht
 
 
-def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, num_cus=0,
+def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, num_slots=0,
                         cu_seqlens_host=None):
     lib = load_library()
     T, Hq, D = q.shape
-    p = make_problem(T, cu_seqlens.numel() - 1, Hq, D, q.dtype, mode, 1.0, seg_chunks, num_cus)
+    p = make_problem(T, cu_seqlens.numel() - 1, Hq, D, q.dtype, mode, 1.0, seg_chunks, num_slots)
     n = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), _host_cu(cu_seqlens,
                                                                       cu_seqlens_host),
@@ -189,12 +189,12 @@ def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, nu
 
 
 def chunk_fwd_plan(g, cu_seqlens, num_heads, head_dim, dtype, *, mode="truncate", seg_chunks=0,
-                   num_cus=0, trunc_log_threshold=-10.0, cu_seqlens_host=None):
+                   num_slots=0, trunc_log_threshold=-10.0, cu_seqlens_host=None):
     """The segment plan the forward uses.  Returns dict(L, seq, c0, c1, warm [U, H])."""
     lib = load_library()
     T = g.shape[0]
     N = cu_seqlens.numel() - 1
-    p = make_problem(T, N, num_heads, head_dim, dtype, mode, 1.0, seg_chunks, num_cus,
+    p = make_problem(T, N, num_heads, head_dim, dtype, mode, 1.0, seg_chunks, num_slots,
                      trunc_log_threshold)
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)

@@ -76,12 +76,12 @@ def test_long_32k_truncate(gdn, oracle_mod):
     d = to_dev(inp)
     H = 8
     plan = gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], H, 128, torch.bfloat16, mode="truncate",
-                              num_cus=256, cu_seqlens_host=inp["cu_seqlens"])
+                              num_slots=256, cu_seqlens_host=inp["cu_seqlens"])
     ref_plan = oracle_mod.plan(inp["g"], inp["cu_seqlens"], H, P=256)
     assert plan["L"] == 16
     for key in ("seq", "c0", "c1", "warm"):
         assert np.array_equal(plan[key], ref_plan[key]), key
-    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None, mode="truncate", num_cus=256,
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None, mode="truncate", num_slots=256,
                           cu_seqlens_host=inp["cu_seqlens"])
     torch.cuda.synchronize()
     o_t, ht_t = oracle_mod.fwd_truncated(*_oracle_args(inp), inp["cu_seqlens"], ref_plan)
