@@ -18,12 +18,13 @@
 //   * the next chunk's Q, K, V, g, beta are fetched into registers while the current chunk is
 //     computed, then written to the second of two LDS buffer sets: the chain never waits on HBM;
 //   * the inverse is formed recursively in place: the four 16x16 diagonal blocks by forward
-//     substitution (one wave, while the others form P = (Q K^T) o decay), the two 16x16
-//     sub-diagonal blocks of the 32x32 halves (Tm_10 = -Tm_11 A_10 Tm_00,
-//     Tm_32 = -Tm_33 A_32 Tm_22), then the lower-left 32x32 block Tm_BL = -Tm_BR (A_BL Tm_TL);
-//     every A block is consumed before it is overwritten;
-//   * K h and Q h share the state's bf16 fragments; a chunk's O is staged in its V tile and
-//     written to HBM at the start of the next chunk.
+//     substitution (one wave), the two 16x16 sub-diagonal blocks of the 32x32 halves
+//     (Tm_10 = -Tm_11 A_10 Tm_00, Tm_32 = -Tm_33 A_32 Tm_22), then the lower-left 32x32 block
+//     Tm_BL = -Tm_BR (A_BL Tm_TL); every A block is consumed before it is overwritten.  The
+//     products that do not need Tm (K h and Q h, which share the state's bf16 fragments, and
+//     P = (Q K^T) o decay) run on the waves the solve leaves idle;
+//   * Q, K, V tiles are XOR-swizzled in LDS so every fragment read is free of bank conflicts;
+//   * a chunk's O is staged in its V tile and written to HBM at the start of the next chunk.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -31,15 +32,27 @@
 
 namespace gdn {
 
+// Q, K, V tiles are 64 x D bf16 without padding; 8-byte units are XOR-swizzled within each row
+// (unit u of row r is stored at unit u ^ f(r), f(r) = 4 (r mod 4) + (r / 4 mod 4)).  Every
+// fragment read in this kernel is 8 bytes per lane: 16 lanes reading one unit of 16 consecutive
+// rows, or (transpose reads) 4 consecutive units of 4 consecutive rows, touch 16 distinct
+// unit positions, i.e. all 32 banks once.
+template <int D>
+struct Swz {
+  __device__ static __forceinline__ int f(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+  // element offset of 8-byte unit u (elements 4u .. 4u + 3) of row r
+  __device__ static __forceinline__ int unit(int r, int u) { return r * D + 4 * (u ^ f(r)); }
+  __device__ static __forceinline__ int elem(int r, int c) { return unit(r, c >> 2) + (c & 3); }
+};
+
 template <int D>
 struct FastSmem {
-  static constexpr int LDE = D + 8;   // bf16 row stride of Q, K, V
   static constexpr int LDT = 64 + 4;  // fp32 row stride of A / Tm
   static constexpr int LDP = 64 + 8;  // bf16 row stride of P
   struct Buf {
-    alignas(16) bf16 q[64 * LDE];
-    alignas(16) bf16 k[64 * LDE];
-    alignas(16) bf16 v[64 * LDE];  // V, then the chunk's O staged for the store
+    alignas(16) bf16 q[64 * D];
+    alignas(16) bf16 k[64 * D];
+    alignas(16) bf16 v[64 * D];    // V, then the chunk's O staged for the store
     alignas(16) float gam[64];     // within-chunk cumsum of g
     alignas(16) float beta[64];
     alignas(16) float eg[64];      // exp(gamma)
@@ -57,7 +70,8 @@ template <int D>
 __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
   using SM = FastSmem<D>;
   using Buf = typename SM::Buf;
-  constexpr int LDE = SM::LDE, LDT = SM::LDT, LDP = SM::LDP;
+  using SW = Swz<D>;
+  constexpr int LDT = SM::LDT, LDP = SM::LDP;
   constexpr int NW = D / 16;           // waves; wave w owns state columns [16 w, 16 w + 16)
   constexpr int NTH = 64 * NW;         // threads
   constexpr int MTD = D / 16;          // 16-row state tiles (d_k)
@@ -153,9 +167,15 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       const int u = tid + NTH * j, r = u / UPR, cu16 = u % UPR;
-      *reinterpret_cast<uint4 *>(&B.k[r * LDE + cu16 * 8]) = pk[j];
-      *reinterpret_cast<uint4 *>(&B.v[r * LDE + cu16 * 8]) = pv[j];
-      if (em) *reinterpret_cast<uint4 *>(&B.q[r * LDE + cu16 * 8]) = pq[j];
+      const int a0 = SW::unit(r, 2 * cu16), a1 = SW::unit(r, 2 * cu16 + 1);
+      *reinterpret_cast<uint2 *>(&B.k[a0]) = uint2{pk[j].x, pk[j].y};
+      *reinterpret_cast<uint2 *>(&B.k[a1]) = uint2{pk[j].z, pk[j].w};
+      *reinterpret_cast<uint2 *>(&B.v[a0]) = uint2{pv[j].x, pv[j].y};
+      *reinterpret_cast<uint2 *>(&B.v[a1]) = uint2{pv[j].z, pv[j].w};
+      if (em) {
+        *reinterpret_cast<uint2 *>(&B.q[a0]) = uint2{pq[j].x, pq[j].y};
+        *reinterpret_cast<uint2 *>(&B.q[a1]) = uint2{pq[j].z, pq[j].w};
+      }
     }
     if (wave == 0) {
       const float gam = wave_inclusive_scan(pg, lane);
@@ -172,9 +192,12 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       const int u = tid + NTH * j, r = u / UPR, cu16 = u % UPR;
-      if (r < o_n)
+      if (r < o_n) {
+        const uint2 lo = *reinterpret_cast<const uint2 *>(&B.v[SW::unit(r, 2 * cu16)]);
+        const uint2 hi = *reinterpret_cast<const uint2 *>(&B.v[SW::unit(r, 2 * cu16 + 1)]);
         *reinterpret_cast<uint4 *>(go_ + ((o_t0 + r) * H + h) * D + cu16 * 8) =
-            *reinterpret_cast<const uint4 *>(&B.v[r * LDE + cu16 * 8]);
+            uint4{lo.x, lo.y, hi.x, hi.y};
+      }
     }
   };
 
@@ -197,14 +220,26 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
     if (more) fetch(c + 1);
     const float glast = B.glast[0];
 
+    // fragment reads from the swizzled tiles (8 bytes per lane each)
+    auto nat8 = [&](const bf16 *t, int row, int c0) {  // elements c0 .. c0 + 7 of a row
+      return cat8(lds_bf16x4(&t[SW::unit(row, c0 >> 2)]), lds_bf16x4(&t[SW::unit(row, (c0 >> 2) + 1)]));
+    };
+    auto perm8 = [&](const bf16 *t, int row, int c0) {  // c0 + 4 gq .. +3 and c0 + 16 + 4 gq .. +3
+      return cat8(lds_bf16x4(&t[SW::unit(row, (c0 >> 2) + gq)]),
+                  lds_bf16x4(&t[SW::unit(row, (c0 >> 2) + 4 + gq)]));
+    };
+    auto tr4 = [&](const bf16 *t, int rowbase, int colbase) {  // rows rowbase .. +3 of column colbase + cl
+      return lds_tr16(&t[SW::unit(rowbase + (cl >> 2), (colbase >> 2) + (cl & 3))]);
+    };
+
     // ---- A = strict_lower(diag(beta) (K K^T o decay)): 10 lower tiles over the waves
     for (int tau = wave; tau < 10; tau += NW) {
       const int bi = tile_bi(tau), bj = tile_bj(tau);
       f32x4 acc = zero4();
 #pragma unroll
       for (int ks = 0; ks < KSD; ++ks)
-        acc = mma_bf16(lds_bf16x8(&B.k[(16 * bi + cl) * LDE + 32 * ks + 8 * gq]),
-                       lds_bf16x8(&B.k[(16 * bj + cl) * LDE + 32 * ks + 8 * gq]), acc);
+        acc = mma_bf16(nat8(B.k, 16 * bi + cl, 32 * ks + 8 * gq), nat8(B.k, 16 * bj + cl, 32 * ks + 8 * gq),
+                       acc);
       const int j = 16 * bj + cl;
       const float gj = B.gam[j];
 #pragma unroll
@@ -215,8 +250,24 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
     }
     __syncthreads();
 
+    // K h and Q h for this wave's columns (the state's bf16 fragments are shared)
+    f32x4 KS[4], QS[4];
+    auto kq_products = [&]() {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) KS[mt] = QS[mt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < KSD; ++ks) {
+        const bf16x8 sb = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt) {
+          KS[mt] = mma_bf16(perm8(B.k, 16 * mt + cl, 32 * ks), sb, KS[mt]);
+          if (emit) QS[mt] = mma_bf16(perm8(B.q, 16 * mt + cl, 32 * ks), sb, QS[mt]);
+        }
+      }
+    };
+
     // ---- wave 0: the four 16x16 diagonal blocks of Tm, in place (lane: block b, column j);
-    //      the other waves: P = (Q K^T) o decay o causal mask
+    //      the other waves: K h and Q h
     if (wave == 0) {
       const int b = lane >> 4, j = lane & 15;
       float *Ab = &sm.at[(16 * b) * LDT + 16 * b];
@@ -230,28 +281,17 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
       }
 #pragma unroll
       for (int r = 0; r < 16; ++r) Ab[r * LDT + j] = x[r];
-    } else if (emit) {
-      for (int tau = wave - 1; tau < 10; tau += NW - 1) {
-        const int bi = tile_bi(tau), bj = tile_bj(tau);
-        f32x4 acc = zero4();
-#pragma unroll
-        for (int ks = 0; ks < KSD; ++ks)
-          acc = mma_bf16(lds_bf16x8(&B.q[(16 * bi + cl) * LDE + 32 * ks + 8 * gq]),
-                         lds_bf16x8(&B.k[(16 * bj + cl) * LDE + 32 * ks + 8 * gq]), acc);
-        const int j = 16 * bj + cl;
-        const float gj = B.gam[j];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * bi + 4 * gq + i;
-          sm.p[r * LDP + j] = (bf16)((j <= r) ? __expf(B.gam[r] - gj) * acc[i] : 0.f);
-        }
-      }
+    } else {
+      kq_products();
     }
     __syncthreads();
 
-    // ---- Tm_10 = -Tm_11 A_10 Tm_00 (wave 0) and Tm_32 = -Tm_33 A_32 Tm_22 (wave 1), in place
-    if (wave < 2) {
-      const int b = 1 + 2 * wave, cc = b - 1;
+    // ---- wave 0: K h and Q h;  waves 1, 2: Tm_10 = -Tm_11 A_10 Tm_00 and
+    //      Tm_32 = -Tm_33 A_32 Tm_22 in place;  the other waves: P = (Q K^T) o decay o mask
+    if (wave == 0) {
+      kq_products();
+    } else if (wave < 3) {
+      const int b = 1 + 2 * (wave - 1), cc = b - 1;
       f32x4 acc = zero4();
 #pragma unroll
       for (int s = 0; s < 4; ++s)
@@ -263,6 +303,22 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
         out = mma_f32(sm.at[(16 * b + cl) * LDT + 16 * b + 4 * gq + i], acc[i], out);
 #pragma unroll
       for (int i = 0; i < 4; ++i) sm.at[(16 * b + 4 * gq + i) * LDT + 16 * cc + cl] = -out[i];
+    } else if (emit) {
+      for (int tau = wave - 3; tau < 10; tau += NW - 3) {
+        const int bi = tile_bi(tau), bj = tile_bj(tau);
+        f32x4 acc = zero4();
+#pragma unroll
+        for (int ks = 0; ks < KSD; ++ks)
+          acc = mma_bf16(nat8(B.q, 16 * bi + cl, 32 * ks + 8 * gq),
+                         nat8(B.k, 16 * bj + cl, 32 * ks + 8 * gq), acc);
+        const int j = 16 * bj + cl;
+        const float gj = B.gam[j];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * bi + 4 * gq + i;
+          sm.p[r * LDP + j] = (bf16)((j <= r) ? __expf(B.gam[r] - gj) * acc[i] : 0.f);
+        }
+      }
     }
     __syncthreads();
 
@@ -302,23 +358,6 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
     }
     __syncthreads();
 
-    // ---- chain: K h and Q h (shared bf16 fragments of the state)
-    f32x4 KS[4], QS[4];
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) KS[mt] = QS[mt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < KSD; ++ks) {
-      const bf16x8 sb = to_bf16x8(S[2 * ks], S[2 * ks + 1]);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const bf16 *kp = &B.k[(16 * mt + cl) * LDE + 32 * ks + 4 * gq];
-        KS[mt] = mma_bf16(cat8(lds_bf16x4(kp), lds_bf16x4(kp + 16)), sb, KS[mt]);
-        if (emit) {
-          const bf16 *qp = &B.q[(16 * mt + cl) * LDE + 32 * ks + 4 * gq];
-          QS[mt] = mma_bf16(cat8(lds_bf16x4(qp), lds_bf16x4(qp + 16)), sb, QS[mt]);
-        }
-      }
-    }
     // ---- residual R = diag(beta) (V - diag(e^gamma) K h) as bf16 fragments over tokens
     bf16x8 rb[2];
 #pragma unroll
@@ -327,7 +366,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
 #pragma unroll
       for (int hlf = 0; hlf < 2; ++hlf) {
         const int mt = 2 * ks + hlf, r0 = 16 * mt + 4 * gq;
-        const bf16x4 v4 = lds_tr16(&B.v[(r0 + (cl >> 2)) * LDE + ncol + 4 * (cl & 3)]);
+        const bf16x4 v4 = tr4(B.v, r0, ncol);
         const f32x4 be = lds_f32x4(&B.beta[r0]), ee = lds_f32x4(&B.eg[r0]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) rv[hlf][i] = be[i] * ((float)v4[i] - ee[i] * KS[mt][i]);
@@ -364,7 +403,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) B.v[(16 * mt + 4 * gq + i) * LDE + ncol + cl] = (bf16)O[mt][i];
+        for (int i = 0; i < 4; ++i) B.v[SW::elem(16 * mt + 4 * gq + i, ncol + cl)] = (bf16)O[mt][i];
       o_t0 = t0;
       o_n = n;
     }
@@ -389,11 +428,9 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
       for (int mt = 0; mt < MTD; ++mt) {
         f32x4 acc = S[mt] * egl;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int rr = 32 * ks + 4 * gq + (cl >> 2), cc = 16 * mt + 4 * (cl & 3);
-          acc = mma_bf16(cat8(lds_tr16(&B.k[rr * LDE + cc]), lds_tr16(&B.k[(rr + 16) * LDE + cc])),
+        for (int ks = 0; ks < 2; ++ks)
+          acc = mma_bf16(cat8(tr4(B.k, 32 * ks + 4 * gq, 16 * mt), tr4(B.k, 32 * ks + 16 + 4 * gq, 16 * mt)),
                          dt[ks], acc);
-        }
         S[mt] = acc;
       }
     }
