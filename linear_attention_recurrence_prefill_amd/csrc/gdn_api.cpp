@@ -39,9 +39,14 @@ std::mutex g_dev_mu;
 
 gdn_status device_info(int *cus);
 
-// The forward kernel a problem runs on: the bf16 kernel sized for two workgroups per CU, or the
-// general kernel (fp32 inputs, and the variant that writes intermediates).
-bool use_fast_fwd(const gdn_problem *p, bool dump) { return p->dtype == GDN_DTYPE_BF16 && !dump; }
+// The forward kernel a problem runs on: for bf16 inputs the warp-specialised pipeline (d = 128)
+// or the 8-wave kernel (d = 64); otherwise the general kernel (fp32 inputs, and the variant that
+// writes intermediates).
+enum class FwdKernel { kGeneral, kFast, kPipelined };
+FwdKernel fwd_kernel_for(const gdn_problem *p, bool dump) {
+  if (p->dtype != GDN_DTYPE_BF16 || dump) return FwdKernel::kGeneral;
+  return p->d_k == 128 ? FwdKernel::kPipelined : FwdKernel::kFast;
+}
 
 // P of the latency model: workgroups that run at once = CUs x resident workgroups per CU.
 gdn_status parallel_slots(const gdn_problem *p, bool dump, int *slots) {
@@ -52,8 +57,12 @@ gdn_status parallel_slots(const gdn_problem *p, bool dump, int *slots) {
   int cus = 0;
   gdn_status s = device_info(&cus);
   if (s != GDN_OK) return s;
-  const int per_cu = use_fast_fwd(p, dump) ? gdn::fwd_fast_blocks_per_cu(p->d_k)
-                                           : gdn::fwd_blocks_per_cu(p->d_k, p->dtype == GDN_DTYPE_BF16);
+  int per_cu = 1;
+  switch (fwd_kernel_for(p, dump)) {
+    case FwdKernel::kPipelined: per_cu = gdn::fwd_ws_blocks_per_cu(); break;
+    case FwdKernel::kFast: per_cu = gdn::fwd_fast_blocks_per_cu(p->d_k); break;
+    default: per_cu = gdn::fwd_blocks_per_cu(p->d_k, p->dtype == GDN_DTYPE_BF16);
+  }
   *slots = cus * per_cu;
   return GDN_OK;
 }
@@ -237,9 +246,12 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
-  hipError_t e = use_fast_fwd(p, dump)
-                     ? gdn::launch_fwd_fast(a, p->d_k, lay.units, stream)
-                     : gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
+  hipError_t e;
+  switch (fwd_kernel_for(p, dump)) {
+    case FwdKernel::kPipelined: e = gdn::launch_fwd_ws(a, lay.units, stream); break;
+    case FwdKernel::kFast: e = gdn::launch_fwd_fast(a, p->d_k, lay.units, stream); break;
+    default: e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
+  }
   if (e != hipSuccess) return hip_fail(e, "forward launch");
   return GDN_OK;
 }

@@ -58,6 +58,10 @@ hipError_t launch_fwd(const FwdArgs &a, int D, bool bf16, bool dump, int64_t max
 // bf16 forward sized for two workgroups per CU (gdn_fwd_fast.hip); no intermediates.
 hipError_t launch_fwd_fast(const FwdArgs &a, int D, int64_t max_units, hipStream_t stream);
 
+// bf16, d = 128: warp-specialised pipeline, one workgroup per CU (gdn_fwd_ws.hip).
+hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream);
+int fwd_ws_blocks_per_cu();
+
 // Workgroups of a forward kernel that fit on one CU at once (from the runtime's occupancy query).
 int fwd_blocks_per_cu(int D, bool bf16);
 int fwd_fast_blocks_per_cu(int D);
