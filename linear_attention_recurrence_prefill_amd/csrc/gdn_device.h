@@ -94,6 +94,24 @@ __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
   return x;
 }
 
+// Wave-wide inclusive prefix sum (64 lanes) with DPP lane moves only (no LDS traffic): Hillis-
+// Steele shifts 1, 2, 4, 8 within each row of 16 lanes (row_shr, lanes shifted in from outside the
+// row read 0), then row 0's total added to row 1 and row 2's to row 3 (row_bcast:15), then the
+// total of rows 0-1 added to rows 2 and 3 (row_bcast:31).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_moved(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROW_MASK, 0xf, true));
+}
+__device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
+  x += dpp_moved<0x111, 0xf>(x);  // row_shr:1
+  x += dpp_moved<0x112, 0xf>(x);  // row_shr:2
+  x += dpp_moved<0x114, 0xf>(x);  // row_shr:4
+  x += dpp_moved<0x118, 0xf>(x);  // row_shr:8
+  x += dpp_moved<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+  x += dpp_moved<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+  return x;
+}
+
 // Wave-wide sum in fp64 (64 lanes); every lane receives the total.
 __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll

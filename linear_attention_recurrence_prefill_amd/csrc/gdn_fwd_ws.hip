@@ -5,24 +5,31 @@
 // "What GDN actually computes", "Lever 1", "Lever 2"): per 64-token chunk, gamma = cumsum(g),
 // A = strict_lower(diag(beta) (K K^T o e^{gamma_r - gamma_i})), Tm = (I + A)^-1, the state chain
 // and the output.  The residual form of Delta is used (same quantity as U - W h):
-//     R = diag(beta) (V - diag(e^gamma) K h),   Delta = Tm R.
+//     Delta = Tm diag(beta) R',   R' = V - diag(e^gamma) K h.
 //
 // Work split.  Everything that does not depend on the state (the gate vectors, A, the inverse,
 // P = (Q K^T) o decay o mask) is "prep"; the rest (K h, Delta, the output, the state update) is
 // the "chain".  A workgroup has eight waves: waves 0-3 run the chain, wave w owning state columns
-// [32 w, 32 w + 32); waves 4-7 prep chunk c + 1 while the chain runs chunk c, and wave 7 streams
-// chunk c + 2's K and Q from HBM into LDS with direct global->LDS loads.  One barrier per chunk
-// hands the prepared chunk over; chain waves never wait for each other (each owns its columns of
-// the state, of V and of the output).
+// [32 w, 32 w + 32); waves 4-6 prep chunk c + 1 while the chain runs chunk c; wave 7 forms chunk
+// c + 2's gate vectors and streams its K and Q from HBM into LDS with direct global->LDS loads.
+// One barrier per chunk hands the prepared chunk over; chain waves never wait for each other
+// (each owns its columns of the state, of V and of the output).
 //
-// Delta by block forward substitution.  With Tm = [[T_TL, 0], [T_BL, T_BR]] over 32-token halves,
-//     Delta_T = T_TL R_T,   Delta_B = T_BR (R_B - A_BL Delta_T),
-// so prep only inverts the two 32x32 diagonal blocks (four 16x16 inverses by substitution on one
-// wave, then Tm_10 = -T_11 A_10 T_00 and Tm_32 = -T_33 A_32 T_22 with fp32 MFMA) and never forms
-// T_BL; the chain spends the same number of MFMAs as with the full Tm.
+// Delta by block forward substitution.  With Tm = [[T_TL, 0], [T_BL, T_BR]] over 32-token halves
+// and beta folded into the diagonal blocks' columns (T'_TL = T_TL diag(beta_T), likewise T'_BR)
+// and out of A's lower-left block's rows (A_BL = diag(beta_B) A'_BL):
+//     Delta_T = T'_TL R'_T,   Delta_B = T'_BR (R'_B - A'_BL Delta_T).
+// Prep therefore inverts only the two 32x32 diagonal blocks (four 16x16 inverses by
+// substitution on one wave, then Tm_10 = -T_11 A_10 T_00 and Tm_32 = -T_33 A_32 T_22 with fp32
+// MFMA) and never forms T_BL; the chain spends the same number of MFMAs as with the full Tm.
 //
 // The output is formed transposed, O^T = e^gamma-scaled (S^T Q^T) + Delta^T P^T, so each lane
 // holds 4 consecutive state columns of one token and writes them with one 8-byte store.
+//
+// Addressing.  Every swizzled LDS access is a lane-constant byte offset (computed once, held in a
+// register) plus an immediate: the swizzles depend on the row only modulo 16, and rows enter in
+// multiples of 16.  Global loads and stores likewise use a uniform base and a lane-constant
+// offset; only a sequence's ragged last chunk takes the per-lane clamped path.
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -32,22 +39,24 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
+constexpr int kRowBytes = kD * 2;  // one bf16 row of a K, Q or V tile
 
 // 64 x 128 bf16 tiles (K, Q, V): rows of 256 bytes; the 16-byte unit c of row r is stored at unit
 // c ^ sw(r).  For the reads below (16 lanes on one 8-byte unit of 16 consecutive rows, or
 // transpose reads of 4 consecutive 8-byte units of 8 consecutive rows) each half-wave touches
 // 32 distinct 8-byte bank pairs.
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-// element offset of the 8-byte unit u (elements 4u .. 4u + 3) of row r
+// byte offset of the 8-byte unit u (elements 4u .. 4u + 3) of row r
 __device__ __forceinline__ int toff(int r, int u) {
-  return r * kD + (((u >> 1) ^ sw(r)) << 3) + ((u & 1) << 2);
+  return r * kRowBytes + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
 }
-// 32 x 32 bf16 blocks (T_TL, T_BR, -A_BL): rows of 64 bytes, unit u of row r at u ^ 2 ((r/4) % 4)
-__device__ __forceinline__ int boff(int r, int u) { return r * 32 + ((u ^ (((r >> 2) & 3) << 1)) << 2); }
-// 64 x 64 bf16 P: rows of 128 bytes, unit u of row r at u ^ 2 ((r/2) % 8)
-__device__ __forceinline__ int poff(int r, int u) { return r * 64 + ((u ^ (((r >> 1) & 7) << 1)) << 2); }
+// 32 x 32 bf16 blocks (T'_TL, T'_BR, -A'_BL): rows of 64 bytes, unit u of row r at
+// u ^ 2 ((r / 4) % 4)
+__device__ __forceinline__ int boff(int r, int u) { return r * 64 + ((u ^ (((r >> 2) & 3) << 1)) << 3); }
+// 64 x 64 bf16 P: rows of 128 bytes, unit u of row r at u ^ 2 ((r / 2) % 8)
+__device__ __forceinline__ int poff(int r, int u) { return r * 128 + ((u ^ (((r >> 1) & 7) << 1)) << 3); }
 
-constexpr int LA = 20;        // fp32 row stride of the 16x16 solve blocks
+constexpr int LA = 20;            // fp32 row stride of the 16x16 solve blocks
 constexpr int AB = 16 * LA + 16;  // fp32 stride between solve blocks (spreads blocks over banks)
 
 struct WsSmem {
@@ -58,63 +67,41 @@ struct WsSmem {
     alignas(16) float gam[64];
     alignas(16) float egl[4];   // e^gamma_last
   };
-  alignas(16) bf16 kq[3][2][64 * kD];  // [set][K, Q], three chunks in flight
-  alignas(16) bf16 v[64 * kD];         // V of the chunk on the chain (each chain wave its columns)
-  alignas(16) bf16 tb[2][3][32 * 32];  // [set][T_TL, T_BR, -A_BL]
-  alignas(16) bf16 p[2][64 * 64];      // [set] P
-  Vec vec[2];
+  alignas(16) char kq[3][2][64 * kRowBytes];  // [set][K, Q], three chunks in flight
+  alignas(16) char v[64 * kRowBytes];         // V of the chunk on the chain (per wave: its columns)
+  alignas(16) char tb[2][3][32 * 64];         // [set][T'_TL, T'_BR, -A'_BL]
+  alignas(16) char p[2][64 * 128];            // [set] P
+  Vec vec[3];  // gate vectors: written one step ahead of prep, read by the chain a step later
   alignas(16) float at[4 * AB];  // A_bb transposed (row i = column i of A_bb), wave 4 only
   alignas(16) float ao[2 * AB];  // A_10, A_32 row-major, wave 4 only
   alignas(16) float tt[4 * AB];  // T_bb row-major, wave 4 only
   alignas(16) int imisc[4];
+  int ready;  // chunk index + 1 whose A_22, A_33, A_32 (wave 7's part of A) are in at / ao
 };
 static_assert(sizeof(WsSmem) <= 160 * 1024, "LDS budget");
 
-__device__ __forceinline__ bf16x4 ld4(const bf16 *p) { return lds_bf16x4(p); }
-__device__ __forceinline__ void st4(bf16 *p, f32x4 x) {
-  *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(x);
+__device__ __forceinline__ bf16x4 ld8(const char *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+__device__ __forceinline__ bf16x8 ld16(const char *p0, const char *p1) { return cat8(ld8(p0), ld8(p1)); }
+__device__ __forceinline__ bf16x4 ldtr(const char *p) {
+  return lds_tr16(reinterpret_cast<const bf16 *>(p));
+}
+__device__ __forceinline__ void st8(char *p, f32x4 x) { *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(x); }
+__device__ __forceinline__ f32x4 ldf4(const float *p) {  // two 8-byte reads (b128 reads are slow)
+  const float2 a = *reinterpret_cast<const float2 *>(p), b = *reinterpret_cast<const float2 *>(p + 2);
+  return f32x4{a.x, a.y, b.x, b.y};
 }
 
-// 16 direct global->LDS loads of 16 bytes per lane (one wave): a 64 x 128 bf16 tile of token
-// rows t0 .. t0 + 63 (rows past the chunk's n tokens repeat its last token) into the swizzled
-// layout.  Instruction j fills LDS rows 4j .. 4j + 3; lane l writes physical unit l % 16 of row
-// 4j + l / 16, which holds logical unit (l % 16) ^ sw(row).
-__device__ __forceinline__ void dma_tile(bf16 *dst, const bf16 *__restrict__ src, int64_t t0,
-                                         int n, int h, int H, int lane) {
-#pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int r = 4 * j + (lane >> 4);
-    const int c = (lane & 15) ^ sw(r);
-    const int64_t t = t0 + min(r, n - 1);
-    __builtin_amdgcn_global_load_lds(src + (t * H + h) * kD + 8 * c,
-                                     (GDN_LDS void *)(dst + 512 * j), 16, 0, 0);
-  }
+// A lane-constant value the compiler must keep in a register (it cannot rematerialise it at
+// each use, which would cost address arithmetic inside the chunk loop).
+__device__ __forceinline__ int pin(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// Fragment reads, 8 bytes per lane each (g = lane / 16, l = lane % 16 of the reading lane).
-// kfrag: elements 32 ks + 4 g .. +3 and 32 ks + 16 + 4 g .. +3 of a 128-wide tile row -- the
-// k-order of a pair of D-layout accumulators used as the other operand.
-__device__ __forceinline__ bf16x8 kfrag(const bf16 *t, int row, int ks, int g) {
-  return cat8(ld4(t + toff(row, 8 * ks + g)), ld4(t + toff(row, 8 * ks + 4 + g)));
-}
-// the same k-order over a row of a 32-wide block or of the 64-wide P
-__device__ __forceinline__ bf16x8 bfrag(const bf16 *t, int row, int g) {
-  return cat8(ld4(t + boff(row, g)), ld4(t + boff(row, 4 + g)));
-}
-__device__ __forceinline__ bf16x8 pfrag(const bf16 *t, int row, int ks, int g) {
-  return cat8(ld4(t + poff(row, 8 * ks + g)), ld4(t + poff(row, 8 * ks + 4 + g)));
-}
-// transpose read of a 128-wide tile: rows rowbase .. rowbase + 3 of column colbase + l
-__device__ __forceinline__ bf16x4 trfrag(const bf16 *t, int rowbase, int colbase, int l) {
-  return lds_tr16(t + toff(rowbase + (l >> 2), (colbase >> 2) + (l & 3)));
-}
-// The lane index as an opaque value: address arithmetic derived from it is formed where it is
-// used instead of being hoisted out of the chunk loop (which would hold ~50 address registers).
-__device__ __forceinline__ int fresh_lane(int lane) {
-  asm volatile("" : "+v"(lane));
-  return lane;
+__device__ __forceinline__ void dma16(const char *g, char *l) {
+  __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
 }
 
 }  // namespace
@@ -142,24 +129,25 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
-  const bf16 *__restrict__ gq_ = static_cast<const bf16 *>(a.q);
-  const bf16 *__restrict__ gk_ = static_cast<const bf16 *>(a.k);
-  const bf16 *__restrict__ gv_ = static_cast<const bf16 *>(a.v);
+  const int64_t tok_bytes = (int64_t)H * kRowBytes;  // stride of one token in q, k, v, o
+  const char *__restrict__ gq_ = static_cast<const char *>(a.q) + (int64_t)h * kRowBytes;
+  const char *__restrict__ gk_ = static_cast<const char *>(a.k) + (int64_t)h * kRowBytes;
+  const char *__restrict__ gv_ = static_cast<const char *>(a.v) + (int64_t)h * kRowBytes;
   const bf16 *__restrict__ gb_ = static_cast<const bf16 *>(a.beta);
-  bf16 *__restrict__ go_ = static_cast<bf16 *>(a.o);
+  char *__restrict__ go_ = static_cast<char *>(a.o) + (int64_t)h * kRowBytes;
 
-  // Parts the chain reads but prep never writes: the upper-right 16x16 blocks of T_TL and T_BR,
+  // Parts the chain reads but prep never writes: the upper-right 16x16 blocks of T'_TL and T'_BR,
   // and P's tiles (0, 1) and (2, 3) above the diagonal.
-  for (int i = tid; i < 2 * 2 * 256; i += 512) {
-    const int set = i >> 9, blk = (i >> 8) & 1, e = i & 255, r = e >> 4, c = 16 + (e & 15);
-    sm.tb[set][blk][boff(r, c >> 2) + (c & 3)] = (bf16)0.f;
+  for (int i = tid; i < 2 * 2 * 64; i += 512) {  // 8-byte units
+    const int set = i >> 7, blk = (i >> 6) & 1, r = (i >> 2) & 15, u = 4 + (i & 3);
+    *reinterpret_cast<uint2 *>(&sm.tb[set][blk][boff(r, u)]) = uint2{0u, 0u};
   }
-  for (int i = tid; i < 2 * 2 * 256; i += 512) {
-    const int set = i >> 9, t = (i >> 8) & 1, e = i & 255;
-    const int r = 32 * t + (e >> 4), c = 32 * t + 16 + (e & 15);
-    sm.p[set][poff(r, c >> 2) + (c & 3)] = (bf16)0.f;
+  for (int i = tid; i < 2 * 2 * 64; i += 512) {
+    const int set = i >> 7, t = (i >> 6) & 1, r = 32 * t + ((i >> 2) & 15), u = 8 * t + 4 + (i & 3);
+    *reinterpret_cast<uint2 *>(&sm.p[set][poff(r, u)]) = uint2{0u, 0u};
   }
 
+  if (tid == 0) sm.ready = 0;
   int cw = c0;
   if (a.truncate && c0 > 0) {
     __syncthreads();  // every wave has read the unit
@@ -174,12 +162,73 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   auto chunk_t0 = [&](int c) { return ts0 + (int64_t)c * kChunk; };
   auto chunk_n = [&](int c) { return (int)min<int64_t>(kChunk, ts1 - chunk_t0(c)); };
 
-  const bool is_chain = wave < 4;
+  // kfrag offsets (chain and prep): elements 32 ks + 4 gq .. +3 and 32 ks + 16 + 4 gq .. +3 of row
+  // cl (+ 16 m rows as an immediate) -- the k-order of a pair of D-layout accumulators used as
+  // the other MFMA operand
+  int o_kf[4][2];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) o_kf[ks][hf] = pin(toff(cl, 8 * ks + 4 * hf + gq));
+  auto kfrag = [&](const char *t, int m, int ks) {
+    return ld16(t + 16 * m * kRowBytes + o_kf[ks][0], t + 16 * m * kRowBytes + o_kf[ks][1]);
+  };
+
+  // Half `half` of A's diagonal-block tiles in fp32: the 16x16 blocks (b0, b0), (b1, b1) stored
+  // transposed into at, and (b1, b0) row-major into ao (b0 = 2 half, b1 = b0 + 1).
+  auto a_half = [&](const char *Kt, const WsSmem::Vec &vc, int half) {
+    const int b0 = 2 * half, b1 = b0 + 1;
+    f32x4 a00 = zero4(), a10 = zero4(), a11 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 f0 = kfrag(Kt, b0, ks), f1 = kfrag(Kt, b1, ks);
+      a00 = mma_bf16(f0, f0, a00);
+      a10 = mma_bf16(f1, f0, a10);
+      a11 = mma_bf16(f1, f1, a11);
+    }
+    const f32x4 gr0 = ldf4(&vc.gam[16 * b0 + 4 * gq]), br0 = ldf4(&vc.beta[16 * b0 + 4 * gq]);
+    const f32x4 gr1 = ldf4(&vc.gam[16 * b1 + 4 * gq]), br1 = ldf4(&vc.beta[16 * b1 + 4 * gq]);
+    const float gi0 = vc.gam[16 * b0 + cl], gi1 = vc.gam[16 * b1 + cl];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int rl = 4 * gq + e;
+      a00[e] = cl < rl ? br0[e] * __expf(gr0[e] - gi0) * a00[e] : 0.f;
+      a11[e] = cl < rl ? br1[e] * __expf(gr1[e] - gi1) * a11[e] : 0.f;
+      a10[e] = br1[e] * __expf(gr1[e] - gi0) * a10[e];
+    }
+    float *t0p = &sm.at[b0 * AB + cl * LA + 4 * gq], *t1p = &sm.at[b1 * AB + cl * LA + 4 * gq];
+    *reinterpret_cast<float2 *>(t0p) = float2{a00[0], a00[1]};
+    *reinterpret_cast<float2 *>(t0p + 2) = float2{a00[2], a00[3]};
+    *reinterpret_cast<float2 *>(t1p) = float2{a11[0], a11[1]};
+    *reinterpret_cast<float2 *>(t1p + 2) = float2{a11[2], a11[3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) sm.ao[half * AB + (4 * gq + e) * LA + cl] = a10[e];
+  };
+
   const int w = wave & 3;
 
-  if (is_chain) {
+  if (wave < 4) {
     // ======================= chain waves: the state recurrence and the output =======================
     const int ncol = 32 * w;  // this wave's first state column
+    // lane-constant offsets: transpose reads of K (rows 4 gq + cl / 4, unit 4 mt + cl % 4) and of
+    // this wave's V columns, 32-wide block rows, P rows, the V tile store, and global offsets
+    int o_tr[8], o_vtr[2], o_bf[2], o_pf[2][2];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o_tr[mt] = pin(toff(4 * gq + (cl >> 2), 4 * mt + (cl & 3)));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) o_vtr[nt] = pin(toff(4 * gq + (cl >> 2), 8 * w + 4 * nt + (cl & 3)));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) o_bf[hf] = pin(boff(cl, 4 * hf + gq));
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) o_pf[ks][hf] = pin(poff(cl, 8 * ks + 4 * hf + gq));
+    const int vr = lane >> 2, vc16 = 4 * w + (lane & 3);  // V rows 16 j + vr, 16-byte unit vc16
+    const int o_vst = pin(vr * kRowBytes + ((vc16 ^ sw(vr)) << 4));
+    const int o_gv = pin((int)(vr * tok_bytes) + vc16 * 16);                // V loads
+    const int o_go = pin((int)(cl * tok_bytes) + (ncol + 4 * gq) * 2);      // O stores
+    auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + rows * kRowBytes + o_tr[mt]); };
+
     // S[mt][nt] holds rows 16 mt + 4 gq + i, column ncol + 16 nt + cl
     f32x4 S[8][2];
     if (cw == 0 && a.h0 != nullptr) {
@@ -200,7 +249,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) S[mt][0] = S[mt][1] = zero4();
     }
-    // V rows of chunk c for this wave's columns (16-byte units; rows past n repeat the chunk's last
+    // V rows of chunk c for this wave's columns (rows past a ragged chunk's end repeat its last
     // token), and their store into the swizzled V tile
     struct VRows {
       uint4 x[4];
@@ -209,19 +258,25 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       const int64_t t0 = chunk_t0(c);
       const int n = chunk_n(c);
       VRows vp;
+      if (n == kChunk) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * j + (lane >> 2);
-        const int64_t t = t0 + min(r, n - 1);
-        vp.x[j] = *reinterpret_cast<const uint4 *>(gv_ + (t * H + h) * kD + ncol + 8 * (lane & 3));
+        for (int j = 0; j < 4; ++j)
+          vp.x[j] = *reinterpret_cast<const uint4 *>(gv_ + (t0 + 16 * j) * tok_bytes + o_gv);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int64_t t = t0 + min(16 * j + vr, n - 1);
+          vp.x[j] = *reinterpret_cast<const uint4 *>(gv_ + t * tok_bytes + vc16 * 16);
+        }
       }
       return vp;
     };
     auto v_store = [&](const VRows &vp) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int r = 16 * j + (lane >> 2), c = 4 * w + (lane & 3);
-        *reinterpret_cast<uint4 *>(&sm.v[r * kD + ((c ^ sw(r)) << 3)]) = vp.x[j];
+        char *p = sm.v + 16 * j * kRowBytes + o_vst;
+        *reinterpret_cast<uint2 *>(p) = uint2{vp.x[j].x, vp.x[j].y};
+        *reinterpret_cast<uint2 *>(p + 8) = uint2{vp.x[j].z, vp.x[j].w};
       }
     };
     // the state as bf16 operand fragments, in the k-order of kfrag
@@ -241,7 +296,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     if (cw < c1) v_store(v_load(cw));
     wait_vm0();  // the initial state is in registers: no load is outstanding when the loop starts
     if (cw < c1) vp = v_load(min(cw + 1, c1 - 1));
-    __syncthreads();  // chunk cw's K and Q are in LDS (prep waves)
+    __syncthreads();  // chunk cw's K and Q are in LDS (wave 7)
 
     for (int c = cw; c <= c1; ++c) {
       if (c > cw) {
@@ -251,13 +306,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int n = chunk_n(cc);
         const bool emit = cc >= c0;
         const int Y = cc & 1;
-        const bf16 *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
-        const WsSmem::Vec &vc = sm.vec[Y];
+        const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
+        const WsSmem::Vec &vc = sm.vec[cc % 3];
 
-        // ---- K h, then the residual R = diag(beta) (V - diag(e^gamma) K h), fp32
+        // ---- K h, then R' = V - diag(e^gamma) K h, fp32
         f32x4 R[4][2];
         {
-          const int ln = fresh_lane(lane), lg = ln >> 4, lc = ln & 15;
           bf16x8 sb[4][2];
           state_frags(sb);
 #pragma unroll
@@ -266,47 +320,41 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 af = kfrag(Kt, 16 * mt + lc, ks, lg);
+              const bf16x8 af = kfrag(Kt, mt, ks);
 #pragma unroll
               for (int nt = 0; nt < 2; ++nt) R[mt][nt] = mma_bf16(af, sb[ks][nt], R[mt][nt]);
             }
         }
-        sched_fence();
-        {
-        const int ln = fresh_lane(lane), lg = ln >> 4, lc = ln & 15;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 be = lds_f32x4(&vc.beta[16 * mt + 4 * gq]);
-          const f32x4 ee = lds_f32x4(&vc.eg[16 * mt + 4 * gq]);
+          const f32x4 ee = ldf4(&vc.eg[16 * mt + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
-            const bf16x4 v4 = trfrag(sm.v, 16 * mt + 4 * lg, ncol + 16 * nt, lc);
+            const bf16x4 v4 = ldtr(sm.v + 16 * mt * kRowBytes + o_vtr[nt]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) R[mt][nt][i] = be[i] * ((float)v4[i] - ee[i] * R[mt][nt][i]);
+            for (int i = 0; i < 4; ++i) R[mt][nt][i] = (float)v4[i] - ee[i] * R[mt][nt][i];
           }
         }
-        }
         v_store(vp);  // chunk cc + 1's V (this wave's columns of chunk cc are consumed)
-        sched_fence();
 
-        // ---- Delta_T = T_TL R_T;  R_B -= A_BL Delta_T;  Delta_B = T_BR R_B.  Delta is kept only
-        //      as bf16 operand fragments: da for the output, dt = Delta o e^{gamma_last - gamma}
-        //      for the state update (both in the k-order of kfrag over tokens)
+        // ---- Delta_T = T'_TL R'_T;  R'_B -= A'_BL Delta_T;  Delta_B = T'_BR R'_B.  Delta is kept
+        //      only as bf16 operand fragments: da for the output, dt = Delta o e^{gamma_last -
+        //      gamma} for the state update (both in the k-order of kfrag over tokens)
         bf16x8 da[2][2], dt[2][2];
         {
-          const int ln = fresh_lane(lane), lg = ln >> 4, lc = ln & 15;
-          const bf16 *TL = sm.tb[Y][0], *BR = sm.tb[Y][1], *NA = sm.tb[Y][2];
+          const char *TL = sm.tb[Y][0], *BR = sm.tb[Y][1], *NA = sm.tb[Y][2];
+          auto bfrag = [&](const char *t, int m) { return ld16(t + 1024 * m + o_bf[0], t + 1024 * m + o_bf[1]); };
           f32x4 Dl[2][2];
           bf16x8 rb[2];
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) rb[nt] = to_bf16x8(R[0][nt], R[1][nt]);
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 af = bfrag(TL, 16 * mt + lc, lg);
+            const bf16x8 af = bfrag(TL, mt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Dl[mt][nt] = mma_bf16(af, rb[nt], zero4());
           }
-          const f32x4 e00 = lds_f32x4(&vc.edt[4 * gq]), e01 = lds_f32x4(&vc.edt[16 + 4 * gq]);
+          const f32x4 e00 = ldf4(&vc.edt[4 * gq]), e01 = ldf4(&vc.edt[16 + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             da[0][nt] = to_bf16x8(Dl[0][nt], Dl[1][nt]);
@@ -314,7 +362,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           }
 #pragma unroll
           for (int mt = 2; mt < 4; ++mt) {
-            const bf16x8 af = bfrag(NA, 16 * (mt - 2) + lc, lg);
+            const bf16x8 af = bfrag(NA, mt - 2);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) R[mt][nt] = mma_bf16(af, da[0][nt], R[mt][nt]);
           }
@@ -322,11 +370,11 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           for (int nt = 0; nt < 2; ++nt) rb[nt] = to_bf16x8(R[2][nt], R[3][nt]);
 #pragma unroll
           for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 af = bfrag(BR, 16 * mt + lc, lg);
+            const bf16x8 af = bfrag(BR, mt);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Dl[mt][nt] = mma_bf16(af, rb[nt], zero4());
           }
-          const f32x4 e10 = lds_f32x4(&vc.edt[32 + 4 * gq]), e11 = lds_f32x4(&vc.edt[48 + 4 * gq]);
+          const f32x4 e10 = ldf4(&vc.edt[32 + 4 * gq]), e11 = ldf4(&vc.edt[48 + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             da[1][nt] = to_bf16x8(Dl[0][nt], Dl[1][nt]);
@@ -334,24 +382,23 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           }
         }
 
-        sched_fence();
         // ---- output, transposed: O^T = scale (e^gamma (S^T Q^T) + Delta^T P^T)
         if (emit) {
-          const bf16 *P = sm.p[Y];
+          const char *P = sm.p[Y];
           bf16x8 sb[4][2];
           state_frags(sb);
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            const int ln = fresh_lane(lane), lg = ln >> 4, lc = ln & 15;
-            const int t = 16 * tt + cl;
             bf16x8 qf[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qf[ks] = kfrag(Qt, 16 * tt + lc, ks, lg);
+            for (int ks = 0; ks < 4; ++ks) qf[ks] = kfrag(Qt, tt, ks);
             bf16x8 pf[2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-              if (ks <= (tt >> 1)) pf[ks] = pfrag(P, 16 * tt + lc, ks, lg);
-            const float et = vc.eg[t];
+              if (ks <= (tt >> 1))
+                pf[ks] = ld16(P + 2048 * tt + o_pf[ks][0], P + 2048 * tt + o_pf[ks][1]);
+            const float et = vc.eg[16 * tt + cl];
+            char *orow = go_ + (t0 + 16 * tt) * tok_bytes + o_go;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               f32x4 acc = zero4();
@@ -362,29 +409,23 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               for (int ks = 0; ks < 2; ++ks)
                 if (ks <= (tt >> 1)) acc = mma_bf16(da[ks][nt], pf[ks], acc);
               acc *= a.scale;
-              if (t < n)
-                *reinterpret_cast<bf16x4 *>(go_ + ((t0 + t) * H + h) * kD + ncol + 16 * nt + 4 * gq) =
-                    to_bf16x4(acc);
+              if (16 * tt + cl < n) *reinterpret_cast<bf16x4 *>(orow + 32 * nt) = to_bf16x4(acc);
             }
-            sched_fence();
           }
         }
 
         vp = v_load(min(cc + 2, c1 - 1));
-        sched_fence();
 
         // ---- state update: h <- e^{gamma_last} h + K^T diag(e^{gamma_last - gamma}) Delta
         {
           const float egl = vc.egl[0];
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt) {
-            const int ln = fresh_lane(lane), lg = ln >> 4, lc = ln & 15;
-            const bf16x8 a0 = cat8(trfrag(Kt, 4 * lg, 16 * mt, lc), trfrag(Kt, 16 + 4 * lg, 16 * mt, lc));
-            const bf16x8 a1 = cat8(trfrag(Kt, 32 + 4 * lg, 16 * mt, lc), trfrag(Kt, 48 + 4 * lg, 16 * mt, lc));
+            const bf16x8 a0 = cat8(trk(Kt, 0, mt), trk(Kt, 16, mt));
+            const bf16x8 a1 = cat8(trk(Kt, 32, mt), trk(Kt, 48, mt));
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt)
               S[mt][nt] = mma_bf16(a1, dt[1][nt], mma_bf16(a0, dt[0][nt], S[mt][nt] * egl));
-            if (mt & 1) sched_fence();
           }
         }
       }
@@ -402,28 +443,35 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             dst[(16 * mt + 4 * gq + i) * kD + ncol + 16 * nt + cl] = S[mt][nt][i];
     }
   } else if (wave == 7) {
-    // ======================= wave 7: K and Q from HBM into LDS, one chunk ahead =====================
-    // (it issues no other LDS instruction, so nothing waits on these loads before the barrier)
-    if (cw < c1) {
-      dma_tile(sm.kq[cw % 3][0], gk_, chunk_t0(cw), chunk_n(cw), h, H, lane);
-      if (cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, chunk_t0(cw), chunk_n(cw), h, H, lane);
+    // ================ wave 7: gate vectors, and K and Q from HBM into LDS, one chunk ahead ===========
+    // It writes the gate vectors before it issues the direct global->LDS loads and touches LDS
+    // no more until the barrier, so nothing waits on those loads early.  DMA instruction j fills
+    // LDS rows 4 j .. 4 j + 3; lane l writes physical unit l % 16 of row 4 j + l / 16, which holds
+    // logical unit (l % 16) ^ sw(row).
+    int o_dma[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int r = 4 * j + (lane >> 4);
+      o_dma[j] = pin((int)(r * tok_bytes) + (((lane & 15) ^ sw(r)) << 4));
     }
-    wait_vm0();
-    __syncthreads();
-    for (int c = cw; c <= c1; ++c) {
-      if (c + 1 < c1) {
-        dma_tile(sm.kq[(c + 1) % 3][0], gk_, chunk_t0(c + 1), chunk_n(c + 1), h, H, lane);
-        if (c + 1 >= c0)
-          dma_tile(sm.kq[(c + 1) % 3][1], gq_, chunk_t0(c + 1), chunk_n(c + 1), h, H, lane);
+    auto dma_tile = [&](char *dst, const char *src, int c) {
+      const int64_t t0 = chunk_t0(c);
+      const int n = chunk_n(c);
+      if (n == kChunk) {
+        const char *base = src + t0 * tok_bytes;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) dma16(base + o_dma[j], dst + 1024 * j);
+      } else {  // ragged last chunk: rows past n repeat the last token
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int r = 4 * j + (lane >> 4);
+          const int64_t t = t0 + min(r, n - 1);
+          dma16(src + t * tok_bytes + (((lane & 15) ^ sw(r)) << 4), dst + 1024 * j);
+        }
       }
-      wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
-      __syncthreads();
-    }
-  } else {
-    // ======================= waves 4-6: everything else that does not need the state ===============
-    // g and beta of this lane's token in chunk c, loaded one chunk ahead as raw values (the
-    // address is clamped to the chunk, so the loads are unconditional and never waited on early);
-    // gb_value masks lanes past the chunk's end and converts
+    };
+    // g and beta of this lane's token in chunk c (the address is clamped to the chunk; lanes past
+    // its end are masked when the vectors are formed)
     struct GB {
       float g;
       unsigned short b;
@@ -435,62 +483,64 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       x.b = reinterpret_cast<const unsigned short *>(gb_)[t * H + h];
       return x;
     };
-    auto gb_value = [&](const GB &x, int n, float &gv, float &bv) {
-      gv = lane < n ? x.g : 0.f;
-      bv = lane < n ? __uint_as_float((unsigned)x.b << 16) : 0.f;
+    // gamma = cumsum(g) and the vectors prep and the chain read, for chunk c
+    auto gate_vectors = [&](const GB &x, int c) {
+      const int n = chunk_n(c);
+      const float gv = lane < n ? x.g : 0.f;
+      const float bv = lane < n ? __uint_as_float((unsigned)x.b << 16) : 0.f;
+      const float gam = wave_inclusive_scan_dpp(gv);
+      const float gl = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gam), n - 1));
+      WsSmem::Vec &vc = sm.vec[c % 3];
+      vc.beta[lane] = bv;
+      vc.eg[lane] = __expf(gam);
+      vc.edt[lane] = __expf(gl - gam);
+      vc.gam[lane] = gam;
+      if (lane == 0) vc.egl[0] = __expf(gl);
     };
     GB gbx{0.f, 0};
-    if (cw < c1) gbx = gb_load(cw);
+    if (cw < c1) {
+      gbx = gb_load(cw);
+      wait_vm0();
+      gate_vectors(gbx, cw);
+      dma_tile(sm.kq[cw % 3][0], gk_, cw);
+      if (cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, cw);
+      if (cw + 1 < c1) gbx = gb_load(cw + 1);
+    }
+    wait_vm0();
+    __syncthreads();
+    for (int c = cw; c <= c1; ++c) {
+      if (c < c1) {  // A's diagonal blocks 2 and 3 and A_32 of the chunk prep works on
+        a_half(sm.kq[c % 3][0], sm.vec[c % 3], 1);
+        __hip_atomic_store(&sm.ready, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      }
+      if (c + 1 < c1) {
+        gate_vectors(gbx, c + 1);
+        dma_tile(sm.kq[(c + 1) % 3][0], gk_, c + 1);
+        if (c + 1 >= c0) dma_tile(sm.kq[(c + 1) % 3][1], gq_, c + 1);
+        if (c + 2 < c1) gbx = gb_load(c + 2);
+      }
+      wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
+      __syncthreads();
+    }
+  } else {
+    // ======================= waves 4-6: everything else that does not need the state ===============
     __syncthreads();
 
     for (int c = cw; c <= c1; ++c) {
       if (c < c1) {
         // ---------------- chunk c ----------------
-        const int n = chunk_n(c);
-        const bool emit = c >= c0, more = c + 1 < c1;
+        const bool emit = c >= c0;
         const int Y = c & 1;
-        const bf16 *Kt = sm.kq[c % 3][0], *Qt = sm.kq[c % 3][1];
-        float gv, bv;
-        gb_value(gbx, n, gv, bv);
-        if (more) gbx = gb_load(c + 1);
-        const float gam = wave_inclusive_scan(gv, lane);
-        const float gl = __shfl(gam, n - 1, 64);
+        const char *Kt = sm.kq[c % 3][0], *Qt = sm.kq[c % 3][1];
+        const WsSmem::Vec &vc = sm.vec[c % 3];
         if (wave == 4) {
-          // ---- gate vectors for the chain
-          WsSmem::Vec &vc = sm.vec[Y];
-          vc.beta[lane] = bv;
-          vc.eg[lane] = __expf(gam);
-          vc.edt[lane] = __expf(gl - gam);
-          vc.gam[lane] = gam;
-          if (lane == 0) vc.egl[0] = __expf(gl);
-          // ---- A's diagonal 16x16 blocks (stored transposed) and A_10, A_32 (row-major), fp32
-#pragma unroll
-          for (int half = 0; half < 2; ++half) {
-            const int b0 = 2 * half, b1 = b0 + 1;
-            f32x4 a00 = zero4(), a10 = zero4(), a11 = zero4();
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-              const bf16x8 f0 = kfrag(Kt, 16 * b0 + cl, ks, gq), f1 = kfrag(Kt, 16 * b1 + cl, ks, gq);
-              a00 = mma_bf16(f0, f0, a00);
-              a10 = mma_bf16(f1, f0, a10);
-              a11 = mma_bf16(f1, f1, a11);
-            }
-            const f32x4 gr0 = lds_f32x4(&vc.gam[16 * b0 + 4 * gq]);
-            const f32x4 br0 = lds_f32x4(&vc.beta[16 * b0 + 4 * gq]);
-            const f32x4 gr1 = lds_f32x4(&vc.gam[16 * b1 + 4 * gq]);
-            const f32x4 br1 = lds_f32x4(&vc.beta[16 * b1 + 4 * gq]);
-            const float gi0 = vc.gam[16 * b0 + cl], gi1 = vc.gam[16 * b1 + cl];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int rl = 4 * gq + e;
-              a00[e] = cl < rl ? br0[e] * __expf(gr0[e] - gi0) * a00[e] : 0.f;
-              a11[e] = cl < rl ? br1[e] * __expf(gr1[e] - gi1) * a11[e] : 0.f;
-              a10[e] = br1[e] * __expf(gr1[e] - gi0) * a10[e];
-            }
-            *reinterpret_cast<f32x4 *>(&sm.at[b0 * AB + cl * LA + 4 * gq]) = a00;
-            *reinterpret_cast<f32x4 *>(&sm.at[b1 * AB + cl * LA + 4 * gq]) = a11;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sm.ao[half * AB + (4 * gq + e) * LA + cl] = a10[e];
+          // ---- A's diagonal blocks 0 and 1 and A_10 (wave 7 forms blocks 2 and 3 and A_32 and
+          //      publishes them through sm.ready; the bounded wait cannot hang)
+          a_half(Kt, vc, 0);
+          for (int it = 0; it < (1 << 22); ++it) {
+            const int r = __hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (__builtin_amdgcn_readfirstlane(r) >= c + 1) break;
+            __builtin_amdgcn_s_sleep(1);
           }
           // ---- the four diagonal inverses by substitution: lane (block gq, column cl)
           {
@@ -502,10 +552,10 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             for (int i = 0; i < 15; ++i) {
               float col[16];
 #pragma unroll
-              for (int q = (i + 1) >> 2; q < 4; ++q) {
-                const f32x4 v4 = lds_f32x4(ab + i * LA + 4 * q);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) col[4 * q + e] = v4[e];
+              for (int q = (i + 1) >> 1; q < 8; ++q) {
+                const float2 v2 = *reinterpret_cast<const float2 *>(ab + i * LA + 2 * q);
+                col[2 * q] = v2.x;
+                col[2 * q + 1] = v2.y;
               }
 #pragma unroll
               for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
@@ -513,14 +563,15 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.tt[gq * AB + r * LA + cl] = x[r];
           }
-          // ---- T_bb as bf16 into T_TL / T_BR: 4 rows of 4 columns per lane
+          // ---- T_bb diag(beta) as bf16 into T'_TL / T'_BR: 4 rows of 4 columns per lane
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
             const int idx = lane + 64 * it, b = idx >> 6, r = (idx >> 2) & 15, qd = idx & 3;
-            const f32x4 t4 = lds_f32x4(&sm.tt[b * AB + r * LA + 4 * qd]);
-            st4(&sm.tb[Y][b >> 1][boff(16 * (b & 1) + r, 4 * (b & 1) + qd)], t4);
+            const f32x4 t4 = ldf4(&sm.tt[b * AB + r * LA + 4 * qd]) * ldf4(&vc.beta[16 * b + 4 * qd]);
+            st8(&sm.tb[Y][b >> 1][boff(16 * (b & 1) + r, 4 * (b & 1) + qd)], t4);
           }
-          // ---- Tm_10 = -T_11 (A_10 T_00), Tm_32 = -T_33 (A_32 T_22), fp32 MFMA
+          // ---- Tm_10 = -T_11 (A_10 T_00), Tm_32 = -T_33 (A_32 T_22), fp32 MFMA, columns scaled
+          //      by beta
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
             const int b = 2 * q + 1, cb = 2 * q;
@@ -531,49 +582,49 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             f32x4 out = zero4();
 #pragma unroll
             for (int e = 0; e < 4; ++e) out = mma_f32(sm.tt[b * AB + cl * LA + 4 * gq + e], X[e], out);
+            const float bc = -vc.beta[16 * cb + cl];
+            bf16 *blk = reinterpret_cast<bf16 *>(sm.tb[Y][q]);
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              sm.tb[Y][q][boff(16 + 4 * gq + e, cl >> 2) + (cl & 3)] = (bf16)(-out[e]);
+              blk[(boff(16 + 4 * gq + e, cl >> 2) >> 1) + (cl & 3)] = (bf16)(bc * out[e]);
           }
         } else {
-          // ---- waves 5 and 6: the tiles of -A below the diagonal 32x32 blocks and P as bf16,
-          //      formed transposed (lane (row r, group) holds 4 consecutive columns i of row r);
-          //      wave 5 takes column blocks 0 and 3, wave 6 blocks 1 and 2 (7 tiles each)
+          // ---- waves 5 and 6: -A'_BL (A's lower-left 32x32 block without the beta row factor)
+          //      and P as bf16, formed transposed (lane (row r, group) holds 4 consecutive
+          //      columns i of row r); wave 5 takes column blocks 0 and 3, wave 6 blocks 1 and 2
 #pragma unroll
           for (int jj = 0; jj < 2; ++jj) {
             const int bj = wave == 5 ? 3 * jj : 1 + jj;
             bf16x8 fa[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) fa[ks] = kfrag(Kt, 16 * bj + cl, ks, gq);
-            f32x4 gi;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gi[e] = __shfl(gam, 16 * bj + 4 * gq + e, 64);
+            for (int ks = 0; ks < 4; ++ks) fa[ks] = kfrag(Kt, bj, ks);
+            const f32x4 gi = ldf4(&vc.gam[16 * bj + 4 * gq]);
             if (bj < 2) {
 #pragma unroll
               for (int bi = 2; bi < 4; ++bi) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Kt, 16 * bi + cl, ks, gq), acc);
+                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Kt, bi, ks), acc);
                 const int r = 16 * bi + cl;
-                const float gr = __shfl(gam, r, 64), br = __shfl(bv, r, 64);
+                const float gr = vc.gam[r];
                 f32x4 val;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = -br * __expf(gr - gi[e]) * acc[e];
-                st4(&sm.tb[Y][2][boff(r - 32, 4 * bj + gq)], val);
+                for (int e = 0; e < 4; ++e) val[e] = -__expf(gr - gi[e]) * acc[e];
+                st8(&sm.tb[Y][2][boff(r - 32, 4 * bj + gq)], val);
               }
             }
             if (emit) {
               for (int bi = bj; bi < 4; ++bi) {
                 f32x4 acc = zero4();
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Qt, 16 * bi + cl, ks, gq), acc);
+                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Qt, bi, ks), acc);
                 const int r = 16 * bi + cl;
-                const float gr = __shfl(gam, r, 64);
+                const float gr = vc.gam[r];
                 f32x4 val;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                   val[e] = (16 * bj + 4 * gq + e <= r) ? __expf(gr - gi[e]) * acc[e] : 0.f;
-                st4(&sm.p[Y][poff(r, 4 * bj + gq)], val);
+                st8(&sm.p[Y][poff(r, 4 * bj + gq)], val);
               }
             }
           }
