@@ -15,13 +15,16 @@
 // One barrier per chunk hands the prepared chunk over; chain waves never wait for each other
 // (each owns its columns of the state, of V and of the output).
 //
-// Delta by block forward substitution.  With Tm = [[T_TL, 0], [T_BL, T_BR]] over 32-token halves
-// and beta folded into the diagonal blocks' columns (T'_TL = T_TL diag(beta_T), likewise T'_BR)
-// and out of A's lower-left block's rows (A_BL = diag(beta_B) A'_BL):
-//     Delta_T = T'_TL R'_T,   Delta_B = T'_BR (R'_B - A'_BL Delta_T).
-// Prep therefore inverts only the two 32x32 diagonal blocks (four 16x16 inverses by
-// substitution on one wave, then Tm_10 = -T_11 A_10 T_00 and Tm_32 = -T_33 A_32 T_22 with fp32
-// MFMA) and never forms T_BL; the chain spends the same number of MFMAs as with the full Tm.
+// Delta by block forward substitution.  Split the chunk into 16-token blocks b = 0..3, write
+// T_b = (I + A_bb)^-1 for the diagonal blocks of (I + A), fold beta into their columns
+// (T'_b = T_b diag(beta_b)) and out of the rows of A's blocks below the diagonal
+// (A_bj = diag(beta_b) A'_bj).  Then (I + A) Delta = diag(beta) R' is solved block by block:
+//     Delta_0 = T'_0 R'_0,               Delta_1 = T'_1 (R'_1 - A'_10 Delta_0),
+//     Delta_2 = T'_2 (R'_2 - A'_20 Delta_0 - A'_21 Delta_1),
+//     Delta_3 = T'_3 (R'_3 - A'_30 Delta_0 - A'_31 Delta_1 - A'_32 Delta_2),
+// with the two 32-token corrections (A'_2j, A'_3j for j < 2) as one K = 32 product.  Prep only
+// inverts four 16x16 blocks (by substitution, on two waves) and never forms Tm's off-diagonal
+// blocks; the chain spends 16 MFMAs per 16 state columns on Delta (12 with a full Tm).
 //
 // The output is formed transposed, O^T = e^gamma-scaled (S^T Q^T) + Delta^T P^T, so each lane
 // holds 4 consecutive state columns of one token and writes them with one 8-byte store.
@@ -50,9 +53,11 @@ __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1
 __device__ __forceinline__ int toff(int r, int u) {
   return r * kRowBytes + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
 }
-// 32 x 32 bf16 blocks (T'_TL, T'_BR, -A'_BL): rows of 64 bytes, unit u of row r at
-// u ^ 2 ((r / 4) % 4)
+// 32 x 32 bf16 block (-A'_BL): rows of 64 bytes, unit u of row r at u ^ 2 ((r / 4) % 4)
 __device__ __forceinline__ int boff(int r, int u) { return r * 64 + ((u ^ (((r >> 2) & 3) << 1)) << 3); }
+// 16 x 16 bf16 blocks (T'_b, -A'_10, -A'_32): rows of 32 bytes, unit u of row r at
+// u ^ 2 ((r / 8) % 2)
+__device__ __forceinline__ int soff(int r, int u) { return r * 32 + ((u ^ (((r >> 3) & 1) << 1)) << 3); }
 // 64 x 64 bf16 P: rows of 128 bytes, unit u of row r at u ^ 2 ((r / 2) % 8)
 __device__ __forceinline__ int poff(int r, int u) { return r * 128 + ((u ^ (((r >> 1) & 7) << 1)) << 3); }
 
@@ -69,14 +74,19 @@ struct WsSmem {
   };
   alignas(16) char kq[3][2][64 * kRowBytes];  // [set][K, Q], three chunks in flight
   alignas(16) char v[64 * kRowBytes];         // V of the chunk on the chain (per wave: its columns)
-  alignas(16) char tb[2][3][32 * 64];         // [set][T'_TL, T'_BR, -A'_BL]
+  struct Blocks {
+    alignas(16) char t[4][16 * 32];  // T'_0 .. T'_3
+    alignas(16) char na10[16 * 32];  // -A'_10
+    alignas(16) char na32[16 * 32];  // -A'_32
+    alignas(16) char nabl[32 * 64];  // -A'_BL (rows 32..63, columns 0..31)
+  };
+  Blocks tb[2];
   alignas(16) char p[2][64 * 128];            // [set] P
   Vec vec[3];  // gate vectors: written one step ahead of prep, read by the chain a step later
   alignas(16) float at[4 * AB];  // A_bb transposed (row i = column i of A_bb), wave 4 only
-  alignas(16) float ao[2 * AB];  // A_10, A_32 row-major, wave 4 only
   alignas(16) float tt[4 * AB];  // T_bb row-major, wave 4 only
   alignas(16) int imisc[4];
-  int ready;  // chunk index + 1 whose A_22, A_33, A_32 (wave 7's part of A) are in at / ao
+  int ready;  // chunk index + 1 whose A_22, A_33 (wave 7's part) are in at
 };
 static_assert(sizeof(WsSmem) <= 160 * 1024, "LDS budget");
 
@@ -99,6 +109,26 @@ __device__ __forceinline__ int pin(int x) {
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The 16x16 tiles waves 5 and 6 form per chunk: tile t is K's row block bj[t] times the row block
+// bi[t] of K (q[t] == 0: A's blocks below the diagonal) or of Q (q[t] == 1: P).  Each wave's list
+// covers two column blocks (wave 5: 0 and 3, wave 6: 1 and 2), 8 tiles each.
+template <int W>
+struct PrepTiles;
+template <>
+struct PrepTiles<5> {
+  static constexpr int n = 8;
+  static constexpr int bj[8] = {0, 0, 0, 0, 0, 0, 0, 3};
+  static constexpr int bi[8] = {1, 2, 3, 0, 1, 2, 3, 3};
+  static constexpr int q[8] = {0, 0, 0, 1, 1, 1, 1, 1};
+};
+template <>
+struct PrepTiles<6> {
+  static constexpr int n = 8;
+  static constexpr int bj[8] = {1, 1, 2, 1, 1, 1, 2, 2};
+  static constexpr int bi[8] = {2, 3, 3, 1, 2, 3, 2, 3};
+  static constexpr int q[8] = {0, 0, 0, 1, 1, 1, 1, 1};
+};
 
 __device__ __forceinline__ void dma16(const char *g, char *l) {
   __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
@@ -136,12 +166,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const bf16 *__restrict__ gb_ = static_cast<const bf16 *>(a.beta);
   char *__restrict__ go_ = static_cast<char *>(a.o) + (int64_t)h * kRowBytes;
 
-  // Parts the chain reads but prep never writes: the upper-right 16x16 blocks of T'_TL and T'_BR,
-  // and P's tiles (0, 1) and (2, 3) above the diagonal.
-  for (int i = tid; i < 2 * 2 * 64; i += 512) {  // 8-byte units
-    const int set = i >> 7, blk = (i >> 6) & 1, r = (i >> 2) & 15, u = 4 + (i & 3);
-    *reinterpret_cast<uint2 *>(&sm.tb[set][blk][boff(r, u)]) = uint2{0u, 0u};
-  }
+  // P's tiles (0, 1) and (2, 3) above the diagonal are read by the chain but never written by prep.
   for (int i = tid; i < 2 * 2 * 64; i += 512) {
     const int set = i >> 7, t = (i >> 6) & 1, r = 32 * t + ((i >> 2) & 15), u = 8 * t + 4 + (i & 3);
     *reinterpret_cast<uint2 *>(&sm.p[set][poff(r, u)]) = uint2{0u, 0u};
@@ -174,16 +199,15 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     return ld16(t + 16 * m * kRowBytes + o_kf[ks][0], t + 16 * m * kRowBytes + o_kf[ks][1]);
   };
 
-  // Half `half` of A's diagonal-block tiles in fp32: the 16x16 blocks (b0, b0), (b1, b1) stored
-  // transposed into at, and (b1, b0) row-major into ao (b0 = 2 half, b1 = b0 + 1).
-  auto a_half = [&](const char *Kt, const WsSmem::Vec &vc, int half) {
+  // A's diagonal 16x16 blocks b0 = 2 half and b1 = b0 + 1 in fp32, stored transposed into at
+  // (row i of the stored block = column i of A_bb)
+  auto a_diag = [&](const char *Kt, const WsSmem::Vec &vc, int half) {
     const int b0 = 2 * half, b1 = b0 + 1;
-    f32x4 a00 = zero4(), a10 = zero4(), a11 = zero4();
+    f32x4 a00 = zero4(), a11 = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 f0 = kfrag(Kt, b0, ks), f1 = kfrag(Kt, b1, ks);
       a00 = mma_bf16(f0, f0, a00);
-      a10 = mma_bf16(f1, f0, a10);
       a11 = mma_bf16(f1, f1, a11);
     }
     const f32x4 gr0 = ldf4(&vc.gam[16 * b0 + 4 * gq]), br0 = ldf4(&vc.beta[16 * b0 + 4 * gq]);
@@ -194,15 +218,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       const int rl = 4 * gq + e;
       a00[e] = cl < rl ? br0[e] * __expf(gr0[e] - gi0) * a00[e] : 0.f;
       a11[e] = cl < rl ? br1[e] * __expf(gr1[e] - gi1) * a11[e] : 0.f;
-      a10[e] = br1[e] * __expf(gr1[e] - gi0) * a10[e];
     }
     float *t0p = &sm.at[b0 * AB + cl * LA + 4 * gq], *t1p = &sm.at[b1 * AB + cl * LA + 4 * gq];
     *reinterpret_cast<float2 *>(t0p) = float2{a00[0], a00[1]};
     *reinterpret_cast<float2 *>(t0p + 2) = float2{a00[2], a00[3]};
     *reinterpret_cast<float2 *>(t1p) = float2{a11[0], a11[1]};
     *reinterpret_cast<float2 *>(t1p + 2) = float2{a11[2], a11[3]};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sm.ao[half * AB + (4 * gq + e) * LA + cl] = a10[e];
   };
 
   const int w = wave & 3;
@@ -213,6 +234,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     // lane-constant offsets: transpose reads of K (rows 4 gq + cl / 4, unit 4 mt + cl % 4) and of
     // this wave's V columns, 32-wide block rows, P rows, the V tile store, and global offsets
     int o_tr[8], o_vtr[2], o_bf[2], o_pf[2][2];
+    const int o_sf = pin(soff(cl, gq));  // 16x16 block row cl, elements 4 gq .. 4 gq + 3
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o_tr[mt] = pin(toff(4 * gq + (cl >> 2), 4 * mt + (cl & 3)));
 #pragma unroll
@@ -337,49 +359,41 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         }
         v_store(vp);  // chunk cc + 1's V (this wave's columns of chunk cc are consumed)
 
-        // ---- Delta_T = T'_TL R'_T;  R'_B -= A'_BL Delta_T;  Delta_B = T'_BR R'_B.  Delta is kept
-        //      only as bf16 operand fragments: da for the output, dt = Delta o e^{gamma_last -
-        //      gamma} for the state update (both in the k-order of kfrag over tokens)
+        // ---- Delta block by block (see the head of this file).  Delta is kept only as bf16 operand
+        //      fragments: da for the output, dt = Delta o e^{gamma_last - gamma} for the state
+        //      update (both in the k-order of kfrag over tokens)
         bf16x8 da[2][2], dt[2][2];
         {
-          const char *TL = sm.tb[Y][0], *BR = sm.tb[Y][1], *NA = sm.tb[Y][2];
-          auto bfrag = [&](const char *t, int m) { return ld16(t + 1024 * m + o_bf[0], t + 1024 * m + o_bf[1]); };
-          f32x4 Dl[2][2];
-          bf16x8 rb[2];
+          const WsSmem::Blocks &B = sm.tb[Y];
+          auto sfrag = [&](const char *blk) { return ld8(blk + o_sf); };
+          auto bfrag = [&](int m) { return ld16(B.nabl + 1024 * m + o_bf[0], B.nabl + 1024 * m + o_bf[1]); };
+          // one 32-token half: Delta_{2h} = T'_{2h} R'_{2h}, Delta_{2h+1} = T'_{2h+1} (R'_{2h+1} -
+          // A'_{2h+1,2h} Delta_{2h})
+          auto half_solve = [&](int hb, const char *na) {
+            const bf16x4 t0 = sfrag(B.t[2 * hb]), t1 = sfrag(B.t[2 * hb + 1]), nf = sfrag(na);
+            f32x4 Dl0[2], Dl1[2];
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) rb[nt] = to_bf16x8(R[0][nt], R[1][nt]);
+            for (int nt = 0; nt < 2; ++nt) Dl0[nt] = mma_bf16_k16(t0, to_bf16x4(R[2 * hb][nt]), zero4());
 #pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 af = bfrag(TL, mt);
+            for (int nt = 0; nt < 2; ++nt)
+              R[2 * hb + 1][nt] = mma_bf16_k16(nf, to_bf16x4(Dl0[nt]), R[2 * hb + 1][nt]);
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Dl[mt][nt] = mma_bf16(af, rb[nt], zero4());
-          }
-          const f32x4 e00 = ldf4(&vc.edt[4 * gq]), e01 = ldf4(&vc.edt[16 + 4 * gq]);
+            for (int nt = 0; nt < 2; ++nt) Dl1[nt] = mma_bf16_k16(t1, to_bf16x4(R[2 * hb + 1][nt]), zero4());
+            const f32x4 e0 = ldf4(&vc.edt[32 * hb + 4 * gq]), e1 = ldf4(&vc.edt[32 * hb + 16 + 4 * gq]);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            da[0][nt] = to_bf16x8(Dl[0][nt], Dl[1][nt]);
-            dt[0][nt] = to_bf16x8(Dl[0][nt] * e00, Dl[1][nt] * e01);
-          }
+            for (int nt = 0; nt < 2; ++nt) {
+              da[hb][nt] = to_bf16x8(Dl0[nt], Dl1[nt]);
+              dt[hb][nt] = to_bf16x8(Dl0[nt] * e0, Dl1[nt] * e1);
+            }
+          };
+          half_solve(0, B.na10);
 #pragma unroll
-          for (int mt = 2; mt < 4; ++mt) {
-            const bf16x8 af = bfrag(NA, mt - 2);
+          for (int mt = 2; mt < 4; ++mt) {  // R'_B -= A'_BL Delta_T
+            const bf16x8 af = bfrag(mt - 2);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) R[mt][nt] = mma_bf16(af, da[0][nt], R[mt][nt]);
           }
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) rb[nt] = to_bf16x8(R[2][nt], R[3][nt]);
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) {
-            const bf16x8 af = bfrag(BR, mt);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) Dl[mt][nt] = mma_bf16(af, rb[nt], zero4());
-          }
-          const f32x4 e10 = ldf4(&vc.edt[32 + 4 * gq]), e11 = ldf4(&vc.edt[48 + 4 * gq]);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            da[1][nt] = to_bf16x8(Dl[0][nt], Dl[1][nt]);
-            dt[1][nt] = to_bf16x8(Dl[0][nt] * e10, Dl[1][nt] * e11);
-          }
+          half_solve(1, B.na32);
         }
 
         // ---- output, transposed: O^T = scale (e^gamma (S^T Q^T) + Delta^T P^T)
@@ -509,8 +523,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     wait_vm0();
     __syncthreads();
     for (int c = cw; c <= c1; ++c) {
-      if (c < c1) {  // A's diagonal blocks 2 and 3 and A_32 of the chunk prep works on
-        a_half(sm.kq[c % 3][0], sm.vec[c % 3], 1);
+      if (c < c1) {  // A's diagonal blocks 2 and 3 of the chunk prep works on
+        a_diag(sm.kq[c % 3][0], sm.vec[c % 3], 1);
         __hip_atomic_store(&sm.ready, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       if (c + 1 < c1) {
@@ -534,9 +548,9 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const char *Kt = sm.kq[c % 3][0], *Qt = sm.kq[c % 3][1];
         const WsSmem::Vec &vc = sm.vec[c % 3];
         if (wave == 4) {
-          // ---- A's diagonal blocks 0 and 1 and A_10 (wave 7 forms blocks 2 and 3 and A_32 and
-          //      publishes them through sm.ready; the bounded wait cannot hang)
-          a_half(Kt, vc, 0);
+          // ---- A's diagonal blocks 0 and 1 (wave 7 forms blocks 2 and 3 and publishes them
+          //      through sm.ready; the bounded wait cannot hang)
+          a_diag(Kt, vc, 0);
           for (int it = 0; it < (1 << 22); ++it) {
             const int r = __hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (__builtin_amdgcn_readfirstlane(r) >= c + 1) break;
@@ -563,71 +577,73 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.tt[gq * AB + r * LA + cl] = x[r];
           }
-          // ---- T_bb diag(beta) as bf16 into T'_TL / T'_BR: 4 rows of 4 columns per lane
+          // ---- T'_b = T_b diag(beta_b) as bf16: 4 rows of 4 columns per lane
 #pragma unroll
           for (int it = 0; it < 4; ++it) {
             const int idx = lane + 64 * it, b = idx >> 6, r = (idx >> 2) & 15, qd = idx & 3;
             const f32x4 t4 = ldf4(&sm.tt[b * AB + r * LA + 4 * qd]) * ldf4(&vc.beta[16 * b + 4 * qd]);
-            st8(&sm.tb[Y][b >> 1][boff(16 * (b & 1) + r, 4 * (b & 1) + qd)], t4);
-          }
-          // ---- Tm_10 = -T_11 (A_10 T_00), Tm_32 = -T_33 (A_32 T_22), fp32 MFMA, columns scaled
-          //      by beta
-#pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int b = 2 * q + 1, cb = 2 * q;
-            f32x4 X = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-              X = mma_f32(sm.ao[q * AB + cl * LA + 4 * s + gq], sm.tt[cb * AB + (4 * s + gq) * LA + cl], X);
-            f32x4 out = zero4();
-#pragma unroll
-            for (int e = 0; e < 4; ++e) out = mma_f32(sm.tt[b * AB + cl * LA + 4 * gq + e], X[e], out);
-            const float bc = -vc.beta[16 * cb + cl];
-            bf16 *blk = reinterpret_cast<bf16 *>(sm.tb[Y][q]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              blk[(boff(16 + 4 * gq + e, cl >> 2) >> 1) + (cl & 3)] = (bf16)(bc * out[e]);
+            st8(&sm.tb[Y].t[b][soff(r, qd)], t4);
           }
         } else {
-          // ---- waves 5 and 6: -A'_BL (A's lower-left 32x32 block without the beta row factor)
-          //      and P as bf16, formed transposed (lane (row r, group) holds 4 consecutive
-          //      columns i of row r); wave 5 takes column blocks 0 and 3, wave 6 blocks 1 and 2
+          // ---- waves 5 and 6: A's 16x16 blocks below the diagonal without their beta row factor,
+          //      negated (-A'_10, -A'_32 and the lower-left 32x32 block -A'_BL), and P, as bf16.
+          //      Tiles are formed transposed (lane (row r, group) holds 4 consecutive columns i
+          //      of row r), all of a wave's tiles at once over the four k-steps so that their
+          //      fragment loads and MFMAs overlap.
+          auto run = [&](auto tiles) {
+            using PT = decltype(tiles);
+            f32x4 acc[PT::n];
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) {
-            const int bj = wave == 5 ? 3 * jj : 1 + jj;
-            bf16x8 fa[4];
+            for (int t = 0; t < PT::n; ++t) acc[t] = zero4();
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) fa[ks] = kfrag(Kt, bj, ks);
-            const f32x4 gi = ldf4(&vc.gam[16 * bj + 4 * gq]);
-            if (bj < 2) {
+            for (int ks = 0; ks < 4; ++ks) {
+              bf16x8 kf4[4], qf4[4];
 #pragma unroll
-              for (int bi = 2; bi < 4; ++bi) {
-                f32x4 acc = zero4();
+              for (int b = 0; b < 4; ++b) {
+                bool needk = false, needq = false;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Kt, bi, ks), acc);
-                const int r = 16 * bi + cl;
-                const float gr = vc.gam[r];
-                f32x4 val;
+                for (int t = 0; t < PT::n; ++t) {
+                  needk |= PT::bj[t] == b || (PT::q[t] == 0 && PT::bi[t] == b);
+                  needq |= PT::q[t] == 1 && PT::bi[t] == b;
+                }
+                if (needk) kf4[b] = kfrag(Kt, b, ks);
+                if (needq && emit) qf4[b] = kfrag(Qt, b, ks);
+              }
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = -__expf(gr - gi[e]) * acc[e];
-                st8(&sm.tb[Y][2][boff(r - 32, 4 * bj + gq)], val);
+              for (int t = 0; t < PT::n; ++t) {
+                if (PT::q[t] == 0)
+                  acc[t] = mma_bf16(kf4[PT::bj[t]], kf4[PT::bi[t]], acc[t]);
+                else if (emit)
+                  acc[t] = mma_bf16(kf4[PT::bj[t]], qf4[PT::bi[t]], acc[t]);
               }
             }
-            if (emit) {
-              for (int bi = bj; bi < 4; ++bi) {
-                f32x4 acc = zero4();
+            WsSmem::Blocks &B = sm.tb[Y];
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fa[ks], kfrag(Qt, bi, ks), acc);
-                const int r = 16 * bi + cl;
-                const float gr = vc.gam[r];
-                f32x4 val;
+            for (int t = 0; t < PT::n; ++t) {
+              const int bj = PT::bj[t], bi = PT::bi[t];
+              if (PT::q[t] == 1 && !emit) continue;
+              const f32x4 gi = ldf4(&vc.gam[16 * bj + 4 * gq]);
+              const int r = 16 * bi + cl;
+              const float gr = vc.gam[r];
+              f32x4 val;
+              if (PT::q[t] == 0) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) val[e] = -__expf(gr - gi[e]) * acc[t][e];
+                char *dst = bi == 1 ? B.na10 + soff(cl, gq)
+                            : (bj == 2 ? B.na32 + soff(cl, gq) : B.nabl + boff(r - 32, 4 * bj + gq));
+                st8(dst, val);
+              } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  val[e] = (16 * bj + 4 * gq + e <= r) ? __expf(gr - gi[e]) * acc[e] : 0.f;
+                  val[e] = (16 * bj + 4 * gq + e <= r) ? __expf(gr - gi[e]) * acc[t][e] : 0.f;
                 st8(&sm.p[Y][poff(r, 4 * bj + gq)], val);
               }
             }
-          }
+          };
+          if (wave == 5)
+            run(PrepTiles<5>{});
+          else
+            run(PrepTiles<6>{});
         }
       }
       __syncthreads();
