@@ -68,6 +68,7 @@ struct WsSmem {
   struct Vec {
     alignas(16) float beta[64];
     alignas(16) float eg[64];   // e^gamma
+    alignas(16) float ego[64];
     alignas(16) float edt[64];  // e^(gamma_last - gamma)
     alignas(16) float gam[64];
     alignas(16) float egl[4];   // e^gamma_last
@@ -411,7 +412,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             for (int ks = 0; ks < 2; ++ks)
               if (ks <= (tt >> 1))
                 pf[ks] = ld16(P + 2048 * tt + o_pf[ks][0], P + 2048 * tt + o_pf[ks][1]);
-            const float et = vc.eg[16 * tt + cl];
+            const float et = vc.ego[16 * tt + cl];
             char *orow = go_ + (t0 + 16 * tt) * tok_bytes + o_go;
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
@@ -422,7 +423,6 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
               for (int ks = 0; ks < 2; ++ks)
                 if (ks <= (tt >> 1)) acc = mma_bf16(da[ks][nt], pf[ks], acc);
-              acc *= a.scale;
               if (16 * tt + cl < n) *reinterpret_cast<bf16x4 *>(orow + 32 * nt) = to_bf16x4(acc);
             }
           }
@@ -507,6 +507,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       WsSmem::Vec &vc = sm.vec[c % 3];
       vc.beta[lane] = bv;
       vc.eg[lane] = __expf(gam);
+      vc.ego[lane] = a.scale * __expf(gam);
       vc.edt[lane] = __expf(gl - gam);
       vc.gam[lane] = gam;
       if (lane == 0) vc.egl[0] = __expf(gl);
@@ -635,7 +636,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  val[e] = (16 * bj + 4 * gq + e <= r) ? __expf(gr - gi[e]) * acc[t][e] : 0.f;
+                  val[e] = (16 * bj + 4 * gq + e <= r) ? a.scale * __expf(gr - gi[e]) * acc[t][e] : 0.f;
                 st8(&sm.p[Y][poff(r, 4 * bj + gq)], val);
               }
             }

@@ -9,15 +9,27 @@ namespace gdn {
 // Warmup window of a segment starting at chunk c0 > 0 of its sequence ("Lever 1"): whole
 // preceding chunks are added one at a time (c0-1, c0-2, ...) until their summed g is below
 // thr; returns the window's first chunk (0 when it reaches the sequence start).  One full
-// wave calls it; sums are formed in fp64 and are identical on every lane.
+// wave calls it; each chunk's sum is formed in fp64 by the same lane-tree on every lane, and
+// the chunks are added in order, four chunks' loads in flight at a time.
 __device__ inline int warm_window(const float *__restrict__ g, int64_t ts0, int c0, int h, int H,
-                           float thr, int lane) {
+                                  float thr, int lane) {
   double acc = 0.0;
   int w = c0;
   while (w > 0 && !(acc < (double)thr)) {
-    --w;
-    const int64_t t = ts0 + (int64_t)w * kChunk + lane;
-    acc += wave_sum_f64((double)g[t * H + h]);
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // chunks w - 1 .. w - 4 (those below 0 are not used)
+      const int cj = max(w - 1 - j, 0);
+      x[j] = g[(ts0 + (int64_t)cj * kChunk + lane) * H + h];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double sj = wave_sum_f64((double)x[j]);
+      if (w > 0 && !(acc < (double)thr)) {
+        --w;
+        acc += sj;
+      }
+    }
   }
   return w;
 }
