@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device copies of MIB MiB each (reads and writes MIB MiB per "
+                         "launch): the reference for scaling HBM traffic counters, then exit")
     return ap.parse_args()
 
 
@@ -98,8 +101,23 @@ def cpu_baseline(inp):
                       f"{dt:.2f} s wall on {threads} of {cores} host threads"}
 
 
+def copy_calibration(mib):
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_mib": mib, "launches": 5}), flush=True)
+    return 0
+
+
 def main():
     args = parse()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration)
     if args.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (--gpus {args.gpus} "
               "not supported; heads and documents shard across GPUs without communication).",
