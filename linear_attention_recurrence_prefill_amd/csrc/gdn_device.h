@@ -49,8 +49,15 @@ __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// Round to nearest even.  Converted in pairs so that each pair packs into one dword with one
+// instruction (a 4-wide conversion is split into single conversions and byte permutes when its
+// result is reinterpreted as integers).
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
-  return bf16x4{(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 lo = __builtin_convertvector((f32x2{x[0], x[1]}), bf16x2);
+  const bf16x2 hi = __builtin_convertvector((f32x2{x[2], x[3]}), bf16x2);
+  return __builtin_bit_cast(bf16x4, (uint2{__builtin_bit_cast(unsigned, lo), __builtin_bit_cast(unsigned, hi)}));
 }
 
 __device__ __forceinline__ bf16x8 to_bf16x8(f32x4 a, f32x4 b) {

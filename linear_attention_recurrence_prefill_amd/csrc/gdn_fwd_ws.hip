@@ -26,13 +26,18 @@
 // inverts four 16x16 blocks (by substitution, on two waves) and never forms Tm's off-diagonal
 // blocks; the chain spends 16 MFMAs per 16 state columns on Delta (12 with a full Tm).
 //
-// The output is formed transposed, O^T = e^gamma-scaled (S^T Q^T) + Delta^T P^T, so each lane
-// holds 4 consecutive state columns of one token and writes them with one 8-byte store.
+// The output is formed transposed, O^T = (S^T Q^T) diag(scale e^gamma) + Delta^T P^T (P carries
+// the scale), so each lane holds 4 consecutive state columns of one token and writes them with
+// one 8-byte store.  The stores go through a buffer resource whose range ends at the chunk's last
+// token, so a ragged chunk needs no branch: the hardware drops the stores past its end.
 //
 // Addressing.  Every swizzled LDS access is a lane-constant byte offset (computed once, held in a
 // register) plus an immediate: the swizzles depend on the row only modulo 16, and rows enter in
 // multiples of 16.  Global loads and stores likewise use a uniform base and a lane-constant
-// offset; only a sequence's ragged last chunk takes the per-lane clamped path.
+// offset; only a sequence's ragged last chunk takes the per-lane clamped path.  The 16-row blocks
+// of the K and Q tiles sit 16 bytes further apart than their size: reads of two blocks at the
+// same lane offset would otherwise be fused into one two-address LDS read, which is issued as two
+// passes over the same banks (twice the cycles of two single reads).
 #include "gdn_device.h"
 #include "gdn_internal.h"
 #include "gdn_tiles.h"
@@ -43,6 +48,8 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;  // one bf16 row of a K, Q or V tile
+constexpr int kBlk = 16 * kRowBytes + 16;  // stride of the 16-row blocks of the K and Q tiles
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 // 64 x 128 bf16 tiles (K, Q, V): rows of 256 bytes; the 16-byte unit c of row r is stored at unit
 // c ^ sw(r).  For the reads below (16 lanes on one 8-byte unit of 16 consecutive rows, or
@@ -68,12 +75,12 @@ struct WsSmem {
   struct Vec {
     alignas(16) float beta[64];
     alignas(16) float eg[64];   // e^gamma
-    alignas(16) float ego[64];
+    alignas(16) float ego[64];  // scale e^gamma
     alignas(16) float edt[64];  // e^(gamma_last - gamma)
     alignas(16) float gam[64];
     alignas(16) float egl[4];   // e^gamma_last
   };
-  alignas(16) char kq[3][2][64 * kRowBytes];  // [set][K, Q], three chunks in flight
+  alignas(16) char kq[3][2][4 * kBlk];  // [set][K, Q], three chunks in flight
   alignas(16) char v[64 * kRowBytes];         // V of the chunk on the chain (per wave: its columns)
   struct Blocks {
     alignas(16) char t[4][16 * 32];  // T'_0 .. T'_3
@@ -197,7 +204,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) o_kf[ks][hf] = pin(toff(cl, 8 * ks + 4 * hf + gq));
   auto kfrag = [&](const char *t, int m, int ks) {
-    return ld16(t + 16 * m * kRowBytes + o_kf[ks][0], t + 16 * m * kRowBytes + o_kf[ks][1]);
+    return ld16(t + m * kBlk + o_kf[ks][0], t + m * kBlk + o_kf[ks][1]);
   };
 
   // A's diagonal 16x16 blocks b0 = 2 half and b1 = b0 + 1 in fp32, stored transposed into at
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     const int o_vst = pin(vr * kRowBytes + ((vc16 ^ sw(vr)) << 4));
     const int o_gv = pin((int)(vr * tok_bytes) + vc16 * 16);                // V loads
     const int o_go = pin((int)(cl * tok_bytes) + (ncol + 4 * gq) * 2);      // O stores
-    auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + rows * kRowBytes + o_tr[mt]); };
+    auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + (rows / 16) * kBlk + o_tr[mt]); };
 
     // S[mt][nt] holds rows 16 mt + 4 gq + i, column ncol + 16 nt + cl
     f32x4 S[8][2];
@@ -397,33 +404,48 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           half_solve(1, B.na32);
         }
 
-        // ---- output, transposed: O^T = scale (e^gamma (S^T Q^T) + Delta^T P^T)
+        // ---- output, transposed: O^T = (S^T Q^T) diag(scale e^gamma) + Delta^T P^T
         if (emit) {
           const char *P = sm.p[Y];
-          bf16x8 sb[4][2];
-          state_frags(sb);
+          float et[4];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) et[tt] = vc.ego[16 * tt + cl];
+          f32x4 acc[4][2];
+#pragma unroll
+          for (int tt = 0; tt < 4; ++tt) acc[tt][0] = acc[tt][1] = zero4();
+          // e^gamma-scaled S^T Q^T, one k-step of all 8 (token block, column block) tiles at a time
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 sbk[2];
+#pragma unroll
+            for (int nt = 0; nt < 2; ++nt) sbk[nt] = to_bf16x8(S[2 * ks][nt], S[2 * ks + 1][nt]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+              const bf16x8 qf = kfrag(Qt, tt, ks);
+#pragma unroll
+              for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mma_bf16(sbk[nt], qf, acc[tt][nt]);
+            }
+          }
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) {
-            bf16x8 qf[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) qf[ks] = kfrag(Qt, tt, ks);
-            bf16x8 pf[2];
+            for (int nt = 0; nt < 2; ++nt) acc[tt][nt] *= et[tt];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
-              if (ks <= (tt >> 1))
-                pf[ks] = ld16(P + 2048 * tt + o_pf[ks][0], P + 2048 * tt + o_pf[ks][1]);
-            const float et = vc.ego[16 * tt + cl];
-            char *orow = go_ + (t0 + 16 * tt) * tok_bytes + o_go;
+              if (ks <= (tt >> 1)) {
+                const bf16x8 pf = ld16(P + 2048 * tt + o_pf[ks][0], P + 2048 * tt + o_pf[ks][1]);
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) acc[tt][nt] = mma_bf16(da[ks][nt], pf, acc[tt][nt]);
+              }
+            // rows of the 16-token block at or past the chunk's end fall outside the buffer range
+            // and are dropped by the store
+            const int nrows = max(0, n - 16 * tt);
+            const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
+                go_ + (t0 + 16 * tt) * tok_bytes, (short)0, nrows * (int)tok_bytes, 0x00020000);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
-              f32x4 acc = zero4();
-#pragma unroll
-              for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(sb[ks][nt], qf[ks], acc);
-              acc *= et;
-#pragma unroll
-              for (int ks = 0; ks < 2; ++ks)
-                if (ks <= (tt >> 1)) acc = mma_bf16(da[ks][nt], pf[ks], acc);
-              if (16 * tt + cl < n) *reinterpret_cast<bf16x4 *>(orow + 32 * nt) = to_bf16x4(acc);
+              const bf16x4 o4 = to_bf16x4(acc[tt][nt]);
+              __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const i32x2 *>(&o4), ob, o_go + 32 * nt, 0, 0);
             }
           }
         }
@@ -474,13 +496,13 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (n == kChunk) {
         const char *base = src + t0 * tok_bytes;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) dma16(base + o_dma[j], dst + 1024 * j);
+        for (int j = 0; j < 16; ++j) dma16(base + o_dma[j], dst + (j >> 2) * kBlk + 1024 * (j & 3));
       } else {  // ragged last chunk: rows past n repeat the last token
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
           const int r = 4 * j + (lane >> 4);
           const int64_t t = t0 + min(r, n - 1);
-          dma16(src + t * tok_bytes + (((lane & 15) ^ sw(r)) << 4), dst + 1024 * j);
+          dma16(src + t * tok_bytes + (((lane & 15) ^ sw(r)) << 4), dst + (j >> 2) * kBlk + 1024 * (j & 3));
         }
       }
     };
