@@ -23,6 +23,11 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
              "-munsafe-fp-atomics"]
 
 
+# Per-source additions.  The pipelined forward kernel is latency-bound on one wave per SIMD; the
+# ILP-first scheduler interleaves its independent MFMA chains and loads better than the default.
+EXTRA_FLAGS = {"gdn_fwd_ws.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -42,8 +47,8 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
             continue
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmd = [hipcc, *HIP_FLAGS, *lang, "-I", os.path.join(ROOT, "include"), "-c", path,
-               "-o", obj]
+        cmd = [hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), *lang, "-I",
+               os.path.join(ROOT, "include"), "-c", path, "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT),

@@ -12,8 +12,10 @@
 // the "chain".  A workgroup has eight waves: waves 0-3 run the chain, wave w owning state columns
 // [32 w, 32 w + 32); waves 4-6 prep chunk c + 1 while the chain runs chunk c; wave 7 forms chunk
 // c + 2's gate vectors and streams its K and Q from HBM into LDS with direct global->LDS loads.
-// One barrier per chunk hands the prepared chunk over; chain waves never wait for each other
-// (each owns its columns of the state, of V and of the output).
+// Each chain wave streams its own columns of the next chunk's V the same way, into a tile only it
+// reads.  One barrier per chunk hands the prepared chunk over; chain waves never wait for each
+// other (each owns its columns of the state, of V and of the output), and their barrier waits for
+// LDS accesses only, not for their global stores and loads.
 //
 // Delta by block forward substitution.  Split the chunk into 16-token blocks b = 0..3, write
 // T_b = (I + A_bb)^-1 for the diagonal blocks of (I + A), fold beta into their columns
@@ -81,7 +83,6 @@ struct WsSmem {
     alignas(16) float egl[4];   // e^gamma_last
   };
   alignas(16) char kq[3][2][4 * kBlk];  // [set][K, Q], three chunks in flight
-  alignas(16) char v[64 * kRowBytes];         // V of the chunk on the chain (per wave: its columns)
   struct Blocks {
     alignas(16) char t[4][16 * 32];  // T'_0 .. T'_3
     alignas(16) char na10[16 * 32];  // -A'_10
@@ -117,6 +118,15 @@ __device__ __forceinline__ int pin(int x) {
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// A workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes are complete
+// before it (lgkmcnt(0)); its global loads and stores may still be in flight.  The signal fences
+// keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // The 16x16 tiles waves 5 and 6 form per chunk: tile t is K's row block bj[t] times the row block
 // bi[t] of K (q[t] == 0: A's blocks below the diagonal) or of Q (q[t] == 1: P).  Each wave's list
@@ -146,6 +156,10 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
+  // V of the chunk on the chain, per chain wave its 32 columns: 64 rows of 64 bytes, the 16-byte
+  // unit u of row r at unit u ^ 2 ((r / 4) % 2).  A variable of its own, so that the compiler
+  // knows the chain waves' direct loads into it cannot touch the tiles they read meanwhile.
+  __shared__ __attribute__((aligned(16))) char vt_s[4][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   // wave-uniform role (scalar branches: a wave never steps through the other role's barriers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -246,16 +260,21 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o_tr[mt] = pin(toff(4 * gq + (cl >> 2), 4 * mt + (cl & 3)));
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) o_vtr[nt] = pin(toff(4 * gq + (cl >> 2), 8 * w + 4 * nt + (cl & 3)));
+    for (int nt = 0; nt < 2; ++nt) {
+      const int r = 4 * gq + (cl >> 2), u = 4 * nt + (cl & 3);
+      o_vtr[nt] = pin(r * 64 + (((u >> 1) ^ (((r >> 2) & 1) << 1)) << 4) + ((u & 1) << 3));
+    }
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) o_bf[hf] = pin(boff(cl, 4 * hf + gq));
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) o_pf[ks][hf] = pin(poff(cl, 8 * ks + 4 * hf + gq));
-    const int vr = lane >> 2, vc16 = 4 * w + (lane & 3);  // V rows 16 j + vr, 16-byte unit vc16
-    const int o_vst = pin(vr * kRowBytes + ((vc16 ^ sw(vr)) << 4));
-    const int o_gv = pin((int)(vr * tok_bytes) + vc16 * 16);                // V loads
+    // direct V loads: instruction j fills rows 16 j .. 16 j + 15 of this wave's V tile; lane l
+    // writes physical unit l % 4 of row 16 j + l / 4, which holds logical unit (l % 4) ^ 2 ((l / 16) % 2)
+    char *const vw = vt_s[w];
+    const int vu = 4 * w + ((lane & 3) ^ (((lane >> 4) & 1) << 1));
+    const int o_gv = pin((int)((lane >> 2) * tok_bytes) + vu * 16);
     const int o_go = pin((int)(cl * tok_bytes) + (ncol + 4 * gq) * 2);      // O stores
     auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + (rows / 16) * kBlk + o_tr[mt]); };
 
@@ -279,34 +298,20 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) S[mt][0] = S[mt][1] = zero4();
     }
-    // V rows of chunk c for this wave's columns (rows past a ragged chunk's end repeat its last
-    // token), and their store into the swizzled V tile
-    struct VRows {
-      uint4 x[4];
-    };
-    auto v_load = [&](int c) {
+    // V of chunk c for this wave's columns into its V tile (rows past a ragged chunk's end repeat
+    // its last token)
+    auto v_dma = [&](int c) {
       const int64_t t0 = chunk_t0(c);
       const int n = chunk_n(c);
-      VRows vp;
       if (n == kChunk) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          vp.x[j] = *reinterpret_cast<const uint4 *>(gv_ + (t0 + 16 * j) * tok_bytes + o_gv);
+        for (int j = 0; j < 4; ++j) dma16(gv_ + (t0 + 16 * j) * tok_bytes + o_gv, vw + 1024 * j);
       } else {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int64_t t = t0 + min(16 * j + vr, n - 1);
-          vp.x[j] = *reinterpret_cast<const uint4 *>(gv_ + t * tok_bytes + vc16 * 16);
+          const int64_t t = t0 + min(16 * j + (lane >> 2), n - 1);
+          dma16(gv_ + t * tok_bytes + vu * 16, vw + 1024 * j);
         }
-      }
-      return vp;
-    };
-    auto v_store = [&](const VRows &vp) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        char *p = sm.v + 16 * j * kRowBytes + o_vst;
-        *reinterpret_cast<uint2 *>(p) = uint2{vp.x[j].x, vp.x[j].y};
-        *reinterpret_cast<uint2 *>(p + 8) = uint2{vp.x[j].z, vp.x[j].w};
       }
     };
     // the state as bf16 operand fragments, in the k-order of kfrag
@@ -317,15 +322,10 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         for (int nt = 0; nt < 2; ++nt) sb[ks][nt] = to_bf16x8(S[2 * ks][nt], S[2 * ks + 1][nt]);
     };
 
-    // V of the first chunk goes to LDS now; the next chunk's V is held in registers until the
-    // first chunk's residual has consumed the V tile (loads run one chunk ahead of their store).
-    // The loads and stores are unconditional (past the unit's last chunk they repeat it, and
-    // rewriting a V tile with its own contents is harmless), so no wait is placed on them
-    // anywhere but at the store.
-    VRows vp{};
-    if (cw < c1) v_store(v_load(cw));
-    wait_vm0();  // the initial state is in registers: no load is outstanding when the loop starts
-    if (cw < c1) vp = v_load(min(cw + 1, c1 - 1));
+    // V of the first chunk; each later chunk's V is loaded once the chunk before it has consumed
+    // the tile (the compiler waits for the direct loads before the tile is read)
+    if (cw < c1) v_dma(cw);
+    wait_vm0();  // the initial state and V are in place: no load is outstanding when the loop starts
     __syncthreads();  // chunk cw's K and Q are in LDS (wave 7)
 
     for (int c = cw; c <= c1; ++c) {
@@ -355,17 +355,26 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               for (int nt = 0; nt < 2; ++nt) R[mt][nt] = mma_bf16(af, sb[ks][nt], R[mt][nt]);
             }
         }
+        // this chunk's V, loaded directly into the tile a step ago, has landed
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        wait_vm0();
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 ee = ldf4(&vc.eg[16 * mt + 4 * gq]);
+          const f32x4 ee = *reinterpret_cast<const f32x4 *>(&vc.eg[16 * mt + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
-            const bf16x4 v4 = ldtr(sm.v + 16 * mt * kRowBytes + o_vtr[nt]);
+            const bf16x4 v4 = ldtr(vw + 1024 * mt + o_vtr[nt]);
 #pragma unroll
             for (int i = 0; i < 4; ++i) R[mt][nt][i] = (float)v4[i] - ee[i] * R[mt][nt][i];
           }
         }
-        v_store(vp);  // chunk cc + 1's V (this wave's columns of chunk cc are consumed)
+        // chunk cc + 1's V into the tile once every read of chunk cc's V has returned (the compiler
+        // does not order the transpose reads against the direct loads by itself)
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __atomic_signal_fence(__ATOMIC_SEQ_CST);
+        if (cc + 1 < c1) v_dma(cc + 1);
 
         // ---- Delta block by block (see the head of this file).  Delta is kept only as bf16 operand
         //      fragments: da for the output, dt = Delta o e^{gamma_last - gamma} for the state
@@ -387,7 +396,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               R[2 * hb + 1][nt] = mma_bf16_k16(nf, to_bf16x4(Dl0[nt]), R[2 * hb + 1][nt]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Dl1[nt] = mma_bf16_k16(t1, to_bf16x4(R[2 * hb + 1][nt]), zero4());
-            const f32x4 e0 = ldf4(&vc.edt[32 * hb + 4 * gq]), e1 = ldf4(&vc.edt[32 * hb + 16 + 4 * gq]);
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               da[hb][nt] = to_bf16x8(Dl0[nt], Dl1[nt]);
@@ -450,7 +460,6 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           }
         }
 
-        vp = v_load(min(cc + 2, c1 - 1));
 
         // ---- state update: h <- e^{gamma_last} h + K^T diag(e^{gamma_last - gamma}) Delta
         {
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
     }
 
     if (a.ht != nullptr && c1 == nchunks_seq) {
@@ -585,18 +594,20 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) x[r] = r == cl ? 1.f : 0.f;
+            // all of the block's columns first (the loads do not depend on the substitution)
+            float col[15][16];
 #pragma unroll
-            for (int i = 0; i < 15; ++i) {
-              float col[16];
+            for (int i = 0; i < 15; ++i)
 #pragma unroll
               for (int q = (i + 1) >> 1; q < 8; ++q) {
                 const float2 v2 = *reinterpret_cast<const float2 *>(ab + i * LA + 2 * q);
-                col[2 * q] = v2.x;
-                col[2 * q + 1] = v2.y;
+                col[i][2 * q] = v2.x;
+                col[i][2 * q + 1] = v2.y;
               }
 #pragma unroll
-              for (int r = i + 1; r < 16; ++r) x[r] -= col[r] * x[i];
-            }
+            for (int i = 0; i < 15; ++i)
+#pragma unroll
+              for (int r = i + 1; r < 16; ++r) x[r] -= col[i][r] * x[i];
 #pragma unroll
             for (int r = 0; r < 16; ++r) sm.tt[gq * AB + r * LA + cl] = x[r];
           }
