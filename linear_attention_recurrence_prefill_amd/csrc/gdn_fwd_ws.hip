@@ -29,9 +29,11 @@
 // blocks; the chain spends 16 MFMAs per 16 state columns on Delta (12 with a full Tm).
 //
 // The output is formed transposed, O^T = (S^T Q^T) diag(scale e^gamma) + Delta^T P^T (P carries
-// the scale), so each lane holds 4 consecutive state columns of one token and writes them with
-// one 8-byte store.  The stores go through a buffer resource whose range ends at the chunk's last
-// token, so a ragged chunk needs no branch: the hardware drops the stores past its end.
+// the scale).  A chain wave labels its 32 state columns so that the lane holding columns
+// 4 i .. 4 i + 3 of one 16-column tile holds the next 4 in the other tile: each lane then writes 8
+// consecutive columns of one token with one 16-byte store.  The stores go through a buffer
+// resource whose range ends at the chunk's last token, so a ragged chunk needs no branch: the
+// hardware drops the stores past its end.
 //
 // Addressing.  Every swizzled LDS access is a lane-constant byte offset (computed once, held in a
 // register) plus an immediate: the swizzles depend on the row only modulo 16, and rows enter in
@@ -51,7 +53,7 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;  // one bf16 row of a K, Q or V tile
 constexpr int kBlk = 16 * kRowBytes + 16;  // stride of the 16-row blocks of the K and Q tiles
-typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 // 64 x 128 bf16 tiles (K, Q, V): rows of 256 bytes; the 16-byte unit c of row r is stored at unit
 // c ^ sw(r).  For the reads below (16 lanes on one 8-byte unit of 16 consecutive rows, or
@@ -105,9 +107,8 @@ __device__ __forceinline__ bf16x4 ldtr(const char *p) {
   return lds_tr16(reinterpret_cast<const bf16 *>(p));
 }
 __device__ __forceinline__ void st8(char *p, f32x4 x) { *reinterpret_cast<bf16x4 *>(p) = to_bf16x4(x); }
-__device__ __forceinline__ f32x4 ldf4(const float *p) {  // two 8-byte reads (b128 reads are slow)
-  const float2 a = *reinterpret_cast<const float2 *>(p), b = *reinterpret_cast<const float2 *>(p + 2);
-  return f32x4{a.x, a.y, b.x, b.y};
+__device__ __forceinline__ f32x4 ldf4(const float *p) {  // 16-byte aligned
+  return *reinterpret_cast<const f32x4 *>(p);
 }
 
 // A lane-constant value the compiler must keep in a register (it cannot rematerialise it at
@@ -254,14 +255,15 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     // ======================= chain waves: the state recurrence and the output =======================
     const int ncol = 32 * w;  // this wave's first state column
     // lane-constant offsets: transpose reads of K (rows 4 gq + cl / 4, unit 4 mt + cl % 4) and of
-    // this wave's V columns, 32-wide block rows, P rows, the V tile store, and global offsets
+    // this wave's V columns (unit 2 (cl % 4) + nt: the column labels below), 32-wide block rows,
+    // P rows, and global offsets
     int o_tr[8], o_vtr[2], o_bf[2], o_pf[2][2];
     const int o_sf = pin(soff(cl, gq));  // 16x16 block row cl, elements 4 gq .. 4 gq + 3
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o_tr[mt] = pin(toff(4 * gq + (cl >> 2), 4 * mt + (cl & 3)));
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
-      const int r = 4 * gq + (cl >> 2), u = 4 * nt + (cl & 3);
+      const int r = 4 * gq + (cl >> 2), u = 2 * (cl & 3) + nt;
       o_vtr[nt] = pin(r * 64 + (((u >> 1) ^ (((r >> 2) & 1) << 1)) << 4) + ((u & 1) << 3));
     }
 #pragma unroll
@@ -275,10 +277,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     char *const vw = vt_s[w];
     const int vu = 4 * w + ((lane & 3) ^ (((lane >> 4) & 1) << 1));
     const int o_gv = pin((int)((lane >> 2) * tok_bytes) + vu * 16);
-    const int o_go = pin((int)(cl * tok_bytes) + (ncol + 4 * gq) * 2);      // O stores
+    const int o_go = pin((int)(cl * tok_bytes) + (ncol + 8 * gq) * 2);      // O stores
     auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + (rows / 16) * kBlk + o_tr[mt]); };
 
-    // S[mt][nt] holds rows 16 mt + 4 gq + i, column ncol + 16 nt + cl
+    // S[mt][nt] holds rows 16 mt + 4 gq + i of column ncol + 8 (cl / 4) + 4 nt + cl % 4 (tile nt's
+    // column n is state column ncol + 8 (n / 4) + 4 nt + n % 4; K h, Delta, the update and V follow
+    // the same labels, and a lane's output columns 4 gq .. 4 gq + 3 of the two tiles are adjacent)
     f32x4 S[8][2];
     if (cw == 0 && a.h0 != nullptr) {
       const float *hp = a.h0 + (int64_t)seq * a.h0_stride + (int64_t)h * kD * kD;
@@ -288,7 +292,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            S[mt][nt][i] = hp[(16 * mt + 4 * gq + i) * kD + ncol + 16 * nt + cl];
+            S[mt][nt][i] = hp[(16 * mt + 4 * gq + i) * kD + ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)];
       // consume the loads here, so that no wait for them is left inside the chunk loop
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
@@ -452,10 +456,9 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
             const int nrows = max(0, n - 16 * tt);
             const __amdgpu_buffer_rsrc_t ob = __builtin_amdgcn_make_buffer_rsrc(
                 go_ + (t0 + 16 * tt) * tok_bytes, (short)0, nrows * (int)tok_bytes, 0x00020000);
-#pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-              const bf16x4 o4 = to_bf16x4(acc[tt][nt]);
-              __builtin_amdgcn_raw_buffer_store_b64(*reinterpret_cast<const i32x2 *>(&o4), ob, o_go + 32 * nt, 0, 0);
+            {
+              const bf16x8 o8 = to_bf16x8(acc[tt][0], acc[tt][1]);
+              __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, o8), ob, o_go, 0, 0);
             }
           }
         }
@@ -485,7 +488,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            dst[(16 * mt + 4 * gq + i) * kD + ncol + 16 * nt + cl] = S[mt][nt][i];
+            dst[(16 * mt + 4 * gq + i) * kD + ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)] = S[mt][nt][i];
     }
   } else if (wave == 7) {
     // ================ wave 7: gate vectors, and K and Q from HBM into LDS, one chunk ahead ===========
