@@ -200,9 +200,12 @@ def kernel_source_sha():
     import hashlib
 
     h = hashlib.sha256()
-    csrc = os.path.join(ROOT, "linear_attention_recurrence_prefill_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
+    pkg = os.path.join(ROOT, "linear_attention_recurrence_prefill_amd")
+    csrc = os.path.join(pkg, "csrc")
+    paths = [os.path.join(csrc, name) for name in sorted(os.listdir(csrc))]
+    paths.append(os.path.join(pkg, "build.py"))  # compiler flags shape the kernel too
+    for path in paths:
+        with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
