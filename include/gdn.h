@@ -65,7 +65,15 @@ typedef enum gdn_status {
 enum { GDN_DTYPE_F32 = 0, GDN_DTYPE_BF16 = 1 };
 
 /* Forward mode.
- *   GDN_MODE_EXACT: the recurrence as defined; every sequence is one chain of chunks.
+ *   GDN_MODE_EXACT: the recurrence as defined.  With bf16 inputs and d = 128, when num_seqs *
+ *     num_heads is below P the sequences are split into segments of L chunks exactly as in the
+ *     truncate mode (L from the same latency model, or seg_chunks), and the result is still
+ *     exact (up to rounding): every (segment, head) first computes the affine map its chunks
+ *     apply to the state, S_end = M S_start + B (M from the identity with V = 0, B from zero);
+ *     the maps are composed along each sequence from its initial state into the true state at
+ *     every segment start; every segment then reruns from that state and writes its outputs.
+ *     This needs 3 x 64 KiB of workspace per (segment, head) (gdn_chunk_fwd_workspace_size).
+ *     Other configurations run every sequence as one chain of chunks.
  *   GDN_MODE_TRUNCATE: history truncation of "How to Speed Up GDN Kernels for Qwen Models",
  *     section "Lever 1: the gate is also a license to parallelize".  When num_seqs * num_heads
  *     is below P, the number of workgroups that run at once, each sequence is split into
@@ -86,9 +94,11 @@ typedef struct gdn_problem {
   int32_t chunk;             /* 64 */
   int32_t dtype;             /* GDN_DTYPE_* */
   int32_t mode;              /* GDN_MODE_* */
-  int32_t seg_chunks;        /* truncate mode: 0 = latency model, > 0 = forced segment length */
+  int32_t seg_chunks;        /* segment length where the mode splits (truncate; exact at bf16,
+                              * d = 128): 0 = latency model, > 0 = forced */
   int32_t num_slots;         /* P of the latency model: workgroups that run at once; 0 = the
-                              * device's CUs x resident workgroups per CU of the forward kernel */
+                              * device's CUs x resident workgroups per CU of the forward kernel
+                              * (then the workspace query needs the device) */
   float trunc_log_threshold; /* truncate mode: -10 */
   float scale;               /* o_t = scale * S_t^T q_t (1 in the pages' formulation) */
   int32_t reserved;          /* must be 0 */
@@ -100,9 +110,10 @@ typedef struct gdn_problem {
 gdn_status gdn_problem_init(gdn_problem *p, int64_t total_tokens, int32_t num_seqs,
                             int32_t num_heads, int32_t head_dim);
 
-/* Bytes of device workspace gdn_chunk_fwd needs for *p.  cu_seqlens_host (optional, N + 1
- * host int32) lets the truncate mode size its segment plan exactly; pass the same pointer (or
- * NULL) to gdn_chunk_fwd. */
+/* Bytes of device workspace gdn_chunk_fwd needs for *p (zero except for the exact mode's
+ * split).  cu_seqlens_host (optional, N + 1 host int32) lets a split mode size its segment plan
+ * exactly (without it the unit count is an upper bound); pass the same pointer (or NULL) to
+ * gdn_chunk_fwd. */
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
                                         size_t *bytes);
 

@@ -125,9 +125,10 @@ int64_t count_chunks(const gdn_problem *p, const int32_t *cu_host) {
 // Segment length of the truncate mode ("How to Speed Up GDN Kernels for Qwen Models", section
 // "Lever 1"): the latency-optimal length is proportional to sqrt(H * Nc / P); it is scaled by 3,
 // rounded to the nearest power of two in log2 and floored at 4 chunks, and the split is used
-// only when num_seqs * H does not fill the P workgroup slots.  Returns 0 for no split.
-int32_t segment_chunks(const gdn_problem *p, int64_t nchunks, int32_t P) {
-  if (p->mode != GDN_MODE_TRUNCATE) return 0;
+// only when num_seqs * H does not fill the P workgroup slots.  Returns 0 for no split.  The exact
+// mode splits by the same rule where the exact split is available (see split_available).
+int32_t segment_chunks(const gdn_problem *p, int64_t nchunks, int32_t P, bool split_ok) {
+  if (p->mode != GDN_MODE_TRUNCATE && !(p->mode == GDN_MODE_EXACT && split_ok)) return 0;
   if (p->seg_chunks > 0) return p->seg_chunks;
   if ((int64_t)p->num_seqs * p->num_heads >= P) return 0;
   const double lstar = 3.0 * std::sqrt((double)p->num_heads * (double)nchunks / (double)P);
@@ -163,23 +164,47 @@ gdn_status check_cu_host(const gdn_problem *p, const int32_t *cu_host) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The exact mode's split (three passes: every unit's affine map (B, M) from its chunks, the maps
+// composed along each sequence into true start states, every unit rerun from its start) is built
+// on the pipelined bf16 d = 128 kernel; other configurations run the exact mode unsplit.
+bool split_available(const gdn_problem *p, bool dump) {
+  return fwd_kernel_for(p, dump) == FwdKernel::kPipelined;
+}
+
 struct FwdLayout {
   int32_t L = 0;
   int64_t units = 0;
-  size_t total = 0;  // workspace bytes (the forward needs none)
+  bool split = false;     // exact mode through the three-pass split
+  size_t unit_bm = 0;     // split: offset of the per-unit (B, M) pairs, [2, units, H, D, D] fp32
+  size_t unit_h0 = 0;     // split: offset of the per-unit start states, [units, H, D, D] fp32
+  size_t total = 0;       // workspace bytes (zero unless split)
 };
 
 gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, bool dump, FwdLayout *lay) {
+  const bool split_ok = split_available(p, dump);
   int slots = 1;
-  if (p->mode == GDN_MODE_TRUNCATE && p->seg_chunks == 0) {
+  if ((p->mode == GDN_MODE_TRUNCATE || (p->mode == GDN_MODE_EXACT && split_ok)) &&
+      p->seg_chunks == 0) {
     gdn_status s = parallel_slots(p, dump, &slots);
     if (s != GDN_OK) return s;
   }
   const int64_t nc = count_chunks(p, cu_host);
-  lay->L = segment_chunks(p, nc, slots);
+  lay->L = segment_chunks(p, nc, slots, split_ok);
   lay->units = max_units(p, cu_host, lay->L);
+  // an exact-mode split in which every sequence stays one unit is no split
+  if (p->mode == GDN_MODE_EXACT && lay->L > 0 && cu_host && lay->units == p->num_seqs) {
+    lay->L = 0;
+    lay->units = p->num_seqs;
+  }
   if (lay->units > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "too many work units");
+  lay->split = p->mode == GDN_MODE_EXACT && lay->L > 0;
   lay->total = 0;
+  if (lay->split) {
+    const size_t per = (size_t)lay->units * p->num_heads * p->d_k * p->d_v * sizeof(float);
+    lay->unit_bm = 0;
+    lay->unit_h0 = align_up(2 * per);
+    lay->total = align_up(lay->unit_h0 + per);
+  }
   return GDN_OK;
 }
 
@@ -219,7 +244,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   if (s != GDN_OK) return s;
   if (ws_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
-  (void)ws;
+  if (lay.total > 0 && !aligned16(ws)) return fail(GDN_ERR_BAD_ALIGNMENT, "workspace alignment");
   gdn::FwdArgs a{};
   a.q = t.q;
   a.k = t.k;
@@ -247,6 +272,32 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
   hipError_t e;
+  if (lay.split) {
+    char *base = static_cast<char *>(ws);
+    float *bm = reinterpret_cast<float *>(base + lay.unit_bm);
+    float *uh0 = reinterpret_cast<float *>(base + lay.unit_h0);
+    a.units = lay.units;
+    a.unit_out = bm;
+    e = gdn::launch_fwd_ws_transition(a, lay.units, stream);
+    if (e != hipSuccess) return hip_fail(e, "exact split: first pass");
+    gdn::SplitArgs sa{};
+    sa.cu = t.cu;
+    sa.N = p->num_seqs;
+    sa.H = p->num_heads;
+    sa.L = lay.L;
+    sa.h0 = t.h0;
+    sa.h0_stride = p->h0_seq_stride;
+    sa.unit_bm = bm;
+    sa.unit_h0 = uh0;
+    sa.units = lay.units;
+    e = gdn::launch_affine_scan(sa, stream);
+    if (e != hipSuccess) return hip_fail(e, "exact split: start states");
+    a.unit_out = nullptr;
+    a.unit_h0 = uh0;
+    e = gdn::launch_fwd_ws(a, lay.units, stream);
+    if (e != hipSuccess) return hip_fail(e, "exact split: final pass");
+    return GDN_OK;
+  }
   switch (fwd_kernel_for(p, dump)) {
     case FwdKernel::kPipelined: e = gdn::launch_fwd_ws(a, lay.units, stream); break;
     case FwdKernel::kFast: e = gdn::launch_fwd_fast(a, p->d_k, lay.units, stream); break;

@@ -155,6 +155,12 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 
 }  // namespace
 
+// kTransition: the first pass of the exact split.  Workgroup (unit, head, z) runs the unit's
+// chunks from a fixed start without output and writes its final state to a.unit_out[z]: z = 0
+// from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
+// with V = 0 (the unit's transition matrix M, so that the state after the unit is
+// M S_start + B for any start state).
+template <bool kTransition>
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
   // V of the chunk on the chain, per chain wave its 32 columns: 64 rows of 64 bytes, the 16-byte
@@ -165,6 +171,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   // wave-uniform role (scalar branches: a wave never steps through the other role's barriers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x, h = blockIdx.y, H = a.H;
+  const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M half
   if (wave == 0) {
     Unit un;
     const bool ok = find_unit(a.cu, a.N, a.L, unit, false, lane, un);
@@ -284,8 +291,20 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     // column n is state column ncol + 8 (n / 4) + 4 nt + n % 4; K h, Delta, the update and V follow
     // the same labels, and a lane's output columns 4 gq .. 4 gq + 3 of the two tiles are adjacent)
     f32x4 S[8][2];
-    if (cw == 0 && a.h0 != nullptr) {
-      const float *hp = a.h0 + (int64_t)seq * a.h0_stride + (int64_t)h * kD * kD;
+    const float *hp = nullptr;  // the start state, or null for zero
+    if (!kTransition && a.unit_h0 != nullptr)
+      hp = a.unit_h0 + ((int64_t)unit * H + h) * kD * kD;  // the exact split's final pass
+    else if (!kTransition && cw == 0)
+      hp = a.h0 == nullptr ? nullptr : a.h0 + (int64_t)seq * a.h0_stride + (int64_t)h * kD * kD;
+    if (is_m) {
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            S[mt][nt][i] = 16 * mt + 4 * gq + i == ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3) ? 1.f : 0.f;
+    } else if (hp != nullptr) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -328,7 +347,11 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 
     // V of the first chunk; each later chunk's V is loaded once the chunk before it has consumed
     // the tile (the compiler waits for the direct loads before the tile is read)
-    if (cw < c1) v_dma(cw);
+    if (is_m) {  // the transition is taken with V = 0: a zero V tile, never reloaded
+      for (int i = lane; i < 64 * 64 / 16; i += 64) reinterpret_cast<uint4 *>(vw)[i] = uint4{0u, 0u, 0u, 0u};
+    } else if (cw < c1) {
+      v_dma(cw);
+    }
     wait_vm0();  // the initial state and V are in place: no load is outstanding when the loop starts
     __syncthreads();  // chunk cw's K and Q are in LDS (wave 7)
 
@@ -338,7 +361,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int cc = c - 1;
         const int64_t t0 = chunk_t0(cc);
         const int n = chunk_n(cc);
-        const bool emit = cc >= c0;
+        const bool emit = !kTransition && cc >= c0;
         const int Y = cc & 1;
         const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
         const WsSmem::Vec &vc = sm.vec[cc % 3];
@@ -378,7 +401,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
         __builtin_amdgcn_s_waitcnt(0xC07F);
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
-        if (cc + 1 < c1) v_dma(cc + 1);
+        if (cc + 1 < c1 && !is_m) v_dma(cc + 1);
 
         // ---- Delta block by block (see the head of this file).  Delta is kept only as bf16 operand
         //      fragments: da for the output, dt = Delta o e^{gamma_last - gamma} for the state
@@ -480,8 +503,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       lds_barrier();
     }
 
-    if (a.ht != nullptr && c1 == nchunks_seq) {
-      float *dst = a.ht + ((int64_t)seq * H + h) * kD * kD;
+    float *dst = nullptr;
+    if (kTransition)
+      dst = a.unit_out + (((int64_t)blockIdx.z * a.units + unit) * H + h) * kD * kD;
+    else if (a.ht != nullptr && c1 == nchunks_seq)
+      dst = a.ht + ((int64_t)seq * H + h) * kD * kD;
+    if (dst != nullptr) {
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -552,7 +579,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       wait_vm0();
       gate_vectors(gbx, cw);
       dma_tile(sm.kq[cw % 3][0], gk_, cw);
-      if (cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, cw);
+      if (!kTransition && cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, cw);
       if (cw + 1 < c1) gbx = gb_load(cw + 1);
     }
     wait_vm0();
@@ -565,7 +592,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (c + 1 < c1) {
         gate_vectors(gbx, c + 1);
         dma_tile(sm.kq[(c + 1) % 3][0], gk_, c + 1);
-        if (c + 1 >= c0) dma_tile(sm.kq[(c + 1) % 3][1], gq_, c + 1);
+        if (!kTransition && c + 1 >= c0) dma_tile(sm.kq[(c + 1) % 3][1], gq_, c + 1);
         if (c + 2 < c1) gbx = gb_load(c + 2);
       }
       wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
@@ -578,7 +605,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     for (int c = cw; c <= c1; ++c) {
       if (c < c1) {
         // ---------------- chunk c ----------------
-        const bool emit = c >= c0;
+        const bool emit = !kTransition && c >= c0;
         const int Y = c & 1;
         const char *Kt = sm.kq[c % 3][0], *Qt = sm.kq[c % 3][1];
         const WsSmem::Vec &vc = sm.vec[c % 3];
@@ -690,13 +717,19 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 
 int fwd_ws_blocks_per_cu() {
   int blocks = 0;
-  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_ws_kernel, 512, 0);
+  const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, fwd_ws_kernel<false>, 512, 0);
   return (e == hipSuccess && blocks > 0) ? blocks : 1;
 }
 
 hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
   if (max_units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ws_kernel, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
+  hipLaunchKernelGGL(fwd_ws_kernel<false>, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_ws_transition(const FwdArgs &a, int64_t units, hipStream_t stream) {
+  if (units <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_ws_kernel<true>, dim3((unsigned)units, a.H, 2), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

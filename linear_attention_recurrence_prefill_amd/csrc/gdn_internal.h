@@ -27,6 +27,22 @@ struct FwdArgs {
   float scale;
   float log_thr;
   int32_t truncate;
+  // exact split (pipelined kernel only): per-unit start states [units, H, D, D] for the final
+  // pass, or the first pass's outputs [2, units, H, D, D] (B from zero, M from the identity)
+  const float *unit_h0;
+  float *unit_out;
+  int64_t units;
+};
+
+// Arguments of the exact split's middle pass (gdn_fwd_split.hip).
+struct SplitArgs {
+  const int32_t *cu;
+  int32_t N, H, L;
+  const float *h0;
+  int64_t h0_stride;
+  const float *unit_bm;  // [2, units, H, D, D]: B, then M
+  float *unit_h0;        // [units, H, D, D]: the true state at each unit's start
+  int64_t units;
 };
 
 // Arguments of the backward kernels (see gdn_bwd.hip).  Workspace arrays (fp32):
@@ -61,6 +77,10 @@ hipError_t launch_fwd_fast(const FwdArgs &a, int D, int64_t max_units, hipStream
 // bf16, d = 128: warp-specialised pipeline, one workgroup per CU (gdn_fwd_ws.hip).
 hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream);
 int fwd_ws_blocks_per_cu();
+// Exact split: the first pass (B and M of every unit, no output; grid (units, H, 2)) and the
+// middle pass (each sequence's units in order: S_start(u + 1) = M_u S_start(u) + B_u).
+hipError_t launch_fwd_ws_transition(const FwdArgs &a, int64_t units, hipStream_t stream);
+hipError_t launch_affine_scan(const SplitArgs &s, hipStream_t stream);
 
 // Workgroups of a forward kernel that fit on one CU at once (from the runtime's occupancy query).
 int fwd_blocks_per_cu(int D, bool bf16);

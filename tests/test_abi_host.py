@@ -114,12 +114,39 @@ def test_host_cu_seqlens_checked(lib):
 
 
 def test_workspace_sizes(lib):
-    p = _problem()
+    # num_slots (P of the latency model) is given, so no device is queried
     n = ctypes.c_size_t(123)
+    p = _problem(num_slots=1)  # num_seqs * H >= P: no split, no scratch
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
-    assert n.value == 0  # the forward needs no scratch
+    assert n.value == 0
+    p = _problem(num_slots=256, dtype=0)  # fp32: the exact mode is never split
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert n.value == 0
+    p = _problem(num_slots=256, mode=1)  # truncate mode: no scratch
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert n.value == 0
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
     assert n.value > 1024 * 8 * 128 * 4
+
+
+def test_exact_split_workspace(lib):
+    """The exact mode's split (bf16, d = 128, num_seqs * H < P) needs per unit and head a pair
+    (B, M) and a start state: 3 fp32 states of 128 x 128."""
+    n = ctypes.c_size_t(0)
+    state = 128 * 128 * 4
+    p = _problem(num_slots=256, seg_chunks=4)
+    cu = (ctypes.c_int32 * 3)(0, 512, 1024)  # 8 chunks each: 2 units each
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu, ctypes.byref(n)) == 0
+    assert n.value == 3 * 4 * 8 * state
+    cu = (ctypes.c_int32 * 3)(0, 256, 1024)  # 4 + 12 chunks: 1 + 3 units
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu, ctypes.byref(n)) == 0
+    assert n.value == 3 * 4 * 8 * state
+    p = _problem(num_slots=256, seg_chunks=16)  # every sequence is one unit: no split
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu, ctypes.byref(n)) == 0
+    assert n.value == 0
+    p = _problem(num_slots=256)  # latency model: L = 4 (floor); without cu a bound on the units
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert n.value >= 3 * 4 * 8 * state
 
 
 def test_status_strings(lib):
