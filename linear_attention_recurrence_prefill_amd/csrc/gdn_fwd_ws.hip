@@ -189,6 +189,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
+  if (kTransition && c1 == nchunks_seq) return;  // a sequence's last unit has no successor
   const int64_t tok_bytes = (int64_t)H * kRowBytes;  // stride of one token in q, k, v, o
   const char *__restrict__ gq_ = static_cast<const char *>(a.q) + (int64_t)h * kRowBytes;
   const char *__restrict__ gk_ = static_cast<const char *>(a.k) + (int64_t)h * kRowBytes;
