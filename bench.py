@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -197,14 +198,23 @@ def main():
 
 
 def kernel_source_sha():
+    """Hash of the timed kernel's translation unit (gdn_fwd_ws.hip and the csrc headers it
+    includes, followed recursively) and of build.py, whose flags shape the code too.  Changes to
+    other kernels leave it, and so the stored traffic figure, valid."""
     import hashlib
 
-    h = hashlib.sha256()
     pkg = os.path.join(ROOT, "linear_attention_recurrence_prefill_amd")
     csrc = os.path.join(pkg, "csrc")
-    paths = [os.path.join(csrc, name) for name in sorted(os.listdir(csrc))]
-    paths.append(os.path.join(pkg, "build.py"))  # compiler flags shape the kernel too
-    for path in paths:
+    seen, todo = [], ["gdn_fwd_ws.hip"]
+    while todo:
+        name = todo.pop(0)
+        if name in seen or not os.path.exists(os.path.join(csrc, name)):
+            continue
+        seen.append(name)
+        with open(os.path.join(csrc, name)) as f:
+            todo += re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M)
+    h = hashlib.sha256()
+    for path in [os.path.join(csrc, n) for n in sorted(seen)] + [os.path.join(pkg, "build.py")]:
         with open(path, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
