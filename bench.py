@@ -199,12 +199,13 @@ def main():
 
 def kernel_source_sha():
     """Hash of the timed kernel's translation unit (gdn_fwd_ws.hip and the csrc headers it
-    includes, followed recursively) and of build.py, whose flags shape the code too.  Changes to
+    includes, followed recursively) and of the compiler flags build.py gives it.  Changes to
     other kernels leave it, and so the stored traffic figure, valid."""
     import hashlib
 
-    pkg = os.path.join(ROOT, "linear_attention_recurrence_prefill_amd")
-    csrc = os.path.join(pkg, "csrc")
+    from linear_attention_recurrence_prefill_amd import build as b
+
+    csrc = b.CSRC
     seen, todo = [], ["gdn_fwd_ws.hip"]
     while todo:
         name = todo.pop(0)
@@ -214,9 +215,10 @@ def kernel_source_sha():
         with open(os.path.join(csrc, name)) as f:
             todo += re.findall(r'^#include "([^"]+)"', f.read(), flags=re.M)
     h = hashlib.sha256()
-    for path in [os.path.join(csrc, n) for n in sorted(seen)] + [os.path.join(pkg, "build.py")]:
-        with open(path, "rb") as f:
+    for name in sorted(seen):
+        with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
+    h.update(repr((b.HIP_FLAGS, b.EXTRA_FLAGS.get("gdn_fwd_ws.hip", []))).encode())
     return h.hexdigest()[:16]
 
 

@@ -33,6 +33,9 @@
 
 namespace gdn {
 
+// bf16, d = 128: the reverse chain on bf16 MFMA with split operands (gdn_bwd_chain.hip).
+hipError_t launch_bwd_chain_bf16(const BwdArgs &b, hipStream_t stream);
+
 namespace {
 
 constexpr int LDF = 64 + 4;  // row stride of 64-wide fp32 LDS tiles
@@ -598,7 +601,7 @@ __global__ __launch_bounds__(256) void sum_dh0_kernel(const float *__restrict__ 
 hipError_t launch_bwd_chain(const BwdArgs &b, int D, bool is_bf16, hipStream_t stream) {
   const dim3 grid(b.N, b.H), block(256);
   if (D == 128) {
-    if (is_bf16) hipLaunchKernelGGL((bwd_chain_kernel<128, bf16>), grid, block, 0, stream, b);
+    if (is_bf16) return launch_bwd_chain_bf16(b, stream);
     else hipLaunchKernelGGL((bwd_chain_kernel<128, float>), grid, block, 0, stream, b);
   } else {
     if (is_bf16) hipLaunchKernelGGL((bwd_chain_kernel<64, bf16>), grid, block, 0, stream, b);
