@@ -35,6 +35,8 @@ namespace gdn {
 
 // bf16, d = 128: the reverse chain on bf16 MFMA with split operands (gdn_bwd_chain.hip).
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, hipStream_t stream);
+// bf16, d = 128: the per-chunk gradients on bf16 MFMA with split operands (gdn_bwd_grad.hip).
+hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
 
 namespace {
 
@@ -615,7 +617,7 @@ hipError_t launch_bwd_grad(const BwdArgs &b, int D, bool is_bf16, int64_t max_ch
   if (max_chunks <= 0) return hipSuccess;
   const dim3 grid((unsigned)max_chunks, b.H), block(256);
   if (D == 128) {
-    if (is_bf16) hipLaunchKernelGGL((bwd_grad_kernel<128, bf16>), grid, block, 0, stream, b);
+    if (is_bf16) return launch_bwd_grad_bf16(b, max_chunks, stream);
     else hipLaunchKernelGGL((bwd_grad_kernel<128, float>), grid, block, 0, stream, b);
   } else {
     if (is_bf16) hipLaunchKernelGGL((bwd_grad_kernel<64, bf16>), grid, block, 0, stream, b);

@@ -1,0 +1,542 @@
+// Per-chunk gradients of the backward for bf16 inputs with d_k = d_v = 128 on gfx950.
+//
+// Per chunk (n <= 64 tokens) and head, from the forward recompute (gamma, Tm = (I + A)^-1, the
+// chunk-start state h, Delta) and the reverse chain (dh' = gradient of the state after the chunk,
+// dDelta), with a = e^gamma, c = e^{gamma_last - gamma}, Gm_ri = e^{gamma_r - gamma_i} (i <= r),
+// dO_s = scale dO:
+//   dR  = Tm^T dDelta                       (gradient of R = diag(beta) (V - diag(a) K h), since
+//                                            Delta = Tm R)
+//   dV  = diag(beta) dR
+//   dA  = strict_lower(-dR Delta^T)         (gradient of A through Tm = (I + A)^-1)
+//   dPm = (dO_s Delta^T) o Gm on i <= r;    E = dA o Gm o beta_row
+//   Y1 = dO_s h^T,  Y2 = Delta dh'^T,  Rh = dR h^T
+//   dQ = diag(a) Y1 + dPm K
+//   dK = dPm^T Q + (E + E^T) K + diag(c) Y2 - diag(beta a) Rh
+//   dbeta_r  = dR_r . V_r - a_r (Rh . K)_r + sum_i dA_ri Gm_ri (k_r . k_i)
+//   dgamma_r = a_r (Y1 . Q)_r - beta_r a_r (Rh . K)_r - c_r (Y2 . K)_r
+//              + row r minus column r sums of (dPm o Q K^T) and of (dA o A)
+//   dgamma_last += sum_r c_r (Y2 . K)_r + e^{gamma_last} <dh', h>;  dg = reverse cumsum of dgamma
+// ((x . y)_r is the dot product of row r of x and y.)  This is the reverse-mode derivative of the
+// chunked form of "How to Speed Up GDN Kernels for Qwen Models" (section "What GDN actually
+// computes"), with the hidden states recomputed ("Lever 2").
+//
+// One workgroup of four waves per (chunk, head).  Products run on v_mfma_f32_16x16x32_bf16 with
+// fp32 accumulation; q, k, v and dO enter exactly, every other operand as a bf16 head plus a bf16
+// remainder (see the reverse chain).  Wave w owns feature columns [32 w, 32 w + 32) of every
+// 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go straight from HBM into
+// the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
+// so results are bitwise reproducible.
+#include "gdn_device.h"
+#include "gdn_internal.h"
+#include "gdn_unit.h"
+
+namespace gdn {
+namespace {
+
+constexpr int kD = 128;
+constexpr int kRowB = kD * 2;
+
+// 64 x 128 bf16 tiles, token-major, 16-byte unit c of row r at c ^ sw(r) (as in the chain)
+__device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
+__device__ __forceinline__ int toff(int r, int u) {
+  return r * kRowB + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
+}
+// 64 x 64 bf16 tiles: rows of 128 bytes, 8-byte unit u of row r at u ^ 2 ((r / 2) % 8)
+__device__ __forceinline__ int poff(int r, int u) {
+  return r * 128 + ((u ^ (((r >> 1) & 7) << 1)) << 3);
+}
+
+__device__ __forceinline__ bf16x4 ld8(const char *p) { return *reinterpret_cast<const bf16x4 *>(p); }
+__device__ __forceinline__ bf16x8 ld16(const char *p) { return *reinterpret_cast<const bf16x8 *>(p); }
+__device__ __forceinline__ bf16x4 ldtr(const char *p) {
+  return lds_tr16(reinterpret_cast<const bf16 *>(p));
+}
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &lo) {
+  const bf16x4 h0 = to_bf16x4(x0), h1 = to_bf16x4(x1);
+  hi = cat8(h0, h1);
+  lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
+}
+__device__ __forceinline__ void st_split(char *hi, char *lo, int off, float x) {
+  const bf16 h = (bf16)x;
+  *reinterpret_cast<bf16 *>(hi + off) = h;
+  *reinterpret_cast<bf16 *>(lo + off) = (bf16)(x - (float)h);
+}
+
+struct GradSmem {
+  alignas(16) char dout[64 * kRowB];
+  alignas(16) char q[64 * kRowB];
+  alignas(16) char k[64 * kRowB];
+  alignas(16) char v[64 * kRowB];   // V; from the tile phase on, E hi and lo
+  alignas(16) char dh[64 * kRowB];  // Delta = hi + lo
+  alignas(16) char dl[64 * kRowB];
+  alignas(16) char eh[64 * kRowB];  // dDelta = hi + lo; from the second phase on, dR
+  alignas(16) char el[64 * kRowB];
+  alignas(16) char tth[64 * 128];   // Tm^T = hi + lo; from the tile phase on, dPm
+  alignas(16) char ttl[64 * 128];
+  alignas(16) float gam[64], a[64], c[64], beta[64];
+  alignas(16) float prg[4][64];  // per-wave partial row terms of dgamma (tiles)
+  alignas(16) float pcg[4][64];  // per-wave partial column terms of dgamma (tiles, subtracted)
+  alignas(16) float prb[4][64];  // per-wave partial row terms of dbeta (tiles)
+  alignas(16) float frg[4][64];  // per-wave row terms of dgamma over the wave's columns
+  alignas(16) float frb[4][64];  // per-wave row terms of dbeta over the wave's columns
+  alignas(16) float fc[4][64];   // per-wave c_r (Y2 . K)_r
+  alignas(16) float hd[4];
+  alignas(16) int imisc[4];
+};
+static_assert(sizeof(GradSmem) <= 160 * 1024, "LDS budget");
+
+__constant__ int kTR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
+__constant__ int kTI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+
+}  // namespace
+
+__global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
+  __shared__ GradSmem sm;
+  const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
+  // locate the chunk: its sequence and its index within that sequence
+  if (w == 0) {
+    int64_t before = 0;
+    int seq = -1, cidx = 0;
+    for (int base = 0; base < b.N; base += 64) {
+      const int nn = base + lane;
+      const int ch = nn < b.N ? max(0, (b.cu[nn + 1] - b.cu[nn] + kChunk - 1) / kChunk) : 0;
+      int sc = ch;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(sc, off, 64);
+        if (lane >= off) sc += y;
+      }
+      const uint64_t hit = __ballot(nn < b.N && before + sc > cg);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        seq = base + l;
+        cidx = (int)(cg - before - __shfl(sc - ch, l, 64));
+        break;
+      }
+      before += __shfl(sc, 63, 64);
+    }
+    if (lane == 0) {
+      sm.imisc[0] = seq;
+      sm.imisc[1] = cidx;
+    }
+  }
+  for (int i = tid; i < 6 * 4 * 64; i += 256) (&sm.prg[0][0])[i] = 0.f;
+  __syncthreads();
+  const int seq = sm.imisc[0];
+  if (seq < 0) return;
+  const int64_t ts0 = b.cu[seq], ts1 = b.cu[seq + 1];
+  if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;
+  const int64_t t0 = ts0 + (int64_t)sm.imisc[1] * kChunk;
+  const int n = (int)min<int64_t>(kChunk, ts1 - t0);
+  const int64_t tok_bytes = (int64_t)H * kRowB;
+  const int64_t dd = (int64_t)kD * kD;
+  const float scale = b.scale;
+  const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
+  const float *dhn = b.dhn + ((int64_t)cg * H + h) * dd;
+
+  // ---- stage: dO, Q, K, V (bf16 as they are), Delta and dDelta split, Tm^T split; zero past n
+  {
+    const char *src[4] = {static_cast<const char *>(b.dout), static_cast<const char *>(b.q),
+                          static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
+    char *dst[4] = {sm.dout, sm.q, sm.k, sm.v};
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int u = tid + 256 * m, r = u >> 4, c16 = u & 15;
+        uint4 x{0u, 0u, 0u, 0u};
+        if (r < n) x = *reinterpret_cast<const uint4 *>(src[s] + (t0 + r) * tok_bytes +
+                                                         (int64_t)h * kRowB + c16 * 16);
+        *reinterpret_cast<uint4 *>(dst[s] + r * kRowB + ((c16 ^ sw(r)) << 4)) = x;
+      }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const float *g = s == 0 ? b.delta : b.ddelta;
+      char *hi = s == 0 ? sm.dh : sm.eh;
+      char *lo = s == 0 ? sm.dl : sm.el;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int u = tid + 256 * m, r = u >> 5, c4 = u & 31;
+        const f32x4 x = r < n ? *reinterpret_cast<const f32x4 *>(g + ((t0 + r) * H + h) * kD + 4 * c4)
+                              : zero4();
+        const bf16x4 xh = to_bf16x4(x);
+        *reinterpret_cast<bf16x4 *>(hi + toff(r, c4)) = xh;
+        *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(x - to_f32x4(xh));
+      }
+    }
+    // Tm (rows i, columns r; zero outside [0, n)^2) into Tm^T[r][i]
+    const float *tm = b.tmat + ((int64_t)cg * H + h) * 64 * 64;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int u = tid + 256 * m, i = u >> 4, r4 = 4 * (u & 15);
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(tm + i * 64 + r4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int off = poff(r4 + j, i >> 2) + 2 * (i & 3);
+        st_split(sm.tth, sm.ttl, off, x[j]);
+      }
+    }
+    if (w == 0) {
+      const float gmv = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
+      const float glast = __shfl(gmv, n - 1, 64);
+      sm.gam[lane] = lane < n ? gmv : glast;
+      sm.a[lane] = lane < n ? __expf(gmv) : 0.f;
+      sm.c[lane] = lane < n ? __expf(glast - gmv) : 0.f;
+      sm.beta[lane] =
+          lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
+    }
+  }
+  __syncthreads();
+
+  // fragment readers
+  // A or B operand over features, natural order: row r, elements 32 ks + 8 gq .. + 7
+  auto rowf = [&](const char *t, int r, int ks) { return ld16(t + toff(r, 8 * ks + 2 * gq)); };
+  // A operand over tokens from a 64 x 64 tile, rows 16 m + cl, tokens in the permuted order
+  auto pfrag = [&](const char *t, int m, int ks) {
+    const int r = 16 * m + cl;
+    return cat8(ld8(t + poff(r, 8 * ks + gq)), ld8(t + poff(r, 8 * ks + 4 + gq)));
+  };
+  // the same from the transpose of a 64 x 64 tile (A[r][i] = t[i][r])
+  auto ptfrag = [&](const char *t, int m, int ks) {
+    const int i = 32 * ks + 4 * gq + (cl >> 2), u = 4 * m + (cl & 3);
+    return cat8(ldtr(t + poff(i, u)), ldtr(t + poff(i + 16, u)));
+  };
+  // B operand over tokens from a 64 x 128 tile, column 4 u0 + cl, tokens in the permuted order
+  auto trfrag = [&](const char *t, int ks, int u0) {
+    const int r = 32 * ks + 4 * gq + (cl >> 2), u = u0 + (cl & 3);
+    return cat8(ldtr(t + toff(r, u)), ldtr(t + toff(r + 16, u)));
+  };
+  // rows 16 m + 4 gq .. + 3 of column 4 u0 + cl of a 64 x 128 tile
+  auto colv = [&](const char *t, int m, int u0) {
+    return to_f32x4(ldtr(t + toff(16 * m + 4 * gq + (cl >> 2), u0 + (cl & 3))));
+  };
+
+  const int fcol = 32 * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
+
+  // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
+  bf16x8 hh[2][4], hl[2][4];
+  f32x4 Y1[4][2], Y2[4][2];
+  float hdot = 0.f;
+  {
+    bf16x8 gh[2][4], gl[2][4];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
+        const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hS + off);
+        const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hS + off + 4);
+        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dhn + off);
+        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+        split8(h0, h1, hh[nt][ks], hl[nt][ks]);
+        split8(d0, d1, gh[nt][ks], gl[nt][ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hdot += h0[j] * d0[j] + h1[j] * d1[j];
+      }
+    // Y1 = dO h^T (scale applied later), Y2 = Delta dh'^T
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) Y1[mt][nt] = Y2[mt][nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ao = rowf(sm.dout, 16 * mt + cl, ks);
+        const bf16x8 ah = rowf(sm.dh, 16 * mt + cl, ks), al = rowf(sm.dl, 16 * mt + cl, ks);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          Y1[mt][nt] = mma_bf16(ao, hh[nt][ks], Y1[mt][nt]);
+          Y1[mt][nt] = mma_bf16(ao, hl[nt][ks], Y1[mt][nt]);
+          Y2[mt][nt] = mma_bf16(ah, gh[nt][ks], Y2[mt][nt]);
+          Y2[mt][nt] = mma_bf16(ah, gl[nt][ks], Y2[mt][nt]);
+          Y2[mt][nt] = mma_bf16(al, gh[nt][ks], Y2[mt][nt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) hdot += __shfl_xor(hdot, off, 64);
+  if (lane == 0) sm.hd[w] = hdot;
+
+  // ---- dR = Tm^T dDelta over this wave's columns (v); dV = diag(beta) dR; dR_r . V_r
+  f32x4 dR[4][2];
+  float rb[4][4];  // row terms of dbeta over this wave's columns: [mt][i]
+  {
+    bf16x8 eb[2][2][2];  // dDelta over tokens: [ks][nt][hi, lo]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        eb[ks][nt][0] = trfrag(sm.eh, ks, 8 * w + 4 * nt);
+        eb[ks][nt][1] = trfrag(sm.el, ks, 8 * w + 4 * nt);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) dR[mt][nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        if (2 * ks + 1 < mt) continue;  // Tm^T[r][i] = 0 for i < r
+        const bf16x8 th = pfrag(sm.tth, mt, ks), tl = pfrag(sm.ttl, mt, ks);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          dR[mt][nt] = mma_bf16(th, eb[ks][nt][0], dR[mt][nt]);
+          dR[mt][nt] = mma_bf16(th, eb[ks][nt][1], dR[mt][nt]);
+          dR[mt][nt] = mma_bf16(tl, eb[ks][nt][0], dR[mt][nt]);
+        }
+      }
+      const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) rb[mt][i] = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x4 vv = colv(sm.v, mt, 8 * w + 4 * nt);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * gq + i;
+          rb[mt][i] += dR[mt][nt][i] * vv[i];
+          if (r < n)
+            static_cast<bf16 *>(b.dv)[((t0 + r) * H + h) * kD + fcol + 16 * nt] =
+                (bf16)(br[i] * dR[mt][nt][i]);
+        }
+      }
+    }
+  }
+  __syncthreads();  // every wave is done with dDelta, Tm^T and V
+  // dR (rows r, this wave's columns) into the dDelta tiles' place
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * gq + i, f = fcol + 16 * nt;
+        st_split(sm.eh, sm.el, toff(r, f >> 2) + 2 * (f & 3), dR[mt][nt][i]);
+      }
+  // zero the tiles above the diagonal of dPm (tth, ttl) and E (v region)
+  for (int i = tid; i < 6 * 64; i += 256) {
+    const int t = i >> 6, rr = (i >> 2) & 15, u = i & 3;
+    // (mi, mr) = (0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3): column block > row block
+    const int mi = t < 3 ? 0 : (t < 5 ? 1 : 2);
+    const int mr = t < 3 ? t + 1 : (t < 5 ? t - 1 : 3);
+    const int off = poff(16 * mi + rr, 4 * mr + u);
+    *reinterpret_cast<uint2 *>(&sm.tth[off]) = uint2{0u, 0u};
+    *reinterpret_cast<uint2 *>(&sm.ttl[off]) = uint2{0u, 0u};
+    *reinterpret_cast<uint2 *>(&sm.v[off]) = uint2{0u, 0u};
+    *reinterpret_cast<uint2 *>(&sm.v[64 * 128 + off]) = uint2{0u, 0u};
+  }
+  __syncthreads();
+
+  // ---- Rh = dR h^T over this wave's columns (d)
+  f32x4 Rh[4][2];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) Rh[mt][nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ah = rowf(sm.eh, 16 * mt + cl, ks), al = rowf(sm.el, 16 * mt + cl, ks);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        Rh[mt][nt] = mma_bf16(ah, hh[nt][ks], Rh[mt][nt]);
+        Rh[mt][nt] = mma_bf16(ah, hl[nt][ks], Rh[mt][nt]);
+        Rh[mt][nt] = mma_bf16(al, hh[nt][ks], Rh[mt][nt]);
+      }
+    }
+  }
+
+  // ---- 64 x 64 tiles on and below the diagonal: dP, dR Delta^T, Q K^T, K K^T
+  char *eth = sm.v, *etl = sm.v + 64 * 128;  // E = hi + lo
+  for (int t = w; t < 10; t += 4) {
+    const int tr = kTR[t], ti = kTI[t];
+    f32x4 dp = zero4(), da = zero4(), qk = zero4(), kk = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int ra = 16 * tr + cl, rb_ = 16 * ti + cl;
+      const bf16x8 ao = rowf(sm.dout, ra, ks), aq = rowf(sm.q, ra, ks), ak = rowf(sm.k, ra, ks);
+      const bf16x8 arh = rowf(sm.eh, ra, ks), arl = rowf(sm.el, ra, ks);
+      const bf16x8 bdh = rowf(sm.dh, rb_, ks), bdl = rowf(sm.dl, rb_, ks), bk = rowf(sm.k, rb_, ks);
+      dp = mma_bf16(ao, bdh, dp);
+      dp = mma_bf16(ao, bdl, dp);
+      da = mma_bf16(arh, bdh, da);
+      da = mma_bf16(arh, bdl, da);
+      da = mma_bf16(arl, bdh, da);
+      qk = mma_bf16(aq, bk, qk);
+      kk = mma_bf16(ak, bk, kk);
+    }
+    const int i = 16 * ti + cl;
+    const float gi = sm.gam[i];
+    float rg4[4], rb4[4], csc = 0.f;  // csc: this column's sum
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 16 * tr + 4 * gq + j;
+      float pm = 0.f, e = 0.f, tg = 0.f, tb = 0.f;
+      if (i <= r && r < n) {
+        const float gm = __expf(sm.gam[r] - gi);
+        pm = scale * dp[j] * gm;
+        tg = pm * qk[j];
+        if (i < r) {
+          const float dA = -da[j];
+          const float gk = gm * kk[j];
+          e = dA * gm * sm.beta[r];
+          tb = dA * gk;
+          tg += dA * sm.beta[r] * gk;
+        }
+      }
+      const int off = poff(r, i >> 2) + 2 * (i & 3);
+      st_split(sm.tth, sm.ttl, off, pm);
+      st_split(eth, etl, off, e);
+      rg4[j] = tg;
+      rb4[j] = tb;
+      csc += tg;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) {
+        rg4[j] += __shfl_xor(rg4[j], off, 64);
+        rb4[j] += __shfl_xor(rb4[j], off, 64);
+      }
+    csc += __shfl_xor(csc, 16, 64);
+    csc += __shfl_xor(csc, 32, 64);
+    if (cl == 0) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sm.prg[w][16 * tr + 4 * gq + j] = rg4[j];
+        sm.prb[w][16 * tr + 4 * gq + j] = rb4[j];
+      }
+    }
+    if (gq == 0) sm.pcg[w][i] = csc;
+  }
+  __syncthreads();
+
+  // ---- dQ = diag(a) Y1 + dPm K;  dK = dPm^T Q + (E + E^T) K + diag(c) Y2 - diag(beta a) Rh
+  float rg[4][4], rc[4][4];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rg[mt][i] = rc[mt][i] = 0.f;
+  {
+    bf16x8 kb[2][2], qb[2][2];  // K and Q over tokens: [ks][nt]
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        kb[ks][nt] = trfrag(sm.k, ks, 8 * w + 4 * nt);
+        qb[ks][nt] = trfrag(sm.q, ks, 8 * w + 4 * nt);
+      }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bool lower = 2 * ks <= mt;      // blocks with tokens i <= rows r exist
+        const bool upper = 2 * ks + 1 >= mt;  // blocks with tokens i >= rows r exist
+        if (lower) {
+          const bf16x8 ph = pfrag(sm.tth, mt, ks), pl = pfrag(sm.ttl, mt, ks);
+          const bf16x8 eh_ = pfrag(eth, mt, ks), el_ = pfrag(etl, mt, ks);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            dq[nt] = mma_bf16(ph, kb[ks][nt], dq[nt]);
+            dq[nt] = mma_bf16(pl, kb[ks][nt], dq[nt]);
+            dk[nt] = mma_bf16(eh_, kb[ks][nt], dk[nt]);
+            dk[nt] = mma_bf16(el_, kb[ks][nt], dk[nt]);
+          }
+        }
+        if (upper) {
+          const bf16x8 ph = ptfrag(sm.tth, mt, ks), pl = ptfrag(sm.ttl, mt, ks);
+          const bf16x8 eh_ = ptfrag(eth, mt, ks), el_ = ptfrag(etl, mt, ks);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            dk[nt] = mma_bf16(ph, qb[ks][nt], dk[nt]);
+            dk[nt] = mma_bf16(pl, qb[ks][nt], dk[nt]);
+            dk[nt] = mma_bf16(eh_, kb[ks][nt], dk[nt]);
+            dk[nt] = mma_bf16(el_, kb[ks][nt], dk[nt]);
+          }
+        }
+      }
+      const f32x4 ar = *reinterpret_cast<const f32x4 *>(&sm.a[16 * mt + 4 * gq]);
+      const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
+      const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const f32x4 qv = colv(sm.q, mt, 8 * w + 4 * nt), kv = colv(sm.k, mt, 8 * w + 4 * nt);
+        const f32x4 y1 = scale * Y1[mt][nt];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * mt + 4 * gq + i;
+          const float dqv = ar[i] * y1[i] + dq[nt][i];
+          const float dkv = dk[nt][i] + cr[i] * Y2[mt][nt][i] - br[i] * ar[i] * Rh[mt][nt][i];
+          if (r < n) {
+            const int64_t gi = ((t0 + r) * H + h) * kD + fcol + 16 * nt;
+            static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
+            static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
+          }
+          rg[mt][i] += ar[i] * y1[i] * qv[i] - br[i] * ar[i] * Rh[mt][nt][i] * kv[i] -
+                       cr[i] * Y2[mt][nt][i] * kv[i];
+          rb[mt][i] -= ar[i] * Rh[mt][nt][i] * kv[i];
+          rc[mt][i] += cr[i] * Y2[mt][nt][i] * kv[i];
+        }
+      }
+    }
+  }
+  // row sums over this wave's 16 columns per tile
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int off = 8; off > 0; off >>= 1) {
+        rg[mt][i] += __shfl_xor(rg[mt][i], off, 64);
+        rb[mt][i] += __shfl_xor(rb[mt][i], off, 64);
+        rc[mt][i] += __shfl_xor(rc[mt][i], off, 64);
+      }
+      if (cl == 0) {
+        const int r = 16 * mt + 4 * gq + i;
+        sm.frg[w][r] = rg[mt][i];
+        sm.frb[w][r] = rb[mt][i];
+        sm.fc[w][r] = rc[mt][i];
+      }
+    }
+  __syncthreads();
+  if (w == 0) {
+    const int r = lane;
+    float dgam = 0.f, dbet = 0.f, csum = 0.f;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      dgam += sm.prg[x][r] - sm.pcg[x][r] + sm.frg[x][r];
+      dbet += sm.prb[x][r] + sm.frb[x][r];
+      csum += sm.fc[x][r];
+    }
+    if (r >= n) {
+      dgam = 0.f;
+      csum = 0.f;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) csum += __shfl_xor(csum, off, 64);
+    const float hdot = sm.hd[0] + sm.hd[1] + sm.hd[2] + sm.hd[3];
+    if (r == n - 1) dgam += csum + __expf(sm.gam[n - 1]) * hdot;
+    // dg_s = sum_{r >= s} dgamma_r (reverse inclusive scan)
+    float x = dgam;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float yv = __shfl_down(x, off, 64);
+      if (r + off < 64) x += yv;
+    }
+    if (r < n) {
+      b.dg[(t0 + r) * H + h] = x;
+      static_cast<bf16 *>(b.dbeta)[(t0 + r) * H + h] = (bf16)dbet;
+    }
+  }
+}
+
+hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream) {
+  if (max_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_grad_bf16_kernel, dim3((unsigned)max_chunks, b.H), dim3(256), 0, stream,
+                     b);
+  return hipGetLastError();
+}
+
+}  // namespace gdn
