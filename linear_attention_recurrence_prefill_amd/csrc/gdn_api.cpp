@@ -2,6 +2,7 @@
 // plan's host-side parameters and kernel dispatch.  Declarations and conventions: include/gdn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -397,14 +398,35 @@ namespace {
 
 struct BwdLayout {
   int64_t nc = 0;  // chunk-count bound: ceil(T / 64) + N
+  // forward recompute through the exact split (bf16, d = 128): segment length and unit bound
+  int32_t L = 0;
+  int64_t units = 0;
   size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
+  size_t unit_bm = 0, unit_h0 = 0;
   size_t total = 0;
 };
 
-BwdLayout bwd_layout(const gdn_problem *p) {
-  BwdLayout L;
+// The recompute's segment length: half the forward's exact-split length (the pass that writes the
+// intermediates runs on the general kernel, which is slower per chunk than the pipelined one, so
+// more and shorter units pay off), at least 4; 0 (unsplit) where the forward would not split.
+gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
   const int64_t T = p->total_tokens, H = p->num_heads, D = p->d_k;
-  L.nc = ceil_div(T, gdn::kChunk) + p->num_seqs;
+  L->nc = ceil_div(T, gdn::kChunk) + p->num_seqs;
+  L->L = 0;
+  L->units = 0;
+  if (split_available(p, false)) {
+    int slots = 1;
+    if (p->seg_chunks == 0) {
+      gdn_status s = parallel_slots(p, false, &slots);
+      if (s != GDN_OK) return s;
+    }
+    gdn_problem pe = *p;
+    pe.mode = GDN_MODE_EXACT;  // the backward is defined for the exact forward
+    const int32_t Lf = segment_chunks(&pe, count_chunks(p, nullptr), slots, true);
+    L->L = (Lf > 0 && p->seg_chunks == 0) ? std::max(4, Lf / 2) : Lf;
+    if (L->L > 0) L->units = max_units(p, nullptr, L->L);
+    if (L->units > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "too many work units");
+  }
   const size_t esz = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -412,17 +434,76 @@ BwdLayout bwd_layout(const gdn_problem *p) {
     off = align_up(off + bytes);
     return at;
   };
-  L.gamma = take(sizeof(float) * T * H);
-  L.tmat = take(sizeof(float) * L.nc * H * 64 * 64);
-  L.w = take(sizeof(float) * L.nc * H * 64 * D);
-  L.hc = take(sizeof(float) * L.nc * H * D * D);
-  L.delta = take(sizeof(float) * T * H * D);
-  L.o = take(esz * T * H * D);
-  L.dhn = take(sizeof(float) * L.nc * H * D * D);
-  L.ddelta = take(sizeof(float) * T * H * D);
-  L.dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
-  L.total = off;
-  return L;
+  L->gamma = take(sizeof(float) * T * H);
+  L->tmat = take(sizeof(float) * L->nc * H * 64 * 64);
+  L->w = take(sizeof(float) * L->nc * H * 64 * D);
+  L->hc = take(sizeof(float) * L->nc * H * D * D);
+  L->delta = take(sizeof(float) * T * H * D);
+  L->o = take(esz * T * H * D);
+  L->dhn = take(sizeof(float) * L->nc * H * D * D);
+  L->ddelta = take(sizeof(float) * T * H * D);
+  L->dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
+  if (L->L > 0) {
+    const size_t per = sizeof(float) * (size_t)L->units * H * D * D;
+    L->unit_bm = take(2 * per);
+    L->unit_h0 = take(per);
+  }
+  L->total = off;
+  return GDN_OK;
+}
+
+// Forward recompute of the backward through the exact split: every unit's affine map (B, M) on
+// the pipelined kernel, the maps composed along each sequence into true start states, then the
+// general kernel writes the intermediates from all units in parallel.
+gdn_status run_fwd_recompute_split(const gdn_problem *p, const Tensors &t, float *dbg[6],
+                                   const BwdLayout &L, char *base, hipStream_t stream) {
+  gdn::FwdArgs a{};
+  a.q = t.q;
+  a.k = t.k;
+  a.v = t.v;
+  a.g = t.g;
+  a.beta = t.beta;
+  a.cu = t.cu;
+  a.h0 = t.h0;
+  a.h0_stride = p->h0_seq_stride;
+  a.o = t.o;
+  a.ht = nullptr;
+  a.T = p->total_tokens;
+  a.N = p->num_seqs;
+  a.H = p->num_heads;
+  a.L = L.L;
+  a.scale = p->scale;
+  a.log_thr = p->trunc_log_threshold;
+  a.truncate = 0;
+  float *bm = reinterpret_cast<float *>(base + L.unit_bm);
+  float *uh0 = reinterpret_cast<float *>(base + L.unit_h0);
+  a.units = L.units;
+  a.unit_out = bm;
+  hipError_t e = gdn::launch_fwd_ws_transition(a, L.units, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward recompute: first pass");
+  gdn::SplitArgs sa{};
+  sa.cu = t.cu;
+  sa.N = p->num_seqs;
+  sa.H = p->num_heads;
+  sa.L = L.L;
+  sa.h0 = t.h0;
+  sa.h0_stride = p->h0_seq_stride;
+  sa.unit_bm = bm;
+  sa.unit_h0 = uh0;
+  sa.units = L.units;
+  e = gdn::launch_affine_scan(sa, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward recompute: start states");
+  a.unit_out = nullptr;
+  a.unit_h0 = uh0;
+  a.dbg_gamma = dbg[0];
+  a.dbg_tmat = dbg[1];
+  a.dbg_w = dbg[2];
+  a.dbg_u = dbg[3];
+  a.dbg_hc = dbg[4];
+  a.dbg_delta = dbg[5];
+  e = gdn::launch_fwd(a, p->d_k, true, true, L.units, stream);
+  if (e != hipSuccess) return hip_fail(e, "backward recompute: intermediates");
+  return GDN_OK;
 }
 
 }  // namespace
@@ -433,7 +514,10 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes) {
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
   if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
-  *bytes = bwd_layout(p).total;
+  BwdLayout L;
+  s = bwd_layout(p, &L);
+  if (s != GDN_OK) return s;
+  *bytes = L.total;
   return GDN_OK;
 }
 
@@ -452,7 +536,9 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     if (!aligned16(x)) return fail(GDN_ERR_BAD_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if ((dht && !aligned16(dht)) || (dh0 && !aligned16(dh0)))
     return fail(GDN_ERR_BAD_ALIGNMENT, "dht / dh0 must be 16-byte aligned");
-  const BwdLayout L = bwd_layout(p);
+  BwdLayout L;
+  s = bwd_layout(p, &L);
+  if (s != GDN_OK) return s;
   if (!workspace) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
   if (workspace_bytes < L.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", L.total);
@@ -465,8 +551,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   // forward recompute with the per-chunk intermediates (o goes to scratch)
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
   float *dbg[6] = {gamma, tmat, w, nullptr, hc, delta};
-  gdn_problem pe = *p;
-  s = run_fwd(&pe, t, nullptr, true, dbg, nullptr, 0, stream);
+  if (L.L > 0) {
+    s = check_tensors(t);
+    if (s == GDN_OK) s = device_info(nullptr);
+    if (s == GDN_OK) s = run_fwd_recompute_split(p, t, dbg, L, base, stream);
+  } else {
+    gdn_problem pe = *p;
+    s = run_fwd(&pe, t, nullptr, true, dbg, nullptr, 0, stream);
+  }
   if (s != GDN_OK) return s;
   gdn::BwdArgs b{};
   b.q = q;

@@ -180,8 +180,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
 
   const int ncol0 = wave * (D / 4);
   f32x4 S[MTD][NT];
-  if (cw == 0 && a.h0 != nullptr) {
-    const float *hp = a.h0 + (int64_t)seq * a.h0_stride + (int64_t)h * D * D;
+  // start state: the unit's true start state when the caller provides one per unit (the exact
+  // split's composed states), else h0 at a sequence's start, else zero
+  const float *hp = a.unit_h0 != nullptr ? a.unit_h0 + ((int64_t)unit * H + h) * D * D
+                    : (cw == 0 && a.h0 != nullptr)
+                        ? a.h0 + (int64_t)seq * a.h0_stride + (int64_t)h * D * D
+                        : nullptr;
+  if (hp != nullptr) {
 #pragma unroll
     for (int mt = 0; mt < MTD; ++mt)
 #pragma unroll

@@ -244,16 +244,19 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.0,
-              need_dh0=True, workspace=None):
+              need_dh0=True, workspace=None, seg_chunks=0, num_slots=0):
     """Backward of the exact forward.  Returns dict(dq, dk, dv, dg, dbeta, dh0).  dh0 is
-    [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D])."""
+    [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D]).
+    seg_chunks / num_slots set the segment length of the forward recompute's split and the
+    workgroup slots it is planned for (0: chosen by the library)."""
     lib = load_library()
     T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
         raise ValueError("dout must be contiguous with v's shape and q's dtype")
     if dht is not None and (dht.shape != (N, H, D, D) or dht.dtype != torch.float32):
         raise ValueError("dht must be float32 [N, H, D, D]")
-    p = make_problem(T, N, H, D, q.dtype, "exact", scale,
+    p = make_problem(T, N, H, D, q.dtype, "exact", scale, seg_chunks=seg_chunks,
+                     num_slots=num_slots,
                      h0_seq_stride=stride if stride is not None else H * D * D)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))

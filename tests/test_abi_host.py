@@ -152,3 +152,19 @@ def test_exact_split_workspace(lib):
 def test_status_strings(lib):
     for s in range(9):
         assert lib.gdn_status_string(s)
+
+
+def test_bwd_recompute_split_workspace(lib):
+    """bf16, d = 128 with num_seqs * H < P: the backward's forward recompute runs the exact split,
+    which adds per (unit, head) a pair (B, M) and a start state (3 fp32 states of 128 x 128).
+    Without the host cu_seqlens the unit count is bounded by ceil((ceil(T / 64) + N) / L) + N:
+    T = 1024, N = 2, L = 4 (half the forward's length, floored at 4) gives 7 units."""
+    n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    p = _problem(num_slots=1)  # num_seqs * H >= P: the recompute is not split
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
+    p = _problem(num_slots=256)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
+    assert n2.value - n1.value == 3 * 7 * 8 * 128 * 128 * 4
+    p = _problem(num_slots=256, dtype=0)  # fp32: the general kernel, never split
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
+    assert n2.value < n1.value * 2

@@ -121,3 +121,25 @@ def test_bwd_deterministic(gdn):
         g2 = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], d["h0"])
         for name in NAMES + ("dh0",):
             assert torch.equal(g1[name], g2[name]), name
+
+
+@pytest.mark.parametrize("seg,slots", [(2, 0), (0, 1)])
+def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots):
+    """The forward recompute split into 2-chunk segments (several units per sequence, h0 and a
+    nonzero dht) and run unsplit (one workgroup slot: num_seqs * H >= P) both match the oracle."""
+    inp = make_inputs([700, 333, 0, 1000, 64], H=2, dk=128, dv=128, dtype="bf16", seed=95,
+                      h0_scale=0.5)
+    d = to_dev(inp)
+    rng = np.random.default_rng(11)
+    from gdn_inputs import bf16_round
+    dout = bf16_round(rng.standard_normal(inp["v"].shape).astype(np.float32))
+    N, H, D = 5, 2, 128
+    dht = (0.3 * rng.standard_normal((N, H, D, D))).astype(np.float32)
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], torch.from_numpy(dout).cuda().to(torch.bfloat16),
+                       d["h0"], torch.from_numpy(dht).cuda(), seg_chunks=seg, num_slots=slots)
+    torch.cuda.synchronize()
+    ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], dout, h0=inp["h0"], dht=dht)
+    print(f"[bwd recompute seg={seg} slots={slots}]", flush=True)
+    for name in NAMES:
+        report(name, np64(gr[name]), ref[name], 5e-3)
+    report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3)
