@@ -10,6 +10,7 @@
 #include <mutex>
 
 #include "../../include/gdn.h"
+#include "gdn_bwd_internal.h"
 #include "gdn_internal.h"
 
 namespace {
@@ -406,6 +407,10 @@ struct BwdLayout {
   size_t total = 0;
 };
 
+// bf16 inputs with d = 128 run the backward on the bf16-MFMA chain and gradient kernels (which
+// need no W); everything else on the general fp32-MFMA kernels.
+bool bwd_bf16_path(const gdn_problem *p) { return p->dtype == GDN_DTYPE_BF16 && p->d_k == 128; }
+
 // The recompute's segment length: half the forward's exact-split length (the pass that writes the
 // intermediates runs on the general kernel, which is slower per chunk than the pipelined one, so
 // more and shorter units pay off), at least 4; 0 (unsplit) where the forward would not split.
@@ -436,7 +441,7 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
   };
   L->gamma = take(sizeof(float) * T * H);
   L->tmat = take(sizeof(float) * L->nc * H * 64 * 64);
-  L->w = take(sizeof(float) * L->nc * H * 64 * D);
+  if (!bwd_bf16_path(p)) L->w = take(sizeof(float) * L->nc * H * 64 * D);  // W: general kernels only
   L->hc = take(sizeof(float) * L->nc * H * D * D);
   L->delta = take(sizeof(float) * T * H * D);
   L->o = take(esz * T * H * D);
@@ -545,7 +550,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   char *base = static_cast<char *>(workspace);
   float *gamma = reinterpret_cast<float *>(base + L.gamma);
   float *tmat = reinterpret_cast<float *>(base + L.tmat);
-  float *w = reinterpret_cast<float *>(base + L.w);
+  const bool fast = bwd_bf16_path(p);
+  float *w = fast ? nullptr : reinterpret_cast<float *>(base + L.w);
   float *hc = reinterpret_cast<float *>(base + L.hc);
   float *delta = reinterpret_cast<float *>(base + L.delta);
   // forward recompute with the per-chunk intermediates (o goes to scratch)
@@ -588,11 +594,45 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.N = p->num_seqs;
   b.H = p->num_heads;
   b.scale = p->scale;
-  const bool bf16 = p->dtype == GDN_DTYPE_BF16;
-  hipError_t e = gdn::launch_bwd_chain(b, p->d_k, bf16, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward chain launch");
-  e = gdn::launch_bwd_grad(b, p->d_k, bf16, L.nc, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
+  hipError_t e;
+  if (fast) {
+    // reverse chain, through the exact split when the recompute was split (same units; the
+    // recompute's per-unit buffers are free again)
+    gdn::BwdUnits u{};
+    u.L = L.L;
+    u.units = L.units;
+    if (L.L > 0) {
+      float *bm = reinterpret_cast<float *>(base + L.unit_bm);
+      float *dend = reinterpret_cast<float *>(base + L.unit_h0);
+      u.unit_out = bm;
+      e = gdn::launch_bwd_chain_bf16_transition(b, u, stream);
+      if (e != hipSuccess) return hip_fail(e, "backward chain: first pass");
+      gdn::SplitArgs sa{};
+      sa.cu = cu_seqlens;
+      sa.N = p->num_seqs;
+      sa.H = p->num_heads;
+      sa.L = L.L;
+      sa.h0 = dht;
+      sa.h0_stride = (int64_t)p->num_heads * p->d_k * p->d_v;
+      sa.unit_bm = bm;
+      sa.unit_h0 = dend;
+      sa.units = L.units;
+      e = gdn::launch_affine_scan_reverse(sa, stream);
+      if (e != hipSuccess) return hip_fail(e, "backward chain: end gradients");
+      u.unit_out = nullptr;
+      u.unit_dend = dend;
+    }
+    e = gdn::launch_bwd_chain_bf16(b, u, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward chain launch");
+    e = gdn::launch_bwd_grad_bf16(b, L.nc, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
+  } else {
+    const bool bf16 = p->dtype == GDN_DTYPE_BF16;
+    e = gdn::launch_bwd_chain(b, p->d_k, bf16, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward chain launch");
+    e = gdn::launch_bwd_grad(b, p->d_k, bf16, L.nc, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
+  }
   if (dh0 && shared_h0) {
     e = gdn::launch_sum_dh0(b.dh0_seq, p->num_seqs, p->num_heads, p->d_k, dh0, stream);
     if (e != hipSuccess) return hip_fail(e, "dh0 reduction launch");

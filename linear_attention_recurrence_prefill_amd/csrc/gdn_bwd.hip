@@ -24,7 +24,8 @@
 // chunked form, which equals the derivative of the token recurrence.
 //
 // Both kernels use fp32 MFMA (v_mfma_f32_16x16x4_f32) on fp32 LDS tiles.  Every reduction has a
-// fixed owner and order, so results are bitwise reproducible.
+// fixed owner and order, so results are bitwise reproducible.  They serve fp32 inputs and d = 64;
+// bf16 inputs with d = 128 run the bf16-MFMA kernels of gdn_bwd_chain.hip and gdn_bwd_grad.hip.
 #include <type_traits>
 
 #include "gdn_device.h"
@@ -33,10 +34,6 @@
 
 namespace gdn {
 
-// bf16, d = 128: the reverse chain on bf16 MFMA with split operands (gdn_bwd_chain.hip).
-hipError_t launch_bwd_chain_bf16(const BwdArgs &b, hipStream_t stream);
-// bf16, d = 128: the per-chunk gradients on bf16 MFMA with split operands (gdn_bwd_grad.hip).
-hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
 
 namespace {
 
@@ -603,7 +600,7 @@ __global__ __launch_bounds__(256) void sum_dh0_kernel(const float *__restrict__ 
 hipError_t launch_bwd_chain(const BwdArgs &b, int D, bool is_bf16, hipStream_t stream) {
   const dim3 grid(b.N, b.H), block(256);
   if (D == 128) {
-    if (is_bf16) return launch_bwd_chain_bf16(b, stream);
+    if (is_bf16) return hipErrorNotSupported;  // bf16, d = 128 runs gdn_bwd_chain.hip
     else hipLaunchKernelGGL((bwd_chain_kernel<128, float>), grid, block, 0, stream, b);
   } else {
     if (is_bf16) hipLaunchKernelGGL((bwd_chain_kernel<64, bf16>), grid, block, 0, stream, b);
@@ -617,7 +614,7 @@ hipError_t launch_bwd_grad(const BwdArgs &b, int D, bool is_bf16, int64_t max_ch
   if (max_chunks <= 0) return hipSuccess;
   const dim3 grid((unsigned)max_chunks, b.H), block(256);
   if (D == 128) {
-    if (is_bf16) return launch_bwd_grad_bf16(b, max_chunks, stream);
+    if (is_bf16) return hipErrorNotSupported;  // bf16, d = 128 runs gdn_bwd_grad.hip
     else hipLaunchKernelGGL((bwd_grad_kernel<128, float>), grid, block, 0, stream, b);
   } else {
     if (is_bf16) hipLaunchKernelGGL((bwd_grad_kernel<64, bf16>), grid, block, 0, stream, b);

@@ -1,12 +1,10 @@
 // Per-chunk gradients of the backward for bf16 inputs with d_k = d_v = 128 on gfx950.
 //
-// Per chunk (n <= 64 tokens) and head, from the forward recompute (gamma, Tm = (I + A)^-1, the
-// chunk-start state h, Delta) and the reverse chain (dh' = gradient of the state after the chunk,
-// dDelta), with a = e^gamma, c = e^{gamma_last - gamma}, Gm_ri = e^{gamma_r - gamma_i} (i <= r),
-// dO_s = scale dO:
-//   dR  = Tm^T dDelta                       (gradient of R = diag(beta) (V - diag(a) K h), since
-//                                            Delta = Tm R)
-//   dV  = diag(beta) dR
+// Per chunk (n <= 64 tokens) and head, from the forward recompute (gamma, the chunk-start state
+// h, Delta) and the reverse chain (dh' = gradient of the state after the chunk, dR = Tm^T dDelta
+// = the gradient of R = diag(beta) (V - diag(a) K h), since Delta = Tm R; the chain also writes
+// dV = diag(beta) dR), with a = e^gamma, c = e^{gamma_last - gamma}, Gm_ri = e^{gamma_r -
+// gamma_i} (i <= r), dO_s = scale dO:
 //   dA  = strict_lower(-dR Delta^T)         (gradient of A through Tm = (I + A)^-1)
 //   dPm = (dO_s Delta^T) o Gm on i <= r;    E = dA o Gm o beta_row
 //   Y1 = dO_s h^T,  Y2 = Delta dh'^T,  Rh = dR h^T
@@ -26,9 +24,8 @@
 // 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go straight from HBM into
 // the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
 // so results are bitwise reproducible.
+#include "gdn_bwd_internal.h"
 #include "gdn_device.h"
-#include "gdn_internal.h"
-#include "gdn_unit.h"
 
 namespace gdn {
 namespace {
@@ -70,9 +67,9 @@ struct GradSmem {
   alignas(16) char v[64 * kRowB];   // V; from the tile phase on, E hi and lo
   alignas(16) char dh[64 * kRowB];  // Delta = hi + lo
   alignas(16) char dl[64 * kRowB];
-  alignas(16) char eh[64 * kRowB];  // dDelta = hi + lo; from the second phase on, dR
+  alignas(16) char eh[64 * kRowB];  // dR = hi + lo
   alignas(16) char el[64 * kRowB];
-  alignas(16) char tth[64 * 128];   // Tm^T = hi + lo; from the tile phase on, dPm
+  alignas(16) char tth[64 * 128];   // dPm = hi + lo
   alignas(16) char ttl[64 * 128];
   alignas(16) float gam[64], a[64], c[64], beta[64];
   alignas(16) float prg[4][64];  // per-wave partial row terms of dgamma (tiles)
@@ -137,7 +134,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
   const float *dhn = b.dhn + ((int64_t)cg * H + h) * dd;
 
-  // ---- stage: dO, Q, K, V (bf16 as they are), Delta and dDelta split, Tm^T split; zero past n
+  // ---- stage: dO, Q, K, V (bf16 as they are), Delta and dR split; zero past n
   {
     const char *src[4] = {static_cast<const char *>(b.dout), static_cast<const char *>(b.q),
                           static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
@@ -154,7 +151,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
       }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const float *g = s == 0 ? b.delta : b.ddelta;
+      const float *g = s == 0 ? b.delta : b.ddelta;  // Delta, dR
       char *hi = s == 0 ? sm.dh : sm.eh;
       char *lo = s == 0 ? sm.dl : sm.el;
 #pragma unroll
@@ -165,18 +162,6 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
         const bf16x4 xh = to_bf16x4(x);
         *reinterpret_cast<bf16x4 *>(hi + toff(r, c4)) = xh;
         *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(x - to_f32x4(xh));
-      }
-    }
-    // Tm (rows i, columns r; zero outside [0, n)^2) into Tm^T[r][i]
-    const float *tm = b.tmat + ((int64_t)cg * H + h) * 64 * 64;
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = tid + 256 * m, i = u >> 4, r4 = 4 * (u & 15);
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(tm + i * 64 + r4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int off = poff(r4 + j, i >> 2) + 2 * (i & 3);
-        st_split(sm.tth, sm.ttl, off, x[j]);
       }
     }
     if (w == 0) {
@@ -260,61 +245,21 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   for (int off = 32; off > 0; off >>= 1) hdot += __shfl_xor(hdot, off, 64);
   if (lane == 0) sm.hd[w] = hdot;
 
-  // ---- dR = Tm^T dDelta over this wave's columns (v); dV = diag(beta) dR; dR_r . V_r
-  f32x4 dR[4][2];
+  // ---- dR_r . V_r over this wave's columns (v)
   float rb[4][4];  // row terms of dbeta over this wave's columns: [mt][i]
-  {
-    bf16x8 eb[2][2][2];  // dDelta over tokens: [ks][nt][hi, lo]
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        eb[ks][nt][0] = trfrag(sm.eh, ks, 8 * w + 4 * nt);
-        eb[ks][nt][1] = trfrag(sm.el, ks, 8 * w + 4 * nt);
-      }
+    for (int i = 0; i < 4; ++i) rb[mt][i] = 0.f;
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
+    for (int nt = 0; nt < 2; ++nt) {
+      const f32x4 vv = colv(sm.v, mt, 8 * w + 4 * nt);
+      const f32x4 rr = colv(sm.eh, mt, 8 * w + 4 * nt) + colv(sm.el, mt, 8 * w + 4 * nt);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) dR[mt][nt] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        if (2 * ks + 1 < mt) continue;  // Tm^T[r][i] = 0 for i < r
-        const bf16x8 th = pfrag(sm.tth, mt, ks), tl = pfrag(sm.ttl, mt, ks);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          dR[mt][nt] = mma_bf16(th, eb[ks][nt][0], dR[mt][nt]);
-          dR[mt][nt] = mma_bf16(th, eb[ks][nt][1], dR[mt][nt]);
-          dR[mt][nt] = mma_bf16(tl, eb[ks][nt][0], dR[mt][nt]);
-        }
-      }
-      const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) rb[mt][i] = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x4 vv = colv(sm.v, mt, 8 * w + 4 * nt);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * gq + i;
-          rb[mt][i] += dR[mt][nt][i] * vv[i];
-          if (r < n)
-            static_cast<bf16 *>(b.dv)[((t0 + r) * H + h) * kD + fcol + 16 * nt] =
-                (bf16)(br[i] * dR[mt][nt][i]);
-        }
-      }
+      for (int i = 0; i < 4; ++i) rb[mt][i] += rr[i] * vv[i];
     }
   }
-  __syncthreads();  // every wave is done with dDelta, Tm^T and V
-  // dR (rows r, this wave's columns) into the dDelta tiles' place
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * gq + i, f = fcol + 16 * nt;
-        st_split(sm.eh, sm.el, toff(r, f >> 2) + 2 * (f & 3), dR[mt][nt][i]);
-      }
+  __syncthreads();  // every wave is done with V
   // zero the tiles above the diagonal of dPm (tth, ttl) and E (v region)
   for (int i = tid; i < 6 * 64; i += 256) {
     const int t = i >> 6, rr = (i >> 2) & 15, u = i & 3;

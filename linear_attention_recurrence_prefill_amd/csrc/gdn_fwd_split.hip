@@ -14,6 +14,7 @@
 // under left multiplication by M, so the eight column blocks of a head walk the units without
 // talking to each other.  Eight waves, wave w owning state rows 16 w .. 16 w + 15 of the block,
 // products in fp32 (v_mfma_f32_16x16x4_f32).
+#include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
 
@@ -45,6 +46,9 @@ __device__ void seq_units(const int32_t *cu, int N, int L, int n, int lane, int6
 
 }  // namespace
 
+// kReverse: the backward's walk, from each sequence's last unit to its first (the maps are the
+// reverse chain's, S the state gradient at a unit's end, s.h0 the gradient after the sequence).
+template <bool kReverse>
 __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   __shared__ __attribute__((aligned(16))) float st[16 * kLS];  // st[col * kLS + row]
   const int cb = blockIdx.x, h = blockIdx.y, n = blockIdx.z, H = s.H;
@@ -62,12 +66,12 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) S[i] = hp[(row0 + i) * kD + col];
   }
-  for (int k = 0; k < count; ++k) {
-    const int64_t u = first + k;
+  for (int step = 0; step < count; ++step) {
+    const int64_t u = first + (kReverse ? count - 1 - step : step);
     float *dst = s.unit_h0 + (u * H + h) * dd;
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[(row0 + i) * kD + col] = S[i];
-    if (k + 1 == count) break;
+    if (step + 1 == count) break;
     // S <- M_u S + B_u.  The contraction index of MFMA j of block b is 16 b + 4 gq + j on both
     // operands, so that each lane reads 4 consecutive entries of M's row and of S's column.
     *reinterpret_cast<f32x4 *>(&st[cl * kLS + row0]) = S;
@@ -92,7 +96,13 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
 
 hipError_t launch_affine_scan(const SplitArgs &s, hipStream_t stream) {
   if (s.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(affine_scan_kernel, dim3(kD / 16, s.H, s.N), dim3(512), 0, stream, s);
+  hipLaunchKernelGGL(affine_scan_kernel<false>, dim3(kD / 16, s.H, s.N), dim3(512), 0, stream, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_affine_scan_reverse(const SplitArgs &s, hipStream_t stream) {
+  if (s.N <= 0) return hipSuccess;
+  hipLaunchKernelGGL(affine_scan_kernel<true>, dim3(kD / 16, s.H, s.N), dim3(512), 0, stream, s);
   return hipGetLastError();
 }
 
