@@ -54,6 +54,10 @@ __device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &l
   hi = cat8(h0, h1);
   lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
 }
+__device__ __forceinline__ void dma16(const char *g, char *l) {
+  __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
+}
+__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void st_split(char *hi, char *lo, int off, float x) {
   const bf16 h = (bf16)x;
   *reinterpret_cast<bf16 *>(hi + off) = h;
@@ -134,46 +138,74 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
   const float *dhn = b.dhn + ((int64_t)cg * H + h) * dd;
 
-  // ---- stage: dO, Q, K, V (bf16 as they are), Delta and dR split; zero past n
+  // ---- stage.  Every load is issued before any is waited for: dO, Q, K, V go straight into LDS
+  //      (direct loads; rows past n repeat the chunk's last token, which every use masks), Delta
+  //      and dR through registers (split; rows past n zero), and each wave's rows of h and dh'
+  //      into registers for its B operands.
+  const int fcol = 32 * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
+  f32x4 hv[2][4][2], gv[2][4][2];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
   {
     const char *src[4] = {static_cast<const char *>(b.dout), static_cast<const char *>(b.q),
                           static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
     char *dst[4] = {sm.dout, sm.q, sm.k, sm.v};
+    // wave w fills rows 16 w .. 16 w + 15; lane l of load j writes physical unit l % 16 of row
+    // 16 w + 4 j + l / 16, which holds logical unit (l % 16) ^ sw(row)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int u = tid + 256 * m, r = u >> 4, c16 = u & 15;
-        uint4 x{0u, 0u, 0u, 0u};
-        if (r < n) x = *reinterpret_cast<const uint4 *>(src[s] + (t0 + r) * tok_bytes +
-                                                         (int64_t)h * kRowB + c16 * 16);
-        *reinterpret_cast<uint4 *>(dst[s] + r * kRowB + ((c16 ^ sw(r)) << 4)) = x;
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * w + 4 * j + (lane >> 4);
+        dma16(src[s] + (t0 + min(r, n - 1)) * tok_bytes + (int64_t)h * kRowB +
+                  (((lane & 15) ^ sw(r)) << 4),
+              dst[s] + (16 * w + 4 * j) * kRowB);
       }
+    f32x4 xr[2][8];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float *g = s == 0 ? b.delta : b.ddelta;  // Delta, dR
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int u = tid + 256 * m, r = u >> 5, c4 = u & 31;
+        xr[s][m] = r < n ? *reinterpret_cast<const f32x4 *>(g + ((t0 + r) * H + h) * kD + 4 * c4)
+                         : zero4();
+      }
+    }
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
+        hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
+        hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
+        gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
+        gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+      }
+    float gmv = 0.f, bev = 0.f;
+    if (w == 0 && lane < n) {
+      gmv = b.gamma[(t0 + lane) * H + h];
+      bev = (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h];
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
       char *hi = s == 0 ? sm.dh : sm.eh;
       char *lo = s == 0 ? sm.dl : sm.el;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const int u = tid + 256 * m, r = u >> 5, c4 = u & 31;
-        const f32x4 x = r < n ? *reinterpret_cast<const f32x4 *>(g + ((t0 + r) * H + h) * kD + 4 * c4)
-                              : zero4();
-        const bf16x4 xh = to_bf16x4(x);
+        const bf16x4 xh = to_bf16x4(xr[s][m]);
         *reinterpret_cast<bf16x4 *>(hi + toff(r, c4)) = xh;
-        *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(x - to_f32x4(xh));
+        *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(xr[s][m] - to_f32x4(xh));
       }
     }
     if (w == 0) {
-      const float gmv = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
       const float glast = __shfl(gmv, n - 1, 64);
       sm.gam[lane] = lane < n ? gmv : glast;
       sm.a[lane] = lane < n ? __expf(gmv) : 0.f;
       sm.c[lane] = lane < n ? __expf(glast - gmv) : 0.f;
-      sm.beta[lane] =
-          lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
+      sm.beta[lane] = bev;
     }
   }
+  wait_vm0();  // this wave's direct loads have landed
   __syncthreads();
 
   // fragment readers
@@ -199,8 +231,6 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
     return to_f32x4(ldtr(t + toff(16 * m + 4 * gq + (cl >> 2), u0 + (cl & 3))));
   };
 
-  const int fcol = 32 * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
-
   // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
   bf16x8 hh[2][4], hl[2][4];
   f32x4 Y1[4][2], Y2[4][2];
@@ -211,11 +241,8 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
-        const f32x4 h0 = *reinterpret_cast<const f32x4 *>(hS + off);
-        const f32x4 h1 = *reinterpret_cast<const f32x4 *>(hS + off + 4);
-        const f32x4 d0 = *reinterpret_cast<const f32x4 *>(dhn + off);
-        const f32x4 d1 = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+        const f32x4 h0 = hv[nt][ks][0], h1 = hv[nt][ks][1];
+        const f32x4 d0 = gv[nt][ks][0], d1 = gv[nt][ks][1];
         split8(h0, h1, hh[nt][ks], hl[nt][ks]);
         split8(d0, d1, gh[nt][ks], gl[nt][ks]);
 #pragma unroll
