@@ -457,11 +457,13 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
   return GDN_OK;
 }
 
-// Forward recompute of the backward through the exact split: every unit's affine map (B, M) on
-// the pipelined kernel, the maps composed along each sequence into true start states, then the
-// general kernel writes the intermediates from all units in parallel.
-gdn_status run_fwd_recompute_split(const gdn_problem *p, const Tensors &t, float *dbg[6],
-                                   const BwdLayout &L, char *base, hipStream_t stream) {
+// Forward recompute of the backward for bf16 inputs with d = 128, on the pipelined forward kernel:
+// the per-chunk start states, Delta and gamma, from all units in parallel when the recompute is
+// split (every unit's affine map (B, M), then the maps composed along each sequence into true
+// start states, as in the forward's exact split).
+gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float *gamma, float *hc,
+                                  float *delta, const BwdLayout &L, char *base,
+                                  hipStream_t stream) {
   gdn::FwdArgs a{};
   a.q = t.q;
   a.k = t.k;
@@ -480,33 +482,35 @@ gdn_status run_fwd_recompute_split(const gdn_problem *p, const Tensors &t, float
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = 0;
-  float *bm = reinterpret_cast<float *>(base + L.unit_bm);
-  float *uh0 = reinterpret_cast<float *>(base + L.unit_h0);
-  a.units = L.units;
-  a.unit_out = bm;
-  hipError_t e = gdn::launch_fwd_ws_transition(a, L.units, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward recompute: first pass");
-  gdn::SplitArgs sa{};
-  sa.cu = t.cu;
-  sa.N = p->num_seqs;
-  sa.H = p->num_heads;
-  sa.L = L.L;
-  sa.h0 = t.h0;
-  sa.h0_stride = p->h0_seq_stride;
-  sa.unit_bm = bm;
-  sa.unit_h0 = uh0;
-  sa.units = L.units;
-  e = gdn::launch_affine_scan(sa, stream);
-  if (e != hipSuccess) return hip_fail(e, "backward recompute: start states");
-  a.unit_out = nullptr;
-  a.unit_h0 = uh0;
-  a.dbg_gamma = dbg[0];
-  a.dbg_tmat = dbg[1];
-  a.dbg_w = dbg[2];
-  a.dbg_u = dbg[3];
-  a.dbg_hc = dbg[4];
-  a.dbg_delta = dbg[5];
-  e = gdn::launch_fwd(a, p->d_k, true, true, L.units, stream);
+  hipError_t e;
+  int64_t units = p->num_seqs;
+  if (L.L > 0) {
+    float *bm = reinterpret_cast<float *>(base + L.unit_bm);
+    float *uh0 = reinterpret_cast<float *>(base + L.unit_h0);
+    units = L.units;
+    a.units = L.units;
+    a.unit_out = bm;
+    e = gdn::launch_fwd_ws_transition(a, L.units, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward recompute: first pass");
+    gdn::SplitArgs sa{};
+    sa.cu = t.cu;
+    sa.N = p->num_seqs;
+    sa.H = p->num_heads;
+    sa.L = L.L;
+    sa.h0 = t.h0;
+    sa.h0_stride = p->h0_seq_stride;
+    sa.unit_bm = bm;
+    sa.unit_h0 = uh0;
+    sa.units = L.units;
+    e = gdn::launch_affine_scan(sa, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward recompute: start states");
+    a.unit_out = nullptr;
+    a.unit_h0 = uh0;
+  }
+  a.dbg_gamma = gamma;
+  a.dbg_hc = hc;
+  a.dbg_delta = delta;
+  e = gdn::launch_fwd_ws_dump(a, units, stream);
   if (e != hipSuccess) return hip_fail(e, "backward recompute: intermediates");
   return GDN_OK;
 }
@@ -557,10 +561,10 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   // forward recompute with the per-chunk intermediates (o goes to scratch)
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
   float *dbg[6] = {gamma, tmat, w, nullptr, hc, delta};
-  if (L.L > 0) {
+  if (fast) {
     s = check_tensors(t);
     if (s == GDN_OK) s = device_info(nullptr);
-    if (s == GDN_OK) s = run_fwd_recompute_split(p, t, dbg, L, base, stream);
+    if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc, delta, L, base, stream);
   } else {
     gdn_problem pe = *p;
     s = run_fwd(&pe, t, nullptr, true, dbg, nullptr, 0, stream);
@@ -596,6 +600,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.scale = p->scale;
   hipError_t e;
   if (fast) {
+    e = gdn::launch_bwd_tm(b, tmat, L.nc, stream);
+    if (e != hipSuccess) return hip_fail(e, "backward: Tm");
     // reverse chain, through the exact split when the recompute was split (same units; the
     // recompute's per-unit buffers are free again)
     gdn::BwdUnits u{};

@@ -421,6 +421,99 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
   }
 }
 
+// Tm = (I + A)^-1 of every chunk, A_ri = beta_r e^{gamma_r - gamma_i} k_r . k_i for i < r < n
+// ("How to Speed Up GDN Kernels for Qwen Models", section "What GDN actually computes"), fp32,
+// zero outside [0, n)^2, into tmat [chunks, H, 64, 64].  One wave per (chunk, head): K K^T on
+// bf16 MFMA (exact products of the bf16 inputs), A into LDS, then forward substitution column by
+// column, lane j holding column j of Tm: Tm[r][j] = [r == j] - sum_{j <= i < r} A[r][i] Tm[i][j].
+__global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict__ tmat) {
+  __shared__ __attribute__((aligned(16))) float am[64][68];
+  const int lane = threadIdx.x, gq = lane >> 4, cl = lane & 15;
+  const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
+  // the chunk's sequence and index within it
+  int64_t before = 0;
+  int seq = -1, cidx = 0;
+  for (int base = 0; base < b.N; base += 64) {
+    const int nn = base + lane;
+    const int ch = nn < b.N ? max(0, (b.cu[nn + 1] - b.cu[nn] + kChunk - 1) / kChunk) : 0;
+    int sc = ch;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(sc, off, 64);
+      if (lane >= off) sc += y;
+    }
+    const uint64_t hit = __ballot(nn < b.N && before + sc > cg);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      seq = base + l;
+      cidx = (int)(cg - before - __shfl(sc - ch, l, 64));
+      break;
+    }
+    before += __shfl(sc, 63, 64);
+  }
+  if (seq < 0) return;
+  const int64_t ts0 = b.cu[seq], ts1 = b.cu[seq + 1];
+  if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;
+  const int64_t t0 = ts0 + (int64_t)cidx * kChunk;
+  const int n = (int)min<int64_t>(kChunk, ts1 - t0);
+  const float gam = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
+  const float bet = lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
+  // K rows as MFMA operands straight from HBM: row 16 m + cl, elements 32 ks + 8 gq .. + 7 (rows
+  // past n read the last token; A masks them)
+  const bf16 *gk = static_cast<const bf16 *>(b.k) + (int64_t)h * kD;
+  bf16x8 kf[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int64_t t = t0 + min(16 * m + cl, n - 1);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[m][ks] = *reinterpret_cast<const bf16x8 *>(gk + t * H * kD + 32 * ks + 8 * gq);
+  }
+#pragma unroll
+  for (int mr = 0; mr < 4; ++mr)
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      f32x4 acc = zero4();
+      if (mi <= mr) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kf[mr][ks], kf[mi][ks], acc);
+      }
+      // acc[e] = k_r . k_i for r = 16 mr + 4 gq + e, i = 16 mi + cl
+      const int i = 16 * mi + cl;
+      const float gi = __shfl(gam, i, 64);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * mr + 4 * gq + e;
+        const float gr = __shfl(gam, r, 64), br = __shfl(bet, r, 64);
+        am[r][i] = (i < r && r < n) ? br * __expf(gr - gi) * acc[e] : 0.f;
+      }
+    }
+  __syncthreads();
+  float x[64];
+#pragma unroll
+  for (int r = 0; r < 64; ++r) {
+    float acc = 0.f;
+#pragma unroll
+    for (int i4 = 0; i4 < r / 4 * 4; i4 += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&am[r][i4]);
+      acc += a4[0] * x[i4] + a4[1] * x[i4 + 1] + a4[2] * x[i4 + 2] + a4[3] * x[i4 + 3];
+    }
+#pragma unroll
+    for (int i = r / 4 * 4; i < r; ++i) acc += am[r][i] * x[i];
+    x[r] = r == lane ? 1.f : (r < lane ? 0.f : -acc);
+  }
+  float *dst = tmat + ((int64_t)cg * H + h) * 64 * 64;
+  const bool col_in = lane < n;
+#pragma unroll
+  for (int r = 0; r < 64; ++r) dst[r * 64 + lane] = (col_in && r < n) ? x[r] : 0.f;
+}
+
+hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream) {
+  if (max_chunks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(bwd_tm_kernel, dim3((unsigned)max_chunks, b.H), dim3(64), 0, stream, b, tmat);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_t stream) {
   const int64_t units = u.L > 0 ? u.units : b.N;
   if (units <= 0) return hipSuccess;

@@ -24,6 +24,8 @@ struct BwdUnits {
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_t stream);
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream);
+// Tm = (I + A)^-1 of every chunk (fp32 [chunks, H, 64, 64]) from k, beta and the recompute's gamma.
+hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream);
 // Per-chunk gradients from the chain's dhn and dR (dV is the chain's).
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
 // The affine scan walked from each sequence's last unit to its first: S_end(u - 1) = M'_u

@@ -155,12 +155,15 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 
 }  // namespace
 
+// kDump: the pass of the backward's forward recompute.  No output; per chunk it writes the state
+// at the chunk's start (a.dbg_hc [chunks, H, D, D]), Delta (a.dbg_delta [T, H, D]) and gamma
+// (a.dbg_gamma [T, H]), all fp32, chunks numbered across sequences.
 // kTransition: the first pass of the exact split.  Workgroup (unit, head, z) runs the unit's
 // chunks from a fixed start without output and writes its final state to a.unit_out[z]: z = 0
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
 // with V = 0 (the unit's transition matrix M, so that the state after the unit is
 // M S_start + B for any start state).
-template <bool kTransition>
+template <bool kTransition, bool kDump = false>
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
   // V of the chunk on the chain, per chain wave its 32 columns: 64 rows of 64 bytes, the 16-byte
@@ -174,11 +177,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M half
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(a.cu, a.N, a.L, unit, false, lane, un);
+    const bool ok = find_unit(a.cu, a.N, a.L, unit, kDump, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;
       sm.imisc[2] = un.c1;
+      if (kDump) sm.imisc[3] = (int)un.chunk_base;
     }
   }
   __syncthreads();
@@ -186,6 +190,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   if (seq < 0) return;
   const int c0 = __builtin_amdgcn_readfirstlane(sm.imisc[1]);
   const int c1 = __builtin_amdgcn_readfirstlane(sm.imisc[2]);
+  const int64_t chunk_base = kDump ? __builtin_amdgcn_readfirstlane(sm.imisc[3]) : 0;
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
@@ -286,6 +291,17 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     const int vu = 4 * w + ((lane & 3) ^ (((lane >> 4) & 1) << 1));
     const int o_gv = pin((int)((lane >> 2) * tok_bytes) + vu * 16);
     const int o_go = pin((int)(cl * tok_bytes) + (ncol + 8 * gq) * 2);      // O stores
+    // dump stores (fp32): the state (row 4 gq of a 128 x 128 matrix) and Delta (token 4 gq), at
+    // this lane's column of tile nt
+    int o_dh[2] = {0, 0}, o_dd[2] = {0, 0};
+    if constexpr (kDump) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int col = ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3);
+        o_dh[nt] = pin((4 * gq * kD + col) * 4);
+        o_dd[nt] = pin((4 * gq * H * kD + col) * 4);
+      }
+    }
     auto trk = [&](const char *t, int rows, int mt) { return ldtr(t + (rows / 16) * kBlk + o_tr[mt]); };
 
     // S[mt][nt] holds rows 16 mt + 4 gq + i of column ncol + 8 (cl / 4) + 4 nt + cl % 4 (tile nt's
@@ -362,7 +378,20 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int cc = c - 1;
         const int64_t t0 = chunk_t0(cc);
         const int n = chunk_n(cc);
-        const bool emit = !kTransition && cc >= c0;
+        const bool emit = !kTransition && !kDump && cc >= c0;
+        if constexpr (kDump) {  // the state at the chunk's start (all rows in range; row offsets
+                                // as scalar operands)
+          const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+              a.dbg_hc + ((chunk_base + cc) * H + h) * kD * kD, (short)0, kD * kD * 4, 0x00020000);
+#pragma unroll
+          for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int nt = 0; nt < 2; ++nt)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[mt][nt][i]), hr,
+                                                      o_dh[nt], (16 * mt + i) * kD * 4, 0);
+        }
         const int Y = cc & 1;
         const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
         const WsSmem::Vec &vc = sm.vec[cc % 3];
@@ -412,6 +441,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           const WsSmem::Blocks &B = sm.tb[Y];
           auto sfrag = [&](const char *blk) { return ld8(blk + o_sf); };
           auto bfrag = [&](int m) { return ld16(B.nabl + 1024 * m + o_bf[0], B.nabl + 1024 * m + o_bf[1]); };
+          const int64_t tok0 = t0;  // (t0 below names the block T'_{2h})
           // one 32-token half: Delta_{2h} = T'_{2h} R'_{2h}, Delta_{2h+1} = T'_{2h+1} (R'_{2h+1} -
           // A'_{2h+1,2h} Delta_{2h})
           auto half_solve = [&](int hb, const char *na) {
@@ -424,6 +454,22 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               R[2 * hb + 1][nt] = mma_bf16_k16(nf, to_bf16x4(Dl0[nt]), R[2 * hb + 1][nt]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Dl1[nt] = mma_bf16_k16(t1, to_bf16x4(R[2 * hb + 1][nt]), zero4());
+            if constexpr (kDump) {  // Delta rows 32 hb + 4 gq + i and 32 hb + 16 + 4 gq + i; rows
+                                    // at or past the chunk's end fall outside the range
+              const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
+                  a.dbg_delta + (tok0 * H + h) * kD, (short)0, n * H * kD * 4, 0x00020000);
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int nt = 0; nt < 2; ++nt) {
+                  // the row goes into the vector offset, which the range check covers
+                  const int v0 = o_dd[nt] + (32 * hb + i) * H * kD * 4;
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Dl0[nt][i]), dr,
+                                                        v0, 0, 0);
+                  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(Dl1[nt][i]), dr,
+                                                        v0 + 16 * H * kD * 4, 0, 0);
+                }
+            }
             const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
             const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
 #pragma unroll
@@ -573,6 +619,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       vc.edt[lane] = __expf(gl - gam);
       vc.gam[lane] = gam;
       if (lane == 0) vc.egl[0] = __expf(gl);
+      if (kDump && lane < n) a.dbg_gamma[(chunk_t0(c) + lane) * H + h] = gam;
     };
     GB gbx{0.f, 0};
     if (cw < c1) {
@@ -580,7 +627,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       wait_vm0();
       gate_vectors(gbx, cw);
       dma_tile(sm.kq[cw % 3][0], gk_, cw);
-      if (!kTransition && cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, cw);
+      if (!kTransition && !kDump && cw >= c0) dma_tile(sm.kq[cw % 3][1], gq_, cw);
       if (cw + 1 < c1) gbx = gb_load(cw + 1);
     }
     wait_vm0();
@@ -593,7 +640,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (c + 1 < c1) {
         gate_vectors(gbx, c + 1);
         dma_tile(sm.kq[(c + 1) % 3][0], gk_, c + 1);
-        if (!kTransition && c + 1 >= c0) dma_tile(sm.kq[(c + 1) % 3][1], gq_, c + 1);
+        if (!kTransition && !kDump && c + 1 >= c0) dma_tile(sm.kq[(c + 1) % 3][1], gq_, c + 1);
         if (c + 2 < c1) gbx = gb_load(c + 2);
       }
       wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
@@ -606,7 +653,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     for (int c = cw; c <= c1; ++c) {
       if (c < c1) {
         // ---------------- chunk c ----------------
-        const bool emit = !kTransition && c >= c0;
+        const bool emit = !kTransition && !kDump && c >= c0;
         const int Y = c & 1;
         const char *Kt = sm.kq[c % 3][0], *Qt = sm.kq[c % 3][1];
         const WsSmem::Vec &vc = sm.vec[c % 3];
@@ -725,6 +772,13 @@ int fwd_ws_blocks_per_cu() {
 hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
   if (max_units <= 0) return hipSuccess;
   hipLaunchKernelGGL(fwd_ws_kernel<false>, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_ws_dump(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
+  if (max_units <= 0) return hipSuccess;
+  hipLaunchKernelGGL((fwd_ws_kernel<false, true>), dim3((unsigned)max_units, a.H), dim3(512), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -80,6 +80,9 @@ int fwd_ws_blocks_per_cu();
 // Exact split: the first pass (B and M of every unit, no output; grid (units, H, 2)) and the
 // middle pass (each sequence's units in order: S_start(u + 1) = M_u S_start(u) + B_u).
 hipError_t launch_fwd_ws_transition(const FwdArgs &a, int64_t units, hipStream_t stream);
+// The backward's recompute on the same pipeline: no output, the per-chunk start states, Delta and
+// gamma to a.dbg_hc, a.dbg_delta, a.dbg_gamma (from a.unit_h0 per unit when given).
+hipError_t launch_fwd_ws_dump(const FwdArgs &a, int64_t max_units, hipStream_t stream);
 hipError_t launch_affine_scan(const SplitArgs &s, hipStream_t stream);
 
 // Workgroups of a forward kernel that fit on one CU at once (from the runtime's occupancy query).
