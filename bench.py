@@ -12,7 +12,8 @@ A step is one forward (gdn_chunk_fwd: o and the final state) on the current stre
 steps run first; then exactly K steps are timed with HIP events on that stream, bracketed by
 device synchronisations.  ``value`` is tokens per second of the headline mode (the page's
 truncated-history split, section "Lever 1"); the exact mode is timed the same way and reported
-beside it.
+beside it, and so is the training backward (gdn_chunk_bwd on the packed 65536-token workload of
+the pages' training runs, object ``backward`` with its own HBM roofline fraction).
 
 ``roofline``: the forward is bound by HBM bandwidth (about 176 flop per byte against the
 MI355X's ~315 flop/byte ridge).  Algorithmic bytes per launch = 1030 B per (token, head)
@@ -43,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
 FLOP_PER_TH = 181_589        # chunked-form matrix products per (token, head), d = 128
 BYTES_PER_TH = 4 * 256 + 4 + 2
+BWD_BYTES_PER_TH = 7 * 256 + 2 * 4 + 2 * 2  # q k v dO dq dk dv (bf16), g dg (fp32), beta dbeta
 STATE_BYTES = 128 * 128 * 4
 PAGE_H200_MS = 0.31          # the page's FlashQLA figure for this workload (H200; context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_long32k.json")
@@ -56,6 +58,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training backward timed beside the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB each (reads and writes MIB MiB per "
                          "launch): the reference for scaling HBM traffic counters, then exit")
@@ -191,10 +195,60 @@ def main():
         line[f"{m}_mode"] = {"ms_per_step": results[m], "value": T / (results[m] / 1e3),
                              "roofline_frac": bytes_launch / (results[m] / 1e3) / 1e9
                              / HBM_PEAK_GBS}
+    if not args.no_backward:
+        line["backward"] = time_backward(gdn, torch, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_backward(gdn, torch, steps, warmup):
+    """The training step's backward (gdn_chunk_bwd: forward recompute, reverse chain, per-chunk
+    gradients) on the packed 65536-token workload of 4096..16384-token documents, H = 8, d = 128,
+    bf16, dO ~ N(0, 1), timed like the forward.  Algorithmic bytes: q, k, v, dO read and dq, dk,
+    dv written in bf16, g read and dg written in fp32, beta read and dbeta written in bf16."""
+    from gdn_inputs import workload
+
+    inp = workload("train")
+    T, H, D = inp["q"].shape
+    dev = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).cuda()
+           for n in ("q", "k", "v", "beta", "dout")}
+    for n in dev:
+        dev[n] = dev[n].to(torch.bfloat16)
+    g = torch.from_numpy(inp["g"]).cuda()
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    import ctypes
+
+    from linear_attention_recurrence_prefill_amd.gdn import make_problem
+
+    p = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact")
+    nbytes = ctypes.c_size_t(0)
+    assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)) == 0
+    ws = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")  # allocated once, outside
+
+    def step():
+        gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes_alg = BWD_BYTES_PER_TH * T * H
+    achieved = nbytes_alg / (ms / 1e3) / 1e9
+    return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
+                        f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
+            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "bytes_per_step": nbytes_alg}}
 
 
 def kernel_source_sha():
