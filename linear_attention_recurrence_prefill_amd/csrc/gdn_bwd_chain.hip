@@ -20,8 +20,9 @@
 // One workgroup of four waves per (unit, head), a unit being a sequence or a segment of it; wave
 // w owns columns [32 w, 32 w + 32) of the state gradient as MFMA accumulator tiles (rows
 // 16 md + 4 gq + i, column 32 w + 16 nt + cl).  K, Q and dO of the next chunk stream from HBM
-// into a second set of LDS tiles with direct global->LDS loads while the current chunk runs; Tm
-// and the gates of the next chunk are loaded into registers and moved to LDS at the chunk turn.
+// into a second set of LDS tiles with direct global->LDS loads while the current chunk runs, and
+// so does Tm^T (already split and laid out by bwd_tm_kernel); the gates of the next chunk are
+// loaded into registers and moved to LDS at the chunk turn.
 // Products that contract over tokens read the token-major tiles with the transposing LDS read.
 // The contraction index of a pair of accumulator tiles used as an MFMA operand is permuted (item
 // j of lane group gq is index 32 ks + 16 (j / 4) + 4 gq + j % 4) and the LDS operand is read in
@@ -82,8 +83,7 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 struct ChainSmem {
   alignas(16) char kqo[2][3][kTile];  // [set][K, Q, dO]: this chunk's and the next chunk's
-  alignas(16) char tth[64 * 128];     // Tm^T = hi + lo (row r, column i)
-  alignas(16) char ttl[64 * 128];
+  alignas(16) char tt[2][2][64 * 128];  // [set][hi, lo]: Tm^T = hi + lo (row r, column i)
   alignas(16) char pth[64 * 128];     // P^T = hi + lo (row i, column r)
   alignas(16) char ptl[64 * 128];
   alignas(16) float gam[64];  // gamma, rows past n hold gamma_last
@@ -184,14 +184,24 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     return cat8(ldtr(t + toff(r, u)), ldtr(t + toff(r + 16, u)));
   };
 
+  // store offsets (bytes): row 4 gq of a 128 x 128 fp32 matrix and token 4 gq of a [T, H, 128]
+  // fp32 tensor, at this lane's column of tile nt
+  int o_st[2], o_tk[2];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    o_st[nt] = (4 * gq * kD + col0 + 16 * nt) * 4;
+    o_tk[nt] = (4 * gq * H * kD + col0 + 16 * nt) * 4;
+  }
+
   auto chunk_t0 = [&](int c) { return ts0 + (int64_t)c * kChunk; };
   auto chunk_n = [&](int c) { return (int)min<int64_t>(kChunk, ts1 - chunk_t0(c)); };
   // next-chunk loads: K, Q, dO by direct loads into tile set `set` (wave w: rows 16 w .. 16 w +
   // 15; lane l of load j writes physical unit l % 16 of row 16 w + 4 j + l / 16, which holds
   // logical unit (l % 16) ^ sw(row); rows past n repeat the chunk's last token); Tm (this
   // thread's 16 entries) and the gates into registers
-  f32x4 tmr[4];
-  float g_r = 0.f, b_r = 0.f;
+  float g_r = 0.f;
+  unsigned short b_r = 0;  // beta's bits: converted at the chunk turn, so that nothing waits
+                           // for the next chunk's loads early
   auto issue = [&](int c, int set) {
     const int64_t t0 = chunk_t0(c);
     const int n = chunk_n(c);
@@ -204,16 +214,14 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       dma16(gqp + off, sm.kqo[set][1] + lo);
       dma16(gdo + off, sm.kqo[set][2] + lo);
     }
-    const float *tm = b.tmat + ((chunk_base + c) * H + h) * 64 * 64;
+    // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
+    const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = tid + 256 * m;
-      tmr[m] = *reinterpret_cast<const f32x4 *>(tm + (u >> 4) * 64 + 4 * (u & 15));
-    }
+    for (int j = 0; j < 4; ++j) dma16(tm + (4 * w + j) * 1024 + 16 * lane, &sm.tt[set][0][0] + (4 * w + j) * 1024);
     if (w == 0) {
       const int64_t t = t0 + min(lane, n - 1);
       g_r = b.gamma[t * H + h];
-      b_r = (float)gb[t * H + h];
+      b_r = reinterpret_cast<const unsigned short *>(gb)[t * H + h];
     }
   };
 
@@ -226,27 +234,23 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     const int64_t cg = chunk_base + c;
     wait_vm0();       // this chunk's loads have landed (and this wave's stores are done)
     __syncthreads();  // ... for every wave; every wave is done with the previous chunk's LDS
-    // ---- Tm^T and the gate vectors of this chunk into LDS, then the next chunk's loads
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int u = tid + 256 * m, i = u >> 4, r4 = 4 * (u & 15);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) st_split(sm.tth, sm.ttl, poff(r4 + j, i >> 2) + 2 * (i & 3), tmr[m][j]);
-    }
+    // ---- the gate vectors of this chunk into LDS, then the next chunk's loads
     if (w == 0) {
       const float glast = __shfl(g_r, n - 1, 64);
       const bool in = lane < n;
       const float ea = __expf(g_r);
+      const float bt = __uint_as_float((unsigned)b_r << 16);
       sm.gam[lane] = in ? g_r : glast;
       sm.as[lane] = in ? xs * ea : 0.f;
       sm.c[lane] = in ? __expf(glast - g_r) : 0.f;
-      sm.ab[lane] = in ? ea * b_r : 0.f;
-      sm.beta[lane] = in ? b_r : 0.f;
+      sm.ab[lane] = in ? ea * bt : 0.f;
+      sm.beta[lane] = in ? bt : 0.f;
     }
     if (c > c0) issue(c - 1, set ^ 1);
     __syncthreads();
-    // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo
-    for (int t = w; t < 10; t += 4) {
+    // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo (the M' half
+    //      runs with dO = 0 and needs neither P nor the dO products below)
+    for (int t = w; t < (is_m ? 0 : 10); t += 4) {
       const int mr = kPtR[t], mi = kPtI[t];
       f32x4 acc = zero4();
 #pragma unroll
@@ -269,15 +273,17 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     const float lam = __expf(sm.gam[63]);
 
     // ---- dh' of this chunk to the workspace
-    if (!kTransition) {
-      float *dhn = b.dhn + (cg * H + h) * dd;
+    if (!kTransition) {  // row offsets as scalar operands
+      const __amdgpu_buffer_rsrc_t hr =
+          __builtin_amdgcn_make_buffer_rsrc(b.dhn + (cg * H + h) * dd, (short)0, (int)dd * 4, 0x00020000);
 #pragma unroll
       for (int md = 0; md < 8; ++md)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            dhn[(16 * md + 4 * gq + i) * kD + col0 + 16 * nt] = G[md][nt][i];
+          for (int nt = 0; nt < 2; ++nt)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[md][nt][i]), hr, o_st[nt],
+                                                  (16 * md + i) * kD * 4, 0);
     }
 
     // ---- dDelta = P^T dO_s + diag(c) K dh'
@@ -304,7 +310,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
+      for (int ks = 0; ks < 2 && !is_m; ++ks) {
         bf16x8 of[2];  // dO over tokens, exact
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) of[nt] = trfrag(Ot, ks, 8 * w + 4 * nt);
@@ -342,7 +348,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (2 * ks + 1 < mt) continue;
-          const bf16x8 th = pfrag(sm.tth, mt, ks), tl = pfrag(sm.ttl, mt, ks);
+          const bf16x8 th = pfrag(sm.tt[set][0], mt, ks), tl = pfrag(sm.tt[set][1], mt, ks);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             dR[mt][nt] = mma_bf16(th, eh[ks][nt], dR[mt][nt]);
@@ -352,21 +358,27 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
         }
       }
     }
-    if (!kTransition) {
+    if (!kTransition) {  // rows at or past the chunk's end fall outside the buffer ranges
+      const int64_t base = (t0 * H + h) * kD;
+      const __amdgpu_buffer_rsrc_t rr =
+          __builtin_amdgcn_make_buffer_rsrc(b.ddelta + base, (short)0, n * H * kD * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+          static_cast<bf16 *>(b.dv) + base, (short)0, n * H * kD * 2, 0x00020000);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int i = 0; i < 4; ++i) {
+          const int row = (16 * mt + i) * H * kD;  // + 4 gq rows in the lane-constant part
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = 16 * mt + 4 * gq + i;
-            if (r < n) {
-              const int64_t gi = ((t0 + r) * H + h) * kD + col0 + 16 * nt;
-              b.ddelta[gi] = dR[mt][nt][i];
-              static_cast<bf16 *>(b.dv)[gi] = (bf16)(br[i] * dR[mt][nt][i]);
-            }
+          for (int nt = 0; nt < 2; ++nt) {
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dR[mt][nt][i]), rr,
+                                                  o_tk[nt] + 4 * row, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_bit_cast(unsigned short, (bf16)(br[i] * dR[mt][nt][i])), vr,
+                o_tk[nt] / 2 + 2 * row, 0, 0);
           }
+        }
       }
     }
 
@@ -380,10 +392,12 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 16 + 4 * gq]);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
-        const bf16x8 o = trfrag(Ot, ks, 8 * w + 4 * nt);
-        const f32x4 o0 = to_f32x4(__builtin_shufflevector(o, o, 0, 1, 2, 3));
-        const f32x4 o1 = to_f32x4(__builtin_shufflevector(o, o, 4, 5, 6, 7));
-        split8(a0 * o0, a1 * o1, yh[ks][nt], yl[ks][nt]);
+        if (!is_m) {
+          const bf16x8 o = trfrag(Ot, ks, 8 * w + 4 * nt);
+          const f32x4 o0 = to_f32x4(__builtin_shufflevector(o, o, 0, 1, 2, 3));
+          const f32x4 o1 = to_f32x4(__builtin_shufflevector(o, o, 4, 5, 6, 7));
+          split8(a0 * o0, a1 * o1, yh[ks][nt], yl[ks][nt]);
+        }
         split8(-(b0 * dR[2 * ks][nt]), -(b1 * dR[2 * ks + 1][nt]), nh[ks][nt], nl[ks][nt]);
       }
     }
@@ -392,12 +406,17 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       f32x4 acc[2] = {lam * G[md][0], lam * G[md][1]};
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        const bf16x8 aq = trfrag(Qt, ks, 4 * md);
         const bf16x8 ak = trfrag(Kt, ks, 4 * md);
+        if (!is_m) {
+          const bf16x8 aq = trfrag(Qt, ks, 4 * md);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc[nt] = mma_bf16(aq, yh[ks][nt], acc[nt]);
+            acc[nt] = mma_bf16(aq, yl[ks][nt], acc[nt]);
+          }
+        }
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) {
-          acc[nt] = mma_bf16(aq, yh[ks][nt], acc[nt]);
-          acc[nt] = mma_bf16(aq, yl[ks][nt], acc[nt]);
           acc[nt] = mma_bf16(ak, nh[ks][nt], acc[nt]);
           acc[nt] = mma_bf16(ak, nl[ks][nt], acc[nt]);
         }
@@ -422,10 +441,12 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 }
 
 // Tm = (I + A)^-1 of every chunk, A_ri = beta_r e^{gamma_r - gamma_i} k_r . k_i for i < r < n
-// ("How to Speed Up GDN Kernels for Qwen Models", section "What GDN actually computes"), fp32,
-// zero outside [0, n)^2, into tmat [chunks, H, 64, 64].  One wave per (chunk, head): K K^T on
-// bf16 MFMA (exact products of the bf16 inputs), A into LDS, then forward substitution column by
-// column, lane j holding column j of Tm: Tm[r][j] = [r == j] - sum_{j <= i < r} A[r][i] Tm[i][j].
+// ("How to Speed Up GDN Kernels for Qwen Models", section "What GDN actually computes"), zero
+// outside [0, n)^2.  One wave per (chunk, head): K K^T on bf16 MFMA (exact products of the bf16
+// inputs), A into LDS, then forward substitution column by column, lane j holding column j of
+// Tm: Tm[r][j] = [r == j] - sum_{j <= i < r} A[r][i] Tm[i][j].  Written for the reverse chain as
+// Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles (poff), 16 KiB per
+// (chunk, head) of tmat.
 __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict__ tmat) {
   __shared__ __attribute__((aligned(16))) float am[64][68];
   const int lane = threadIdx.x, gq = lane >> 4, cl = lane & 15;
@@ -502,10 +523,18 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
     for (int i = r / 4 * 4; i < r; ++i) acc += am[r][i] * x[i];
     x[r] = r == lane ? 1.f : (r < lane ? 0.f : -acc);
   }
-  float *dst = tmat + ((int64_t)cg * H + h) * 64 * 64;
+  // row `lane` of Tm^T (column lane of Tm), 4 entries per 8-byte unit
+  char *dst = reinterpret_cast<char *>(tmat) + ((int64_t)cg * H + h) * 16384;
   const bool col_in = lane < n;
 #pragma unroll
-  for (int r = 0; r < 64; ++r) dst[r * 64 + lane] = (col_in && r < n) ? x[r] : 0.f;
+  for (int u = 0; u < 16; ++u) {
+    f32x4 v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = (col_in && 4 * u + e < n) ? x[4 * u + e] : 0.f;
+    const bf16x4 hi = to_bf16x4(v);
+    *reinterpret_cast<bf16x4 *>(dst + poff(lane, u)) = hi;
+    *reinterpret_cast<bf16x4 *>(dst + 8192 + poff(lane, u)) = to_bf16x4(v - to_f32x4(hi));
+  }
 }
 
 hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream) {

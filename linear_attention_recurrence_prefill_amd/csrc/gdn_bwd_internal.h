@@ -24,7 +24,8 @@ struct BwdUnits {
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_t stream);
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream);
-// Tm = (I + A)^-1 of every chunk (fp32 [chunks, H, 64, 64]) from k, beta and the recompute's gamma.
+// Tm = (I + A)^-1 of every chunk from k, beta and the recompute's gamma, stored for the reverse
+// chain as Tm^T = hi + lo: two bf16 64 x 64 tiles in its LDS layout, 16 KiB per (chunk, head).
 hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream);
 // Per-chunk gradients from the chain's dhn and dR (dV is the chain's).
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
