@@ -448,7 +448,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 // Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles (poff), 16 KiB per
 // (chunk, head) of tmat.
 __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict__ tmat) {
-  __shared__ __attribute__((aligned(16))) float am[64][68];
+  __shared__ __attribute__((aligned(16))) float am[64][68];  // A^T, then the output tiles
   const int lane = threadIdx.x, gq = lane >> 4, cl = lane & 15;
   const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
   // the chunk's sequence and index within it
@@ -477,8 +477,9 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;
   const int64_t t0 = ts0 + (int64_t)cidx * kChunk;
   const int n = (int)min<int64_t>(kChunk, ts1 - t0);
-  const float gam = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
-  const float bet = lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
+  __shared__ float sg[64], sb[64];
+  sg[lane] = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
+  sb[lane] = lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
   // K rows as MFMA operands straight from HBM: row 16 m + cl, elements 32 ks + 8 gq .. + 7 (rows
   // past n read the last token; A masks them)
   const bf16 *gk = static_cast<const bf16 *>(b.k) + (int64_t)h * kD;
@@ -490,6 +491,8 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
     for (int ks = 0; ks < 4; ++ks)
       kf[m][ks] = *reinterpret_cast<const bf16x8 *>(gk + t * H * kD + 32 * ks + 8 * gq);
   }
+  __syncthreads();
+  // A transposed: am[i][r] = A[r][i]
 #pragma unroll
   for (int mr = 0; mr < 4; ++mr)
 #pragma unroll
@@ -500,31 +503,36 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
         for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kf[mr][ks], kf[mi][ks], acc);
       }
       // acc[e] = k_r . k_i for r = 16 mr + 4 gq + e, i = 16 mi + cl
-      const int i = 16 * mi + cl;
-      const float gi = __shfl(gam, i, 64);
+      const int i = 16 * mi + cl, r0 = 16 * mr + 4 * gq;
+      const float gi = sg[i];
+      f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * mr + 4 * gq + e;
-        const float gr = __shfl(gam, r, 64), br = __shfl(bet, r, 64);
-        am[r][i] = (i < r && r < n) ? br * __expf(gr - gi) * acc[e] : 0.f;
+        const int r = r0 + e;
+        v[e] = (i < r && r < n) ? sb[r] * __expf(sg[r] - gi) * acc[e] : 0.f;
       }
+      *reinterpret_cast<f32x4 *>(&am[i][r0]) = v;
     }
   __syncthreads();
+  // column `lane` of Tm, right-looking: once row r is final, it is taken out of every later row,
+  // so the chain from row r to row r + 1 is one multiply-add
   float x[64];
 #pragma unroll
-  for (int r = 0; r < 64; ++r) {
-    float acc = 0.f;
+  for (int r = 0; r < 64; ++r) x[r] = r == lane ? 1.f : 0.f;
 #pragma unroll
-    for (int i4 = 0; i4 < r / 4 * 4; i4 += 4) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&am[r][i4]);
-      acc += a4[0] * x[i4] + a4[1] * x[i4 + 1] + a4[2] * x[i4 + 2] + a4[3] * x[i4 + 3];
+  for (int r = 0; r < 63; ++r) {
+#pragma unroll
+    for (int s4 = (r + 1) / 4 * 4; s4 < 64; s4 += 4) {
+      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&am[r][s4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (s4 + e > r) x[s4 + e] -= a4[e] * x[r];
     }
-#pragma unroll
-    for (int i = r / 4 * 4; i < r; ++i) acc += am[r][i] * x[i];
-    x[r] = r == lane ? 1.f : (r < lane ? 0.f : -acc);
   }
-  // row `lane` of Tm^T (column lane of Tm), 4 entries per 8-byte unit
-  char *dst = reinterpret_cast<char *>(tmat) + ((int64_t)cg * H + h) * 16384;
+  __syncthreads();  // every read of A is done: its space takes the output tiles
+  // row `lane` of Tm^T (column lane of Tm) = hi + lo, in the chain's LDS layout, then out with
+  // contiguous 16-byte stores
+  char *stage = reinterpret_cast<char *>(&am[0][0]);
   const bool col_in = lane < n;
 #pragma unroll
   for (int u = 0; u < 16; ++u) {
@@ -532,9 +540,15 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (col_in && 4 * u + e < n) ? x[4 * u + e] : 0.f;
     const bf16x4 hi = to_bf16x4(v);
-    *reinterpret_cast<bf16x4 *>(dst + poff(lane, u)) = hi;
-    *reinterpret_cast<bf16x4 *>(dst + 8192 + poff(lane, u)) = to_bf16x4(v - to_f32x4(hi));
+    *reinterpret_cast<bf16x4 *>(stage + poff(lane, u)) = hi;
+    *reinterpret_cast<bf16x4 *>(stage + 8192 + poff(lane, u)) = to_bf16x4(v - to_f32x4(hi));
   }
+  __syncthreads();
+  char *dst = reinterpret_cast<char *>(tmat) + ((int64_t)cg * H + h) * 16384;
+#pragma unroll
+  for (int j = 0; j < 16; ++j)
+    *reinterpret_cast<uint4 *>(dst + 1024 * j + 16 * lane) =
+        *reinterpret_cast<const uint4 *>(stage + 1024 * j + 16 * lane);
 }
 
 hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream) {
