@@ -17,9 +17,9 @@
 // or hi * hi' + hi * lo' + lo * hi' (both split): about 16 significant bits per operand, so the
 // chain keeps close to fp32 accuracy over thousands of chunks.
 //
-// One workgroup of four waves per (unit, head), a unit being a sequence or a segment of it; wave
-// w owns columns [32 w, 32 w + 32) of the state gradient as MFMA accumulator tiles (rows
-// 16 md + 4 gq + i, column 32 w + 16 nt + cl).  K, Q and dO of the next chunk stream from HBM
+// One workgroup of eight waves per (unit, head), a unit being a sequence or a segment of it;
+// wave w owns columns [16 w, 16 w + 16) of the state gradient as MFMA accumulator tiles (rows
+// 16 md + 4 gq + i, column 16 w + cl).  K, Q and dO of the next chunk stream from HBM
 // into a second set of LDS tiles with direct global->LDS loads while the current chunk runs, and
 // so does Tm^T (already split and laid out by bwd_tm_kernel); the gates of the next chunk are
 // loaded into registers and moved to LDS at the chunk turn.
@@ -43,6 +43,11 @@ namespace {
 constexpr int kD = 128;
 constexpr int kRowB = kD * 2;  // bytes per row of a 64 x 128 bf16 tile
 constexpr int kTile = 64 * kRowB;
+// Eight waves of 16 state-gradient columns each (kNT = 1 column tile of 16 per wave): two waves
+// per SIMD, so that one wave's MFMA, LDS and store latencies overlap the other's work.
+constexpr int kWaves = 8;
+constexpr int kNT = 8 / kWaves;
+constexpr int kThreads = 64 * kWaves;
 
 // 64 x 128 bf16 token-major tiles: the 16-byte unit c of row r is stored at unit c ^ sw(r), so
 // that 16 lanes reading one 8-byte unit of 16 consecutive rows, and the transposing read of 4
@@ -103,7 +108,7 @@ __constant__ int kPtI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 }  // namespace
 
 template <bool kTransition>
-__global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits us) {
+__global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits us) {
   __shared__ ChainSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -121,7 +126,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
   }
   // P^T's tiles below the diagonal (row block > column block) are read but never written: zero
   // them once (Tm^T is written whole every chunk)
-  for (int i = tid; i < 6 * 64; i += 256) {
+  for (int i = tid; i < 6 * 64; i += kThreads) {
     const int t = i >> 6, rr = (i >> 2) & 15, u = i & 3;
     const int mi = t < 1 ? 1 : (t < 3 ? 2 : 3), mr = t < 1 ? 0 : (t < 3 ? t - 1 : t - 3);
     const int off = poff(16 * mi + rr, 4 * mr + u);
@@ -142,11 +147,11 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
   const char *__restrict__ gqp = static_cast<const char *>(b.q) + (int64_t)h * kRowB;
   const char *__restrict__ gdo = static_cast<const char *>(b.dout) + (int64_t)h * kRowB;
   const bf16 *__restrict__ gb = static_cast<const bf16 *>(b.beta);
-  const int col0 = 32 * w + cl;  // this lane's column in tile nt: col0 + 16 nt
+  const int col0 = 16 * kNT * w + cl;  // this lane's column in tile nt: col0 + 16 nt
   const int64_t dd = (int64_t)kD * kD;
   const float xs = is_m ? 0.f : b.scale;  // the M' half runs with dO = 0
 
-  f32x4 G[8][2];  // dh'
+  f32x4 G[8][kNT];  // dh'
   {
     const float *src = nullptr;
     if (!kTransition)
@@ -156,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 #pragma unroll
     for (int md = 0; md < 8; ++md)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * md + 4 * gq + i, cc = col0 + 16 * nt;
@@ -186,9 +191,9 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 
   // store offsets (bytes): row 4 gq of a 128 x 128 fp32 matrix and token 4 gq of a [T, H, 128]
   // fp32 tensor, at this lane's column of tile nt
-  int o_st[2], o_tk[2];
+  int o_st[kNT], o_tk[kNT];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
+  for (int nt = 0; nt < kNT; ++nt) {
     o_st[nt] = (4 * gq * kD + col0 + 16 * nt) * 4;
     o_tk[nt] = (4 * gq * H * kD + col0 + 16 * nt) * 4;
   }
@@ -206,10 +211,10 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     const int64_t t0 = chunk_t0(c);
     const int n = chunk_n(c);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 16 * w + 4 * j + (lane >> 4);
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
       const int64_t off = (t0 + min(r, n - 1)) * tok_bytes + (((lane & 15) ^ sw(r)) << 4);
-      const int lo = (16 * w + 4 * j) * kRowB;
+      const int lo = ((64 / kWaves) * w + 4 * j) * kRowB;
       dma16(gk + off, sm.kqo[set][0] + lo);
       dma16(gqp + off, sm.kqo[set][1] + lo);
       dma16(gdo + off, sm.kqo[set][2] + lo);
@@ -217,7 +222,9 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
     const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(tm + (4 * w + j) * 1024 + 16 * lane, &sm.tt[set][0][0] + (4 * w + j) * 1024);
+    for (int j = 0; j < 16 / kWaves; ++j)
+      dma16(tm + ((16 / kWaves) * w + j) * 1024 + 16 * lane,
+            &sm.tt[set][0][0] + ((16 / kWaves) * w + j) * 1024);
     if (w == 0) {
       const int64_t t = t0 + min(lane, n - 1);
       g_r = b.gamma[t * H + h];
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     __syncthreads();
     // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo (the M' half
     //      runs with dO = 0 and needs neither P nor the dO products below)
-    for (int t = w; t < (is_m ? 0 : 10); t += 4) {
+    for (int t = w; t < (is_m ? 0 : 10); t += kWaves) {
       const int mr = kPtR[t], mi = kPtI[t];
       f32x4 acc = zero4();
 #pragma unroll
@@ -281,29 +288,29 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt)
+          for (int nt = 0; nt < kNT; ++nt)
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[md][nt][i]), hr, o_st[nt],
                                                   (16 * md + i) * kD * 4, 0);
     }
 
     // ---- dDelta = P^T dO_s + diag(c) K dh'
-    f32x4 dD[4][2];
+    f32x4 dD[4][kNT];
     {
-      f32x4 kd[4][2], x[4][2];
+      f32x4 kd[4][kNT], x[4][kNT];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) kd[mt][nt] = x[mt][nt] = zero4();
+        for (int nt = 0; nt < kNT; ++nt) kd[mt][nt] = x[mt][nt] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        bf16x8 gh[2], gl[2];
+        bf16x8 gh[kNT], gl[kNT];
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) split8(G[2 * ks][nt], G[2 * ks + 1][nt], gh[nt], gl[nt]);
+        for (int nt = 0; nt < kNT; ++nt) split8(G[2 * ks][nt], G[2 * ks + 1][nt], gh[nt], gl[nt]);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           const bf16x8 a = kfrag(Kt, mt, ks);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             kd[mt][nt] = mma_bf16(a, gh[nt], kd[mt][nt]);
             kd[mt][nt] = mma_bf16(a, gl[nt], kd[mt][nt]);
           }
@@ -311,15 +318,15 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       }
 #pragma unroll
       for (int ks = 0; ks < 2 && !is_m; ++ks) {
-        bf16x8 of[2];  // dO over tokens, exact
+        bf16x8 of[kNT];  // dO over tokens, exact
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) of[nt] = trfrag(Ot, ks, 8 * w + 4 * nt);
+        for (int nt = 0; nt < kNT; ++nt) of[nt] = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
           if (2 * ks + 1 < mt) continue;  // P^T[i][r] = 0 for r < i: tokens 0..31 vs rows >= 32
           const bf16x8 ah = pfrag(sm.pth, mt, ks), al = pfrag(sm.ptl, mt, ks);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             x[mt][nt] = mma_bf16(ah, of[nt], x[mt][nt]);
             x[mt][nt] = mma_bf16(al, of[nt], x[mt][nt]);
           }
@@ -329,28 +336,28 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       for (int mt = 0; mt < 4; ++mt) {
         const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) dD[mt][nt] = xs * x[mt][nt] + cr * kd[mt][nt];
+        for (int nt = 0; nt < kNT; ++nt) dD[mt][nt] = xs * x[mt][nt] + cr * kd[mt][nt];
       }
     }
 
     // ---- dR = Tm^T dDelta (Tm^T[r][i] = 0 for i < r); dV = diag(beta) dR
-    f32x4 dR[4][2];
+    f32x4 dR[4][kNT];
     {
-      bf16x8 eh[2][2], el[2][2];  // dDelta over tokens: [ks][nt]
+      bf16x8 eh[2][kNT], el[2][kNT];  // dDelta over tokens: [ks][nt]
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) split8(dD[2 * ks][nt], dD[2 * ks + 1][nt], eh[ks][nt], el[ks][nt]);
+        for (int nt = 0; nt < kNT; ++nt) split8(dD[2 * ks][nt], dD[2 * ks + 1][nt], eh[ks][nt], el[ks][nt]);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) dR[mt][nt] = zero4();
+        for (int nt = 0; nt < kNT; ++nt) dR[mt][nt] = zero4();
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           if (2 * ks + 1 < mt) continue;
           const bf16x8 th = pfrag(sm.tt[set][0], mt, ks), tl = pfrag(sm.tt[set][1], mt, ks);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             dR[mt][nt] = mma_bf16(th, eh[ks][nt], dR[mt][nt]);
             dR[mt][nt] = mma_bf16(th, el[ks][nt], dR[mt][nt]);
             dR[mt][nt] = mma_bf16(tl, eh[ks][nt], dR[mt][nt]);
@@ -371,7 +378,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
         for (int i = 0; i < 4; ++i) {
           const int row = (16 * mt + i) * H * kD;  // + 4 gq rows in the lane-constant part
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dR[mt][nt][i]), rr,
                                                   o_tk[nt] + 4 * row, 0, 0);
             __builtin_amdgcn_raw_buffer_store_b16(
@@ -383,7 +390,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     }
 
     // ---- dh = lambda dh' + Q^T (scale a o dO) - K^T (a beta o dR)
-    bf16x8 yh[2][2], yl[2][2], nh[2][2], nl[2][2];
+    bf16x8 yh[2][kNT], yl[2][kNT], nh[2][kNT], nl[2][kNT];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sm.as[32 * ks + 4 * gq]);
@@ -391,9 +398,9 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
       const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 4 * gq]);
       const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 16 + 4 * gq]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         if (!is_m) {
-          const bf16x8 o = trfrag(Ot, ks, 8 * w + 4 * nt);
+          const bf16x8 o = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
           const f32x4 o0 = to_f32x4(__builtin_shufflevector(o, o, 0, 1, 2, 3));
           const f32x4 o1 = to_f32x4(__builtin_shufflevector(o, o, 4, 5, 6, 7));
           split8(a0 * o0, a1 * o1, yh[ks][nt], yl[ks][nt]);
@@ -403,26 +410,28 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
     }
 #pragma unroll
     for (int md = 0; md < 8; ++md) {
-      f32x4 acc[2] = {lam * G[md][0], lam * G[md][1]};
+      f32x4 acc[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) acc[nt] = lam * G[md][nt];
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 ak = trfrag(Kt, ks, 4 * md);
         if (!is_m) {
           const bf16x8 aq = trfrag(Qt, ks, 4 * md);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             acc[nt] = mma_bf16(aq, yh[ks][nt], acc[nt]);
             acc[nt] = mma_bf16(aq, yl[ks][nt], acc[nt]);
           }
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           acc[nt] = mma_bf16(ak, nh[ks][nt], acc[nt]);
           acc[nt] = mma_bf16(ak, nl[ks][nt], acc[nt]);
         }
       }
-      G[md][0] = acc[0];
-      G[md][1] = acc[1];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) G[md][nt] = acc[nt];
     }
   }
   float *dst = nullptr;
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(256) void bwd_chain_bf16_kernel(BwdArgs b, BwdUnits
 #pragma unroll
     for (int md = 0; md < 8; ++md)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) dst[(16 * md + 4 * gq + i) * kD + col0 + 16 * nt] = G[md][nt][i];
   }
@@ -560,7 +569,7 @@ hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipS
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_t stream) {
   const int64_t units = u.L > 0 ? u.units : b.N;
   if (units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_chain_bf16_kernel<false>, dim3((unsigned)units, b.H), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_chain_bf16_kernel<false>, dim3((unsigned)units, b.H), dim3(kThreads), 0,
                      stream, b, u);
   return hipGetLastError();
 }
@@ -568,7 +577,7 @@ hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream) {
   if (u.units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_chain_bf16_kernel<true>, dim3((unsigned)u.units, b.H, 2), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_chain_bf16_kernel<true>, dim3((unsigned)u.units, b.H, 2), dim3(kThreads), 0,
                      stream, b, u);
   return hipGetLastError();
 }
