@@ -18,9 +18,9 @@
 // chunked form of "How to Speed Up GDN Kernels for Qwen Models" (section "What GDN actually
 // computes"), with the hidden states recomputed ("Lever 2").
 //
-// One workgroup of four waves per (chunk, head).  Products run on v_mfma_f32_16x16x32_bf16 with
+// One workgroup of eight waves per (chunk, head).  Products run on v_mfma_f32_16x16x32_bf16 with
 // fp32 accumulation; q, k, v and dO enter exactly, every other operand as a bf16 head plus a bf16
-// remainder (see the reverse chain).  Wave w owns feature columns [32 w, 32 w + 32) of every
+// remainder (see the reverse chain).  Wave w owns feature columns [16 w, 16 w + 16) of every
 // 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go straight from HBM into
 // the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
 // so results are bitwise reproducible.
@@ -32,6 +32,11 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowB = kD * 2;
+// Eight waves of 16 feature columns each (kNT = 1 column tile of 16 per wave): two waves per
+// SIMD, so that one wave's latencies overlap the other's work.
+constexpr int kWaves = 8;
+constexpr int kNT = 8 / kWaves;
+constexpr int kThreads = 64 * kWaves;
 
 // 64 x 128 bf16 tiles, token-major, 16-byte unit c of row r at c ^ sw(r) (as in the chain)
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
@@ -76,13 +81,13 @@ struct GradSmem {
   alignas(16) char tth[64 * 128];   // dPm = hi + lo
   alignas(16) char ttl[64 * 128];
   alignas(16) float gam[64], a[64], c[64], beta[64];
-  alignas(16) float prg[4][64];  // per-wave partial row terms of dgamma (tiles)
-  alignas(16) float pcg[4][64];  // per-wave partial column terms of dgamma (tiles, subtracted)
-  alignas(16) float prb[4][64];  // per-wave partial row terms of dbeta (tiles)
-  alignas(16) float frg[4][64];  // per-wave row terms of dgamma over the wave's columns
-  alignas(16) float frb[4][64];  // per-wave row terms of dbeta over the wave's columns
-  alignas(16) float fc[4][64];   // per-wave c_r (Y2 . K)_r
-  alignas(16) float hd[4];
+  alignas(16) float prg[kWaves][64];  // per-wave partial row terms of dgamma (tiles)
+  alignas(16) float pcg[kWaves][64];  // per-wave partial column terms of dgamma (tiles, subtracted)
+  alignas(16) float prb[kWaves][64];  // per-wave partial row terms of dbeta (tiles)
+  alignas(16) float frg[kWaves][64];  // per-wave row terms of dgamma over the wave's columns
+  alignas(16) float frb[kWaves][64];  // per-wave row terms of dbeta over the wave's columns
+  alignas(16) float fc[kWaves][64];   // per-wave c_r (Y2 . K)_r
+  alignas(16) float hd[kWaves];
   alignas(16) int imisc[4];
 };
 static_assert(sizeof(GradSmem) <= 160 * 1024, "LDS budget");
@@ -92,7 +97,7 @@ __constant__ int kTI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 }  // namespace
 
-__global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
+__global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -124,7 +129,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
       sm.imisc[1] = cidx;
     }
   }
-  for (int i = tid; i < 6 * 4 * 64; i += 256) (&sm.prg[0][0])[i] = 0.f;
+  for (int i = tid; i < 6 * kWaves * 64; i += kThreads) (&sm.prg[0][0])[i] = 0.f;
   __syncthreads();
   const int seq = sm.imisc[0];
   if (seq < 0) return;
@@ -142,36 +147,36 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   //      (direct loads; rows past n repeat the chunk's last token, which every use masks), Delta
   //      and dR through registers (split; rows past n zero), and each wave's rows of h and dh'
   //      into registers for its B operands.
-  const int fcol = 32 * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
-  f32x4 hv[2][4][2], gv[2][4][2];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
+  const int fcol = 16 * kNT * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
+  f32x4 hv[kNT][4][2], gv[kNT][4][2];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
   {
     const char *src[4] = {static_cast<const char *>(b.dout), static_cast<const char *>(b.q),
                           static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
     char *dst[4] = {sm.dout, sm.q, sm.k, sm.v};
-    // wave w fills rows 16 w .. 16 w + 15; lane l of load j writes physical unit l % 16 of row
-    // 16 w + 4 j + l / 16, which holds logical unit (l % 16) ^ sw(row)
+    // wave w fills rows 8 w .. 8 w + 7; lane l of load j writes physical unit l % 16 of row
+    // 8 w + 4 j + l / 16, which holds logical unit (l % 16) ^ sw(row)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = 16 * w + 4 * j + (lane >> 4);
+      for (int j = 0; j < 16 / kWaves; ++j) {
+        const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
         dma16(src[s] + (t0 + min(r, n - 1)) * tok_bytes + (int64_t)h * kRowB +
                   (((lane & 15) ^ sw(r)) << 4),
-              dst[s] + (16 * w + 4 * j) * kRowB);
+              dst[s] + ((64 / kWaves) * w + 4 * j) * kRowB);
       }
-    f32x4 xr[2][8];
+    f32x4 xr[2][8 * 4 / kWaves];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const float *g = s == 0 ? b.delta : b.ddelta;  // Delta, dR
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int u = tid + 256 * m, r = u >> 5, c4 = u & 31;
+      for (int m = 0; m < 8 * 4 / kWaves; ++m) {
+        const int u = tid + kThreads * m, r = u >> 5, c4 = u & 31;
         xr[s][m] = r < n ? *reinterpret_cast<const f32x4 *>(g + ((t0 + r) * H + h) * kD + 4 * c4)
                          : zero4();
       }
     }
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
@@ -190,8 +195,8 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
       char *hi = s == 0 ? sm.dh : sm.eh;
       char *lo = s == 0 ? sm.dl : sm.el;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        const int u = tid + 256 * m, r = u >> 5, c4 = u & 31;
+      for (int m = 0; m < 8 * 4 / kWaves; ++m) {
+        const int u = tid + kThreads * m, r = u >> 5, c4 = u & 31;
         const bf16x4 xh = to_bf16x4(xr[s][m]);
         *reinterpret_cast<bf16x4 *>(hi + toff(r, c4)) = xh;
         *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(xr[s][m] - to_f32x4(xh));
@@ -232,13 +237,13 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   };
 
   // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
-  bf16x8 hh[2][4], hl[2][4];
-  f32x4 Y1[4][2], Y2[4][2];
+  bf16x8 hh[kNT][4], hl[kNT][4];
+  f32x4 Y1[4][kNT], Y2[4][kNT];
   float hdot = 0.f;
   {
-    bf16x8 gh[2][4], gl[2][4];
+    bf16x8 gh[kNT][4], gl[kNT][4];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const f32x4 h0 = hv[nt][ks][0], h1 = hv[nt][ks][1];
@@ -252,13 +257,13 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) Y1[mt][nt] = Y2[mt][nt] = zero4();
+      for (int nt = 0; nt < kNT; ++nt) Y1[mt][nt] = Y2[mt][nt] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const bf16x8 ao = rowf(sm.dout, 16 * mt + cl, ks);
         const bf16x8 ah = rowf(sm.dh, 16 * mt + cl, ks), al = rowf(sm.dl, 16 * mt + cl, ks);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
+        for (int nt = 0; nt < kNT; ++nt) {
           Y1[mt][nt] = mma_bf16(ao, hh[nt][ks], Y1[mt][nt]);
           Y1[mt][nt] = mma_bf16(ao, hl[nt][ks], Y1[mt][nt]);
           Y2[mt][nt] = mma_bf16(ah, gh[nt][ks], Y2[mt][nt]);
@@ -279,16 +284,16 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rb[mt][i] = 0.f;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      const f32x4 vv = colv(sm.v, mt, 8 * w + 4 * nt);
-      const f32x4 rr = colv(sm.eh, mt, 8 * w + 4 * nt) + colv(sm.el, mt, 8 * w + 4 * nt);
+    for (int nt = 0; nt < kNT; ++nt) {
+      const f32x4 vv = colv(sm.v, mt, 4 * kNT * w + 4 * nt);
+      const f32x4 rr = colv(sm.eh, mt, 4 * kNT * w + 4 * nt) + colv(sm.el, mt, 4 * kNT * w + 4 * nt);
 #pragma unroll
       for (int i = 0; i < 4; ++i) rb[mt][i] += rr[i] * vv[i];
     }
   }
   __syncthreads();  // every wave is done with V
   // zero the tiles above the diagonal of dPm (tth, ttl) and E (v region)
-  for (int i = tid; i < 6 * 64; i += 256) {
+  for (int i = tid; i < 6 * 64; i += kThreads) {
     const int t = i >> 6, rr = (i >> 2) & 15, u = i & 3;
     // (mi, mr) = (0, 1), (0, 2), (0, 3), (1, 2), (1, 3), (2, 3): column block > row block
     const int mi = t < 3 ? 0 : (t < 5 ? 1 : 2);
@@ -302,16 +307,16 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
   __syncthreads();
 
   // ---- Rh = dR h^T over this wave's columns (d)
-  f32x4 Rh[4][2];
+  f32x4 Rh[4][kNT];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) Rh[mt][nt] = zero4();
+    for (int nt = 0; nt < kNT; ++nt) Rh[mt][nt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
       const bf16x8 ah = rowf(sm.eh, 16 * mt + cl, ks), al = rowf(sm.el, 16 * mt + cl, ks);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < kNT; ++nt) {
         Rh[mt][nt] = mma_bf16(ah, hh[nt][ks], Rh[mt][nt]);
         Rh[mt][nt] = mma_bf16(ah, hl[nt][ks], Rh[mt][nt]);
         Rh[mt][nt] = mma_bf16(al, hh[nt][ks], Rh[mt][nt]);
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
 
   // ---- 64 x 64 tiles on and below the diagonal: dP, dR Delta^T, Q K^T, K K^T
   char *eth = sm.v, *etl = sm.v + 64 * 128;  // E = hi + lo
-  for (int t = w; t < 10; t += 4) {
+  for (int t = w; t < 10; t += kWaves) {
     const int tr = kTR[t], ti = kTI[t];
     f32x4 dp = zero4(), da = zero4(), qk = zero4(), kk = zero4();
 #pragma unroll
@@ -391,17 +396,19 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) rg[mt][i] = rc[mt][i] = 0.f;
   {
-    bf16x8 kb[2][2], qb[2][2];  // K and Q over tokens: [ks][nt]
+    bf16x8 kb[2][kNT], qb[2][kNT];  // K and Q over tokens: [ks][nt]
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        kb[ks][nt] = trfrag(sm.k, ks, 8 * w + 4 * nt);
-        qb[ks][nt] = trfrag(sm.q, ks, 8 * w + 4 * nt);
+      for (int nt = 0; nt < kNT; ++nt) {
+        kb[ks][nt] = trfrag(sm.k, ks, 4 * kNT * w + 4 * nt);
+        qb[ks][nt] = trfrag(sm.q, ks, 4 * kNT * w + 4 * nt);
       }
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      f32x4 dq[2] = {zero4(), zero4()}, dk[2] = {zero4(), zero4()};
+      f32x4 dq[kNT], dk[kNT];
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) dq[nt] = dk[nt] = zero4();
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bool lower = 2 * ks <= mt;      // blocks with tokens i <= rows r exist
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
           const bf16x8 ph = pfrag(sm.tth, mt, ks), pl = pfrag(sm.ttl, mt, ks);
           const bf16x8 eh_ = pfrag(eth, mt, ks), el_ = pfrag(etl, mt, ks);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             dq[nt] = mma_bf16(ph, kb[ks][nt], dq[nt]);
             dq[nt] = mma_bf16(pl, kb[ks][nt], dq[nt]);
             dk[nt] = mma_bf16(eh_, kb[ks][nt], dk[nt]);
@@ -421,7 +428,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
           const bf16x8 ph = ptfrag(sm.tth, mt, ks), pl = ptfrag(sm.ttl, mt, ks);
           const bf16x8 eh_ = ptfrag(eth, mt, ks), el_ = ptfrag(etl, mt, ks);
 #pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
+          for (int nt = 0; nt < kNT; ++nt) {
             dk[nt] = mma_bf16(ph, qb[ks][nt], dk[nt]);
             dk[nt] = mma_bf16(pl, qb[ks][nt], dk[nt]);
             dk[nt] = mma_bf16(eh_, kb[ks][nt], dk[nt]);
@@ -433,8 +440,8 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
       const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
       const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const f32x4 qv = colv(sm.q, mt, 8 * w + 4 * nt), kv = colv(sm.k, mt, 8 * w + 4 * nt);
+      for (int nt = 0; nt < kNT; ++nt) {
+        const f32x4 qv = colv(sm.q, mt, 4 * kNT * w + 4 * nt), kv = colv(sm.k, mt, 4 * kNT * w + 4 * nt);
         const f32x4 y1 = scale * Y1[mt][nt];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -477,7 +484,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
     const int r = lane;
     float dgam = 0.f, dbet = 0.f, csum = 0.f;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < kWaves; ++x) {
       dgam += sm.prg[x][r] - sm.pcg[x][r] + sm.frg[x][r];
       dbet += sm.prb[x][r] + sm.frb[x][r];
       csum += sm.fc[x][r];
@@ -488,7 +495,9 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) csum += __shfl_xor(csum, off, 64);
-    const float hdot = sm.hd[0] + sm.hd[1] + sm.hd[2] + sm.hd[3];
+    float hdot = 0.f;
+#pragma unroll
+    for (int x = 0; x < kWaves; ++x) hdot += sm.hd[x];
     if (r == n - 1) dgam += csum + __expf(sm.gam[n - 1]) * hdot;
     // dg_s = sum_{r >= s} dgamma_r (reverse inclusive scan)
     float x = dgam;
@@ -506,7 +515,7 @@ __global__ __launch_bounds__(256) void bwd_grad_bf16_kernel(BwdArgs b) {
 
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream) {
   if (max_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_grad_bf16_kernel, dim3((unsigned)max_chunks, b.H), dim3(256), 0, stream,
+  hipLaunchKernelGGL(bwd_grad_bf16_kernel, dim3((unsigned)max_chunks, b.H), dim3(kThreads), 0, stream,
                      b);
   return hipGetLastError();
 }
