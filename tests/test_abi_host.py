@@ -158,7 +158,8 @@ def test_bwd_recompute_split_workspace(lib):
     """bf16, d = 128 with num_seqs * H < P: the backward's forward recompute runs the exact split,
     which adds per (unit, head) a pair (B, M) and a start state (3 fp32 states of 128 x 128).
     Without the host cu_seqlens the unit count is bounded by ceil((ceil(T / 64) + N) / L) + N:
-    T = 1024, N = 2, L = 4 (half the forward's length, floored at 4) gives 7 units."""
+    T = 1024, N = 2, L = 4 (the forward's rule: 3 sqrt(8 * 16 / 256) rounds to 2, floored at 4)
+    gives 7 units."""
     n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
     p = _problem(num_slots=1)  # num_seqs * H >= P: the recompute is not split
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
