@@ -13,7 +13,8 @@ steps run first; then exactly K steps are timed with HIP events on that stream, 
 device synchronisations.  ``value`` is tokens per second of the headline mode (the page's
 truncated-history split, section "Lever 1"); the exact mode is timed the same way and reported
 beside it, and so is the training backward (gdn_chunk_bwd on the packed 65536-token workload of
-the pages' training runs, object ``backward`` with its own HBM roofline fraction).
+the pages' training runs, object ``backward`` with its own HBM roofline fraction) and the
+single-token decode step (object ``decode``).
 
 ``roofline``: the forward is bound by HBM bandwidth (about 176 flop per byte against the
 MI355X's ~315 flop/byte ridge).  Algorithmic bytes per launch = 1030 B per (token, head)
@@ -197,10 +198,49 @@ def main():
                              / HBM_PEAK_GBS}
     if not args.no_backward:
         line["backward"] = time_backward(gdn, torch, args.steps, args.warmup)
+        line["decode"] = time_decode(gdn, torch, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def time_decode(gdn, torch, steps, warmup):
+    """One decode step (gdn_decode_step) on the fork workload's serving shape: 80 sequences x
+    16 heads, d = 128, bf16 inputs, fp32 states updated in place.  Algorithmic bytes per step:
+    every state read and written once (2 x 64 KiB), q, k, v, o in bf16, g fp32, beta bf16."""
+    B, H, D = 80, 16, 128
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    q = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen), dim=-1)
+    k = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen), dim=-1)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    v = torch.randn(B, H, D, device="cuda", generator=gen).to(torch.bfloat16)
+    g = -torch.nn.functional.softplus(torch.randn(B, H, device="cuda", generator=gen) - 3.0)
+    beta = torch.sigmoid(torch.randn(B, H, device="cuda", generator=gen)).to(torch.bfloat16)
+    state = 0.1 * torch.randn(B, H, D, D, device="cuda", generator=gen)
+    out = torch.empty_like(v)
+
+    def step():
+        gdn.decode_step(q, k, v, g, beta, state, out=out)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    nbytes = B * H * (2 * D * D * 4 + 4 * D * 2 + 4 + 2)
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {"workload": f"{B} sequences x {H} heads, d_k=d_v={D}, bf16 inputs, fp32 state",
+            "us_per_step": ms * 1e3, "tokens_per_s": B / (ms / 1e3),
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                         "bytes_per_step": nbytes}}
 
 
 def time_backward(gdn, torch, steps, warmup):

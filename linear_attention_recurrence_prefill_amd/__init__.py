@@ -4,7 +4,7 @@
 ``python -m linear_attention_recurrence_prefill_amd.build``); the C ABI is ``include/gdn.h``.
 """
 from .gdn import (GdnError, chunk_bwd, chunk_fwd, chunk_fwd_intermediates, chunk_fwd_plan,
-                  load_library)
+                  decode_step, load_library)
 
 __all__ = ["GdnError", "chunk_fwd", "chunk_bwd", "chunk_fwd_plan", "chunk_fwd_intermediates",
-           "load_library"]
+           "decode_step", "load_library"]

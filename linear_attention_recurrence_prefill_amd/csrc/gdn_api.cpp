@@ -10,6 +10,7 @@
 
 #include "../../include/gdn.h"
 #include "gdn_bwd_internal.h"
+#include "gdn_decode.h"
 #include "gdn_internal.h"
 
 namespace {
@@ -648,6 +649,38 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
 }  // extern "C"
 
 extern "C" {
+
+gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t dtype,
+                           float scale, const void *q, const void *k, const void *v,
+                           const float *g, const void *beta, float *state, void *o,
+                           hipStream_t stream) {
+  if (batch < 1 || num_heads < 1 || (int64_t)batch * num_heads > INT32_MAX)
+    return fail(GDN_ERR_BAD_SHAPE, "batch and num_heads must be >= 1");
+  if (head_dim != 64 && head_dim != 128) return fail(GDN_ERR_BAD_SHAPE, "head_dim must be 64 or 128");
+  if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_BAD_DTYPE, "dtype %d", dtype);
+  if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
+  if (!q || !k || !v || !g || !beta || !state || !o)
+    return fail(GDN_ERR_NULL_ARG, "q, k, v, g, beta, state and o are required");
+  const void *ptrs[] = {q, k, v, state, o};
+  for (const void *x : ptrs)
+    if (!aligned16(x)) return fail(GDN_ERR_BAD_ALIGNMENT, "tensor pointers must be 16-byte aligned");
+  gdn_status s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  gdn::DecodeArgs a{};
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.g = g;
+  a.beta = beta;
+  a.state = state;
+  a.o = o;
+  a.B = batch;
+  a.H = num_heads;
+  a.scale = scale;
+  const hipError_t e = gdn::launch_decode_step(a, head_dim, dtype == GDN_DTYPE_BF16, stream);
+  if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  return GDN_OK;
+}
 
 const char *gdn_status_string(gdn_status s) {
   switch (s) {

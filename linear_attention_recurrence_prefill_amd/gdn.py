@@ -23,7 +23,7 @@ _MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
 # Every exported entry point of include/gdn.h.
 EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
            "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
-           "gdn_chunk_bwd", "gdn_status_string", "gdn_last_error")
+           "gdn_chunk_bwd", "gdn_decode_step", "gdn_status_string", "gdn_last_error")
 
 
 class GdnError(RuntimeError):
@@ -74,6 +74,10 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, vp, sz, vp]
     lib.gdn_chunk_bwd.restype = st
+    lib.gdn_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
+                                    vp]
+    lib.gdn_decode_step.restype = st
     lib.gdn_status_string.argtypes = [st]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -272,4 +276,29 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
                              _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                              _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
                              workspace.numel(), _stream()))
+    return out
+
+
+def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
+    """One decode step (gdn_decode_step): q, k, v [B, H, D] (bf16 or fp32), g [B, H] fp32,
+    beta [B, H] (q's dtype), state [B, H, D, D] fp32, advanced in place by one token.  Returns
+    o [B, H, D] (q's dtype)."""
+    lib = load_library()
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, D]")
+    B, H, D = q.shape
+    for name, t, shape in (("k", k, (B, H, D)), ("v", v, (B, H, D)), ("g", g, (B, H)),
+                           ("beta", beta, (B, H)), ("state", state, (B, H, D, D))):
+        if tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous {list(shape)}")
+    if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or \
+            v.dtype != q.dtype or beta.dtype != q.dtype:
+        raise ValueError("q, k, v, beta must share a dtype (bfloat16 or float32)")
+    if g.dtype != torch.float32 or state.dtype != torch.float32:
+        raise ValueError("g and state must be float32")
+    if out is None:
+        out = torch.empty_like(v)
+    dt = GDN_DTYPE_BF16 if q.dtype == torch.bfloat16 else GDN_DTYPE_F32
+    _check(lib.gdn_decode_step(B, H, D, dt, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                               _ptr(beta), _ptr(state), _ptr(out), _stream()))
     return out

@@ -169,3 +169,19 @@ def test_bwd_recompute_split_workspace(lib):
     p = _problem(num_slots=256, dtype=0)  # fp32: the general kernel, never split
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
     assert n2.value < n1.value * 2
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0, 8, 128, 1), 2), ((4, 0, 128, 1), 2), ((4, 8, 96, 1), 2), ((4, 8, 128, 5), 3)])
+def test_decode_step_rejects_bad_sizes(lib, args, status):
+    buf = (ctypes.c_char * 64)()
+    ptr = ctypes.cast(buf, ctypes.c_void_p)
+    st = lib.gdn_decode_step(*args, 1.0, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None)
+    assert st == status
+    assert lib.gdn_last_error()
+
+
+def test_decode_step_rejects_null_pointer(lib):
+    buf = (ctypes.c_char * 64)()
+    ptr = ctypes.cast(buf, ctypes.c_void_p)
+    assert lib.gdn_decode_step(4, 8, 128, 1, 1.0, ptr, None, ptr, ptr, ptr, ptr, ptr, None) == 1
