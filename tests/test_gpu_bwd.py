@@ -143,3 +143,43 @@ def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots):
     for name in NAMES:
         report(name, np64(gr[name]), ref[name], 5e-3)
     report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3)
+
+
+def test_fork_backward_through_shared_prefix(gdn, oracle_mod):
+    """Shared-prefix fork, backward ("Musings on long-context fine-tuning", section "Backward
+    through P"): a prefix runs once and its final state starts every branch.  On the GPU the
+    branches' backward with that shared initial state gives dh0 summed over the branches; it is
+    the prefix's dht, and the prefix's backward with its own dO and that dht gives the prefix's
+    gradients.  Reference: the oracle's backward of each concatenated prefix + branch with dO zero
+    on the prefix, summed over the branches on the prefix's tokens, plus the oracle's backward of
+    the prefix alone with its own dO; the branch tokens' gradients come from the same
+    concatenations."""
+    P, lens, H, D = 300, [150, 97, 220], 2, 128
+    pre = make_inputs([P], H=H, dk=D, dv=D, dtype="bf16", seed=301, with_dout=True)
+    br = make_inputs(lens, H=H, dk=D, dv=D, dtype="bf16", seed=302, with_dout=True)
+    dp, db = to_dev(pre), to_dev(br)
+    _, ht = gdn.chunk_fwd(*args_of(dp), dp["cu_seqlens"], None)
+    shared = ht[0].contiguous()
+    gb = gdn.chunk_bwd(*args_of(db), db["cu_seqlens"], db["dout"], shared)
+    gp = gdn.chunk_bwd(*args_of(dp), dp["cu_seqlens"], dp["dout"], None,
+                       gb["dh0"].unsqueeze(0).contiguous())
+    torch.cuda.synchronize()
+
+    names = ("q", "k", "v", "g", "beta")
+    ref_p = oracle_mod.bwd(*[pre[x] for x in names], pre["cu_seqlens"], pre["dout"])
+    ref_b = {n: np.zeros(br[n[1:]].shape) for n in NAMES}  # dq -> q's shape, ...
+    ref_p = {n: np.array(ref_p[n], dtype=np.float64) for n in NAMES}
+    cu = br["cu_seqlens"]
+    for i in range(len(lens)):
+        s0, s1 = int(cu[i]), int(cu[i + 1])
+        cat = [np.concatenate([pre[x], br[x][s0:s1]]) for x in names]
+        dout = np.concatenate([np.zeros_like(pre["dout"]), br["dout"][s0:s1]])
+        r = oracle_mod.bwd(*cat, np.array([0, P + s1 - s0], dtype=np.int32), dout)
+        for n in NAMES:
+            ref_p[n] += r[n][:P]
+            ref_b[n][s0:s1] = r[n][P:]
+    print("[fork backward]", flush=True)
+    for n in NAMES:
+        report(f"prefix {n}", np64(gp[n]), ref_p[n], 5e-3)
+    for n in NAMES:
+        report(f"branch {n}", np64(gb[n]), ref_b[n], 5e-3)
