@@ -13,7 +13,7 @@
  * inter-chunk state chain and the output), on the stream the caller passes.
  *
  * Layouts (row-major, token-major, contiguous; T = total_tokens, N = num_seqs, H = num_heads):
- *   q, k        [T, H, d_k]      dtype (bf16 or fp32)
+ *   q, k        [T, Hk, d_k]     dtype (bf16 or fp32); Hk = num_k_heads (= H unless grouped)
  *   v, o        [T, H, d_v]      dtype
  *   g           [T, H]           fp32: the log-gate, alpha_t = exp(g_t)
  *   beta        [T, H]           dtype: the write strength
@@ -88,7 +88,7 @@ enum { GDN_MODE_EXACT = 0, GDN_MODE_TRUNCATE = 1 };
 typedef struct gdn_problem {
   int64_t total_tokens;      /* T = cu_seqlens[N] (>= 0) */
   int32_t num_seqs;          /* N >= 1 */
-  int32_t num_heads;         /* H >= 1 (q, k and v heads are equal) */
+  int32_t num_heads;         /* H >= 1: heads of v, o, g, beta and of the state */
   int32_t d_k;               /* 64 or 128 */
   int32_t d_v;               /* equal to d_k */
   int32_t chunk;             /* 64 */
@@ -101,7 +101,11 @@ typedef struct gdn_problem {
                               * (then the workspace query needs the device) */
   float trunc_log_threshold; /* truncate mode: -10 */
   float scale;               /* o_t = scale * S_t^T q_t (1 in the pages' formulation) */
-  int32_t reserved;          /* must be 0 */
+  int32_t num_k_heads;       /* heads of q and k: 0 (= num_heads) or a divisor of num_heads;
+                              * value head h reads key head h / (num_heads / num_k_heads) (the
+                              * grouped layouts of "How to Speed Up GDN Kernels for Qwen Models",
+                              * section "Using it, and the fine print", where value heads are a
+                              * multiple of key heads) */
   int64_t h0_seq_stride;     /* elements between consecutive sequences' h0; 0 = broadcast */
 } gdn_problem;
 
@@ -158,7 +162,8 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes);
 
 /* Backward of the exact forward (mode must be GDN_MODE_EXACT): given dout (dtype, [T, H, d_v])
- * and optionally dht ([N, H, d_k, d_v] fp32, NULL = zero), writes dq, dk (dtype, [T, H, d_k]),
+ * and optionally dht ([N, H, d_k, d_v] fp32, NULL = zero), writes dq, dk (dtype, [T, Hk, d_k];
+ * with grouped heads, the sums over each key head's value heads),
  * dv (dtype, [T, H, d_v]), dg (fp32, [T, H]) and dbeta (dtype, [T, H]).  dh0 (optional, fp32)
  * receives the gradient of the initial states: [N, H, d_k, d_v] per sequence, or [H, d_k, d_v]
  * summed over all sequences when h0_seq_stride is 0 (a state shared by every sequence collects

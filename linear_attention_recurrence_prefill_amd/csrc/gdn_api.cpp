@@ -107,14 +107,20 @@ gdn_status check_problem(const gdn_problem *p) {
     return fail(GDN_ERR_BAD_MODE, "mode %d", p->mode);
   if (p->mode == GDN_MODE_TRUNCATE && !(p->trunc_log_threshold < 0.f))
     return fail(GDN_ERR_BAD_MODE, "trunc_log_threshold must be negative");
-  if (p->seg_chunks < 0 || p->num_slots < 0 || p->reserved != 0)
-    return fail(GDN_ERR_BAD_SHAPE, "seg_chunks / num_slots / reserved out of range");
+  if (p->seg_chunks < 0 || p->num_slots < 0)
+    return fail(GDN_ERR_BAD_SHAPE, "seg_chunks / num_slots out of range");
+  if (p->num_k_heads < 0 || p->num_k_heads > p->num_heads ||
+      (p->num_k_heads > 0 && p->num_heads % p->num_k_heads != 0))
+    return fail(GDN_ERR_BAD_SHAPE, "num_k_heads must be 0 or a divisor of num_heads");
   if (p->h0_seq_stride < 0) return fail(GDN_ERR_BAD_SHAPE, "h0_seq_stride must be >= 0");
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
   return GDN_OK;
 }
 
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Heads of q and k (num_k_heads, 0 meaning one per value head).
+int32_t k_heads(const gdn_problem *p) { return p->num_k_heads > 0 ? p->num_k_heads : p->num_heads; }
 
 // Number of chunks: exact from the host copy of cu_seqlens, else ceil(T / 64).
 int64_t count_chunks(const gdn_problem *p, const int32_t *cu_host) {
@@ -269,6 +275,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.T = p->total_tokens;
   a.N = p->num_seqs;
   a.H = p->num_heads;
+  a.HK = k_heads(p);
   a.L = lay.L;
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
@@ -404,6 +411,7 @@ struct BwdLayout {
   int64_t units = 0;
   size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
   size_t unit_bm = 0, unit_h0 = 0;
+  size_t dq_part = 0, dk_part = 0;  // grouped heads: per-value-head dq, dk (fp32)
   size_t total = 0;
 };
 
@@ -453,6 +461,10 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
     L->unit_bm = take(2 * per);
     L->unit_h0 = take(per);
   }
+  if (k_heads(p) < H) {
+    L->dq_part = take(sizeof(float) * T * H * D);
+    L->dk_part = take(sizeof(float) * T * H * D);
+  }
   L->total = off;
   return GDN_OK;
 }
@@ -478,6 +490,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
   a.T = p->total_tokens;
   a.N = p->num_seqs;
   a.H = p->num_heads;
+  a.HK = k_heads(p);
   a.L = L.L;
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
@@ -593,10 +606,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.hc = hc;
   b.delta = delta;
   b.dhn = reinterpret_cast<float *>(base + L.dhn);
+  const bool grouped = k_heads(p) < p->num_heads;
+  b.dq_part = grouped ? reinterpret_cast<float *>(base + L.dq_part) : nullptr;
+  b.dk_part = grouped ? reinterpret_cast<float *>(base + L.dk_part) : nullptr;
   b.ddelta = reinterpret_cast<float *>(base + L.ddelta);
   b.T = p->total_tokens;
   b.N = p->num_seqs;
   b.H = p->num_heads;
+  b.HK = k_heads(p);
   b.scale = p->scale;
   hipError_t e;
   if (fast) {
@@ -638,6 +655,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     if (e != hipSuccess) return hip_fail(e, "backward chain launch");
     e = gdn::launch_bwd_grad(b, p->d_k, bf16, L.nc, stream);
     if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
+  }
+  if (grouped) {  // dq, dk of each key head: the sum over its value heads
+    e = gdn::launch_group_sum(b.dq_part, p->total_tokens, p->num_heads, k_heads(p), p->d_k,
+                              p->dtype == GDN_DTYPE_BF16, dq, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_group_sum(b.dk_part, p->total_tokens, p->num_heads, k_heads(p), p->d_k,
+                                p->dtype == GDN_DTYPE_BF16, dk, stream);
+    if (e != hipSuccess) return hip_fail(e, "grouped heads: dq, dk sums");
   }
   if (dh0 && shared_h0) {
     e = gdn::launch_sum_dh0(b.dh0_seq, p->num_seqs, p->num_heads, p->d_k, dh0, stream);

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs b) {
   constexpr int NT = D / 64, MTD = D / 16;
   __shared__ SM sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
-  const int seq = blockIdx.x, h = blockIdx.y, H = b.H;
+  const int seq = blockIdx.x, h = blockIdx.y, H = b.H, hk = h / (H / b.HK);
   if (wave == 0) {
     Unit un;
     const bool ok = find_unit(b.cu, b.N, 0, seq, true, lane, un);
@@ -136,8 +136,9 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs b) {
       const int r = i / D, col = i % D;
       const bool ok = r < n;
       const int64_t gi = ((t0 + r) * H + h) * D + col;
-      sm.q[r * LD + col] = ok ? to_f32(gq_[gi]) : 0.f;
-      sm.k[r * LD + col] = ok ? to_f32(gk_[gi]) : 0.f;
+      const int64_t gik = ((t0 + r) * b.HK + hk) * D + col;  // q and k: the key head
+      sm.q[r * LD + col] = ok ? to_f32(gq_[gik]) : 0.f;
+      sm.k[r * LD + col] = ok ? to_f32(gk_[gik]) : 0.f;
       sm.dout[r * LD + col] = ok ? b.scale * to_f32(gdo[gi]) : 0.f;
       sm.w[r * LD + col] = b.w[((cg * H + h) * 64 + r) * D + col];
     }
@@ -255,7 +256,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
   constexpr int NB = D / 64;  // 64-column blocks
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
-  const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
+  const int cg = blockIdx.x, h = blockIdx.y, H = b.H, hk = h / (H / b.HK);
   // locate the chunk: its sequence and its index within that sequence
   if (wave == 0) {
     int64_t before = 0;
@@ -318,8 +319,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
     __syncthreads();
     load_rows64(sm.x0, gdo, t0, n, h, H, D, 64 * cb, dsc, tid);
     load_rows64(sm.x1, b.delta, t0, n, h, H, D, 64 * cb, 1.f, tid);
-    load_rows64(sm.qk, gq_, t0, n, h, H, D, 64 * cb, 1.f, tid);
-    load_rows64(sm.kk, gk_, t0, n, h, H, D, 64 * cb, 1.f, tid);
+    load_rows64(sm.qk, gq_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid);
+    load_rows64(sm.kk, gk_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -373,7 +374,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
                          dw[s]);
     }
     __syncthreads();
-    load_rows64(sm.x1, gk_, t0, n, h, H, D, 64 * kb, 1.f, tid);
+    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -489,8 +490,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
     }
     __syncthreads();
     // operand tiles of this block: x0 = Q, x1 = K, qk = dW, kk = dDelta
-    load_rows64(sm.x0, gq_, t0, n, h, H, D, 64 * kb, 1.f, tid);
-    load_rows64(sm.x1, gk_, t0, n, h, H, D, 64 * kb, 1.f, tid);
+    load_rows64(sm.x0, gq_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
+    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
     load_rows64(sm.kk, b.ddelta, t0, n, h, H, D, 64 * kb, 1.f, tid);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -520,8 +521,13 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
         if (r < n) {
           const int64_t gi = ((t0 + r) * H + h) * D + col;
           vv = to_f32(gv_[gi]);
-          static_cast<E *>(b.dq)[gi] = from_f32<E>(dq);
-          static_cast<E *>(b.dk)[gi] = from_f32<E>(dkv);
+          if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
+            b.dq_part[gi] = dq;
+            b.dk_part[gi] = dkv;
+          } else {
+            static_cast<E *>(b.dq)[gi] = from_f32<E>(dq);
+            static_cast<E *>(b.dk)[gi] = from_f32<E>(dkv);
+          }
           static_cast<E *>(b.dv)[gi] = from_f32<E>(br * tdu[i]);
         }
         prg[s][i] += ar * y1[s][i] * qv + br * ar * tdw[i] * kv - cr * y2[s][i] * kv;
@@ -595,6 +601,28 @@ __global__ __launch_bounds__(256) void sum_dh0_kernel(const float *__restrict__ 
   float acc = 0.f;
   for (int n = 0; n < N; ++n) acc += src[(int64_t)n * per_seq + i];
   dst[i] = acc;
+}
+
+__global__ __launch_bounds__(256) void group_sum_kernel(const float *__restrict__ part, int64_t T,
+                                                       int H, int HK, int D, int is_bf16,
+                                                       void *__restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // element of out [T, HK, D]
+  if (i >= T * HK * D) return;
+  const int64_t t = i / ((int64_t)HK * D);
+  const int hk = (int)(i / D % HK), d = (int)(i % D), G = H / HK;
+  float s = 0.f;
+  for (int j = 0; j < G; ++j) s += part[(t * H + hk * G + j) * D + d];
+  if (is_bf16) static_cast<bf16 *>(out)[i] = (bf16)s;
+  else static_cast<float *>(out)[i] = s;
+}
+
+hipError_t launch_group_sum(const float *part, int64_t T, int32_t H, int32_t HK, int32_t D,
+                            bool bf16, void *out, hipStream_t stream) {
+  const int64_t n = T * HK * D;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     part, T, H, HK, D, bf16 ? 1 : 0, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_bwd_chain(const BwdArgs &b, int D, bool is_bf16, hipStream_t stream) {

@@ -143,8 +143,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;  // malformed cu_seqlens: touch nothing
   if (kTransition && c0 == 0) return;  // a sequence's first unit has no predecessor
   const int64_t tok_bytes = (int64_t)H * kRowB;
-  const char *__restrict__ gk = static_cast<const char *>(b.k) + (int64_t)h * kRowB;
-  const char *__restrict__ gqp = static_cast<const char *>(b.q) + (int64_t)h * kRowB;
+  const int hk = h / (H / b.HK);                   // this value head's key head
+  const int64_t tok_qk = (int64_t)b.HK * kRowB;    // stride of one token in q, k
+  const char *__restrict__ gk = static_cast<const char *>(b.k) + (int64_t)hk * kRowB;
+  const char *__restrict__ gqp = static_cast<const char *>(b.q) + (int64_t)hk * kRowB;
   const char *__restrict__ gdo = static_cast<const char *>(b.dout) + (int64_t)h * kRowB;
   const bf16 *__restrict__ gb = static_cast<const bf16 *>(b.beta);
   const int col0 = 16 * kNT * w + cl;  // this lane's column in tile nt: col0 + 16 nt
@@ -213,11 +215,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 #pragma unroll
     for (int j = 0; j < 16 / kWaves; ++j) {
       const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
-      const int64_t off = (t0 + min(r, n - 1)) * tok_bytes + (((lane & 15) ^ sw(r)) << 4);
+      const int64_t t = t0 + min(r, n - 1);
+      const int u = ((lane & 15) ^ sw(r)) << 4;
       const int lo = ((64 / kWaves) * w + 4 * j) * kRowB;
-      dma16(gk + off, sm.kqo[set][0] + lo);
-      dma16(gqp + off, sm.kqo[set][1] + lo);
-      dma16(gdo + off, sm.kqo[set][2] + lo);
+      dma16(gk + t * tok_qk + u, sm.kqo[set][0] + lo);
+      dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
+      dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
     }
     // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
     const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
@@ -491,14 +494,15 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
   sb[lane] = lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
   // K rows as MFMA operands straight from HBM: row 16 m + cl, elements 32 ks + 8 gq .. + 7 (rows
   // past n read the last token; A masks them)
-  const bf16 *gk = static_cast<const bf16 *>(b.k) + (int64_t)h * kD;
+  const int hk = h / (H / b.HK);  // this value head's key head
+  const bf16 *gk = static_cast<const bf16 *>(b.k) + (int64_t)hk * kD;
   bf16x8 kf[4][4];
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const int64_t t = t0 + min(16 * m + cl, n - 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
-      kf[m][ks] = *reinterpret_cast<const bf16x8 *>(gk + t * H * kD + 32 * ks + 8 * gq);
+      kf[m][ks] = *reinterpret_cast<const bf16x8 *>(gk + t * b.HK * kD + 32 * ks + 8 * gq);
   }
   __syncthreads();
   // A transposed: am[i][r] = A[r][i]

@@ -138,6 +138,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   const int64_t t0 = ts0 + (int64_t)sm.imisc[1] * kChunk;
   const int n = (int)min<int64_t>(kChunk, ts1 - t0);
   const int64_t tok_bytes = (int64_t)H * kRowB;
+  const int hk = h / (H / b.HK);                  // this value head's key head
+  const int64_t tok_qk = (int64_t)b.HK * kRowB;   // stride of one token in q, k
   const int64_t dd = (int64_t)kD * kD;
   const float scale = b.scale;
   const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
@@ -160,8 +162,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
       for (int j = 0; j < 16 / kWaves; ++j) {
         const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
-        dma16(src[s] + (t0 + min(r, n - 1)) * tok_bytes + (int64_t)h * kRowB +
-                  (((lane & 15) ^ sw(r)) << 4),
+        const bool qk = s == 1 || s == 2;  // q and k: the key head's rows
+        dma16(src[s] + (t0 + min(r, n - 1)) * (qk ? tok_qk : tok_bytes) +
+                  (int64_t)(qk ? hk : h) * kRowB + (((lane & 15) ^ sw(r)) << 4),
               dst[s] + ((64 / kWaves) * w + 4 * j) * kRowB);
       }
     f32x4 xr[2][8 * 4 / kWaves];
@@ -450,8 +453,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
           const float dkv = dk[nt][i] + cr[i] * Y2[mt][nt][i] - br[i] * ar[i] * Rh[mt][nt][i];
           if (r < n) {
             const int64_t gi = ((t0 + r) * H + h) * kD + fcol + 16 * nt;
-            static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
-            static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
+            if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
+              b.dq_part[gi] = dqv;
+              b.dk_part[gi] = dkv;
+            } else {
+              static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
+              static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
+            }
           }
           rg[mt][i] += ar[i] * y1[i] * qv[i] - br[i] * ar[i] * Rh[mt][nt][i] * kv[i] -
                        cr[i] * Y2[mt][nt][i] * kv[i];

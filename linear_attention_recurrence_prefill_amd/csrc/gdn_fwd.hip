@@ -152,6 +152,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
+  const int hk = h / (H / a.HK);  // this value head's key head
   const E *__restrict__ gq_ = static_cast<const E *>(a.q);
   const E *__restrict__ gk_ = static_cast<const E *>(a.k);
   const E *__restrict__ gv_ = static_cast<const E *>(a.v);
@@ -209,9 +210,9 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     __syncthreads();  // the previous chunk is done with LDS
 
     // ---- stage K, V (and Q) token-major in LDS
-    load_tile<E, D, LDE>(sm.k, gk_, t0, n, h, H, tid);
+    load_tile<E, D, LDE>(sm.k, gk_, t0, n, hk, a.HK, tid);
     load_tile<E, D, LDE>(sm.vw, gv_, t0, n, h, H, tid);
-    if (emit) load_tile<E, D, LDE>(sm.q, gq_, t0, n, h, H, tid);
+    if (emit) load_tile<E, D, LDE>(sm.q, gq_, t0, n, hk, a.HK, tid);
 
     // ---- gate cumsum and folded decay factors (row a1)
     if (wave == 0) {

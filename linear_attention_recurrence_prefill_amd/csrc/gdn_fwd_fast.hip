@@ -98,6 +98,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
+  const int hk = h / (H / a.HK);  // this value head's key head
   const bf16 *__restrict__ gq_ = static_cast<const bf16 *>(a.q);
   const bf16 *__restrict__ gk_ = static_cast<const bf16 *>(a.k);
   const bf16 *__restrict__ gv_ = static_cast<const bf16 *>(a.v);
@@ -150,9 +151,10 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
       pq[j] = pk[j] = pv[j] = uint4{0u, 0u, 0u, 0u};
       if (r < n) {
         const int64_t off = ((t0 + r) * H + h) * D + cu16 * 8;
-        pk[j] = *reinterpret_cast<const uint4 *>(gk_ + off);
+        const int64_t off_qk = ((t0 + r) * a.HK + hk) * D + cu16 * 8;
+        pk[j] = *reinterpret_cast<const uint4 *>(gk_ + off_qk);
         pv[j] = *reinterpret_cast<const uint4 *>(gv_ + off);
-        if (em) pq[j] = *reinterpret_cast<const uint4 *>(gq_ + off);
+        if (em) pq[j] = *reinterpret_cast<const uint4 *>(gq_ + off_qk);
       }
     }
     if (wave == 0) {

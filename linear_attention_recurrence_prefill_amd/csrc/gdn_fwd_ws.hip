@@ -195,9 +195,11 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
   if (kTransition && c1 == nchunks_seq) return;  // a sequence's last unit has no successor
-  const int64_t tok_bytes = (int64_t)H * kRowBytes;  // stride of one token in q, k, v, o
-  const char *__restrict__ gq_ = static_cast<const char *>(a.q) + (int64_t)h * kRowBytes;
-  const char *__restrict__ gk_ = static_cast<const char *>(a.k) + (int64_t)h * kRowBytes;
+  const int64_t tok_bytes = (int64_t)H * kRowBytes;      // stride of one token in v, o
+  const int64_t tok_qk = (int64_t)a.HK * kRowBytes;      // ... in q, k
+  const int hk = h / (H / a.HK);                          // this value head's key head
+  const char *__restrict__ gq_ = static_cast<const char *>(a.q) + (int64_t)hk * kRowBytes;
+  const char *__restrict__ gk_ = static_cast<const char *>(a.k) + (int64_t)hk * kRowBytes;
   const char *__restrict__ gv_ = static_cast<const char *>(a.v) + (int64_t)h * kRowBytes;
   const bf16 *__restrict__ gb_ = static_cast<const bf16 *>(a.beta);
   char *__restrict__ go_ = static_cast<char *>(a.o) + (int64_t)h * kRowBytes;
@@ -574,13 +576,13 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const int r = 4 * j + (lane >> 4);
-      o_dma[j] = pin((int)(r * tok_bytes) + (((lane & 15) ^ sw(r)) << 4));
+      o_dma[j] = pin((int)(r * tok_qk) + (((lane & 15) ^ sw(r)) << 4));
     }
     auto dma_tile = [&](char *dst, const char *src, int c) {
       const int64_t t0 = chunk_t0(c);
       const int n = chunk_n(c);
       if (n == kChunk) {
-        const char *base = src + t0 * tok_bytes;
+        const char *base = src + t0 * tok_qk;
 #pragma unroll
         for (int j = 0; j < 16; ++j) dma16(base + o_dma[j], dst + (j >> 2) * kBlk + 1024 * (j & 3));
       } else {  // ragged last chunk: rows past n repeat the last token
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         for (int j = 0; j < 16; ++j) {
           const int r = 4 * j + (lane >> 4);
           const int64_t t = t0 + min(r, n - 1);
-          dma16(src + t * tok_bytes + (((lane & 15) ^ sw(r)) << 4), dst + (j >> 2) * kBlk + 1024 * (j & 3));
+          dma16(src + t * tok_qk + (((lane & 15) ^ sw(r)) << 4), dst + (j >> 2) * kBlk + 1024 * (j & 3));
         }
       }
     };

@@ -23,6 +23,7 @@ struct FwdArgs {
   float *dbg_gamma, *dbg_tmat, *dbg_w, *dbg_u, *dbg_hc, *dbg_delta;  // intermediates (or null)
   int64_t T;
   int32_t N, H;
+  int32_t HK;  // heads of q and k (H / HK value heads share one)
   int32_t L;  // segment length in chunks, 0 = whole sequences
   float scale;
   float log_thr;
@@ -57,8 +58,12 @@ struct BwdArgs {
   float *dg, *dh0_seq;
   const float *gamma, *tmat, *w, *hc, *delta;
   float *dhn, *ddelta;
+  // grouped heads (HK < H): dq and dk of every value head, fp32 [T, H, D], summed per key head
+  // afterwards (null when HK == H: dq and dk are written directly)
+  float *dq_part, *dk_part;
   int64_t T;
   int32_t N, H;
+  int32_t HK;  // heads of q and k
   float scale;
 };
 
@@ -102,5 +107,9 @@ hipError_t launch_bwd_grad(const BwdArgs &b, int D, bool bf16, int64_t max_chunk
                            hipStream_t stream);
 hipError_t launch_sum_dh0(const float *dh0_seq, int32_t N, int32_t H, int32_t D, float *dh0,
                           hipStream_t stream);
+// Grouped heads: out[t, hk, :] = sum over the H / HK value heads of key head hk of part[t, h, :]
+// (fixed order), in the input dtype.
+hipError_t launch_group_sum(const float *part, int64_t T, int32_t H, int32_t HK, int32_t D,
+                            bool bf16, void *out, hipStream_t stream);
 
 }  // namespace gdn

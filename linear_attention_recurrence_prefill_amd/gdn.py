@@ -38,7 +38,7 @@ class GdnProblem(ctypes.Structure):
                 ("d_v", ctypes.c_int32), ("chunk", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("mode", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32), ("trunc_log_threshold", ctypes.c_float),
-                ("scale", ctypes.c_float), ("reserved", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("num_k_heads", ctypes.c_int32),
                 ("h0_seq_stride", ctypes.c_int64)]
 
 
@@ -102,7 +102,8 @@ def _stream():
 
 
 def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact", scale=1.0,
-                 seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, h0_seq_stride=None):
+                 seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, h0_seq_stride=None,
+                 num_k_heads=0):
     lib = load_library()
     p = GdnProblem()
     _check(lib.gdn_problem_init(ctypes.byref(p), int(total_tokens), int(num_seqs),
@@ -115,13 +116,19 @@ def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact
     p.trunc_log_threshold = float(trunc_log_threshold)
     if h0_seq_stride is not None:
         p.h0_seq_stride = int(h0_seq_stride)
+    p.num_k_heads = int(num_k_heads)
     return p
 
 
 def _validate(q, k, v, g, beta, cu_seqlens, h0):
-    T, H, D = q.shape
-    if k.shape != (T, H, D) or v.shape != (T, H, D):
-        raise ValueError("q, k, v must all be [T, H, D]")
+    """Sizes of a call: q, k [T, Hk, D], v [T, H, D] with Hk dividing H (grouped heads: value
+    head h reads key head h // (H // Hk)), g, beta [T, H]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be [T, heads, D]")
+    T, Hk, D = q.shape
+    H = v.shape[1]
+    if k.shape != (T, Hk, D) or v.shape != (T, H, D) or Hk < 1 or H % Hk != 0:
+        raise ValueError("q and k must be [T, Hk, D] and v [T, H, D] with Hk dividing H")
     if g.shape != (T, H) or beta.shape != (T, H):
         raise ValueError("g and beta must be [T, H]")
     if q.dtype not in (torch.bfloat16, torch.float32):
@@ -146,7 +153,7 @@ def _validate(q, k, v, g, beta, cu_seqlens, h0):
             stride = H * D * D
         else:
             raise ValueError("h0 must be [N, H, D, D] or [H, D, D] (shared by all sequences)")
-    return T, H, D, N, stride
+    return T, H, D, N, stride, Hk
 
 
 def _host_cu(cu_seqlens, cu_seqlens_host):
@@ -161,9 +168,9 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
               cu_seqlens_host=None, out=None, final_state=None, workspace=None):
     """Forward of the chunked gated delta rule.  Returns (o, ht or None)."""
     lib = load_library()
-    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_slots,
-                     trunc_log_threshold, stride)
+                     trunc_log_threshold, stride, num_k_heads=Hk)
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
@@ -182,9 +189,12 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
 
 def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, num_slots=0,
                         cu_seqlens_host=None):
+    """Workspace bytes of chunk_fwd for q [T, Hk, D] and H value heads (H = Hk if not given)."""
     lib = load_library()
     T, Hq, D = q.shape
-    p = make_problem(T, cu_seqlens.numel() - 1, Hq, D, q.dtype, mode, 1.0, seg_chunks, num_slots)
+    heads = Hq if H is None else H
+    p = make_problem(T, cu_seqlens.numel() - 1, heads, D, q.dtype, mode, 1.0, seg_chunks,
+                     num_slots, num_k_heads=Hq)
     n = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), _host_cu(cu_seqlens,
                                                                       cu_seqlens_host),
@@ -221,11 +231,11 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
     o, ht, dict(gamma [T,H], tmat [Nc,H,64,64], w [Nc,H,64,D], u [Nc,H,64,D],
     hc [Nc,H,D,D], delta [T,H,D])."""
     lib = load_library()
-    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if num_chunks is None:
         cu = cu_seqlens.cpu().tolist()
         num_chunks = sum((cu[i + 1] - cu[i] + 63) // 64 for i in range(N))
-    p = make_problem(T, N, H, D, q.dtype, "exact", scale, h0_seq_stride=stride)
+    p = make_problem(T, N, H, D, q.dtype, "exact", scale, h0_seq_stride=stride, num_k_heads=Hk)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(ws_bytes)))
     ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
@@ -254,14 +264,14 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
     seg_chunks / num_slots set the segment length of the forward recompute's split and the
     workgroup slots it is planned for (0: chosen by the library)."""
     lib = load_library()
-    T, H, D, N, stride = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
         raise ValueError("dout must be contiguous with v's shape and q's dtype")
     if dht is not None and (dht.shape != (N, H, D, D) or dht.dtype != torch.float32):
         raise ValueError("dht must be float32 [N, H, D, D]")
     p = make_problem(T, N, H, D, q.dtype, "exact", scale, seg_chunks=seg_chunks,
                      num_slots=num_slots,
-                     h0_seq_stride=stride if stride is not None else H * D * D)
+                     h0_seq_stride=stride if stride is not None else H * D * D, num_k_heads=Hk)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
     if workspace is None or workspace.numel() < ws_bytes.value:

@@ -66,7 +66,7 @@ def test_problem_defaults(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("chunk", 32, 2), ("d_k", 96, 2), ("d_v", 64, 2), ("num_heads", 0, 2), ("num_seqs", 0, 2),
-    ("total_tokens", -1, 2), ("dtype", 7, 3), ("mode", 5, 4), ("reserved", 1, 2),
+    ("total_tokens", -1, 2), ("dtype", 7, 3), ("mode", 5, 4), ("num_k_heads", 3, 2), ("num_k_heads", -1, 2), ("num_k_heads", 16, 2),
     ("h0_seq_stride", -1, 2)])
 def test_bad_problem_rejected_on_host(lib, field, value, status):
     p = _problem(**{field: value})
