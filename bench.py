@@ -24,8 +24,18 @@ MI355X's ~315 flop/byte ridge).  Algorithmic bytes per launch = 1030 B per (toke
 rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/ (null when not measured for the
 current kernel).
 
+``timing``: the same K steps again with an event between consecutive steps give the per-step
+median, p10 and p90 (``ms_per_step`` and ``value`` come from the bracketing events alone), and
+``host_call_us`` is the host's wall time for one call after a device synchronisation (argument
+checks, segment planning, launches).  ``roofline.median`` holds %HBM, %MFMA and the roofline
+fraction max(B / bandwidth, F / rate) / t at the median time against the datasheet peaks,
+``roofline.median_vs_measured_peaks`` the same against ``measured_peaks`` (the library's stream
+copy of 1 GiB and its loop of bf16 MFMAs, timed on this GPU).  Events between steps add a few
+microseconds to each measured step, which shows in the 26 us decode step's median.
+
 ``cpu_baseline``: the fp64 token-recurrent oracle (plain C, OpenMP over (sequence, head) pairs)
-timed on this host on the same workload (8 (sequence, head) units, so at most 8 threads).
+timed on this host on the same workload (8 (sequence, head) units, so at most 8 threads), and
+with one thread on two of the heads, scaled to eight.
 """
 from __future__ import annotations
 
@@ -59,6 +69,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-measured-peaks", action="store_true",
+                    help="skip the on-device copy and bf16 matmul peak measurements")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip the training backward timed beside the forward")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -78,6 +90,14 @@ def time_steps(gdn, torch, sets, mode, steps, warmup):
                       mode=mode, cu_seqlens_host=cu_host, out=outs[i % len(sets)],
                       final_state=hts[i % len(sets)])
 
+    return timed(torch, step, steps, warmup)
+
+
+def timed(torch, step, steps, warmup):
+    """Times ``step(i)``: ``warmup`` untimed calls, then exactly ``steps`` calls between two HIP
+    events on the current stream (device synchronisations on both sides): the mean per step.  A
+    second pass of ``steps`` calls with an event between consecutive calls gives the per-call
+    distribution (median, p10, p90; events between calls, so kept apart from the mean)."""
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -88,7 +108,63 @@ def time_steps(gdn, torch, sets, mode, steps, warmup):
         step(i)
     end.record(stream)
     torch.cuda.synchronize()
-    return start.elapsed_time(end) / steps
+    mean = start.elapsed_time(end) / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    return {"mean_ms": mean, "median_ms": float(np.median(per)),
+            "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90))}
+
+
+def host_call_us(torch, step, calls=20):
+    """Host wall time of one call after a device synchronisation (argument checks, planning and
+    kernel launches; the GPU work itself runs asynchronously): the median over ``calls``."""
+    out = []
+    for i in range(calls):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        step(i)
+        out.append((time.perf_counter() - t0) * 1e6)
+    torch.cuda.synchronize()
+    return float(np.median(out))
+
+
+def measured_peaks(gdn, torch):
+    """Peaks measured on this GPU, beside the datasheet ones: the HBM bandwidth of the library's
+    stream-copy kernel on 1 GiB (read + write bytes over the time; torch's copy beside it) and the
+    bf16 matrix-core rate of its register-resident MFMA loop (an 8192^3 torch.matmul beside it)."""
+    n = (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    t = timed(torch, lambda i: gdn.calib_copy(src, dst), 20, 3)
+    hbm = 2 * n * 4 / (t["median_ms"] / 1e3) / 1e9
+    assert torch.equal(dst[:: 1 << 16], src[:: 1 << 16])
+    t = timed(torch, lambda i: dst.copy_(src), 20, 3)
+    hbm_torch = 2 * n * 4 / (t["median_ms"] / 1e3) / 1e9
+    del src, dst
+    out = torch.empty(8 * 256 * 64, dtype=torch.float32, device="cuda")
+    mfma = {}
+    for w in (4, 8):
+        flops = gdn.calib_mfma_bf16(out, w, 2000)
+        t = timed(torch, lambda i: gdn.calib_mfma_bf16(out, w, 2000), 10, 2)
+        mfma[w] = flops / (t["median_ms"] / 1e3) / 1e12
+    m = 8192
+    a = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    b = torch.randn(m, m, device="cuda").to(torch.bfloat16)
+    c = torch.empty(m, m, device="cuda", dtype=torch.bfloat16)
+    t = timed(torch, lambda i: torch.matmul(a, b, out=c), 20, 3)
+    gemm = 2 * m ** 3 / (t["median_ms"] / 1e3) / 1e12
+    return {"hbm_GBps": hbm,
+            "hbm_how": "gdn_calib_copy stream copy of 1 GiB (read + write), median of 20",
+            "hbm_torch_copy_GBps": hbm_torch,
+            "bf16_TFLOPs": max(mfma.values()),
+            "bf16_how": "gdn_calib_mfma_bf16 (4 independent v_mfma_f32_32x32x16_bf16 chains per "
+                        "wave, 4 and 8 waves per CU, the better), median of 10",
+            "bf16_gemm_torch_TFLOPs": gemm}
 
 
 def cpu_baseline(inp):
@@ -102,9 +178,24 @@ def cpu_baseline(inp):
     t0 = time.perf_counter()
     oracle.fwd_recurrent(*args, inp["cu_seqlens"], nthreads=threads)
     dt = time.perf_counter() - t0
+    t0 = time.perf_counter()  # one thread on two of the eight heads
+    oracle.fwd_recurrent(*[np.ascontiguousarray(a[:, :2]) for a in args], inp["cu_seqlens"],
+                         nthreads=1)
+    dt1 = (time.perf_counter() - t0) * 4
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                         "")
+    except OSError:
+        pass
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"full workload: 1 x {T} tokens x 8 heads, fp64 token recurrence, "
-                      f"{dt:.2f} s wall on {threads} of {cores} host threads"}
+                      f"{dt:.2f} s wall on {threads} of {cores} host threads",
+            "one_thread_tokens_per_s": T / dt1,
+            "one_thread_sample": f"1 thread on heads 0-1 of the same input, {dt1 / 4:.2f} s, "
+                                 "scaled to 8 heads",
+            "nproc": cores, "cpu_model": model}
 
 
 def copy_calibration(mib):
@@ -155,14 +246,18 @@ def main():
     results = {}
     modes = ["truncate", "exact"] if args.mode == "both" else [args.mode]
     for m in modes:
-        ms = time_steps(gdn, torch, sets, m, args.steps, args.warmup)
-        results[m] = ms
+        results[m] = time_steps(gdn, torch, sets, m, args.steps, args.warmup)
     head = modes[0]
-    ms = results[head]
+    ms = results[head]["mean_ms"]
     value = T / (ms / 1e3)
     bytes_launch = BYTES_PER_TH * T * H + STATE_BYTES * H
     flops_launch = FLOP_PER_TH * T * H
     achieved = bytes_launch / (ms / 1e3) / 1e9
+    cu_host = [0, T]
+    host_us = host_call_us(torch, lambda i: gdn.chunk_fwd(
+        sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["g"], sets[0]["beta"],
+        sets[0]["cu_seqlens"], None, mode=head, cu_seqlens_host=cu_host))
+    peaks = None if args.no_measured_peaks else measured_peaks(gdn, torch)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -191,11 +286,19 @@ def main():
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "mfma_frac": flops_launch / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                      "bytes_per_launch": bytes_launch, "flops_per_launch": flops_launch},
+        "timing": dict(results[head], host_call_us=host_us,
+                       tokens_per_s_median=T / (results[head]["median_ms"] / 1e3)),
     }
+    line["roofline"].update(fractions(results[head]["median_ms"], bytes_launch, flops_launch,
+                                      peaks))
+    if peaks is not None:
+        line["measured_peaks"] = peaks
     for m in modes[1:]:
-        line[f"{m}_mode"] = {"ms_per_step": results[m], "value": T / (results[m] / 1e3),
-                             "roofline_frac": bytes_launch / (results[m] / 1e3) / 1e9
-                             / HBM_PEAK_GBS}
+        r = results[m]
+        line[f"{m}_mode"] = {"ms_per_step": r["mean_ms"], "value": T / (r["mean_ms"] / 1e3),
+                             "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
+                             / HBM_PEAK_GBS, "timing": r,
+                             **fractions(r["median_ms"], bytes_launch, flops_launch, peaks)}
     if not args.no_backward:
         line["backward"] = time_backward(gdn, torch, args.steps, args.warmup)
         line["decode"] = time_decode(gdn, torch, args.steps, args.warmup)
@@ -203,6 +306,24 @@ def main():
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def fractions(median_ms, nbytes, nflops, peaks):
+    """The four figures of the roofline at the median time: %HBM = bytes / (t * peak bandwidth),
+    %MFMA = flops / (t * peak bf16 rate), and the roofline fraction max(bytes / bandwidth,
+    flops / rate) / t, against the datasheet peaks and (when measured) this GPU's."""
+    t = median_ms / 1e3
+    out = {"median": {"hbm_frac": nbytes / t / 1e9 / HBM_PEAK_GBS,
+                      "mfma_frac": nflops / t / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                      "roofline_frac": max(nbytes / 1e9 / HBM_PEAK_GBS,
+                                           nflops / 1e12 / BF16_MFMA_PEAK_TFLOPS) / t}}
+    if peaks is not None:
+        out["median_vs_measured_peaks"] = {
+            "hbm_frac": nbytes / t / 1e9 / peaks["hbm_GBps"],
+            "mfma_frac": nflops / t / 1e12 / peaks["bf16_TFLOPs"],
+            "roofline_frac": max(nbytes / 1e9 / peaks["hbm_GBps"],
+                                 nflops / 1e12 / peaks["bf16_TFLOPs"]) / t}
+    return out
 
 
 def time_decode(gdn, torch, steps, warmup):
@@ -220,24 +341,14 @@ def time_decode(gdn, torch, steps, warmup):
     state = 0.1 * torch.randn(B, H, D, D, device="cuda", generator=gen)
     out = torch.empty_like(v)
 
-    def step():
-        gdn.decode_step(q, k, v, g, beta, state, out=out)
-
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    r = timed(torch, lambda i: gdn.decode_step(q, k, v, g, beta, state, out=out), steps, warmup)
+    ms = r["mean_ms"]
     nbytes = B * H * (2 * D * D * 4 + 4 * D * 2 + 4 + 2)
     achieved = nbytes / (ms / 1e3) / 1e9
     return {"workload": f"{B} sequences x {H} heads, d_k=d_v={D}, bf16 inputs, fp32 state",
             "us_per_step": ms * 1e3, "tokens_per_s": B / (ms / 1e3),
+            "median_us": r["median_ms"] * 1e3, "p10_us": r["p10_ms"] * 1e3,
+            "p90_us": r["p90_ms"] * 1e3,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes}}
@@ -267,25 +378,16 @@ def time_backward(gdn, torch, steps, warmup):
     assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)) == 0
     ws = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")  # allocated once, outside
 
-    def step():
+    def step(i):
         gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / steps
+    r = timed(torch, step, steps, warmup)
+    ms = r["mean_ms"]
     nbytes_alg = BWD_BYTES_PER_TH * T * H
     achieved = nbytes_alg / (ms / 1e3) / 1e9
     return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
                         f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
-            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3),
+            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes_alg}}

@@ -1,10 +1,11 @@
 """MI355X (gfx950) Gated DeltaNet chunked prefill.
 
 ``gdn`` holds the Python binding of the HIP library (``libgdn_mi355x.so``, built by
-``python -m linear_attention_recurrence_prefill_amd.build``); the C ABI is ``include/gdn.h``.
+``python -m linear_attention_recurrence_prefill_amd.build``); the C ABI is ``include/gdn.h`` (and
+``include/gdn_calib.h`` for the measurement kernels).
 """
-from .gdn import (GdnError, chunk_bwd, chunk_fwd, chunk_fwd_intermediates, chunk_fwd_plan,
-                  decode_step, load_library)
+from .gdn import (GdnError, calib_copy, calib_mfma_bf16, chunk_bwd, chunk_fwd,
+                  chunk_fwd_intermediates, chunk_fwd_plan, decode_step, load_library)
 
 __all__ = ["GdnError", "chunk_fwd", "chunk_bwd", "chunk_fwd_plan", "chunk_fwd_intermediates",
-           "decode_step", "load_library"]
+           "decode_step", "calib_copy", "calib_mfma_bf16", "load_library"]

@@ -9,7 +9,9 @@
 #include <mutex>
 
 #include "../../include/gdn.h"
+#include "../../include/gdn_calib.h"
 #include "gdn_bwd_internal.h"
+#include "gdn_calib_internal.h"
 #include "gdn_decode.h"
 #include "gdn_internal.h"
 
@@ -704,6 +706,31 @@ gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t head_dim, i
   a.scale = scale;
   const hipError_t e = gdn::launch_decode_step(a, head_dim, dtype == GDN_DTYPE_BF16, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_calib_copy(const void *src, void *dst, size_t bytes, hipStream_t stream) {
+  if (!src || !dst) return fail(GDN_ERR_NULL_ARG, "src and dst are required");
+  if (!aligned16(src) || !aligned16(dst))
+    return fail(GDN_ERR_BAD_ALIGNMENT, "src and dst must be 16-byte aligned");
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 40))
+    return fail(GDN_ERR_BAD_SHAPE, "bytes must be a positive multiple of 16 (at most 2^40)");
+  int cus = 0;
+  gdn_status s = device_info(&cus);
+  if (s != GDN_OK) return s;
+  const hipError_t e = gdn::launch_calib_copy(src, dst, (int64_t)(bytes / 16), cus, stream);
+  if (e != hipSuccess) return hip_fail(e, "calibration copy launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_calib_mfma_bf16(float *out, int waves_per_cu, int iters, hipStream_t stream) {
+  if (!out) return fail(GDN_ERR_NULL_ARG, "out is required");
+  if (waves_per_cu < 1 || waves_per_cu > 8 || iters < 1 || iters > (1 << 20))
+    return fail(GDN_ERR_BAD_SHAPE, "waves_per_cu must be in 1..8 and iters in 1..2^20");
+  gdn_status s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  const hipError_t e = gdn::launch_calib_mfma(out, waves_per_cu * 256, iters, stream);
+  if (e != hipSuccess) return hip_fail(e, "calibration MFMA launch");
   return GDN_OK;
 }
 

@@ -23,7 +23,8 @@ _MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
 # Every exported entry point of include/gdn.h.
 EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
            "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
-           "gdn_chunk_bwd", "gdn_decode_step", "gdn_status_string", "gdn_last_error")
+           "gdn_chunk_bwd", "gdn_decode_step", "gdn_status_string", "gdn_last_error",
+           "gdn_calib_copy", "gdn_calib_mfma_bf16")
 
 
 class GdnError(RuntimeError):
@@ -78,6 +79,10 @@ def load_library() -> ctypes.CDLL:
                                     ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                     vp]
     lib.gdn_decode_step.restype = st
+    lib.gdn_calib_copy.argtypes = [vp, vp, sz, vp]
+    lib.gdn_calib_copy.restype = st
+    lib.gdn_calib_mfma_bf16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+    lib.gdn_calib_mfma_bf16.restype = st
     lib.gdn_status_string.argtypes = [st]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -312,3 +317,24 @@ def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
     _check(lib.gdn_decode_step(B, H, D, dt, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                _ptr(beta), _ptr(state), _ptr(out), _stream()))
     return out
+
+
+def calib_copy(src, dst):
+    """Stream copy of ``src`` into ``dst`` (same byte size, a multiple of 16) by the library's
+    calibration kernel (gdn_calib_copy): the HBM bandwidth a plain kernel reaches."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes or not src.is_contiguous() or \
+            not dst.is_contiguous():
+        raise ValueError("src and dst must be contiguous and of the same byte size")
+    _check(lib.gdn_calib_copy(_ptr(src), _ptr(dst), nbytes, _stream()))
+
+
+def calib_mfma_bf16(out, waves_per_cu, iters):
+    """The calibration loop of bf16 MFMAs (gdn_calib_mfma_bf16); ``out`` float32 with at least
+    waves_per_cu * 256 * 64 elements.  Returns the flop count of the call."""
+    lib = load_library()
+    if out.dtype != torch.float32 or out.numel() < waves_per_cu * 256 * 64:
+        raise ValueError("out must be float32 with waves_per_cu * 256 * 64 elements")
+    _check(lib.gdn_calib_mfma_bf16(_ptr(out), int(waves_per_cu), int(iters), _stream()))
+    return waves_per_cu * 256 * iters * 4 * 32768

@@ -1,19 +1,22 @@
 """Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
-include/gdn.h declares, and rejects bad arguments before touching the device."""
+include/*.h declares, and rejects bad arguments before touching the device."""
 import ctypes
+import glob
 import os
 import re
 
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gdn.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
 def _declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(gdn_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 @pytest.fixture(scope="module")
@@ -185,3 +188,29 @@ def test_decode_step_rejects_null_pointer(lib):
     buf = (ctypes.c_char * 64)()
     ptr = ctypes.cast(buf, ctypes.c_void_p)
     assert lib.gdn_decode_step(4, 8, 128, 1, 1.0, ptr, None, ptr, ptr, ptr, ptr, ptr, None) == 1
+
+
+def _aligned_ptr(buf):
+    return ctypes.c_void_p((ctypes.addressof(buf) + 15) & ~15)
+
+
+@pytest.mark.parametrize("nbytes,status", [(0, 2), (24, 2), (15, 2)])
+def test_calib_copy_rejects_bad_sizes(lib, nbytes, status):
+    buf = (ctypes.c_char * 128)()
+    ptr = _aligned_ptr(buf)
+    assert lib.gdn_calib_copy(ptr, ptr, nbytes, None) == status
+    assert lib.gdn_last_error()
+
+
+def test_calib_copy_rejects_null_and_misaligned(lib):
+    buf = (ctypes.c_char * 128)()
+    ptr = _aligned_ptr(buf)
+    assert lib.gdn_calib_copy(None, ptr, 64, None) == 1
+    assert lib.gdn_calib_copy(ctypes.c_void_p(ptr.value + 4), ptr, 64, None) == 7
+
+
+@pytest.mark.parametrize("waves,iters", [(0, 10), (9, 10), (4, 0), (4, (1 << 20) + 1)])
+def test_calib_mfma_rejects_bad_sizes(lib, waves, iters):
+    buf = (ctypes.c_char * 128)()
+    assert lib.gdn_calib_mfma_bf16(_aligned_ptr(buf), waves, iters, None) == 2
+    assert lib.gdn_calib_mfma_bf16(None, 4, 10, None) == 1
