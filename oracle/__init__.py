@@ -16,7 +16,9 @@ Sources, cited by page title and section:
   "Lever 2" (gate cumsum once per chunk, triangular inverse reused).
 * "Musings on long-context fine-tuning": section "Isolating the recurrent layers" (decay first,
   then correct; the query reads the updated state; ``initial_state`` and ``cu_seqlens``);
-  section "Backward through P" (gradients of a shared state add up).
+  section "Backward through P" (gradients of a shared state add up); the q/k L2 normalisation
+  whose backward kernel that page times (its OOM in the normalisation backward) is the optional
+  first step ``qk_l2norm``: each (token, head) row of q and k divided by sqrt(|row|^2 + 1e-6).
 
 Parity pins for every function are in ``tests/test_oracle_pins.py``.
 """
@@ -73,6 +75,8 @@ def _load():
                                              _D, _D, ctypes.c_int]
     lib.gdn_oracle_bwd.argtypes = [i64, i32, i32, i32, i32, _I32, _D, _D, _D, _D, _D, _D, i64,
                                    dbl, _D, _D, _D, _D, _D, _D, _D, _D, ctypes.c_int]
+    lib.gdn_oracle_l2norm.argtypes = [i64, i32, _D, dbl, _D]
+    lib.gdn_oracle_l2norm_bwd.argtypes = [i64, i32, _D, _D, dbl, _D]
     lib.gdn_oracle_max_threads.restype = ctypes.c_int
     _lib = lib
     return lib
@@ -115,9 +119,38 @@ def max_threads() -> int:
     return int(_load().gdn_oracle_max_threads())
 
 
-def fwd_recurrent(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, nthreads=0):
-    """Token-by-token forward (the plain definition).  Returns (o [T,H,dv], ht [N,H,dk,dv])."""
+L2NORM_EPS = 1e-6
+
+
+def l2norm(x, eps=L2NORM_EPS):
+    """Each row over the last axis divided by sqrt(|row|^2 + eps)."""
     lib = _load()
+    x = _f64(x)
+    y = np.zeros_like(x)
+    d = x.shape[-1]
+    if lib.gdn_oracle_l2norm(x.size // d, d, _ptr(x), float(eps), _ptr(y)):
+        raise ValueError("gdn_oracle_l2norm: bad arguments")
+    return y
+
+
+def l2norm_bwd(x, dy, eps=L2NORM_EPS):
+    """Gradient with respect to x of <l2norm(x), dy>."""
+    lib = _load()
+    x, dy = _f64(x), _f64(dy)
+    dx = np.zeros_like(x)
+    d = x.shape[-1]
+    if lib.gdn_oracle_l2norm_bwd(x.size // d, d, _ptr(x), _ptr(dy), float(eps), _ptr(dx)):
+        raise ValueError("gdn_oracle_l2norm_bwd: bad arguments")
+    return dx
+
+
+def fwd_recurrent(q, k, v, g, beta, cu_seqlens, h0=None, scale=1.0, nthreads=0,
+                  qk_l2norm=False):
+    """Token-by-token forward (the plain definition).  Returns (o [T,H,dv], ht [N,H,dk,dv]).
+    qk_l2norm: q and k are L2-normalised per (token, head) row first."""
+    lib = _load()
+    if qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     cu = _cu(cu_seqlens)
     T, N, H, dk, dv = _shape(q, v, cu)
@@ -194,9 +227,11 @@ def plan(g, cu_seqlens, H, chunk=64, P=256, seg_chunks=0, log_threshold=-10.0):
 
 
 def fwd_truncated(q, k, v, g, beta, cu_seqlens, plan_dict, h0=None, scale=1.0, chunk=64,
-                  nthreads=0):
+                  nthreads=0, qk_l2norm=False):
     """Truncated-history forward following ``plan_dict`` (from :func:`plan`)."""
     lib = _load()
+    if qk_l2norm:
+        q, k = l2norm(q), l2norm(k)
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     cu = _cu(cu_seqlens)
     T, N, H, dk, dv = _shape(q, v, cu)
@@ -217,9 +252,17 @@ def fwd_truncated(q, k, v, g, beta, cu_seqlens, plan_dict, h0=None, scale=1.0, c
     return o, ht
 
 
-def bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, scale=1.0, nthreads=0):
+def bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, scale=1.0, nthreads=0,
+        qk_l2norm=False):
     """Backward of the token recurrence.  Returns dict(dq, dk, dv, dg, dbeta, dh0) with dh0 per
-    sequence [N, H, dk, dv] (sum it over sequences that share one initial state)."""
+    sequence [N, H, dk, dv] (sum it over sequences that share one initial state).  qk_l2norm:
+    the gradients of the normalised q, k pass back through the normalisation."""
+    if qk_l2norm:
+        out = bwd(l2norm(q), l2norm(k), v, g, beta, cu_seqlens, dout, h0=h0, dht=dht, scale=scale,
+                  nthreads=nthreads)
+        out["dq"] = l2norm_bwd(q, out["dq"])
+        out["dk"] = l2norm_bwd(k, out["dk"])
+        return out
     lib = _load()
     q, k, v, g, beta, dout = map(_f64, (q, k, v, g, beta, dout))
     cu = _cu(cu_seqlens)

@@ -520,6 +520,35 @@ int gdn_oracle_bwd(int64_t T, int32_t N, int32_t H, int32_t dk, int32_t dv, cons
   return 0;
 }
 
+/* L2 normalisation of rows (the optional first step of the op on q and k): y = x / sqrt(|x|^2 +
+ * eps) per row of d elements. */
+int gdn_oracle_l2norm(int64_t rows, int32_t d, const double *x, double eps, double *y) {
+  if (rows < 0 || d < 1 || !(eps >= 0.0) || (rows > 0 && (!x || !y))) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double s = 0.0;
+    for (int32_t i = 0; i < d; ++i) s += x[r * d + i] * x[r * d + i];
+    const double inv = 1.0 / sqrt(s + eps);
+    for (int32_t i = 0; i < d; ++i) y[r * d + i] = x[r * d + i] * inv;
+  }
+  return 0;
+}
+
+/* Its backward: with r = (|x|^2 + eps)^(-1/2) and y = r x, dy_i/dx_j = r delta_ij - r^3 x_i x_j,
+ * so dx = r (dy - y (y . dy)). */
+int gdn_oracle_l2norm_bwd(int64_t rows, int32_t d, const double *x, const double *dy, double eps,
+                          double *dx) {
+  if (rows < 0 || d < 1 || !(eps >= 0.0) || (rows > 0 && (!x || !dy || !dx))) return -1;
+  for (int64_t r = 0; r < rows; ++r) {
+    double s = 0.0;
+    for (int32_t i = 0; i < d; ++i) s += x[r * d + i] * x[r * d + i];
+    const double inv = 1.0 / sqrt(s + eps);
+    double ydy = 0.0;
+    for (int32_t i = 0; i < d; ++i) ydy += inv * x[r * d + i] * dy[r * d + i];
+    for (int32_t i = 0; i < d; ++i) dx[r * d + i] = inv * (dy[r * d + i] - inv * x[r * d + i] * ydy);
+  }
+  return 0;
+}
+
 int gdn_oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

@@ -12,7 +12,10 @@ state before instead of after the update) fails at least one of them:
   form of a segment (the exact split);
 * the backward against central finite differences, the beta = 0 special case, and the sum of
   gradients at a shared initial state;
-* the truncation plan's rule and its provable error bound.
+* the truncation plan's rule and its provable error bound;
+* the optional q/k L2 normalisation: its closed form, its backward against central differences,
+  scale invariance of the normalised forward, and the normalised backward against central
+  differences.
 """
 import os
 
@@ -468,3 +471,95 @@ def test_truncation_error_bound(oracle_mod):
                 assert err <= np.linalg.norm(q[t, h]) * decay * sw * (1 + 1e-9) + 1e-15
     assert n_trunc > 0
     assert np.linalg.norm(htt - ht) <= np.exp(-10.0) * np.linalg.norm(ht)
+
+
+# --------------------------------------------------------------------------- q/k L2 normalisation
+def test_l2norm_closed_form(oracle_mod):
+    """y = x / sqrt(|x|^2 + eps): same direction, |y|^2 = s / (s + eps); exactly unit for eps = 0;
+    a row of zeros stays zero."""
+    rng = np.random.default_rng(41)
+    x = rng.standard_normal((7, 3, 16)) * rng.uniform(0.01, 5.0, (7, 3, 1))
+    x[2, 1] = 0.0
+    s = np.sum(x * x, axis=-1)
+    for eps in (0.0, 1e-6, 0.3):
+        if eps == 0.0:
+            x0 = x.copy()
+            x0[2, 1] = 1.0  # 0 / 0 is not defined
+            y = oracle_mod.l2norm(x0, eps=0.0)
+            np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-14)
+            continue
+        y = oracle_mod.l2norm(x, eps=eps)
+        np.testing.assert_allclose(np.sum(y * y, axis=-1), s / (s + eps), rtol=1e-13, atol=1e-300)
+        cosv = np.sum(x * y, axis=-1) / np.maximum(np.linalg.norm(x, axis=-1) *
+                                                   np.linalg.norm(y, axis=-1), 1e-300)
+        np.testing.assert_allclose(cosv[s > 0], 1.0, rtol=1e-13)
+        assert np.all(y[2, 1] == 0.0)
+
+
+def test_l2norm_backward_finite_differences(oracle_mod):
+    """The normalisation's backward against central differences of <l2norm(x), dy>."""
+    rng = np.random.default_rng(42)
+    x = rng.standard_normal((4, 2, 6)) * 0.7
+    dy = rng.standard_normal(x.shape)
+    for eps_n in (1e-6, 0.25):
+        dx = oracle_mod.l2norm_bwd(x, dy, eps=eps_n)
+        num = np.zeros_like(x)
+        h = 1e-6
+        for idx in np.ndindex(x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num[idx] = (np.sum(oracle_mod.l2norm(xp, eps=eps_n) * dy)
+                        - np.sum(oracle_mod.l2norm(xm, eps=eps_n) * dy)) / (2 * h)
+        np.testing.assert_allclose(dx, num, rtol=1e-6, atol=1e-8)
+
+
+def test_qk_l2norm_forward_is_scale_invariant(oracle_mod):
+    """With the normalisation, scaling any (token, head) row of q or k by a positive factor leaves
+    o and ht unchanged (up to the eps term); without it, the same scaling changes them."""
+    inp = make_inputs([37, 0, 70], H=2, dk=16, dv=16, dtype="f32", seed=43, h0_scale=0.5)
+    rng = np.random.default_rng(44)
+    args = _args(inp)
+    fq = rng.uniform(0.5, 4.0, inp["q"].shape[:2] + (1,))
+    fk = rng.uniform(0.5, 4.0, inp["k"].shape[:2] + (1,))
+    scaled = [args[0] * fq, args[1] * fk] + args[2:]
+    cu = inp["cu_seqlens"]
+    o1, h1 = oracle_mod.fwd_recurrent(*args, cu, h0=inp["h0"], qk_l2norm=True)
+    o2, h2 = oracle_mod.fwd_recurrent(*scaled, cu, h0=inp["h0"], qk_l2norm=True)
+    assert _rel(o2, o1) < 1e-5 and _rel(h2, h1) < 1e-5
+    o3, _ = oracle_mod.fwd_recurrent(*scaled, cu, h0=inp["h0"])
+    assert _rel(o3, o1) > 0.1
+    # and the inputs' own rows are already near unit length, so normalising them changes little
+    o0, _ = oracle_mod.fwd_recurrent(*args, cu, h0=inp["h0"])
+    assert _rel(o0, o1) < 1e-5
+
+
+def test_qk_l2norm_backward_matches_finite_differences(oracle_mod):
+    """Central differences of L = <o, dO> + <ht, dht> through the normalisation, for q and k
+    with rows far from unit length."""
+    lens = [6, 9]
+    inp = make_inputs(lens, H=2, dk=4, dv=3, dtype="f32", seed=45, h0_scale=0.5)
+    cu = inp["cu_seqlens"]
+    rng = np.random.default_rng(46)
+    args = [x.astype(np.float64) for x in _args(inp)]
+    args[0] = args[0] * rng.uniform(0.3, 3.0, args[0].shape[:2] + (1,))
+    args[1] = args[1] * rng.uniform(0.3, 3.0, args[1].shape[:2] + (1,))
+    h0 = inp["h0"].astype(np.float64)
+    dout = rng.standard_normal((15, 2, 3))
+    dht = rng.standard_normal((2, 2, 4, 3))
+    gr = oracle_mod.bwd(*args, cu, dout, h0=h0, dht=dht, qk_l2norm=True)
+
+    def loss(a):
+        o, ht = oracle_mod.fwd_recurrent(*a, cu, h0=h0, qk_l2norm=True)
+        return float(np.sum(o * dout) + np.sum(ht * dht))
+
+    h = 1e-6
+    for ai, name in ((0, "dq"), (1, "dk"), (3, "dg")):
+        num = np.zeros_like(args[ai])
+        for idx in np.ndindex(args[ai].shape):
+            ap = [a.copy() for a in args]
+            am = [a.copy() for a in args]
+            ap[ai][idx] += h
+            am[ai][idx] -= h
+            num[idx] = (loss(ap) - loss(am)) / (2 * h)
+        np.testing.assert_allclose(gr[name], num, rtol=1e-6, atol=1e-7, err_msg=name)
