@@ -12,7 +12,8 @@ A step is one forward (gdn_chunk_fwd: o and the final state) on the current stre
 steps run first; then exactly K steps are timed with HIP events on that stream, bracketed by
 device synchronisations.  ``value`` is tokens per second of the headline mode (the page's
 truncated-history split, section "Lever 1"); the exact mode is timed the same way and reported
-beside it, and so is the training backward (gdn_chunk_bwd on the packed 65536-token workload of
+beside it, so is the same forward with q and k L2-normalised inside the kernel (object
+``qk_l2norm``; the same algorithmic bytes), and so is the training backward (gdn_chunk_bwd on the packed 65536-token workload of
 the pages' training runs, object ``backward`` with its own HBM roofline fraction) and the
 single-token decode step (object ``decode``).
 
@@ -79,7 +80,7 @@ def parse():
     return ap.parse_args()
 
 
-def time_steps(gdn, torch, sets, mode, steps, warmup):
+def time_steps(gdn, torch, sets, mode, steps, warmup, qk_l2norm=False):
     outs = [torch.empty_like(s["v"]) for s in sets]
     hts = [torch.empty((1, 8, 128, 128), dtype=torch.float32, device="cuda") for _ in sets]
     cu_host = [0, sets[0]["q"].shape[0]]
@@ -88,7 +89,7 @@ def time_steps(gdn, torch, sets, mode, steps, warmup):
         s = sets[i % len(sets)]
         gdn.chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"], None,
                       mode=mode, cu_seqlens_host=cu_host, out=outs[i % len(sets)],
-                      final_state=hts[i % len(sets)])
+                      final_state=hts[i % len(sets)], qk_l2norm=qk_l2norm)
 
     return timed(torch, step, steps, warmup)
 
@@ -299,6 +300,11 @@ def main():
                              "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
                              / HBM_PEAK_GBS, "timing": r,
                              **fractions(r["median_ms"], bytes_launch, flops_launch, peaks)}
+    r = time_steps(gdn, torch, sets, head, args.steps, args.warmup, qk_l2norm=True)
+    line["qk_l2norm"] = {"mode": head, "ms_per_step": r["mean_ms"],
+                         "value": T / (r["mean_ms"] / 1e3),
+                         "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                         "timing": r}
     if not args.no_backward:
         line["backward"] = time_backward(gdn, torch, args.steps, args.warmup)
         line["decode"] = time_decode(gdn, torch, args.steps, args.warmup)

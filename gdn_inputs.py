@@ -102,6 +102,18 @@ def make_inputs(lengths, H, dk, dv, dtype, seed, h0_scale=0.0, n_h0=None, g_mu=-
     return out
 
 
+def scale_qk_rows(inp, seed, lo=0.3, hi=3.0):
+    """A copy of ``inp`` whose q and k rows are scaled by factors drawn from U[lo, hi] per
+    (token, head) and rounded back to the input dtype: inputs for the in-kernel L2
+    normalisation, whose rows are not of unit length."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = dict(inp)
+    for name in ("q", "k"):
+        x = inp[name] * rng.uniform(lo, hi, inp[name].shape[:2] + (1,))
+        out[name] = bf16_round(x) if inp["dtype"] == "bf16" else x.astype(np.float32)
+    return out
+
+
 def workload(name: str, **overrides):
     """Inputs of one named workload (see the module docstring)."""
     seed = WORKLOAD_SEEDS[name]

@@ -106,6 +106,11 @@ typedef struct gdn_problem {
                               * grouped layouts of "How to Speed Up GDN Kernels for Qwen Models",
                               * section "Using it, and the fine print", where value heads are a
                               * multiple of key heads) */
+  int32_t qk_l2norm;         /* 1: q and k are L2-normalised per (token, head) row inside the
+                              * kernels, q / sqrt(|q|^2 + 1e-6) (likewise k), and the backward
+                              * returns the gradients of the raw q and k; 0: used as given.
+                              * Supported for bf16 with d = 128 and for fp32 inputs. */
+  int32_t reserved;          /* must be 0 */
   int64_t h0_seq_stride;     /* elements between consecutive sequences' h0; 0 = broadcast */
 } gdn_problem;
 

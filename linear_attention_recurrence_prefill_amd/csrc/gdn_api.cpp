@@ -114,6 +114,11 @@ gdn_status check_problem(const gdn_problem *p) {
   if (p->num_k_heads < 0 || p->num_k_heads > p->num_heads ||
       (p->num_k_heads > 0 && p->num_heads % p->num_k_heads != 0))
     return fail(GDN_ERR_BAD_SHAPE, "num_k_heads must be 0 or a divisor of num_heads");
+  if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
+    return fail(GDN_ERR_BAD_MODE, "qk_l2norm must be 0 or 1");
+  if (p->qk_l2norm && p->dtype == GDN_DTYPE_BF16 && p->d_k != 128)
+    return fail(GDN_ERR_BAD_MODE, "qk_l2norm with bf16 inputs needs d = 128");
+  if (p->reserved != 0) return fail(GDN_ERR_BAD_SHAPE, "reserved must be 0");
   if (p->h0_seq_stride < 0) return fail(GDN_ERR_BAD_SHAPE, "h0_seq_stride must be >= 0");
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
   return GDN_OK;
@@ -282,6 +287,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
+  a.l2norm = p->qk_l2norm;
   hipError_t e;
   if (lay.split) {
     char *base = static_cast<char *>(ws);
@@ -370,6 +376,8 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
                                        size_t workspace_bytes, hipStream_t stream) {
   if (p && p->mode != GDN_MODE_EXACT)
     return fail(GDN_ERR_BAD_MODE, "intermediates are defined for the exact mode only");
+  if (p && p->qk_l2norm && p->dtype == GDN_DTYPE_BF16)
+    return fail(GDN_ERR_BAD_MODE, "intermediates with qk_l2norm need fp32 inputs");
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
   float *dbg[6] = {gamma, tmat, w, u, hc, delta};
   return run_fwd(p, t, nullptr, true, dbg, workspace, workspace_bytes, stream);
@@ -497,6 +505,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
   a.truncate = 0;
+  a.l2norm = p->qk_l2norm;
   hipError_t e;
   int64_t units = p->num_seqs;
   if (L.L > 0) {
@@ -553,6 +562,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
   if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
+  if (p->qk_l2norm) return fail(GDN_ERR_BAD_MODE, "the backward of qk_l2norm is not built yet");
   if (!dout || !dq || !dk || !dv || !dg || !dbeta)
     return fail(GDN_ERR_NULL_ARG, "dout, dq, dk, dv, dg and dbeta are required");
   const void *ptrs[] = {dout, dq, dk, dv, dg, dbeta};

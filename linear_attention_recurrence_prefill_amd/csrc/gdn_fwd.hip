@@ -123,6 +123,21 @@ __device__ __forceinline__ void solve_offdiag_block(float *__restrict__ t,
   for (int i = 0; i < 4; ++i) t[(16 * b + 4 * gq + i) * LDT + 16 * c + cl] = -out[i];
 }
 
+// The optional q/k L2 normalisation on a 64-row fp32 tile in LDS: row r / sqrt(|row r|^2 + eps),
+// four threads per row (rows past a ragged chunk's end are zero and stay zero).
+template <int D, int LDE>
+__device__ __forceinline__ void normalize_rows(float *__restrict__ t, int tid) {
+  const int r = tid >> 2, part = tid & 3;
+  float s = 0.f;
+#pragma unroll
+  for (int i = part; i < D; i += 4) s += t[r * LDE + i] * t[r * LDE + i];
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  const float inv = 1.f / sqrtf(s + kL2NormEps);
+#pragma unroll
+  for (int i = part; i < D; i += 4) t[r * LDE + i] *= inv;
+}
+
 template <int D, bool BF16, bool DUMP>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   using SM = FwdSmem<D, BF16>;
@@ -228,6 +243,13 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       if (DUMP && a.dbg_gamma && lane < n) a.dbg_gamma[(t0 + lane) * H + h] = gam;
     }
     __syncthreads();
+    if constexpr (!BF16) {  // q/k L2 normalisation (fp32 tiles; bf16 runs it on the pipelined kernel)
+      if (a.l2norm) {
+        normalize_rows<D, LDE>(sm.k, tid);
+        if (emit) normalize_rows<D, LDE>(sm.q, tid);
+        __syncthreads();
+      }
+    }
 
     // ---- K K^T -> A (row a2) and Q K^T (kept in registers until A is consumed)
     f32x4 qk[3];

@@ -54,6 +54,7 @@ constexpr int kD = 128;
 constexpr int kRowBytes = kD * 2;  // one bf16 row of a K, Q or V tile
 constexpr int kBlk = 16 * kRowBytes + 16;  // stride of the 16-row blocks of the K and Q tiles
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 // 64 x 128 bf16 tiles (K, Q, V): rows of 256 bytes; the 16-byte unit c of row r is stored at unit
 // c ^ sw(r).  For the reads below (16 lanes on one 8-byte unit of 16 consecutive rows, or
@@ -163,9 +164,16 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
 // with V = 0 (the unit's transition matrix M, so that the state after the unit is
 // M S_start + B for any start state).
-template <bool kTransition, bool kDump = false>
+// kNorm: q and k are L2-normalised per row.  The tiles stay as loaded; wave 7 computes each row's
+// inverse norm 1 / sqrt(|row|^2 + eps) once the chunk's K and Q have landed in LDS, and every use
+// folds it into the per-token factors it already applies (A and P by rows and columns, e^gamma in
+// R', scale e^gamma in the output, e^{gamma_last - gamma} in the update), so the normalised rows
+// are never rounded to bf16.
+template <bool kTransition, bool kDump = false, bool kNorm = false>
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
+  // kNorm: inverse row norms [chunk slot][K, Q][row], the slot as for the gate vectors
+  __shared__ __attribute__((aligned(16))) float rn_s[kNorm ? 3 : 1][2][64];
   // V of the chunk on the chain, per chain wave its 32 columns: 64 rows of 64 bytes, the 16-byte
   // unit u of row r at unit u ^ 2 ((r / 4) % 2).  A variable of its own, so that the compiler
   // knows the chain waves' direct loads into it cannot touch the tiles they read meanwhile.
@@ -239,7 +247,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 
   // A's diagonal 16x16 blocks b0 = 2 half and b1 = b0 + 1 in fp32, stored transposed into at
   // (row i of the stored block = column i of A_bb)
-  auto a_diag = [&](const char *Kt, const WsSmem::Vec &vc, int half) {
+  auto a_diag = [&](const char *Kt, const WsSmem::Vec &vc, const float *rk, int half) {
     const int b0 = 2 * half, b1 = b0 + 1;
     f32x4 a00 = zero4(), a11 = zero4();
 #pragma unroll
@@ -251,11 +259,16 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     const f32x4 gr0 = ldf4(&vc.gam[16 * b0 + 4 * gq]), br0 = ldf4(&vc.beta[16 * b0 + 4 * gq]);
     const f32x4 gr1 = ldf4(&vc.gam[16 * b1 + 4 * gq]), br1 = ldf4(&vc.beta[16 * b1 + 4 * gq]);
     const float gi0 = vc.gam[16 * b0 + cl], gi1 = vc.gam[16 * b1 + cl];
+    f32x4 nr0 = {1.f, 1.f, 1.f, 1.f}, nr1 = nr0;  // row x column inverse norms (kNorm)
+    if constexpr (kNorm) {
+      nr0 = ldf4(&rk[16 * b0 + 4 * gq]) * rk[16 * b0 + cl];
+      nr1 = ldf4(&rk[16 * b1 + 4 * gq]) * rk[16 * b1 + cl];
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int rl = 4 * gq + e;
-      a00[e] = cl < rl ? br0[e] * __expf(gr0[e] - gi0) * a00[e] : 0.f;
-      a11[e] = cl < rl ? br1[e] * __expf(gr1[e] - gi1) * a11[e] : 0.f;
+      a00[e] = cl < rl ? br0[e] * nr0[e] * __expf(gr0[e] - gi0) * a00[e] : 0.f;
+      a11[e] = cl < rl ? br1[e] * nr1[e] * __expf(gr1[e] - gi1) * a11[e] : 0.f;
     }
     float *t0p = &sm.at[b0 * AB + cl * LA + 4 * gq], *t1p = &sm.at[b1 * AB + cl * LA + 4 * gq];
     *reinterpret_cast<float2 *>(t0p) = float2{a00[0], a00[1]};
@@ -397,6 +410,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int Y = cc & 1;
         const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
         const WsSmem::Vec &vc = sm.vec[cc % 3];
+        const float *rkc = rn_s[kNorm ? cc % 3 : 0][0], *rqc = rn_s[kNorm ? cc % 3 : 0][1];
 
         // ---- K h, then R' = V - diag(e^gamma) K h, fp32
         f32x4 R[4][2];
@@ -420,7 +434,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 ee = *reinterpret_cast<const f32x4 *>(&vc.eg[16 * mt + 4 * gq]);
+          f32x4 ee = *reinterpret_cast<const f32x4 *>(&vc.eg[16 * mt + 4 * gq]);
+          if constexpr (kNorm) ee *= ldf4(&rkc[16 * mt + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             const bf16x4 v4 = ldtr(vw + 1024 * mt + o_vtr[nt]);
@@ -472,8 +487,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
                                                         v0 + 16 * H * kD * 4, 0, 0);
                 }
             }
-            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
-            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
+            f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
+            f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
+            if constexpr (kNorm) {
+              e0 *= ldf4(&rkc[32 * hb + 4 * gq]);
+              e1 *= ldf4(&rkc[32 * hb + 16 + 4 * gq]);
+            }
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               da[hb][nt] = to_bf16x8(Dl0[nt], Dl1[nt]);
@@ -495,7 +514,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           const char *P = sm.p[Y];
           float et[4];
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) et[tt] = vc.ego[16 * tt + cl];
+          for (int tt = 0; tt < 4; ++tt) et[tt] = vc.ego[16 * tt + cl] * (kNorm ? rqc[16 * tt + cl] : 1.f);
           f32x4 acc[4][2];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) acc[tt][0] = acc[tt][1] = zero4();
@@ -623,6 +642,28 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (lane == 0) vc.egl[0] = __expf(gl);
       if (kDump && lane < n) a.dbg_gamma[(chunk_t0(c) + lane) * H + h] = gam;
     };
+    // kNorm: inverse norms of the rows of chunk c's K (and Q) tiles, once they are in LDS.  Lane r
+    // sums row r, reading its 16-byte units in an order rotated by r (no two lanes of a 16-row
+    // block on one bank group).
+    auto row_norms = [&](int c, bool with_q) {
+      const int base = (lane >> 4) * kBlk + (lane & 15) * kRowBytes;
+      auto inv_norm = [&](const char *t) {
+        float s = 0.f;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          const bf16x8 x = *reinterpret_cast<const bf16x8 *>(t + base + (((u + lane) & 15) << 4));
+          const bf16x2 p0 = __builtin_shufflevector(x, x, 0, 1), p1 = __builtin_shufflevector(x, x, 2, 3);
+          const bf16x2 p2 = __builtin_shufflevector(x, x, 4, 5), p3 = __builtin_shufflevector(x, x, 6, 7);
+          s = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, s, false);
+          s = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, s, false);
+        }
+        return 1.f / sqrtf(s + kL2NormEps);
+      };
+      rn_s[c % 3][0][lane] = inv_norm(sm.kq[c % 3][0]);
+      if (with_q) rn_s[c % 3][1][lane] = inv_norm(sm.kq[c % 3][1]);
+    };
     GB gbx{0.f, 0};
     if (cw < c1) {
       gbx = gb_load(cw);
@@ -633,10 +674,11 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (cw + 1 < c1) gbx = gb_load(cw + 1);
     }
     wait_vm0();
+    if (kNorm && cw < c1) row_norms(cw, !kTransition && !kDump && cw >= c0);
     __syncthreads();
     for (int c = cw; c <= c1; ++c) {
       if (c < c1) {  // A's diagonal blocks 2 and 3 of the chunk prep works on
-        a_diag(sm.kq[c % 3][0], sm.vec[c % 3], 1);
+        a_diag(sm.kq[c % 3][0], sm.vec[c % 3], rn_s[kNorm ? c % 3 : 0][0], 1);
         __hip_atomic_store(&sm.ready, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       }
       if (c + 1 < c1) {
@@ -646,6 +688,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         if (c + 2 < c1) gbx = gb_load(c + 2);
       }
       wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
+      if (kNorm && c + 1 < c1) row_norms(c + 1, !kTransition && !kDump && c + 1 >= c0);
       __syncthreads();
     }
   } else {
@@ -662,7 +705,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         if (wave == 4) {
           // ---- A's diagonal blocks 0 and 1 (wave 7 forms blocks 2 and 3 and publishes them
           //      through sm.ready; the bounded wait cannot hang)
-          a_diag(Kt, vc, 0);
+          a_diag(Kt, vc, rn_s[kNorm ? c % 3 : 0][0], 0);
           for (int it = 0; it < (1 << 22); ++it) {
             const int r = __hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (__builtin_amdgcn_readfirstlane(r) >= c + 1) break;
@@ -739,17 +782,20 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               const f32x4 gi = ldf4(&vc.gam[16 * bj + 4 * gq]);
               const int r = 16 * bi + cl;
               const float gr = vc.gam[r];
+              f32x4 nf = {1.f, 1.f, 1.f, 1.f};  // row x column inverse norms (kNorm)
+              if constexpr (kNorm)
+                nf = ldf4(&rn_s[c % 3][0][16 * bj + 4 * gq]) * rn_s[c % 3][PT::q[t]][r];
               f32x4 val;
               if (PT::q[t] == 0) {
 #pragma unroll
-                for (int e = 0; e < 4; ++e) val[e] = -__expf(gr - gi[e]) * acc[t][e];
+                for (int e = 0; e < 4; ++e) val[e] = -nf[e] * __expf(gr - gi[e]) * acc[t][e];
                 char *dst = bi == 1 ? B.na10 + soff(cl, gq)
                             : (bj == 2 ? B.na32 + soff(cl, gq) : B.nabl + boff(r - 32, 4 * bj + gq));
                 st8(dst, val);
               } else {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  val[e] = (16 * bj + 4 * gq + e <= r) ? a.scale * __expf(gr - gi[e]) * acc[t][e] : 0.f;
+                  val[e] = (16 * bj + 4 * gq + e <= r) ? a.scale * nf[e] * __expf(gr - gi[e]) * acc[t][e] : 0.f;
                 st8(&sm.p[Y][poff(r, 4 * bj + gq)], val);
               }
             }
@@ -773,20 +819,32 @@ int fwd_ws_blocks_per_cu() {
 
 hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
   if (max_units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ws_kernel<false>, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
+  if (a.l2norm)
+    hipLaunchKernelGGL((fwd_ws_kernel<false, false, true>), dim3((unsigned)max_units, a.H),
+                       dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_ws_kernel<false>, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_ws_dump(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
   if (max_units <= 0) return hipSuccess;
-  hipLaunchKernelGGL((fwd_ws_kernel<false, true>), dim3((unsigned)max_units, a.H), dim3(512), 0,
-                     stream, a);
+  if (a.l2norm)
+    hipLaunchKernelGGL((fwd_ws_kernel<false, true, true>), dim3((unsigned)max_units, a.H),
+                       dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_ws_kernel<false, true>), dim3((unsigned)max_units, a.H), dim3(512), 0,
+                       stream, a);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_ws_transition(const FwdArgs &a, int64_t units, hipStream_t stream) {
   if (units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fwd_ws_kernel<true>, dim3((unsigned)units, a.H, 2), dim3(512), 0, stream, a);
+  if (a.l2norm)
+    hipLaunchKernelGGL((fwd_ws_kernel<true, false, true>), dim3((unsigned)units, a.H, 2),
+                       dim3(512), 0, stream, a);
+  else
+    hipLaunchKernelGGL(fwd_ws_kernel<true>, dim3((unsigned)units, a.H, 2), dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -7,6 +7,8 @@
 namespace gdn {
 
 constexpr int kChunk = 64;
+// eps of the optional q/k L2 normalisation: row / sqrt(|row|^2 + eps)
+constexpr float kL2NormEps = 1e-6f;
 
 // Arguments of the fused forward kernel.  A "unit" is one (sequence, chunk range) pair: each
 // sequence is one unit (L == 0) or is split into units of L chunks; the kernel runs one
@@ -28,6 +30,7 @@ struct FwdArgs {
   float scale;
   float log_thr;
   int32_t truncate;
+  int32_t l2norm;  // q and k rows divided by sqrt(|row|^2 + kL2NormEps) inside the kernel
   // exact split (pipelined kernel only): per-unit start states [units, H, D, D] for the final
   // pass, or the first pass's outputs [2, units, H, D, D] (B from zero, M from the identity)
   const float *unit_h0;

@@ -40,6 +40,7 @@ class GdnProblem(ctypes.Structure):
                 ("mode", ctypes.c_int32), ("seg_chunks", ctypes.c_int32),
                 ("num_slots", ctypes.c_int32), ("trunc_log_threshold", ctypes.c_float),
                 ("scale", ctypes.c_float), ("num_k_heads", ctypes.c_int32),
+                ("qk_l2norm", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("h0_seq_stride", ctypes.c_int64)]
 
 
@@ -108,7 +109,7 @@ def _stream():
 
 def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact", scale=1.0,
                  seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, h0_seq_stride=None,
-                 num_k_heads=0):
+                 num_k_heads=0, qk_l2norm=False):
     lib = load_library()
     p = GdnProblem()
     _check(lib.gdn_problem_init(ctypes.byref(p), int(total_tokens), int(num_seqs),
@@ -122,6 +123,7 @@ def make_problem(total_tokens, num_seqs, num_heads, head_dim, dtype, mode="exact
     if h0_seq_stride is not None:
         p.h0_seq_stride = int(h0_seq_stride)
     p.num_k_heads = int(num_k_heads)
+    p.qk_l2norm = 1 if qk_l2norm else 0
     return p
 
 
@@ -170,12 +172,14 @@ def _host_cu(cu_seqlens, cu_seqlens_host):
 
 def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
               seg_chunks=0, num_slots=0, trunc_log_threshold=-10.0, output_final_state=True,
-              cu_seqlens_host=None, out=None, final_state=None, workspace=None):
-    """Forward of the chunked gated delta rule.  Returns (o, ht or None)."""
+              cu_seqlens_host=None, out=None, final_state=None, workspace=None,
+              qk_l2norm=False):
+    """Forward of the chunked gated delta rule.  Returns (o, ht or None).  qk_l2norm: q and k
+    are L2-normalised per (token, head) row inside the kernels."""
     lib = load_library()
     T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_slots,
-                     trunc_log_threshold, stride, num_k_heads=Hk)
+                     trunc_log_threshold, stride, num_k_heads=Hk, qk_l2norm=qk_l2norm)
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
@@ -231,7 +235,7 @@ def chunk_fwd_plan(g, cu_seqlens, num_heads, head_dim, dtype, *, mode="truncate"
 
 
 def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
-                            num_chunks=None):
+                            num_chunks=None, qk_l2norm=False):
     """Exact forward that also returns the per-chunk intermediates (fp32):
     o, ht, dict(gamma [T,H], tmat [Nc,H,64,64], w [Nc,H,64,D], u [Nc,H,64,D],
     hc [Nc,H,D,D], delta [T,H,D])."""
@@ -240,7 +244,8 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
     if num_chunks is None:
         cu = cu_seqlens.cpu().tolist()
         num_chunks = sum((cu[i + 1] - cu[i] + 63) // 64 for i in range(N))
-    p = make_problem(T, N, H, D, q.dtype, "exact", scale, h0_seq_stride=stride, num_k_heads=Hk)
+    p = make_problem(T, N, H, D, q.dtype, "exact", scale, h0_seq_stride=stride, num_k_heads=Hk,
+                     qk_l2norm=qk_l2norm)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(ws_bytes)))
     ws = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
@@ -263,11 +268,12 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.0,
-              need_dh0=True, workspace=None, seg_chunks=0, num_slots=0):
+              need_dh0=True, workspace=None, seg_chunks=0, num_slots=0, qk_l2norm=False):
     """Backward of the exact forward.  Returns dict(dq, dk, dv, dg, dbeta, dh0).  dh0 is
     [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D]).
     seg_chunks / num_slots set the segment length of the forward recompute's split and the
-    workgroup slots it is planned for (0: chosen by the library)."""
+    workgroup slots it is planned for (0: chosen by the library).  qk_l2norm: backward of the
+    forward with q and k normalised inside the kernels (dq, dk are the raw inputs' gradients)."""
     lib = load_library()
     T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
@@ -276,7 +282,8 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
         raise ValueError("dht must be float32 [N, H, D, D]")
     p = make_problem(T, N, H, D, q.dtype, "exact", scale, seg_chunks=seg_chunks,
                      num_slots=num_slots,
-                     h0_seq_stride=stride if stride is not None else H * D * D, num_k_heads=Hk)
+                     h0_seq_stride=stride if stride is not None else H * D * D, num_k_heads=Hk,
+                     qk_l2norm=qk_l2norm)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
     if workspace is None or workspace.numel() < ws_bytes.value:

@@ -69,7 +69,8 @@ def test_problem_defaults(lib):
 
 @pytest.mark.parametrize("field,value,status", [
     ("chunk", 32, 2), ("d_k", 96, 2), ("d_v", 64, 2), ("num_heads", 0, 2), ("num_seqs", 0, 2),
-    ("total_tokens", -1, 2), ("dtype", 7, 3), ("mode", 5, 4), ("num_k_heads", 3, 2), ("num_k_heads", -1, 2), ("num_k_heads", 16, 2),
+    ("total_tokens", -1, 2), ("dtype", 7, 3), ("mode", 5, 4), ("num_k_heads", 3, 2),
+    ("num_k_heads", -1, 2), ("num_k_heads", 16, 2), ("qk_l2norm", 2, 4), ("reserved", 1, 2),
     ("h0_seq_stride", -1, 2)])
 def test_bad_problem_rejected_on_host(lib, field, value, status):
     p = _problem(**{field: value})
@@ -214,3 +215,13 @@ def test_calib_mfma_rejects_bad_sizes(lib, waves, iters):
     buf = (ctypes.c_char * 128)()
     assert lib.gdn_calib_mfma_bf16(_aligned_ptr(buf), waves, iters, None) == 2
     assert lib.gdn_calib_mfma_bf16(None, 4, 10, None) == 1
+
+
+def test_qk_l2norm_needs_d128_for_bf16(lib):
+    n = ctypes.c_size_t(0)
+    p = _problem(qk_l2norm=1, d_k=64, d_v=64)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 4
+    p = _problem(qk_l2norm=1, d_k=64, d_v=64, dtype=0, num_slots=256)  # fp32: general kernel
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    p = _problem(qk_l2norm=1, num_slots=256)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
