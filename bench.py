@@ -389,11 +389,19 @@ def time_backward(gdn, torch, steps, warmup):
 
     r = timed(torch, step, steps, warmup)
     ms = r["mean_ms"]
+    # the same backward with q and k normalised inside the kernels (its own, larger workspace)
+    pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact", qk_l2norm=True)
+    assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pn), ctypes.byref(nbytes)) == 0
+    wsn = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")
+    rn = timed(torch, lambda i: gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu,
+                                              dev["dout"], workspace=wsn, qk_l2norm=True),
+               steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
     achieved = nbytes_alg / (ms / 1e3) / 1e9
     return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
                         f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
             "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
+            "qk_l2norm_ms_per_step": rn["mean_ms"],
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes_alg}}

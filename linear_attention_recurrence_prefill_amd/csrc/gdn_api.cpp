@@ -421,7 +421,8 @@ struct BwdLayout {
   int64_t units = 0;
   size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
   size_t unit_bm = 0, unit_h0 = 0;
-  size_t dq_part = 0, dk_part = 0;  // grouped heads: per-value-head dq, dk (fp32)
+  size_t dq_part = 0, dk_part = 0;  // grouped heads or qk_l2norm: per-value-head dq, dk (fp32)
+  size_t rq = 0, rk = 0;            // qk_l2norm: inverse row norms of q and k (fp32 [T, Hk])
   size_t total = 0;
 };
 
@@ -471,9 +472,15 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
     L->unit_bm = take(2 * per);
     L->unit_h0 = take(per);
   }
-  if (k_heads(p) < H) {
+  // partials: grouped heads (summed per key head), and the general kernels' normalised q, k
+  // (finished by the normalisation's backward kernel; the bf16 d = 128 kernel finishes in place)
+  if (k_heads(p) < H || (p->qk_l2norm && !bwd_bf16_path(p))) {
     L->dq_part = take(sizeof(float) * T * H * D);
     L->dk_part = take(sizeof(float) * T * H * D);
+  }
+  if (p->qk_l2norm) {
+    L->rq = take(sizeof(float) * T * k_heads(p));
+    L->rk = take(sizeof(float) * T * k_heads(p));
   }
   L->total = off;
   return GDN_OK;
@@ -562,7 +569,6 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
   if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
-  if (p->qk_l2norm) return fail(GDN_ERR_BAD_MODE, "the backward of qk_l2norm is not built yet");
   if (!dout || !dq || !dk || !dv || !dg || !dbeta)
     return fail(GDN_ERR_NULL_ARG, "dout, dq, dk, dv, dg and dbeta are required");
   const void *ptrs[] = {dout, dq, dk, dv, dg, dbeta};
@@ -619,8 +625,13 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.delta = delta;
   b.dhn = reinterpret_cast<float *>(base + L.dhn);
   const bool grouped = k_heads(p) < p->num_heads;
-  b.dq_part = grouped ? reinterpret_cast<float *>(base + L.dq_part) : nullptr;
-  b.dk_part = grouped ? reinterpret_cast<float *>(base + L.dk_part) : nullptr;
+  const bool part = grouped || (p->qk_l2norm && !fast);
+  b.dq_part = part ? reinterpret_cast<float *>(base + L.dq_part) : nullptr;
+  b.dk_part = part ? reinterpret_cast<float *>(base + L.dk_part) : nullptr;
+  float *rq = p->qk_l2norm ? reinterpret_cast<float *>(base + L.rq) : nullptr;
+  float *rk = p->qk_l2norm ? reinterpret_cast<float *>(base + L.rk) : nullptr;
+  b.rq = rq;
+  b.rk = rk;
   b.ddelta = reinterpret_cast<float *>(base + L.ddelta);
   b.T = p->total_tokens;
   b.N = p->num_seqs;
@@ -628,6 +639,13 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.HK = k_heads(p);
   b.scale = p->scale;
   hipError_t e;
+  const bool bf = p->dtype == GDN_DTYPE_BF16;
+  if (p->qk_l2norm) {  // the rows' inverse norms, folded in by the kernels below
+    e = gdn::launch_row_rnorm(q, p->total_tokens * k_heads(p), p->d_k, bf, rq, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_row_rnorm(k, p->total_tokens * k_heads(p), p->d_k, bf, rk, stream);
+    if (e != hipSuccess) return hip_fail(e, "q/k inverse norms");
+  }
   if (fast) {
     e = gdn::launch_bwd_tm(b, tmat, L.nc, stream);
     if (e != hipSuccess) return hip_fail(e, "backward: Tm");
@@ -668,12 +686,19 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     e = gdn::launch_bwd_grad(b, p->d_k, bf16, L.nc, stream);
     if (e != hipSuccess) return hip_fail(e, "backward gradient launch");
   }
-  if (grouped) {  // dq, dk of each key head: the sum over its value heads
+  if (p->qk_l2norm && !fast) {  // the normalisation's backward (and the per-key-head sums)
+    e = gdn::launch_l2norm_bwd(b.dq_part, q, rq, p->total_tokens, p->num_heads, k_heads(p),
+                               p->d_k, bf, dq, stream);
+    if (e == hipSuccess)
+      e = gdn::launch_l2norm_bwd(b.dk_part, k, rk, p->total_tokens, p->num_heads, k_heads(p),
+                                 p->d_k, bf, dk, stream);
+    if (e != hipSuccess) return hip_fail(e, "q/k normalisation backward");
+  } else if (grouped) {  // dq, dk of each key head: the sum over its value heads
     e = gdn::launch_group_sum(b.dq_part, p->total_tokens, p->num_heads, k_heads(p), p->d_k,
-                              p->dtype == GDN_DTYPE_BF16, dq, stream);
+                              bf, dq, stream);
     if (e == hipSuccess)
       e = gdn::launch_group_sum(b.dk_part, p->total_tokens, p->num_heads, k_heads(p), p->d_k,
-                                p->dtype == GDN_DTYPE_BF16, dk, stream);
+                                bf, dk, stream);
     if (e != hipSuccess) return hip_fail(e, "grouped heads: dq, dk sums");
   }
   if (dh0 && shared_h0) {

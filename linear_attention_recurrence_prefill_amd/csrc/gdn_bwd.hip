@@ -55,10 +55,13 @@ __device__ __forceinline__ f32x4 tile_mma(const float *A, int ars, int acs, cons
 // n zero, into a 64 x LDF fp32 LDS tile.
 template <class E>
 __device__ __forceinline__ void load_rows64(float *dst, const E *src, int64_t t0, int n, int h,
-                                            int H, int D, int c0, float mul, int tid) {
+                                            int H, int D, int c0, float mul, int tid,
+                                            const float *rs = nullptr) {
+  // rs (optional): per-row factors [T, H] (the q/k L2 normalisation's inverse norms)
   for (int i = tid; i < 64 * 64; i += 256) {
     const int r = i >> 6, c = i & 63;
-    dst[r * LDF + c] = r < n ? mul * to_f32(src[((t0 + r) * H + h) * D + c0 + c]) : 0.f;
+    const float m = rs != nullptr && r < n ? mul * rs[(t0 + r) * H + h] : mul;
+    dst[r * LDF + c] = r < n ? m * to_f32(src[((t0 + r) * H + h) * D + c0 + c]) : 0.f;
   }
 }
 
@@ -137,8 +140,9 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs b) {
       const bool ok = r < n;
       const int64_t gi = ((t0 + r) * H + h) * D + col;
       const int64_t gik = ((t0 + r) * b.HK + hk) * D + col;  // q and k: the key head
-      sm.q[r * LD + col] = ok ? to_f32(gq_[gik]) : 0.f;
-      sm.k[r * LD + col] = ok ? to_f32(gk_[gik]) : 0.f;
+      const int64_t rk_i = (t0 + r) * b.HK + hk;  // q/k L2 normalisation: the rows' factors
+      sm.q[r * LD + col] = ok ? (b.rq ? b.rq[rk_i] : 1.f) * to_f32(gq_[gik]) : 0.f;
+      sm.k[r * LD + col] = ok ? (b.rk ? b.rk[rk_i] : 1.f) * to_f32(gk_[gik]) : 0.f;
       sm.dout[r * LD + col] = ok ? b.scale * to_f32(gdo[gi]) : 0.f;
       sm.w[r * LD + col] = b.w[((cg * H + h) * 64 + r) * D + col];
     }
@@ -319,8 +323,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
     __syncthreads();
     load_rows64(sm.x0, gdo, t0, n, h, H, D, 64 * cb, dsc, tid);
     load_rows64(sm.x1, b.delta, t0, n, h, H, D, 64 * cb, 1.f, tid);
-    load_rows64(sm.qk, gq_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid);
-    load_rows64(sm.kk, gk_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid);
+    load_rows64(sm.qk, gq_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid, b.rq);
+    load_rows64(sm.kk, gk_, t0, n, hk, b.HK, D, 64 * cb, 1.f, tid, b.rk);
     __syncthreads();
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
                          dw[s]);
     }
     __syncthreads();
-    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
+    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid, b.rk);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -490,8 +494,8 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
     }
     __syncthreads();
     // operand tiles of this block: x0 = Q, x1 = K, qk = dW, kk = dDelta
-    load_rows64(sm.x0, gq_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
-    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid);
+    load_rows64(sm.x0, gq_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid, b.rq);
+    load_rows64(sm.x1, gk_, t0, n, hk, b.HK, D, 64 * kb, 1.f, tid, b.rk);
     load_rows64(sm.kk, b.ddelta, t0, n, h, H, D, 64 * kb, 1.f, tid);
 #pragma unroll
     for (int s = 0; s < 4; ++s)
@@ -521,9 +525,10 @@ __global__ __launch_bounds__(256) void bwd_grad_kernel(BwdArgs b) {
         if (r < n) {
           const int64_t gi = ((t0 + r) * H + h) * D + col;
           vv = to_f32(gv_[gi]);
-          if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
-            b.dq_part[gi] = dq;
-            b.dk_part[gi] = dkv;
+          if (b.dq_part != nullptr) {  // grouped heads or normalised q, k: finished afterwards
+            const int64_t ri = (t0 + r) * b.HK + hk;
+            b.dq_part[gi] = b.rq ? b.rq[ri] * dq : dq;
+            b.dk_part[gi] = b.rk ? b.rk[ri] * dkv : dkv;
           } else {
             static_cast<E *>(b.dq)[gi] = from_f32<E>(dq);
             static_cast<E *>(b.dk)[gi] = from_f32<E>(dkv);
@@ -614,6 +619,102 @@ __global__ __launch_bounds__(256) void group_sum_kernel(const float *__restrict_
   for (int j = 0; j < G; ++j) s += part[(t * H + hk * G + j) * D + d];
   if (is_bf16) static_cast<bf16 *>(out)[i] = (bf16)s;
   else static_cast<float *>(out)[i] = s;
+}
+
+// 1 / sqrt(|row|^2 + eps) per row of x [rows, D]: each row read as 16-byte units by UPR
+// consecutive lanes (64 / UPR rows per wave), summed by a butterfly within the lane group.
+template <class E, int D>
+__global__ __launch_bounds__(256) void row_rnorm_kernel(const E *__restrict__ x, int64_t rows,
+                                                        float *__restrict__ r) {
+  constexpr int EPU = 16 / (int)sizeof(E);  // elements per 16-byte unit
+  constexpr int UPR = D / EPU;              // lanes per row: 8 .. 32
+  constexpr int RPW = 64 / UPR;             // rows per wave
+  const int lane = threadIdx.x & 63, sub = lane / UPR, part = lane % UPR;
+  const int64_t wave = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  const int64_t waves = (int64_t)gridDim.x * 4;
+  for (int64_t row0 = wave * RPW; row0 < rows; row0 += waves * RPW) {  // wave-uniform
+    const int64_t row = row0 + sub;
+    float s = 0.f;
+    if (row < rows) {
+      const uint4 u = *reinterpret_cast<const uint4 *>(x + row * D + part * EPU);
+      const unsigned wd[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if constexpr (sizeof(E) == 2) {
+          const float lo = __uint_as_float(wd[j] << 16), hi = __uint_as_float(wd[j] & 0xFFFF0000u);
+          s += lo * lo + hi * hi;
+        } else {
+          const float v = __uint_as_float(wd[j]);
+          s += v * v;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = UPR / 2; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+    if (part == 0 && row < rows) r[row] = 1.f / sqrtf(s + kL2NormEps);
+  }
+}
+
+// One wave per row (t, hk) of x [T, HK, D]; lane holds elements D / 64 * lane .. + D / 64 - 1.
+template <class E, int D>
+__global__ __launch_bounds__(256) void l2norm_bwd_kernel(const float *__restrict__ part,
+                                                         const E *__restrict__ x,
+                                                         const float *__restrict__ r, int64_t T,
+                                                         int H, int HK, E *__restrict__ out) {
+  constexpr int PER = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int64_t row = ((int64_t)blockIdx.x * 256 + threadIdx.x) >> 6;
+  if (row >= T * HK) return;  // wave-uniform
+  const int64_t t = row / HK;
+  const int hk = (int)(row % HK), G = H / HK;
+  float z[PER], xv[PER], s = 0.f;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int d = PER * lane + e;
+    float acc = 0.f;
+    for (int j = 0; j < G; ++j) acc += part[(t * H + (int64_t)hk * G + j) * D + d];
+    z[e] = acc;
+    xv[e] = to_f32(x[row * D + d]);
+    s += xv[e] * acc;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
+  const float rr = r[row], cf = rr * rr * s;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) out[row * D + PER * lane + e] = from_f32<E>(z[e] - cf * xv[e]);
+}
+
+hipError_t launch_row_rnorm(const void *x, int64_t rows, int32_t D, bool is_bf16, float *r,
+                            hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int upr = D * (is_bf16 ? 2 : 4) / 16, rpb = 4 * (64 / upr);
+  int64_t blocks = (rows + rpb - 1) / rpb;
+  if (blocks > 65536) blocks = 65536;
+  const dim3 grid((unsigned)blocks), block(256);
+  if (D == 128) {
+    if (is_bf16) hipLaunchKernelGGL((row_rnorm_kernel<bf16, 128>), grid, block, 0, stream, static_cast<const bf16 *>(x), rows, r);
+    else hipLaunchKernelGGL((row_rnorm_kernel<float, 128>), grid, block, 0, stream, static_cast<const float *>(x), rows, r);
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((row_rnorm_kernel<bf16, 64>), grid, block, 0, stream, static_cast<const bf16 *>(x), rows, r);
+    else hipLaunchKernelGGL((row_rnorm_kernel<float, 64>), grid, block, 0, stream, static_cast<const float *>(x), rows, r);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_l2norm_bwd(const float *part, const void *x, const float *r, int64_t T,
+                             int32_t H, int32_t HK, int32_t D, bool is_bf16, void *out,
+                             hipStream_t stream) {
+  const int64_t rows = T * HK;
+  if (rows <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((rows + 3) / 4)), block(256);
+  if (D == 128) {
+    if (is_bf16) hipLaunchKernelGGL((l2norm_bwd_kernel<bf16, 128>), grid, block, 0, stream, part, static_cast<const bf16 *>(x), r, T, H, HK, static_cast<bf16 *>(out));
+    else hipLaunchKernelGGL((l2norm_bwd_kernel<float, 128>), grid, block, 0, stream, part, static_cast<const float *>(x), r, T, H, HK, static_cast<float *>(out));
+  } else {
+    if (is_bf16) hipLaunchKernelGGL((l2norm_bwd_kernel<bf16, 64>), grid, block, 0, stream, part, static_cast<const bf16 *>(x), r, T, H, HK, static_cast<bf16 *>(out));
+    else hipLaunchKernelGGL((l2norm_bwd_kernel<float, 64>), grid, block, 0, stream, part, static_cast<const float *>(x), r, T, H, HK, static_cast<float *>(out));
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_group_sum(const float *part, int64_t T, int32_t H, int32_t HK, int32_t D,

@@ -96,6 +96,7 @@ struct ChainSmem {
   alignas(16) float c[64];    // e^{gamma_last - gamma}, 0 past n
   alignas(16) float ab[64];   // e^gamma beta, 0 past n
   alignas(16) float beta[64];
+  alignas(16) float rq[64], rk[64];  // q/k L2 normalisation: inverse row norms (1 without)
   alignas(16) int imisc[4];
 };
 static_assert(sizeof(ChainSmem) <= 160 * 1024, "LDS budget");
@@ -206,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   // 15; lane l of load j writes physical unit l % 16 of row 16 w + 4 j + l / 16, which holds
   // logical unit (l % 16) ^ sw(row); rows past n repeat the chunk's last token); Tm (this
   // thread's 16 entries) and the gates into registers
-  float g_r = 0.f;
+  float g_r = 0.f, rq_r = 1.f, rk_r = 1.f;
   unsigned short b_r = 0;  // beta's bits: converted at the chunk turn, so that nothing waits
                            // for the next chunk's loads early
   auto issue = [&](int c, int set) {
@@ -232,6 +233,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const int64_t t = t0 + min(lane, n - 1);
       g_r = b.gamma[t * H + h];
       b_r = reinterpret_cast<const unsigned short *>(gb)[t * H + h];
+      if (b.rq != nullptr) {
+        rq_r = b.rq[t * b.HK + hk];
+        rk_r = b.rk[t * b.HK + hk];
+      }
     }
   };
 
@@ -250,11 +255,14 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const bool in = lane < n;
       const float ea = __expf(g_r);
       const float bt = __uint_as_float((unsigned)b_r << 16);
+      // normalised q, k: the rows' inverse norms fold into the factors of Q and K below
       sm.gam[lane] = in ? g_r : glast;
-      sm.as[lane] = in ? xs * ea : 0.f;
-      sm.c[lane] = in ? __expf(glast - g_r) : 0.f;
-      sm.ab[lane] = in ? ea * bt : 0.f;
+      sm.as[lane] = in ? xs * ea * rq_r : 0.f;
+      sm.c[lane] = in ? __expf(glast - g_r) * rk_r : 0.f;
+      sm.ab[lane] = in ? ea * bt * rk_r : 0.f;
       sm.beta[lane] = in ? bt : 0.f;
+      sm.rq[lane] = rq_r;
+      sm.rk[lane] = rk_r;
     }
     if (c > c0) issue(c - 1, set ^ 1);
     __syncthreads();
@@ -267,12 +275,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kfrag(Qt, mr, ks), kfrag(Kt, mi, ks), acc);
       // acc[j] = q_r . k_i for r = 16 mr + 4 gq + j, i = 16 mi + cl
       const int i = 16 * mi + cl;
-      const float gi = sm.gam[i];
+      const float gi = sm.gam[i], ki = sm.rk[i];
       f32x4 p;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * mr + 4 * gq + j;
-        p[j] = (i <= r && r < n) ? __expf(sm.gam[r] - gi) * acc[j] : 0.f;
+        p[j] = (i <= r && r < n) ? (sm.rq[r] * ki) * __expf(sm.gam[r] - gi) * acc[j] : 0.f;
       }
       const bf16x4 hi = to_bf16x4(p);
       const int off = poff(i, 4 * mr + gq);
@@ -489,12 +497,14 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;
   const int64_t t0 = ts0 + (int64_t)cidx * kChunk;
   const int n = (int)min<int64_t>(kChunk, ts1 - t0);
-  __shared__ float sg[64], sb[64];
+  __shared__ float sg[64], sb[64], srk[64];
+  const int hk = h / (H / b.HK);  // this value head's key head
   sg[lane] = lane < n ? b.gamma[(t0 + lane) * H + h] : 0.f;
   sb[lane] = lane < n ? (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h] : 0.f;
+  // q/k L2 normalisation: k_r . k_i of the normalised rows = rk_r rk_i (k_r . k_i)
+  srk[lane] = b.rk != nullptr && lane < n ? b.rk[(t0 + lane) * b.HK + hk] : 1.f;
   // K rows as MFMA operands straight from HBM: row 16 m + cl, elements 32 ks + 8 gq .. + 7 (rows
   // past n read the last token; A masks them)
-  const int hk = h / (H / b.HK);  // this value head's key head
   const bf16 *gk = static_cast<const bf16 *>(b.k) + (int64_t)hk * kD;
   bf16x8 kf[4][4];
 #pragma unroll
@@ -517,12 +527,12 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
       }
       // acc[e] = k_r . k_i for r = 16 mr + 4 gq + e, i = 16 mi + cl
       const int i = 16 * mi + cl, r0 = 16 * mr + 4 * gq;
-      const float gi = sg[i];
+      const float gi = sg[i], ki = srk[i];
       f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = r0 + e;
-        v[e] = (i < r && r < n) ? sb[r] * __expf(sg[r] - gi) * acc[e] : 0.f;
+        v[e] = (i < r && r < n) ? sb[r] * (srk[r] * ki) * __expf(sg[r] - gi) * acc[e] : 0.f;
       }
       *reinterpret_cast<f32x4 *>(&am[i][r0]) = v;
     }

@@ -81,6 +81,7 @@ struct GradSmem {
   alignas(16) char tth[64 * 128];   // dPm = hi + lo
   alignas(16) char ttl[64 * 128];
   alignas(16) float gam[64], a[64], c[64], beta[64];
+  alignas(16) float rq[64], rk[64];  // q/k L2 normalisation: inverse row norms (1 without)
   alignas(16) float prg[kWaves][64];  // per-wave partial row terms of dgamma (tiles)
   alignas(16) float pcg[kWaves][64];  // per-wave partial column terms of dgamma (tiles, subtracted)
   alignas(16) float prb[kWaves][64];  // per-wave partial row terms of dbeta (tiles)
@@ -97,6 +98,8 @@ __constant__ int kTI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 }  // namespace
 
+// kNorm: q and k were L2-normalised in the forward (b.rq, b.rk hold the inverse row norms).
+template <bool kNorm>
 __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
@@ -188,10 +191,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
         gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
         gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
       }
-    float gmv = 0.f, bev = 0.f;
+    float gmv = 0.f, bev = 0.f, rqv = 1.f, rkv = 1.f;
     if (w == 0 && lane < n) {
       gmv = b.gamma[(t0 + lane) * H + h];
       bev = (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h];
+      if (kNorm) {
+        rqv = b.rq[(t0 + lane) * b.HK + hk];
+        rkv = b.rk[(t0 + lane) * b.HK + hk];
+      }
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -211,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       sm.a[lane] = lane < n ? __expf(gmv) : 0.f;
       sm.c[lane] = lane < n ? __expf(glast - gmv) : 0.f;
       sm.beta[lane] = bev;
+      sm.rq[lane] = rqv;
+      sm.rk[lane] = rkv;
     }
   }
   wait_vm0();  // this wave's direct loads have landed
@@ -347,27 +356,31 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       kk = mma_bf16(ak, bk, kk);
     }
     const int i = 16 * ti + cl;
-    const float gi = sm.gam[i];
+    const float gi = sm.gam[i], ki = sm.rk[i];
     float rg4[4], rb4[4], csc = 0.f;  // csc: this column's sum
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * tr + 4 * gq + j;
       float pm = 0.f, e = 0.f, tg = 0.f, tb = 0.f;
+      // normalised q, k (factors 1 without): qk and kk of the normalised rows are rq_r rk_i qk
+      // and rk_r rk_i kk; the stored tiles carry rq_r dPm rk_i and rk_r E rk_i, so that the
+      // products below give rq dQ and rk dK of the normalised rows
+      const float qs = sm.rq[r] * ki, ks2 = sm.rk[r] * ki;
       if (i <= r && r < n) {
         const float gm = __expf(sm.gam[r] - gi);
         pm = scale * dp[j] * gm;
-        tg = pm * qk[j];
+        tg = pm * (qs * qk[j]);
         if (i < r) {
           const float dA = -da[j];
-          const float gk = gm * kk[j];
+          const float gk = gm * (ks2 * kk[j]);
           e = dA * gm * sm.beta[r];
           tb = dA * gk;
           tg += dA * sm.beta[r] * gk;
         }
       }
       const int off = poff(r, i >> 2) + 2 * (i & 3);
-      st_split(sm.tth, sm.ttl, off, pm);
-      st_split(eth, etl, off, e);
+      st_split(sm.tth, sm.ttl, off, qs * pm);
+      st_split(eth, etl, off, ks2 * e);
       rg4[j] = tg;
       rb4[j] = tb;
       csc += tg;
@@ -394,10 +407,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 
   // ---- dQ = diag(a) Y1 + dPm K;  dK = dPm^T Q + (E + E^T) K + diag(c) Y2 - diag(beta a) Rh
   float rg[4][4], rc[4][4];
+  // normalised q, k: Z = rq dQ and W = rk dK of the normalised rows, held until the row dots
+  // q_r . Z_r and k_r . W_r over all columns are known; then dq = Z - rq^2 q (q . Z) (likewise
+  // dk), the normalisation's backward
+  static_assert(kNT == 1, "one column tile per wave");
+  constexpr bool norm = kNorm;
+  float zq[4][4], zk[4][4], pq[4][4], pk[4][4];
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) rg[mt][i] = rc[mt][i] = 0.f;
+    for (int i = 0; i < 4; ++i) rg[mt][i] = rc[mt][i] = zq[mt][i] = zk[mt][i] = pq[mt][i] = pk[mt][i] = 0.f;
   {
     bf16x8 kb[2][kNT], qb[2][kNT];  // K and Q over tokens: [ks][nt]
 #pragma unroll
@@ -440,8 +459,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
         }
       }
       const f32x4 ar = *reinterpret_cast<const f32x4 *>(&sm.a[16 * mt + 4 * gq]);
-      const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
+      const f32x4 cr0 = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
       const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
+      // normalised q, k: every term of row r that carries q_r (k_r) takes rq_r (rk_r)
+      const f32x4 rqr = *reinterpret_cast<const f32x4 *>(&sm.rq[16 * mt + 4 * gq]);
+      const f32x4 rkr = *reinterpret_cast<const f32x4 *>(&sm.rk[16 * mt + 4 * gq]);
+      const f32x4 aq = ar * rqr, ak = ar * rkr, cr = cr0 * rkr;
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const f32x4 qv = colv(sm.q, mt, 4 * kNT * w + 4 * nt), kv = colv(sm.k, mt, 4 * kNT * w + 4 * nt);
@@ -449,9 +472,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * mt + 4 * gq + i;
-          const float dqv = ar[i] * y1[i] + dq[nt][i];
-          const float dkv = dk[nt][i] + cr[i] * Y2[mt][nt][i] - br[i] * ar[i] * Rh[mt][nt][i];
-          if (r < n) {
+          const float dqv = aq[i] * y1[i] + dq[nt][i];
+          const float dkv = dk[nt][i] + cr[i] * Y2[mt][nt][i] - br[i] * ak[i] * Rh[mt][nt][i];
+          if constexpr (norm) {
+            zq[mt][i] = dqv;
+            zk[mt][i] = dkv;
+            pq[mt][i] += qv[i] * dqv;
+            pk[mt][i] += kv[i] * dkv;
+          } else if (r < n) {
             const int64_t gi = ((t0 + r) * H + h) * kD + fcol + 16 * nt;
             if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
               b.dq_part[gi] = dqv;
@@ -461,15 +489,17 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
               static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
             }
           }
-          rg[mt][i] += ar[i] * y1[i] * qv[i] - br[i] * ar[i] * Rh[mt][nt][i] * kv[i] -
+          rg[mt][i] += aq[i] * y1[i] * qv[i] - br[i] * ak[i] * Rh[mt][nt][i] * kv[i] -
                        cr[i] * Y2[mt][nt][i] * kv[i];
-          rb[mt][i] -= ar[i] * Rh[mt][nt][i] * kv[i];
+          rb[mt][i] -= ak[i] * Rh[mt][nt][i] * kv[i];
           rc[mt][i] += cr[i] * Y2[mt][nt][i] * kv[i];
         }
       }
     }
   }
-  // row sums over this wave's 16 columns per tile
+  // row sums over this wave's 16 columns per tile (the row dots of the normalisation go to the
+  // dO tile's space, free since the tile phase)
+  float *fq = reinterpret_cast<float *>(sm.dout), *fk = fq + kWaves * 64;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -480,14 +510,55 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
         rb[mt][i] += __shfl_xor(rb[mt][i], off, 64);
         rc[mt][i] += __shfl_xor(rc[mt][i], off, 64);
       }
+      if constexpr (norm) {
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+          pq[mt][i] += __shfl_xor(pq[mt][i], off, 64);
+          pk[mt][i] += __shfl_xor(pk[mt][i], off, 64);
+        }
+      }
       if (cl == 0) {
         const int r = 16 * mt + 4 * gq + i;
         sm.frg[w][r] = rg[mt][i];
         sm.frb[w][r] = rb[mt][i];
         sm.fc[w][r] = rc[mt][i];
+        if constexpr (norm) {
+          fq[w * 64 + r] = pq[mt][i];
+          fk[w * 64 + r] = pk[mt][i];
+        }
       }
     }
   __syncthreads();
+  if constexpr (norm) {  // dq = Z - rq^2 q (q . Z), dk = W - rk^2 k (k . W), summed over waves in order
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      f32x4 tq = zero4(), tk = zero4();
+#pragma unroll
+      for (int x = 0; x < kWaves; ++x) {
+        tq += *reinterpret_cast<const f32x4 *>(&fq[x * 64 + 16 * mt + 4 * gq]);
+        tk += *reinterpret_cast<const f32x4 *>(&fk[x * 64 + 16 * mt + 4 * gq]);
+      }
+      const f32x4 qv = colv(sm.q, mt, 4 * kNT * w), kv = colv(sm.k, mt, 4 * kNT * w);
+      const f32x4 rqr = *reinterpret_cast<const f32x4 *>(&sm.rq[16 * mt + 4 * gq]);
+      const f32x4 rkr = *reinterpret_cast<const f32x4 *>(&sm.rk[16 * mt + 4 * gq]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * mt + 4 * gq + i;
+        if (r < n) {
+          const float dqv = zq[mt][i] - rqr[i] * rqr[i] * qv[i] * tq[i];
+          const float dkv = zk[mt][i] - rkr[i] * rkr[i] * kv[i] * tk[i];
+          const int64_t gi = ((t0 + r) * H + h) * kD + fcol;
+          if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
+            b.dq_part[gi] = dqv;
+            b.dk_part[gi] = dkv;
+          } else {
+            static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
+            static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
+          }
+        }
+      }
+    }
+  }
   if (w == 0) {
     const int r = lane;
     float dgam = 0.f, dbet = 0.f, csum = 0.f;
@@ -523,8 +594,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream) {
   if (max_chunks <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_grad_bf16_kernel, dim3((unsigned)max_chunks, b.H), dim3(kThreads), 0, stream,
-                     b);
+  if (b.rq != nullptr)
+    hipLaunchKernelGGL(bwd_grad_bf16_kernel<true>, dim3((unsigned)max_chunks, b.H), dim3(kThreads),
+                       0, stream, b);
+  else
+    hipLaunchKernelGGL(bwd_grad_bf16_kernel<false>, dim3((unsigned)max_chunks, b.H), dim3(kThreads),
+                       0, stream, b);
   return hipGetLastError();
 }
 

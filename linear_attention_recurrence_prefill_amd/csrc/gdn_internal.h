@@ -64,6 +64,10 @@ struct BwdArgs {
   // grouped heads (HK < H): dq and dk of every value head, fp32 [T, H, D], summed per key head
   // afterwards (null when HK == H: dq and dk are written directly)
   float *dq_part, *dk_part;
+  // q/k L2 normalisation: the inverse row norms 1 / sqrt(|row|^2 + eps) of q and k, fp32 [T, HK]
+  // (null: no normalisation).  The kernels fold them into their per-token factors and write
+  // r * (gradient of the normalised rows) to dq_part, dk_part; l2norm_bwd_kernel finishes.
+  const float *rq, *rk;
   int64_t T;
   int32_t N, H;
   int32_t HK;  // heads of q and k
@@ -112,6 +116,16 @@ hipError_t launch_sum_dh0(const float *dh0_seq, int32_t N, int32_t H, int32_t D,
                           hipStream_t stream);
 // Grouped heads: out[t, hk, :] = sum over the H / HK value heads of key head hk of part[t, h, :]
 // (fixed order), in the input dtype.
+// Inverse L2 norms 1 / sqrt(|row|^2 + kL2NormEps) of the `rows` rows of x ([rows, D], bf16 or
+// fp32) into r [rows].
+hipError_t launch_row_rnorm(const void *x, int64_t rows, int32_t D, bool bf16, float *r,
+                            hipStream_t stream);
+// Backward of the q/k L2 normalisation, with the per-key-head sum of grouped heads: for each row
+// (t, hk) of x [T, HK, D], Z = sum over the H / HK value heads of part [T, H, D] (each holding
+// r * the gradient of the normalised row) and dx = Z - r^2 x (x . Z), into out (x's dtype).
+hipError_t launch_l2norm_bwd(const float *part, const void *x, const float *r, int64_t T,
+                             int32_t H, int32_t HK, int32_t D, bool bf16, void *out,
+                             hipStream_t stream);
 hipError_t launch_group_sum(const float *part, int64_t T, int32_t H, int32_t HK, int32_t D,
                             bool bf16, void *out, hipStream_t stream);
 

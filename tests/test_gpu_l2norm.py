@@ -108,3 +108,38 @@ def test_l2norm_rejected_where_not_built(gdn):
     args = [_dev(inp[x], torch.bfloat16 if x != "g" else None) for x in NAMES]
     with pytest.raises(gdn.GdnError):
         gdn.chunk_fwd(*args, _dev(inp["cu_seqlens"]), None, qk_l2norm=True)
+
+
+@pytest.mark.parametrize("dtype,d,G,seg", [("bf16", 128, 1, 0), ("bf16", 128, 2, 2),
+                                           ("f32", 64, 1, 0), ("f32", 128, 2, 0)])
+def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg):
+    """Gradients of the raw q, k (through the normalisation) and of v, g, beta, h0 against the
+    oracle's backward with the normalisation; grouped heads sum dq, dk over each group."""
+    inp = make_inputs([300, 65, 0, 260], H=4, dk=d, dv=d, dtype=dtype, seed=521, h0_scale=0.5,
+                      with_dout=True)
+    inp = scale_qk_rows(inp, seed=522)
+    gi = dict(inp)
+    for x in ("q", "k"):
+        gi[x] = np.ascontiguousarray(inp[x][:, ::G])
+    ref = dict(gi)
+    for x in ("q", "k"):
+        ref[x] = np.ascontiguousarray(np.repeat(gi[x], G, axis=1))
+    tdt = _tdt(inp)
+    rng = np.random.default_rng(523)
+    N = len(inp["cu_seqlens"]) - 1
+    dht = (0.3 * rng.standard_normal((N, 4, d, d))).astype(np.float32)
+    args = [_dev(gi[x], tdt if x != "g" else None) for x in NAMES]
+    print(f"[l2norm bwd {dtype} d={d} G={G} seg={seg}]", flush=True)
+    gr = gdn.chunk_bwd(*args, _dev(inp["cu_seqlens"]), _dev(inp["dout"], tdt), _dev(inp["h0"]),
+                       _dev(dht), scale=0.7, seg_chunks=seg, num_slots=256 if seg else 0,
+                       qk_l2norm=True)
+    torch.cuda.synchronize()
+    r = oracle_mod.bwd(*[ref[x] for x in NAMES], inp["cu_seqlens"], inp["dout"], h0=inp["h0"],
+                       dht=dht, scale=0.7, qk_l2norm=True)
+    T = inp["g"].shape[0]
+    tol = tol_for(dtype)
+    for n in ("dq", "dk"):
+        summed = np.asarray(r[n]).reshape(T, 4 // G, G, d).sum(axis=2)
+        report(n, np64(gr[n]), summed, tol)
+    for n in ("dv", "dg", "dbeta", "dh0"):
+        report(n, np64(gr[n]), r[n], tol)
