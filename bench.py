@@ -70,6 +70,8 @@ def parse():
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-l2norm", action="store_true",
+                    help="skip the forward and backward timed with q/k L2 normalisation")
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the on-device copy and bf16 matmul peak measurements")
     ap.add_argument("--no-backward", action="store_true",
@@ -300,13 +302,15 @@ def main():
                              "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
                              / HBM_PEAK_GBS, "timing": r,
                              **fractions(r["median_ms"], bytes_launch, flops_launch, peaks)}
-    r = time_steps(gdn, torch, sets, head, args.steps, args.warmup, qk_l2norm=True)
-    line["qk_l2norm"] = {"mode": head, "ms_per_step": r["mean_ms"],
-                         "value": T / (r["mean_ms"] / 1e3),
-                         "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                         "timing": r}
+    if not args.no_l2norm:
+        r = time_steps(gdn, torch, sets, head, args.steps, args.warmup, qk_l2norm=True)
+        line["qk_l2norm"] = {"mode": head, "ms_per_step": r["mean_ms"],
+                             "value": T / (r["mean_ms"] / 1e3),
+                             "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
+                             / HBM_PEAK_GBS, "timing": r}
     if not args.no_backward:
-        line["backward"] = time_backward(gdn, torch, args.steps, args.warmup)
+        line["backward"] = time_backward(gdn, torch, args.steps, args.warmup,
+                                         with_l2norm=not args.no_l2norm)
         line["decode"] = time_decode(gdn, torch, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
@@ -360,7 +364,7 @@ def time_decode(gdn, torch, steps, warmup):
                          "bytes_per_step": nbytes}}
 
 
-def time_backward(gdn, torch, steps, warmup):
+def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
     """The training step's backward (gdn_chunk_bwd: forward recompute, reverse chain, per-chunk
     gradients) on the packed 65536-token workload of 4096..16384-token documents, H = 8, d = 128,
     bf16, dO ~ N(0, 1), timed like the forward.  Algorithmic bytes: q, k, v, dO read and dq, dk,
@@ -389,19 +393,22 @@ def time_backward(gdn, torch, steps, warmup):
 
     r = timed(torch, step, steps, warmup)
     ms = r["mean_ms"]
-    # the same backward with q and k normalised inside the kernels (its own, larger workspace)
-    pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact", qk_l2norm=True)
-    assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pn), ctypes.byref(nbytes)) == 0
-    wsn = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")
-    rn = timed(torch, lambda i: gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu,
-                                              dev["dout"], workspace=wsn, qk_l2norm=True),
-               steps, warmup)
+    rn = None
+    if with_l2norm:  # the same backward with q and k normalised inside the kernels
+        pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact",
+                          qk_l2norm=True)
+        assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pn),
+                                                               ctypes.byref(nbytes)) == 0
+        wsn = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")
+        rn = timed(torch, lambda i: gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"],
+                                                  cu, dev["dout"], workspace=wsn, qk_l2norm=True),
+                   steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
     achieved = nbytes_alg / (ms / 1e3) / 1e9
     return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
                         f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
             "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
-            "qk_l2norm_ms_per_step": rn["mean_ms"],
+            "qk_l2norm_ms_per_step": rn["mean_ms"] if rn else None,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes_alg}}
