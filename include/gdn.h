@@ -185,15 +185,18 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
  * recurrent step on one token): every (sequence b, head h) state advances by one token of the
  * recurrence above, in place,
  *     S <- exp(g) (I - beta k k^T) S + beta k v^T,    o = scale * S^T q   (S after the update).
- * Layouts (sequence-major, contiguous): q, k, v, o [batch, num_heads, head_dim] in dtype
- * (GDN_DTYPE_*); g [batch, num_heads] fp32; beta [batch, num_heads] in dtype; state
- * [batch, num_heads, head_dim, head_dim] fp32, read and overwritten.  head_dim is 64 or 128
- * (d_k = d_v).  All tensors are caller-owned device memory, 16-byte aligned; no workspace.
- * Arguments are validated before anything is enqueued (batch, num_heads >= 1; pointers). */
-gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t dtype,
-                           float scale, const void *q, const void *k, const void *v,
-                           const float *g, const void *beta, float *state, void *o,
-                           hipStream_t stream);
+ * Layouts (sequence-major, contiguous): q, k [batch, Hk, head_dim] and v, o [batch, num_heads,
+ * head_dim] in dtype (GDN_DTYPE_*), Hk = num_k_heads (0 = num_heads; otherwise a divisor of
+ * num_heads, value head h reading key head h / (num_heads / Hk) as in gdn_problem); g
+ * [batch, num_heads] fp32; beta [batch, num_heads] in dtype; state [batch, num_heads, head_dim,
+ * head_dim] fp32, read and overwritten.  qk_l2norm = 1: q and k are L2-normalised first, as in
+ * gdn_problem.  head_dim is 64 or 128 (d_k = d_v).  All tensors are caller-owned device
+ * memory, 16-byte aligned; no workspace.  Arguments are validated before anything is enqueued
+ * (batch, num_heads >= 1; num_k_heads; qk_l2norm in {0, 1}; pointers). */
+gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t num_k_heads, int32_t head_dim,
+                           int32_t dtype, int32_t qk_l2norm, float scale, const void *q,
+                           const void *k, const void *v, const float *g, const void *beta,
+                           float *state, void *o, hipStream_t stream);
 
 /* Static description of a status code. */
 const char *gdn_status_string(gdn_status s);

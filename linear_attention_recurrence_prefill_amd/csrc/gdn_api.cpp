@@ -712,12 +712,16 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
 
 extern "C" {
 
-gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t head_dim, int32_t dtype,
-                           float scale, const void *q, const void *k, const void *v,
-                           const float *g, const void *beta, float *state, void *o,
-                           hipStream_t stream) {
+gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t num_k_heads, int32_t head_dim,
+                           int32_t dtype, int32_t qk_l2norm, float scale, const void *q,
+                           const void *k, const void *v, const float *g, const void *beta,
+                           float *state, void *o, hipStream_t stream) {
   if (batch < 1 || num_heads < 1 || (int64_t)batch * num_heads > INT32_MAX)
     return fail(GDN_ERR_BAD_SHAPE, "batch and num_heads must be >= 1");
+  if (num_k_heads < 0 || num_k_heads > num_heads ||
+      (num_k_heads > 0 && num_heads % num_k_heads != 0))
+    return fail(GDN_ERR_BAD_SHAPE, "num_k_heads must be 0 or a divisor of num_heads");
+  if (qk_l2norm != 0 && qk_l2norm != 1) return fail(GDN_ERR_BAD_MODE, "qk_l2norm must be 0 or 1");
   if (head_dim != 64 && head_dim != 128) return fail(GDN_ERR_BAD_SHAPE, "head_dim must be 64 or 128");
   if (dtype != GDN_DTYPE_F32 && dtype != GDN_DTYPE_BF16) return fail(GDN_ERR_BAD_DTYPE, "dtype %d", dtype);
   if (!std::isfinite(scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
@@ -738,6 +742,8 @@ gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t head_dim, i
   a.o = o;
   a.B = batch;
   a.H = num_heads;
+  a.HK = num_k_heads > 0 ? num_k_heads : num_heads;
+  a.l2norm = qk_l2norm;
   a.scale = scale;
   const hipError_t e = gdn::launch_decode_step(a, head_dim, dtype == GDN_DTYPE_BF16, stream);
   if (e != hipSuccess) return hip_fail(e, "decode step launch");

@@ -7,6 +7,8 @@
 // With u = k^T S and w = q^T S (one pass over S gives both) this is
 //     t  = v - e^g u,    S' = e^g S + beta k t^T,    o = scale (e^g w + beta (q . k) t),
 // so S is read once and written once: the step is bound by HBM bandwidth (2 d^2 fp32 per state).
+// With the q/k L2 normalisation, q = rq q_in and k = rk k_in with the rows' inverse norms: the
+// factors fold into u, w, q . k and beta, and the rows are never rewritten.
 //
 // One workgroup of 256 threads per (sequence, head).  Thread (row group rg, column group cg)
 // holds rows rg * RPT .. + RPT - 1 of columns 4 cg .. 4 cg + 3 in registers (16-byte loads and
@@ -14,6 +16,7 @@
 // groups through LDS in a fixed order.
 #include "gdn_decode.h"
 #include "gdn_device.h"
+#include "gdn_internal.h"
 
 namespace gdn {
 namespace {
@@ -32,11 +35,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   constexpr int RPT = D / RG;    // rows per thread
   __shared__ float sq[D], sk[D], sv[D], st[D];
   __shared__ __attribute__((aligned(16))) float pu[RG][D], pw[RG][D];
-  __shared__ float sqk;
+  __shared__ float sqk, srq, srk;
   const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
   const int64_t bh = blockIdx.x;  // (sequence, head) pair, sequence-major
-  const E *q = static_cast<const E *>(a.q) + bh * D;
-  const E *k = static_cast<const E *>(a.k) + bh * D;
+  const int64_t bk = bh / a.H * a.HK + (int)(bh % a.H) / (a.H / a.HK);  // (sequence, key head)
+  const E *q = static_cast<const E *>(a.q) + bk * D;
+  const E *k = static_cast<const E *>(a.k) + bk * D;
   const E *v = static_cast<const E *>(a.v) + bh * D;
   float *S = a.state + bh * D * D;
   if (tid < D) {
@@ -52,12 +56,26 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
   const float eg = __expf(a.g[bh]);
   const float beta = ld_any(static_cast<const E *>(a.beta), bh);
   __syncthreads();
-  if (tid < 64) {  // q . k, fixed order
-    float s = 0.f;
-    for (int i = tid; i < D; i += 64) s += sq[i] * sk[i];
+  if (tid < 64) {  // q . k (and |q|^2, |k|^2 for the normalisation), fixed order
+    float s = 0.f, nq = 0.f, nk = 0.f;
+    for (int i = tid; i < D; i += 64) {
+      s += sq[i] * sk[i];
+      nq += sq[i] * sq[i];
+      nk += sk[i] * sk[i];
+    }
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off, 64);
-    if (tid == 0) sqk = s;
+    for (int off = 32; off > 0; off >>= 1) {
+      s += __shfl_xor(s, off, 64);
+      nq += __shfl_xor(nq, off, 64);
+      nk += __shfl_xor(nk, off, 64);
+    }
+    if (tid == 0) {
+      const float rq = a.l2norm ? 1.f / sqrtf(nq + kL2NormEps) : 1.f;
+      const float rk = a.l2norm ? 1.f / sqrtf(nk + kL2NormEps) : 1.f;
+      sqk = rq * rk * s;
+      srq = rq;
+      srk = rk;
+    }
   }
   f32x4 u = zero4(), w = zero4();
 #pragma unroll
@@ -76,8 +94,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(DecodeArgs a) {
       us += pu[g][tid];
       ws += pw[g][tid];
     }
+    us *= srk;  // the normalised rows' u and w (factors 1 without the normalisation)
+    ws *= srq;
     const float t = sv[tid] - eg * us;
-    st[tid] = beta * t;
+    st[tid] = beta * srk * t;
     st_any(static_cast<E *>(a.o) + bh * D, tid, a.scale * (eg * ws + beta * sqk * t));
   }
   __syncthreads();

@@ -76,7 +76,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                   vp, vp, sz, vp]
     lib.gdn_chunk_bwd.restype = st
-    lib.gdn_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+    lib.gdn_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32,
                                     ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp, vp, vp, vp,
                                     vp]
     lib.gdn_decode_step.restype = st
@@ -301,16 +302,21 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
     return out
 
 
-def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
-    """One decode step (gdn_decode_step): q, k, v [B, H, D] (bf16 or fp32), g [B, H] fp32,
-    beta [B, H] (q's dtype), state [B, H, D, D] fp32, advanced in place by one token.  Returns
-    o [B, H, D] (q's dtype)."""
+def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None, qk_l2norm=False):
+    """One decode step (gdn_decode_step): q, k [B, Hk, D] and v [B, H, D] (bf16 or fp32; Hk
+    dividing H, value head h reading key head h // (H // Hk)), g [B, H] fp32, beta [B, H] (q's
+    dtype), state [B, H, D, D] fp32, advanced in place by one token.  qk_l2norm: q and k rows
+    are L2-normalised in the kernel.  Returns o [B, H, D] (q's dtype)."""
     lib = load_library()
-    if q.dim() != 3:
-        raise ValueError("q must be [B, H, D]")
-    B, H, D = q.shape
-    for name, t, shape in (("k", k, (B, H, D)), ("v", v, (B, H, D)), ("g", g, (B, H)),
-                           ("beta", beta, (B, H)), ("state", state, (B, H, D, D))):
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k and v must be [B, heads, D]")
+    B, Hk, D = q.shape
+    H = v.shape[1]
+    if Hk < 1 or H % Hk != 0:
+        raise ValueError("q's heads must divide v's heads")
+    for name, t, shape in (("q", q, (B, Hk, D)), ("k", k, (B, Hk, D)), ("v", v, (B, H, D)),
+                           ("g", g, (B, H)), ("beta", beta, (B, H)),
+                           ("state", state, (B, H, D, D))):
         if tuple(t.shape) != shape or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous {list(shape)}")
     if q.dtype not in (torch.bfloat16, torch.float32) or k.dtype != q.dtype or \
@@ -321,8 +327,9 @@ def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None):
     if out is None:
         out = torch.empty_like(v)
     dt = GDN_DTYPE_BF16 if q.dtype == torch.bfloat16 else GDN_DTYPE_F32
-    _check(lib.gdn_decode_step(B, H, D, dt, float(scale), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
-                               _ptr(beta), _ptr(state), _ptr(out), _stream()))
+    _check(lib.gdn_decode_step(B, H, Hk, D, dt, 1 if qk_l2norm else 0, float(scale), _ptr(q),
+                               _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(out),
+                               _stream()))
     return out
 
 

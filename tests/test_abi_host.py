@@ -176,7 +176,9 @@ def test_bwd_recompute_split_workspace(lib):
 
 
 @pytest.mark.parametrize("args,status", [
-    ((0, 8, 128, 1), 2), ((4, 0, 128, 1), 2), ((4, 8, 96, 1), 2), ((4, 8, 128, 5), 3)])
+    ((0, 8, 0, 128, 1, 0), 2), ((4, 0, 0, 128, 1, 0), 2), ((4, 8, 0, 96, 1, 0), 2),
+    ((4, 8, 0, 128, 5, 0), 3), ((4, 8, 3, 128, 1, 0), 2), ((4, 8, 16, 128, 1, 0), 2),
+    ((4, 8, -1, 128, 1, 0), 2), ((4, 8, 2, 128, 1, 2), 4)])
 def test_decode_step_rejects_bad_sizes(lib, args, status):
     buf = (ctypes.c_char * 64)()
     ptr = ctypes.cast(buf, ctypes.c_void_p)
@@ -188,7 +190,8 @@ def test_decode_step_rejects_bad_sizes(lib, args, status):
 def test_decode_step_rejects_null_pointer(lib):
     buf = (ctypes.c_char * 64)()
     ptr = ctypes.cast(buf, ctypes.c_void_p)
-    assert lib.gdn_decode_step(4, 8, 128, 1, 1.0, ptr, None, ptr, ptr, ptr, ptr, ptr, None) == 1
+    assert lib.gdn_decode_step(4, 8, 0, 128, 1, 0, 1.0, ptr, None, ptr, ptr, ptr, ptr, ptr,
+                               None) == 1
 
 
 def _aligned_ptr(buf):
