@@ -66,7 +66,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps before the timed ones (the card's clock settles within "
+                         "about 250 back-to-back forward launches)")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -100,12 +102,28 @@ def timed(torch, step, steps, warmup):
     """Times ``step(i)``: ``warmup`` untimed calls, then exactly ``steps`` calls between two HIP
     events on the current stream (device synchronisations on both sides): the mean per step.  A
     second pass of ``steps`` calls with an event between consecutive calls gives the per-call
-    distribution (median, p10, p90; events between calls, so kept apart from the mean)."""
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
+    distribution (median, p10, p90; events between calls, so kept apart from the mean).  The
+    warmup itself is also timed, after its first 10 calls, over ``steps`` calls (``early_ms``):
+    the card's clock ramps over the first ~20 ms of back-to-back work, so that window runs
+    slower than the sustained rate the timed pass measures."""
     stream = torch.cuda.current_stream()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    early = None
+    w0 = min(10, warmup)
+    for i in range(w0):
+        step(i)
+    if warmup >= w0 + steps:
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            step(w0 + i)
+        end.record(stream)
+        torch.cuda.synchronize()
+        early = start.elapsed_time(end) / steps
+        w0 += steps
+    for i in range(w0, warmup):
+        step(i)
+    torch.cuda.synchronize()
     start.record(stream)
     for i in range(steps):
         step(i)
@@ -120,7 +138,8 @@ def timed(torch, step, steps, warmup):
     torch.cuda.synchronize()
     per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
     return {"mean_ms": mean, "median_ms": float(np.median(per)),
-            "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90))}
+            "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
+            "early_ms": early}
 
 
 def host_call_us(torch, step, calls=20):
