@@ -165,10 +165,12 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 // with V = 0 (the unit's transition matrix M, so that the state after the unit is
 // M S_start + B for any start state).
 // kNorm: q and k are L2-normalised per row.  The tiles stay as loaded; wave 7 computes each row's
-// inverse norm 1 / sqrt(|row|^2 + eps) once the chunk's K and Q have landed in LDS, and every use
-// folds it into the per-token factors it already applies (A and P by rows and columns, e^gamma in
-// R', scale e^gamma in the output, e^{gamma_last - gamma} in the update), so the normalised rows
-// are never rounded to bf16.
+// inverse norm 1 / sqrt(|row|^2 + eps) once the chunk's K and Q have landed in LDS and folds it
+// into the per-token factors: in place into the chain's gate vectors (e^gamma of R', scale
+// e^gamma of the output, e^{gamma_last - gamma} of the update; no other wave touches that chunk's
+// vectors at that point), and through rn_s into A and P, whose prep applies it by rows and
+// columns.  The normalised rows are never rounded to bf16, and the chain's code is the same as
+// without the normalisation.
 template <bool kTransition, bool kDump = false, bool kNorm = false>
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
@@ -410,7 +412,6 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int Y = cc & 1;
         const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];
         const WsSmem::Vec &vc = sm.vec[cc % 3];
-        const float *rkc = rn_s[kNorm ? cc % 3 : 0][0], *rqc = rn_s[kNorm ? cc % 3 : 0][1];
 
         // ---- K h, then R' = V - diag(e^gamma) K h, fp32
         f32x4 R[4][2];
@@ -434,8 +435,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         __atomic_signal_fence(__ATOMIC_SEQ_CST);
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          f32x4 ee = *reinterpret_cast<const f32x4 *>(&vc.eg[16 * mt + 4 * gq]);
-          if constexpr (kNorm) ee *= ldf4(&rkc[16 * mt + 4 * gq]);
+          const f32x4 ee = *reinterpret_cast<const f32x4 *>(&vc.eg[16 * mt + 4 * gq]);
 #pragma unroll
           for (int nt = 0; nt < 2; ++nt) {
             const bf16x4 v4 = ldtr(vw + 1024 * mt + o_vtr[nt]);
@@ -487,12 +487,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
                                                         v0 + 16 * H * kD * 4, 0, 0);
                 }
             }
-            f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
-            f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
-            if constexpr (kNorm) {
-              e0 *= ldf4(&rkc[32 * hb + 4 * gq]);
-              e1 *= ldf4(&rkc[32 * hb + 16 + 4 * gq]);
-            }
+            const f32x4 e0 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 4 * gq]);
+            const f32x4 e1 = *reinterpret_cast<const f32x4 *>(&vc.edt[32 * hb + 16 + 4 * gq]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) {
               da[hb][nt] = to_bf16x8(Dl0[nt], Dl1[nt]);
@@ -514,7 +510,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           const char *P = sm.p[Y];
           float et[4];
 #pragma unroll
-          for (int tt = 0; tt < 4; ++tt) et[tt] = vc.ego[16 * tt + cl] * (kNorm ? rqc[16 * tt + cl] : 1.f);
+          for (int tt = 0; tt < 4; ++tt) et[tt] = vc.ego[16 * tt + cl];
           f32x4 acc[4][2];
 #pragma unroll
           for (int tt = 0; tt < 4; ++tt) acc[tt][0] = acc[tt][1] = zero4();
@@ -661,8 +657,14 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         }
         return 1.f / sqrtf(s + kL2NormEps);
       };
-      rn_s[c % 3][0][lane] = inv_norm(sm.kq[c % 3][0]);
-      if (with_q) rn_s[c % 3][1][lane] = inv_norm(sm.kq[c % 3][1]);
+      const float rk = inv_norm(sm.kq[c % 3][0]);
+      const float rq = with_q ? inv_norm(sm.kq[c % 3][1]) : 1.f;
+      rn_s[c % 3][0][lane] = rk;
+      rn_s[c % 3][1][lane] = rq;
+      WsSmem::Vec &vc = sm.vec[c % 3];  // written by gate_vectors earlier in this step
+      vc.eg[lane] *= rk;
+      vc.edt[lane] *= rk;
+      vc.ego[lane] *= rq;
     };
     GB gbx{0.f, 0};
     if (cw < c1) {
