@@ -181,16 +181,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
                          : zero4();
       }
     }
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
-        hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
-        hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
-        gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
-        gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
-      }
     float gmv = 0.f, bev = 0.f, rqv = 1.f, rkv = 1.f;
     if (w == 0 && lane < n) {
       gmv = b.gamma[(t0 + lane) * H + h];
@@ -224,6 +214,18 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   }
   wait_vm0();  // this wave's direct loads have landed
   __syncthreads();
+  // h and dh' rows of this wave into registers: first used after the tile phase, so the loads
+  // run while it computes
+#pragma unroll
+  for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
+      hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
+      hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
+      gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
+      gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+    }
 
   // fragment readers
   // A or B operand over features, natural order: row r, elements 32 ks + 8 gq .. + 7
@@ -247,47 +249,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   auto colv = [&](const char *t, int m, int u0) {
     return to_f32x4(ldtr(t + toff(16 * m + 4 * gq + (cl >> 2), u0 + (cl & 3))));
   };
-
-  // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
-  bf16x8 hh[kNT][4], hl[kNT][4];
-  f32x4 Y1[4][kNT], Y2[4][kNT];
-  float hdot = 0.f;
-  {
-    bf16x8 gh[kNT][4], gl[kNT][4];
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const f32x4 h0 = hv[nt][ks][0], h1 = hv[nt][ks][1];
-        const f32x4 d0 = gv[nt][ks][0], d1 = gv[nt][ks][1];
-        split8(h0, h1, hh[nt][ks], hl[nt][ks]);
-        split8(d0, d1, gh[nt][ks], gl[nt][ks]);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) hdot += h0[j] * d0[j] + h1[j] * d1[j];
-      }
-    // Y1 = dO h^T (scale applied later), Y2 = Delta dh'^T
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) Y1[mt][nt] = Y2[mt][nt] = zero4();
-#pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 ao = rowf(sm.dout, 16 * mt + cl, ks);
-        const bf16x8 ah = rowf(sm.dh, 16 * mt + cl, ks), al = rowf(sm.dl, 16 * mt + cl, ks);
-#pragma unroll
-        for (int nt = 0; nt < kNT; ++nt) {
-          Y1[mt][nt] = mma_bf16(ao, hh[nt][ks], Y1[mt][nt]);
-          Y1[mt][nt] = mma_bf16(ao, hl[nt][ks], Y1[mt][nt]);
-          Y2[mt][nt] = mma_bf16(ah, gh[nt][ks], Y2[mt][nt]);
-          Y2[mt][nt] = mma_bf16(ah, gl[nt][ks], Y2[mt][nt]);
-          Y2[mt][nt] = mma_bf16(al, gh[nt][ks], Y2[mt][nt]);
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) hdot += __shfl_xor(hdot, off, 64);
-  if (lane == 0) sm.hd[w] = hdot;
 
   // ---- dR_r . V_r over this wave's columns (v)
   float rb[4][4];  // row terms of dbeta over this wave's columns: [mt][i]
@@ -317,24 +278,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
     *reinterpret_cast<uint2 *>(&sm.v[64 * 128 + off]) = uint2{0u, 0u};
   }
   __syncthreads();
-
-  // ---- Rh = dR h^T over this wave's columns (d)
-  f32x4 Rh[4][kNT];
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
-#pragma unroll
-    for (int nt = 0; nt < kNT; ++nt) Rh[mt][nt] = zero4();
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 ah = rowf(sm.eh, 16 * mt + cl, ks), al = rowf(sm.el, 16 * mt + cl, ks);
-#pragma unroll
-      for (int nt = 0; nt < kNT; ++nt) {
-        Rh[mt][nt] = mma_bf16(ah, hh[nt][ks], Rh[mt][nt]);
-        Rh[mt][nt] = mma_bf16(ah, hl[nt][ks], Rh[mt][nt]);
-        Rh[mt][nt] = mma_bf16(al, hh[nt][ks], Rh[mt][nt]);
-      }
-    }
-  }
 
   // ---- 64 x 64 tiles on and below the diagonal: dP, dR Delta^T, Q K^T, K K^T
   char *eth = sm.v, *etl = sm.v + 64 * 128;  // E = hi + lo
@@ -403,6 +346,65 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
     }
     if (gq == 0) sm.pcg[w][i] = csc;
   }
+  // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
+  bf16x8 hh[kNT][4], hl[kNT][4];
+  f32x4 Y1[4][kNT], Y2[4][kNT];
+  float hdot = 0.f;
+  {
+    bf16x8 gh[kNT][4], gl[kNT][4];
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const f32x4 h0 = hv[nt][ks][0], h1 = hv[nt][ks][1];
+        const f32x4 d0 = gv[nt][ks][0], d1 = gv[nt][ks][1];
+        split8(h0, h1, hh[nt][ks], hl[nt][ks]);
+        split8(d0, d1, gh[nt][ks], gl[nt][ks]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hdot += h0[j] * d0[j] + h1[j] * d1[j];
+      }
+    // Y1 = dO h^T (scale applied later), Y2 = Delta dh'^T
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) Y1[mt][nt] = Y2[mt][nt] = zero4();
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 ao = rowf(sm.dout, 16 * mt + cl, ks);
+        const bf16x8 ah = rowf(sm.dh, 16 * mt + cl, ks), al = rowf(sm.dl, 16 * mt + cl, ks);
+#pragma unroll
+        for (int nt = 0; nt < kNT; ++nt) {
+          Y1[mt][nt] = mma_bf16(ao, hh[nt][ks], Y1[mt][nt]);
+          Y1[mt][nt] = mma_bf16(ao, hl[nt][ks], Y1[mt][nt]);
+          Y2[mt][nt] = mma_bf16(ah, gh[nt][ks], Y2[mt][nt]);
+          Y2[mt][nt] = mma_bf16(ah, gl[nt][ks], Y2[mt][nt]);
+          Y2[mt][nt] = mma_bf16(al, gh[nt][ks], Y2[mt][nt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) hdot += __shfl_xor(hdot, off, 64);
+  if (lane == 0) sm.hd[w] = hdot;
+
+  // ---- Rh = dR h^T over this wave's columns (d)
+  f32x4 Rh[4][kNT];
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt) Rh[mt][nt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 ah = rowf(sm.eh, 16 * mt + cl, ks), al = rowf(sm.el, 16 * mt + cl, ks);
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt) {
+        Rh[mt][nt] = mma_bf16(ah, hh[nt][ks], Rh[mt][nt]);
+        Rh[mt][nt] = mma_bf16(ah, hl[nt][ks], Rh[mt][nt]);
+        Rh[mt][nt] = mma_bf16(al, hh[nt][ks], Rh[mt][nt]);
+      }
+    }
+  }
+
   __syncthreads();
 
   // ---- dQ = diag(a) Y1 + dPm K;  dK = dPm^T Q + (E + E^T) K + diag(c) Y2 - diag(beta a) Rh
