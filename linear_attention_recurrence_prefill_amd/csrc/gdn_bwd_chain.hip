@@ -220,8 +220,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const int u = ((lane & 15) ^ sw(r)) << 4;
       const int lo = ((64 / kWaves) * w + 4 * j) * kRowB;
       dma16(gk + t * tok_qk + u, sm.kqo[set][0] + lo);
-      dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
-      dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
+      if (!is_m) {  // the M' half runs with dO = 0 and reads neither Q nor dO
+        dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
+        dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
+      }
     }
     // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
     const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
