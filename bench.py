@@ -60,6 +60,8 @@ BWD_BYTES_PER_TH = 7 * 256 + 2 * 4 + 2 * 2  # q k v dO dq dk dv (bf16), g dg (fp
 STATE_BYTES = 128 * 128 * 4
 PAGE_H200_MS = 0.31          # the page's FlashQLA figure for this workload (H200; context only)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_long32k.json")
+BWD_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_bwd_train65k.json")
+BWD_SOURCES = ("gdn_bwd_chain.hip", "gdn_bwd_grad.hip", "gdn_fwd_split.hip", "gdn_fwd_ws.hip")
 
 
 def parse():
@@ -424,25 +426,31 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
                    steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
     achieved = nbytes_alg / (ms / 1e3) / 1e9
+    traffic = None  # measured HBM bytes per call (rocprofv3), while the kernels are unchanged
+    if os.path.exists(BWD_TRAFFIC_FILE):
+        with open(BWD_TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        if rec.get("kernel_source_sha") == kernel_source_sha(BWD_SOURCES):
+            traffic = rec.get("bytes_per_call")
     return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
                         f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
             "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
             "qk_l2norm_ms_per_step": rn["mean_ms"] if rn else None,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "bytes_per_step": nbytes_alg}}
+                         "bytes_per_step": nbytes_alg, "traffic": traffic}}
 
 
-def kernel_source_sha():
-    """Hash of the timed kernel's translation unit (gdn_fwd_ws.hip and the csrc headers it
-    includes, followed recursively) and of the compiler flags build.py gives it.  Changes to
-    other kernels leave it, and so the stored traffic figure, valid."""
+def kernel_source_sha(sources=("gdn_fwd_ws.hip",)):
+    """Hash of the timed kernels' translation units (by default gdn_fwd_ws.hip) and the csrc
+    headers they include, followed recursively, and of the compiler flags build.py gives them.
+    Changes to other kernels leave it, and so the stored traffic figure, valid."""
     import hashlib
 
     from linear_attention_recurrence_prefill_amd import build as b
 
     csrc = b.CSRC
-    seen, todo = [], ["gdn_fwd_ws.hip"]
+    seen, todo = [], list(sources)
     while todo:
         name = todo.pop(0)
         if name in seen or not os.path.exists(os.path.join(csrc, name)):
@@ -454,7 +462,9 @@ def kernel_source_sha():
     for name in sorted(seen):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(f.read())
-    h.update(repr((b.HIP_FLAGS, b.EXTRA_FLAGS.get("gdn_fwd_ws.hip", []))).encode())
+    extra = (b.EXTRA_FLAGS.get(sources[0], []) if len(sources) == 1
+             else [b.EXTRA_FLAGS.get(x, []) for x in sources])
+    h.update(repr((b.HIP_FLAGS, extra)).encode())
     return h.hexdigest()[:16]
 
 
