@@ -101,3 +101,29 @@ def test_grouped_backward(gdn, oracle_mod, dtype, d, G):
         report(n, np64(gr[n]), summed, tol)
     for n in ("dv", "dg", "dbeta", "dh0"):
         report(n, np64(gr[n]), r[n], tol)
+
+
+@pytest.mark.parametrize("mode", ["truncate", "exact"])
+def test_grouped_many_heads_normalised(gdn, oracle_mod, mode):
+    """A Qwen-style layer shape: 32 value heads over 4 key heads (groups of 8), q and k
+    normalised in the kernels, 8192 tokens in three documents, bf16 d = 128."""
+    from gdn_inputs import scale_qk_rows
+
+    G = 8
+    inp = scale_qk_rows(make_inputs([4096, 2500, 1596], H=32, dk=128, dv=128, dtype="bf16",
+                                    seed=404, h0_scale=0.5), seed=405)
+    gi, ref = _grouped(inp, G)
+    o, ht = gdn.chunk_fwd(*_args(gi, torch.bfloat16), _dev(inp["cu_seqlens"], None),
+                          _dev(inp["h0"], None), mode=mode, num_slots=256,
+                          cu_seqlens_host=inp["cu_seqlens"], qk_l2norm=True)
+    torch.cuda.synchronize()
+    if mode == "exact":
+        o_ref, ht_ref = oracle_mod.fwd_recurrent(*[ref[x] for x in NAMES], inp["cu_seqlens"],
+                                                 h0=inp["h0"], qk_l2norm=True)
+    else:
+        plan = oracle_mod.plan(inp["g"], inp["cu_seqlens"], 32, P=256)
+        o_ref, ht_ref = oracle_mod.fwd_truncated(*[ref[x] for x in NAMES], inp["cu_seqlens"],
+                                                 plan, h0=inp["h0"], qk_l2norm=True)
+    print(f"[grouped 32/4 heads, normalised, {mode}]", flush=True)
+    report("o", np64(o), o_ref, 5e-3)
+    report("ht", np64(ht), ht_ref, 5e-3)
