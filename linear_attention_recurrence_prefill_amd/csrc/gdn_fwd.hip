@@ -130,12 +130,12 @@ __device__ __forceinline__ void normalize_rows(float *__restrict__ t, int tid) {
   const int r = tid >> 2, part = tid & 3;
   float s = 0.f;
 #pragma unroll
-  for (int i = part; i < D; i += 4) s += t[r * LDE + i] * t[r * LDE + i];
+  for (int j = 0; j < D / 4; ++j) s += t[r * LDE + part + 4 * j] * t[r * LDE + part + 4 * j];
   s += __shfl_xor(s, 1, 64);
   s += __shfl_xor(s, 2, 64);
   const float inv = 1.f / sqrtf(s + kL2NormEps);
 #pragma unroll
-  for (int i = part; i < D; i += 4) t[r * LDE + i] *= inv;
+  for (int j = 0; j < D / 4; ++j) t[r * LDE + part + 4 * j] *= inv;
 }
 
 template <int D, bool BF16, bool DUMP>
