@@ -109,7 +109,9 @@ typedef struct gdn_problem {
   int32_t qk_l2norm;         /* 1: q and k are L2-normalised per (token, head) row inside the
                               * kernels, q / sqrt(|q|^2 + 1e-6) (likewise k), and the backward
                               * returns the gradients of the raw q and k; 0: used as given.
-                              * Supported for bf16 with d = 128 and for fp32 inputs. */
+                              * bf16 with d = 128 never rounds the normalised rows (the norms
+                              * fold into the kernel's per-token factors); bf16 with d = 64 and
+                              * the intermediates call round them to bf16. */
   int32_t reserved;          /* must be 0 */
   int64_t h0_seq_stride;     /* elements between consecutive sequences' h0; 0 = broadcast */
 } gdn_problem;

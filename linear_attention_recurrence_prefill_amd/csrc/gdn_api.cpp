@@ -116,8 +116,6 @@ gdn_status check_problem(const gdn_problem *p) {
     return fail(GDN_ERR_BAD_SHAPE, "num_k_heads must be 0 or a divisor of num_heads");
   if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
     return fail(GDN_ERR_BAD_MODE, "qk_l2norm must be 0 or 1");
-  if (p->qk_l2norm && p->dtype == GDN_DTYPE_BF16 && p->d_k != 128)
-    return fail(GDN_ERR_BAD_MODE, "qk_l2norm with bf16 inputs needs d = 128");
   if (p->reserved != 0) return fail(GDN_ERR_BAD_SHAPE, "reserved must be 0");
   if (p->h0_seq_stride < 0) return fail(GDN_ERR_BAD_SHAPE, "h0_seq_stride must be >= 0");
   if (!std::isfinite(p->scale)) return fail(GDN_ERR_BAD_SHAPE, "scale must be finite");
@@ -376,8 +374,6 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
                                        size_t workspace_bytes, hipStream_t stream) {
   if (p && p->mode != GDN_MODE_EXACT)
     return fail(GDN_ERR_BAD_MODE, "intermediates are defined for the exact mode only");
-  if (p && p->qk_l2norm && p->dtype == GDN_DTYPE_BF16)
-    return fail(GDN_ERR_BAD_MODE, "intermediates with qk_l2norm need fp32 inputs");
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
   float *dbg[6] = {gamma, tmat, w, u, hc, delta};
   return run_fwd(p, t, nullptr, true, dbg, workspace, workspace_bytes, stream);

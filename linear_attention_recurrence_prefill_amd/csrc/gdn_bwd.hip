@@ -60,8 +60,10 @@ __device__ __forceinline__ void load_rows64(float *dst, const E *src, int64_t t0
   // rs (optional): per-row factors [T, H] (the q/k L2 normalisation's inverse norms)
   for (int i = tid; i < 64 * 64; i += 256) {
     const int r = i >> 6, c = i & 63;
-    const float m = rs != nullptr && r < n ? mul * rs[(t0 + r) * H + h] : mul;
-    dst[r * LDF + c] = r < n ? m * to_f32(src[((t0 + r) * H + h) * D + c0 + c]) : 0.f;
+    const float x = r < n ? to_f32(src[((t0 + r) * H + h) * D + c0 + c]) : 0.f;
+    // normalised rows are rounded to the input dtype, as the forward kernels use them
+    dst[r * LDF + c] = rs != nullptr && r < n ? mul * to_f32(from_f32<E>(rs[(t0 + r) * H + h] * x))
+                                              : mul * x;
   }
 }
 
@@ -141,8 +143,11 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs b) {
       const int64_t gi = ((t0 + r) * H + h) * D + col;
       const int64_t gik = ((t0 + r) * b.HK + hk) * D + col;  // q and k: the key head
       const int64_t rk_i = (t0 + r) * b.HK + hk;  // q/k L2 normalisation: the rows' factors
-      sm.q[r * LD + col] = ok ? (b.rq ? b.rq[rk_i] : 1.f) * to_f32(gq_[gik]) : 0.f;
-      sm.k[r * LD + col] = ok ? (b.rk ? b.rk[rk_i] : 1.f) * to_f32(gk_[gik]) : 0.f;
+      // normalised rows are rounded to the input dtype, as the forward kernels use them
+      sm.q[r * LD + col] = !ok ? 0.f : b.rq ? to_f32(from_f32<E>(b.rq[rk_i] * to_f32(gq_[gik])))
+                                            : to_f32(gq_[gik]);
+      sm.k[r * LD + col] = !ok ? 0.f : b.rk ? to_f32(from_f32<E>(b.rk[rk_i] * to_f32(gk_[gik])))
+                                            : to_f32(gk_[gik]);
       sm.dout[r * LD + col] = ok ? b.scale * to_f32(gdo[gi]) : 0.f;
       sm.w[r * LD + col] = b.w[((cg * H + h) * 64 + r) * D + col];
     }

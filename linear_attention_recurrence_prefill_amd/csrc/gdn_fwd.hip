@@ -138,6 +138,25 @@ __device__ __forceinline__ void normalize_rows(float *__restrict__ t, int tid) {
   for (int j = 0; j < D / 4; ++j) t[r * LDE + part + 4 * j] *= inv;
 }
 
+// The same on a bf16 tile: the scaled rows are rounded back to bf16 (the d = 64 bf16 path's
+// reading of the normalisation, as a separate normalisation writing bf16 would give).
+template <int D, int LDE>
+__device__ __forceinline__ void normalize_rows(bf16 *__restrict__ t, int tid) {
+  const int r = tid >> 2, part = tid & 3;
+  float s = 0.f;
+#pragma unroll
+  for (int j = 0; j < D / 4; ++j) {
+    const float x = (float)t[r * LDE + part + 4 * j];
+    s += x * x;
+  }
+  s += __shfl_xor(s, 1, 64);
+  s += __shfl_xor(s, 2, 64);
+  const float inv = 1.f / sqrtf(s + kL2NormEps);
+#pragma unroll
+  for (int j = 0; j < D / 4; ++j)
+    t[r * LDE + part + 4 * j] = (bf16)(inv * (float)t[r * LDE + part + 4 * j]);
+}
+
 template <int D, bool BF16, bool DUMP>
 __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   using SM = FwdSmem<D, BF16>;
@@ -243,12 +262,10 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       if (DUMP && a.dbg_gamma && lane < n) a.dbg_gamma[(t0 + lane) * H + h] = gam;
     }
     __syncthreads();
-    if constexpr (!BF16) {  // q/k L2 normalisation (fp32 tiles; bf16 runs it on the pipelined kernel)
-      if (a.l2norm) {
-        normalize_rows<D, LDE>(sm.k, tid);
-        if (emit) normalize_rows<D, LDE>(sm.q, tid);
-        __syncthreads();
-      }
+    if (a.l2norm) {  // q/k L2 normalisation of the staged tiles
+      normalize_rows<D, LDE>(sm.k, tid);
+      if (emit) normalize_rows<D, LDE>(sm.q, tid);
+      __syncthreads();
     }
 
     // ---- K K^T -> A (row a2) and Q K^T (kept in registers until A is consumed)

@@ -162,10 +162,40 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
       pb = lane < n ? (float)gb_[(t0 + lane) * H + h] : 0.f;
     }
   };
+  // q/k L2 normalisation of one 16-byte unit of a row whose UPR units sit in UPR consecutive
+  // lanes: the row's sum of squares by a butterfly over those lanes, then the unit scaled and
+  // rounded back to bf16 (rows past the chunk's end are zero and stay zero)
+  auto norm_unit = [&](uint4 &x) {
+    unsigned wd[4] = {x.x, x.y, x.z, x.w};
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = __uint_as_float(wd[i] << 16), hi = __uint_as_float(wd[i] & 0xFFFF0000u);
+      s += lo * lo + hi * hi;
+    }
+#pragma unroll
+    for (int off = 1; off < UPR; off <<= 1) s += __shfl_xor(s, off, 64);
+    const float r = 1.f / sqrtf(s + kL2NormEps);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const bf16 lo = (bf16)(r * __uint_as_float(wd[i] << 16));
+      const bf16 hi = (bf16)(r * __uint_as_float(wd[i] & 0xFFFF0000u));
+      wd[i] = (unsigned)__builtin_bit_cast(unsigned short, lo) |
+              ((unsigned)__builtin_bit_cast(unsigned short, hi) << 16);
+    }
+    x = uint4{wd[0], wd[1], wd[2], wd[3]};
+  };
   auto commit = [&](int c, Buf &B) {
     const bool em = c >= c0;
     const int64_t t0 = ts0 + (int64_t)c * kChunk;
     const int n = (int)min<int64_t>(kChunk, ts1 - t0);
+    if (a.l2norm) {
+#pragma unroll
+      for (int j = 0; j < UPT; ++j) {
+        norm_unit(pk[j]);
+        if (em) norm_unit(pq[j]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < UPT; ++j) {
       const int u = tid + NTH * j, r = u / UPR, cu16 = u % UPR;

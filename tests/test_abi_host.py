@@ -220,11 +220,9 @@ def test_calib_mfma_rejects_bad_sizes(lib, waves, iters):
     assert lib.gdn_calib_mfma_bf16(None, 4, 10, None) == 1
 
 
-def test_qk_l2norm_needs_d128_for_bf16(lib):
+@pytest.mark.parametrize("dtype,d", [(1, 64), (1, 128), (0, 64), (0, 128)])
+def test_qk_l2norm_accepted_for_every_dtype_and_size(lib, dtype, d):
     n = ctypes.c_size_t(0)
-    p = _problem(qk_l2norm=1, d_k=64, d_v=64)
-    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 4
-    p = _problem(qk_l2norm=1, d_k=64, d_v=64, dtype=0, num_slots=256)  # fp32: general kernel
+    p = _problem(qk_l2norm=1, d_k=d, d_v=d, dtype=dtype, num_slots=256)
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
-    p = _problem(qk_l2norm=1, num_slots=256)
-    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0

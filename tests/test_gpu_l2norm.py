@@ -103,14 +103,16 @@ def test_l2norm_long_32k_truncate(gdn, oracle_mod):
     report("ht", np64(ht), ht_t, 5e-3)
 
 
-def test_l2norm_rejected_where_not_built(gdn):
-    inp = make_inputs([70], H=2, dk=64, dv=64, dtype="bf16", seed=515)
-    args = [_dev(inp[x], torch.bfloat16 if x != "g" else None) for x in NAMES]
-    with pytest.raises(gdn.GdnError):
-        gdn.chunk_fwd(*args, _dev(inp["cu_seqlens"]), None, qk_l2norm=True)
+@pytest.mark.parametrize("mode,seg", [("exact", 0), ("truncate", 2)])
+def test_l2norm_bf16_d64(gdn, oracle_mod, mode, seg):
+    """bf16 with d = 64 (the rows normalised as they are staged and rounded to bf16)."""
+    inp = make_inputs([1, 63, 64, 65, 130, 0, 300], H=4, dk=64, dv=64, dtype="bf16", seed=515,
+                      h0_scale=0.5)
+    _run_fwd(gdn, oracle_mod, inp, f"l2norm bf16 d=64 {mode}", mode=mode, seg=seg, scale=0.7)
 
 
 @pytest.mark.parametrize("dtype,d,G,seg", [("bf16", 128, 1, 0), ("bf16", 128, 2, 2),
+                                           ("bf16", 64, 1, 0), ("bf16", 64, 2, 0),
                                            ("f32", 64, 1, 0), ("f32", 128, 2, 0)])
 def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg):
     """Gradients of the raw q, k (through the normalisation) and of v, g, beta, h0 against the

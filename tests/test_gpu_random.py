@@ -31,7 +31,7 @@ def _case(seed):
     d = [64, 128][rng.integers(2)]
     H = int(rng.choice([1, 2, 4, 6]))
     G = int(rng.choice([g for g in (1, 2, 3, 6) if H % g == 0]))
-    norm = bool(rng.integers(2)) and not (dtype == "bf16" and d == 64)
+    norm = bool(rng.integers(2))
     mode = ["exact", "truncate"][rng.integers(2)]
     seg = int(rng.choice([0, 2, 3]))
     lengths = [int(x) for x in rng.choice([0, 1, 63, 64, 65, 130, 257, 400], rng.integers(1, 6))]
