@@ -352,3 +352,13 @@ def calib_mfma_bf16(out, waves_per_cu, iters):
         raise ValueError("out must be float32 with waves_per_cu * 256 * 64 elements")
     _check(lib.gdn_calib_mfma_bf16(_ptr(out), int(waves_per_cu), int(iters), _stream()))
     return waves_per_cu * 256 * iters * 4 * 32768
+
+
+# The C entry points' names (include/gdn.h, include/gdn_calib.h), one binding each.
+gdn_chunk_fwd = chunk_fwd
+gdn_chunk_fwd_plan = chunk_fwd_plan
+gdn_chunk_fwd_intermediates = chunk_fwd_intermediates
+gdn_chunk_bwd = chunk_bwd
+gdn_decode_step = decode_step
+gdn_calib_copy = calib_copy
+gdn_calib_mfma_bf16 = calib_mfma_bf16

@@ -226,3 +226,14 @@ def test_qk_l2norm_accepted_for_every_dtype_and_size(lib, dtype, d):
     p = _problem(qk_l2norm=1, d_k=d, d_v=d, dtype=dtype, num_slots=256)
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+
+
+def test_binding_has_every_compute_entry_point():
+    """The Python binding offers each C compute entry point under its C name."""
+    import linear_attention_recurrence_prefill_amd as pkg
+
+    names = [n for n in _declared_functions()
+             if n not in ("gdn_problem_init", "gdn_chunk_fwd_workspace_size",
+                          "gdn_chunk_bwd_workspace_size", "gdn_status_string", "gdn_last_error")]
+    for n in names:
+        assert callable(getattr(pkg, n)), n
