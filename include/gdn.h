@@ -22,6 +22,8 @@
  *               h0_seq_stride = 0 broadcasts one state to every sequence (a shared prefix, as in
  *               "Musings on long-context fine-tuning", section "Isolating the recurrent layers")
  *   ht          [N, H, d_k, d_v] fp32, the state after each sequence's last token
+ *   T = 0 (every sequence empty) is allowed: the per-token pointers may then be NULL, each final
+ *   state is its initial state and the backward's dh0 is dht.
  *
  * Conventions.
  *   Ownership: every tensor pointer is a device pointer owned by the caller; the library never

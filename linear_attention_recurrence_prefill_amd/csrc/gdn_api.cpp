@@ -231,8 +231,9 @@ struct Tensors {
   float *ht;
 };
 
-gdn_status check_tensors(const Tensors &t) {
-  if (!t.q || !t.k || !t.v || !t.g || !t.beta || !t.cu || !t.o)
+// The per-token arrays may be NULL only when there are no tokens.
+gdn_status check_tensors(const Tensors &t, int64_t T) {
+  if (!t.cu || (T > 0 && (!t.q || !t.k || !t.v || !t.g || !t.beta || !t.o)))
     return fail(GDN_ERR_NULL_ARG, "q, k, v, g, beta, cu_seqlens and o are required");
   const void *ptrs[] = {t.q, t.k, t.v, t.g, t.beta, t.o};
   for (const void *x : ptrs)
@@ -246,12 +247,18 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
                    float *dbg[6], void *ws, size_t ws_bytes, hipStream_t stream) {
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
-  s = check_tensors(t);
+  s = check_tensors(t, p->total_tokens);
   if (s != GDN_OK) return s;
   s = check_cu_host(p, cu_host);
   if (s != GDN_OK) return s;
   s = device_info(nullptr);
   if (s != GDN_OK) return s;
+  if (p->total_tokens == 0) {  // every sequence is empty: its final state is its initial state
+    if (!t.ht) return GDN_OK;
+    hipError_t e = gdn::launch_copy_states(t.h0, p->h0_seq_stride, p->num_seqs, p->num_heads,
+                                           p->d_k, t.ht, stream);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "final states of empty sequences");
+  }
   FwdLayout lay;
   s = fwd_layout(p, cu_host, dump, &lay);
   if (s != GDN_OK) return s;
@@ -385,7 +392,8 @@ gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_
                               hipStream_t stream) {
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
-  if (!g || !cu_seqlens || !plan_out) return fail(GDN_ERR_NULL_ARG, "g, cu_seqlens, plan_out");
+  if ((!g && p->total_tokens > 0) || !cu_seqlens || !plan_out)
+    return fail(GDN_ERR_NULL_ARG, "g, cu_seqlens, plan_out");
   s = check_cu_host(p, cu_seqlens_host);
   if (s != GDN_OK) return s;
   s = device_info(nullptr);
@@ -565,13 +573,26 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
   if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
-  if (!dout || !dq || !dk || !dv || !dg || !dbeta)
+  if (p->total_tokens > 0 && (!dout || !dq || !dk || !dv || !dg || !dbeta))
     return fail(GDN_ERR_NULL_ARG, "dout, dq, dk, dv, dg and dbeta are required");
   const void *ptrs[] = {dout, dq, dk, dv, dg, dbeta};
   for (const void *x : ptrs)
     if (!aligned16(x)) return fail(GDN_ERR_BAD_ALIGNMENT, "tensor pointers must be 16-byte aligned");
   if ((dht && !aligned16(dht)) || (dh0 && !aligned16(dh0)))
     return fail(GDN_ERR_BAD_ALIGNMENT, "dht / dh0 must be 16-byte aligned");
+  if (p->total_tokens == 0) {  // no tokens: every state passes through unchanged, so dh0 = dht
+    if (!cu_seqlens) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is required");
+    if (!dh0) return GDN_OK;
+    s = device_info(nullptr);
+    if (s != GDN_OK) return s;
+    const bool shared = h0 != nullptr && p->h0_seq_stride == 0;
+    const int64_t per_seq = (int64_t)p->num_heads * p->d_k * p->d_k;
+    hipError_t e = (shared && dht)
+                       ? gdn::launch_sum_dh0(dht, p->num_seqs, p->num_heads, p->d_k, dh0, stream)
+                       : gdn::launch_copy_states(dht, per_seq, shared ? 1 : p->num_seqs,
+                                                 p->num_heads, p->d_k, dh0, stream);
+    return e == hipSuccess ? GDN_OK : hip_fail(e, "dh0 of empty sequences");
+  }
   BwdLayout L;
   s = bwd_layout(p, &L);
   if (s != GDN_OK) return s;
@@ -589,7 +610,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
   float *dbg[6] = {gamma, tmat, w, nullptr, hc, delta};
   if (fast) {
-    s = check_tensors(t);
+    s = check_tensors(t, p->total_tokens);
     if (s == GDN_OK) s = device_info(nullptr);
     if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc, delta, L, base, stream);
   } else {

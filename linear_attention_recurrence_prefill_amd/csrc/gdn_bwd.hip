@@ -613,6 +613,16 @@ __global__ __launch_bounds__(256) void sum_dh0_kernel(const float *__restrict__ 
   dst[i] = acc;
 }
 
+// dst[n] = src[n * src_stride] (or 0 without src) for the N states of per_seq floats each.
+__global__ __launch_bounds__(256) void copy_states_kernel(const float *__restrict__ src,
+                                                         int64_t src_stride, int64_t n_total,
+                                                         int64_t per_seq,
+                                                         float *__restrict__ dst) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_total;
+       i += (int64_t)gridDim.x * 256)
+    dst[i] = src ? src[i / per_seq * src_stride + i % per_seq] : 0.f;
+}
+
 __global__ __launch_bounds__(256) void group_sum_kernel(const float *__restrict__ part, int64_t T,
                                                        int H, int HK, int D, int is_bf16,
                                                        void *__restrict__ out) {
@@ -762,6 +772,16 @@ hipError_t launch_sum_dh0(const float *dh0_seq, int32_t N, int32_t H, int32_t D,
   const int64_t per_seq = (int64_t)H * D * D;
   hipLaunchKernelGGL(sum_dh0_kernel, dim3((unsigned)((per_seq + 255) / 256)), dim3(256), 0,
                      stream, dh0_seq, N, per_seq, dh0);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_states(const float *src, int64_t src_stride, int32_t N, int32_t H,
+                              int32_t D, float *dst, hipStream_t stream) {
+  const int64_t per_seq = (int64_t)H * D * D, n_total = per_seq * N;
+  int64_t blocks = (n_total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(copy_states_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, src,
+                     src_stride, n_total, per_seq, dst);
   return hipGetLastError();
 }
 

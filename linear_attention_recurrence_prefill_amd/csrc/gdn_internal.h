@@ -114,6 +114,9 @@ hipError_t launch_bwd_grad(const BwdArgs &b, int D, bool bf16, int64_t max_chunk
                            hipStream_t stream);
 hipError_t launch_sum_dh0(const float *dh0_seq, int32_t N, int32_t H, int32_t D, float *dh0,
                           hipStream_t stream);
+// dst[n] = src[n * src_stride] for N states [H, D, D] (fp32); zeros when src is NULL.
+hipError_t launch_copy_states(const float *src, int64_t src_stride, int32_t N, int32_t H,
+                              int32_t D, float *dst, hipStream_t stream);
 // Grouped heads: out[t, hk, :] = sum over the H / HK value heads of key head hk of part[t, h, :]
 // (fixed order), in the input dtype.
 // Inverse L2 norms 1 / sqrt(|row|^2 + kL2NormEps) of the `rows` rows of x ([rows, D], bf16 or

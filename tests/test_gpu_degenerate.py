@@ -100,3 +100,24 @@ def test_zero_rows_under_l2norm(gdn, oracle_mod, dtype, d):
         a[rng.random(a.shape[:2]) < 0.2] = 0.0
         inp[x] = bf16_round(a) if dtype == "bf16" else a
     _run(gdn, oracle_mod, inp, f"zero rows l2norm {dtype} d={d}", "exact", norm=True)
+
+
+@pytest.mark.parametrize("dtype,d", CASES)
+def test_all_documents_empty(gdn, dtype, d):
+    """T = 0 (every document empty): the final states are the initial states, nothing else is
+    written, and the backward passes dht through to dh0."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H, N = 2, 3
+    q = torch.zeros((0, H, d), device="cuda", dtype=tdt)
+    g = torch.zeros((0, H), device="cuda")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda")
+    h0 = torch.randn((N, H, d, d), device="cuda")
+    for mode in ("exact", "truncate"):
+        o, ht = gdn.chunk_fwd(q, q, q, g, g.to(tdt), cu, h0, mode=mode, num_slots=256)
+        torch.cuda.synchronize()
+        assert o.shape == (0, H, d) and torch.equal(ht, h0), mode
+    dht = torch.randn((N, H, d, d), device="cuda")
+    gr = gdn.chunk_bwd(q, q, q, g, g.to(tdt), cu, q, h0, dht)
+    torch.cuda.synchronize()
+    assert gr["dq"].shape == (0, H, d)
+    assert torch.equal(gr["dh0"], dht)
