@@ -8,35 +8,35 @@ adds up to".  Inputs are seeded synthetic values (gdn_inputs.py), resident in HB
 timed region.  Three input sets of the same shape rotate between steps so the 256 MB last-level
 cache cannot serve a repeated working set.
 
-A step is one forward (gdn_chunk_fwd: o and the final state) on the current stream.  W warmup
-steps run first; then exactly K steps are timed with HIP events on that stream, bracketed by
-device synchronisations.  ``value`` is tokens per second of the headline mode (the page's
-truncated-history split, section "Lever 1"); the exact mode is timed the same way and reported
-beside it, so is the same forward with q and k L2-normalised inside the kernel (object
-``qk_l2norm``; the same algorithmic bytes), and so is the training backward (gdn_chunk_bwd on the packed 65536-token workload of
-the pages' training runs, object ``backward`` with its own HBM roofline fraction) and the
-single-token decode step (object ``decode``).
+A step is one forward (gdn_chunk_fwd: o and the final state) on the current stream.  The
+on-device peaks are measured first (which also brings the card to its sustained clock); then W
+warmup steps run, and exactly K steps are timed on that stream between device
+synchronisations, with HIP events only between windows of 5 back-to-back steps.  ``value`` is
+tokens per second at the median window's time per step (``ms_per_step``), in the headline mode
+(the page's truncated-history split, section "Lever 1"); the exact mode is timed the same way and
+reported beside it, so is the same forward with q and k L2-normalised inside the kernel (object
+``qk_l2norm``), the forward on the pages' other workloads (object ``workloads``: the 8192-token
+packed batch, the fork's 65536-token prefix and its 80 branches, the 65536-token training
+batch), the training backward (object ``backward``) and the single-token decode step (object
+``decode``).
 
 ``roofline``: the forward is bound by HBM bandwidth (about 176 flop per byte against the
 MI355X's ~315 flop/byte ridge).  Algorithmic bytes per launch = 1030 B per (token, head)
 (q, k, v, o in bf16, g in fp32, beta in bf16) + 64 KiB per (sequence, head) of final state.
-``achieved`` = those bytes / the measured time per launch (one launch per step); ``peak`` is the
-8 TB/s HBM3E datasheet figure.  ``traffic`` is the measured HBM bytes per launch from the
-rocprofv3 FETCH_SIZE / WRITE_SIZE runs recorded in profiles/ (null when not measured for the
-current kernel).
+``achieved`` = those bytes / the average launch duration over the whole timed region (one
+launch per step; ``timing.mean_ms``); ``peak`` is the 8 TB/s HBM3E datasheet figure.
+``traffic`` is the measured HBM bytes per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+recorded in profiles/ (null when not measured for the current kernel).  ``roofline.median``
+holds %HBM, %MFMA and the roofline fraction max(B / bandwidth, F / rate) / t at the median time
+against the datasheet peaks, ``roofline.median_vs_measured_peaks`` the same against
+``measured_peaks`` (the library's stream copy of 1 GiB and its loop of bf16 MFMAs, timed on this
+GPU).  ``timing.host_call_us`` is the host's wall time for one call after a device
+synchronisation (argument checks, segment planning, launches).
 
-``timing``: the same K steps again with an event between consecutive steps give the per-step
-median, p10 and p90 (``ms_per_step`` and ``value`` come from the bracketing events alone), and
-``host_call_us`` is the host's wall time for one call after a device synchronisation (argument
-checks, segment planning, launches).  ``roofline.median`` holds %HBM, %MFMA and the roofline
-fraction max(B / bandwidth, F / rate) / t at the median time against the datasheet peaks,
-``roofline.median_vs_measured_peaks`` the same against ``measured_peaks`` (the library's stream
-copy of 1 GiB and its loop of bf16 MFMAs, timed on this GPU).  Events between steps add a few
-microseconds to each measured step, which shows in the 26 us decode step's median.
-
-``cpu_baseline``: the fp64 token-recurrent oracle (plain C, OpenMP over (sequence, head) pairs)
-timed on this host on the same workload (8 (sequence, head) units, so at most 8 threads), and
-with one thread on two of the heads, scaled to eight.
+``cpu_baseline``: the fp64 token-recurrent oracle (plain C built with gcc -O2 -fopenmp, as for
+the tests; OpenMP over (sequence, head) pairs) timed on this host on the same workload (8
+(sequence, head) units, so at most 8 threads), and with one thread on two of the heads, scaled
+to eight.
 """
 from __future__ import annotations
 
@@ -68,9 +68,9 @@ def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=300,
-                    help="untimed steps before the timed ones (the card's clock settles within "
-                         "about 250 back-to-back forward launches)")
+    ap.add_argument("--warmup", type=int, default=20,
+                    help="untimed steps before the timed ones (after the on-device peak "
+                         "measurements, which bring the card to its sustained clock)")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
     ap.add_argument("--mode", choices=["truncate", "exact", "both"], default="both")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -79,7 +79,10 @@ def parse():
     ap.add_argument("--no-measured-peaks", action="store_true",
                     help="skip the on-device copy and bf16 matmul peak measurements")
     ap.add_argument("--no-backward", action="store_true",
-                    help="skip the training backward timed beside the forward")
+                    help="skip the training backward and the decode step timed beside the "
+                         "forward")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the forward on the pages' other workloads")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB each (reads and writes MIB MiB per "
                          "launch): the reference for scaling HBM traffic counters, then exit")
@@ -100,48 +103,31 @@ def time_steps(gdn, torch, sets, mode, steps, warmup, qk_l2norm=False):
     return timed(torch, step, steps, warmup)
 
 
-def timed(torch, step, steps, warmup):
-    """Times ``step(i)``: ``warmup`` untimed calls, then exactly ``steps`` calls between two HIP
-    events on the current stream (device synchronisations on both sides): the mean per step.  A
-    second pass of ``steps`` calls with an event between consecutive calls gives the per-call
-    distribution (median, p10, p90; events between calls, so kept apart from the mean).  The
-    warmup itself is also timed, after its first 10 calls, over ``steps`` calls (``early_ms``):
-    the card's clock ramps over the first ~20 ms of back-to-back work, so that window runs
-    slower than the sustained rate the timed pass measures."""
+def timed(torch, step, steps, warmup, window=5):
+    """Times ``step(i)``: ``warmup`` untimed calls, then exactly ``steps`` calls on the current
+    stream between device synchronisations.  Events are recorded only between windows of
+    ``window`` back-to-back calls (one before the first call, one after each window), so each
+    window's calls run back to back as in a real sequence of calls.  ``mean_ms`` is the whole
+    timed region over ``steps``; ``median_ms``, ``p10_ms`` and ``p90_ms`` are over the windows'
+    per-call means."""
     stream = torch.cuda.current_stream()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    early = None
-    w0 = min(10, warmup)
-    for i in range(w0):
-        step(i)
-    if warmup >= w0 + steps:
-        torch.cuda.synchronize()
-        start.record(stream)
-        for i in range(steps):
-            step(w0 + i)
-        end.record(stream)
-        torch.cuda.synchronize()
-        early = start.elapsed_time(end) / steps
-        w0 += steps
-    for i in range(w0, warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        step(i)
-    end.record(stream)
-    torch.cuda.synchronize()
-    mean = start.elapsed_time(end) / steps
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    sizes = [min(window, steps - i) for i in range(0, steps, window)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(sizes) + 1)]
     ev[0].record(stream)
-    for i in range(steps):
-        step(i)
-        ev[i + 1].record(stream)
+    i = 0
+    for w, n in enumerate(sizes):
+        for _ in range(n):
+            step(warmup + i)
+            i += 1
+        ev[w + 1].record(stream)
     torch.cuda.synchronize()
-    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
-    return {"mean_ms": mean, "median_ms": float(np.median(per)),
+    per = np.array([ev[w].elapsed_time(ev[w + 1]) / n for w, n in enumerate(sizes)])
+    return {"mean_ms": ev[0].elapsed_time(ev[-1]) / steps, "median_ms": float(np.median(per)),
             "p10_ms": float(np.percentile(per, 10)), "p90_ms": float(np.percentile(per, 90)),
-            "early_ms": early}
+            "windows": len(sizes), "window_calls": window}
 
 
 def host_call_us(torch, step, calls=20):
@@ -214,6 +200,7 @@ def cpu_baseline(inp):
     except OSError:
         pass
     return {"value": T / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "build": "gcc -O2 -fopenmp (the oracle as built for the tests, not tuned)",
             "sample": f"full workload: 1 x {T} tokens x 8 heads, fp64 token recurrence, "
                       f"{dt:.2f} s wall on {threads} of {cores} host threads",
             "one_thread_tokens_per_s": T / dt1,
@@ -250,6 +237,7 @@ def main():
     import linear_attention_recurrence_prefill_amd as gdn
 
     gdn.load_library()
+    peaks = None if args.no_measured_peaks else measured_peaks(gdn, torch)
     inp = workload("long")
     T, H, D = inp["q"].shape
     tdt = torch.bfloat16
@@ -272,16 +260,16 @@ def main():
     for m in modes:
         results[m] = time_steps(gdn, torch, sets, m, args.steps, args.warmup)
     head = modes[0]
-    ms = results[head]["mean_ms"]
+    r = results[head]
+    ms = r["median_ms"]
     value = T / (ms / 1e3)
     bytes_launch = BYTES_PER_TH * T * H + STATE_BYTES * H
     flops_launch = FLOP_PER_TH * T * H
-    achieved = bytes_launch / (ms / 1e3) / 1e9
+    achieved = bytes_launch / (r["mean_ms"] / 1e3) / 1e9  # over the average launch duration
     cu_host = [0, T]
     host_us = host_call_us(torch, lambda i: gdn.chunk_fwd(
         sets[0]["q"], sets[0]["k"], sets[0]["v"], sets[0]["g"], sets[0]["beta"],
         sets[0]["cu_seqlens"], None, mode=head, cu_seqlens_host=cu_host))
-    peaks = None if args.no_measured_peaks else measured_peaks(gdn, torch)
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
@@ -298,6 +286,7 @@ def main():
         "ms_per_step": ms,
         "higher_is_better": True,
         "scaling": "weak",
+        # the pages' FlashQLA time for this exact workload (H200): context, not a target
         "vs_baseline": value / (T / (PAGE_H200_MS / 1e3)),
         "dtype": "bf16",
         "data": "synthetic (seeded; q,k L2-normalised N(0,1), v N(0,1), g=-softplus(N(-3,1)), "
@@ -308,27 +297,33 @@ def main():
                    "head_dim": D, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "mfma_frac": flops_launch / (ms / 1e3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                     "mfma_frac": flops_launch / (r["mean_ms"] / 1e3) / 1e12
+                     / BF16_MFMA_PEAK_TFLOPS,
                      "bytes_per_launch": bytes_launch, "flops_per_launch": flops_launch},
-        "timing": dict(results[head], host_call_us=host_us,
-                       tokens_per_s_median=T / (results[head]["median_ms"] / 1e3)),
+        "timing": dict(r, host_call_us=host_us),
+        "context": {"page_h200_ms": PAGE_H200_MS,
+                    "note": "the pages' FlashQLA time for this workload on an H200 (other "
+                            "hardware, other kernels): context, not a baseline"},
     }
-    line["roofline"].update(fractions(results[head]["median_ms"], bytes_launch, flops_launch,
-                                      peaks))
+    line["roofline"].update(fractions(ms, bytes_launch, flops_launch, peaks))
     if peaks is not None:
         line["measured_peaks"] = peaks
     for m in modes[1:]:
-        r = results[m]
-        line[f"{m}_mode"] = {"ms_per_step": r["mean_ms"], "value": T / (r["mean_ms"] / 1e3),
-                             "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
-                             / HBM_PEAK_GBS, "timing": r,
-                             **fractions(r["median_ms"], bytes_launch, flops_launch, peaks)}
+        rm = results[m]
+        line[f"{m}_mode"] = {"ms_per_step": rm["median_ms"],
+                             "value": T / (rm["median_ms"] / 1e3),
+                             "roofline_frac": bytes_launch / (rm["mean_ms"] / 1e3) / 1e9
+                             / HBM_PEAK_GBS, "timing": rm,
+                             **fractions(rm["median_ms"], bytes_launch, flops_launch, peaks)}
     if not args.no_l2norm:
-        r = time_steps(gdn, torch, sets, head, args.steps, args.warmup, qk_l2norm=True)
-        line["qk_l2norm"] = {"mode": head, "ms_per_step": r["mean_ms"],
-                             "value": T / (r["mean_ms"] / 1e3),
-                             "roofline_frac": bytes_launch / (r["mean_ms"] / 1e3) / 1e9
-                             / HBM_PEAK_GBS, "timing": r}
+        rn = time_steps(gdn, torch, sets, head, args.steps, args.warmup, qk_l2norm=True)
+        line["qk_l2norm"] = {"mode": head, "ms_per_step": rn["median_ms"],
+                             "value": T / (rn["median_ms"] / 1e3),
+                             "roofline_frac": bytes_launch / (rn["mean_ms"] / 1e3) / 1e9
+                             / HBM_PEAK_GBS, "timing": rn}
+    del sets, base
+    if not args.no_workloads:
+        line["workloads"] = time_workloads(gdn, torch, args.steps, args.warmup)
     if not args.no_backward:
         line["backward"] = time_backward(gdn, torch, args.steps, args.warmup,
                                          with_l2norm=not args.no_l2norm)
@@ -337,6 +332,85 @@ def main():
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
     return 0
+
+
+def synth(torch, lengths, H, D, seed, sets=1):
+    """Seeded synthetic inputs drawn on the GPU with the recipe of gdn_inputs.py (q, k rows
+    L2-normalised N(0, 1), v ~ N(0, 1), g = -softplus(N(-3, 1)) fp32, beta = sigmoid(N(0, 1)),
+    bf16), ``sets`` independent draws over the same documents: timing inputs only (the parity
+    tests draw theirs with numpy)."""
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    T = int(sum(lengths))
+    cu = torch.tensor(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32), device="cuda")
+    out = []
+    for _ in range(sets):
+        q = torch.nn.functional.normalize(torch.randn(T, H, D, device="cuda", generator=gen), dim=-1)
+        k = torch.nn.functional.normalize(torch.randn(T, H, D, device="cuda", generator=gen), dim=-1)
+        v = torch.randn(T, H, D, device="cuda", generator=gen)
+        g = -torch.nn.functional.softplus(torch.randn(T, H, device="cuda", generator=gen) - 3.0)
+        beta = torch.sigmoid(torch.randn(T, H, device="cuda", generator=gen))
+        out.append({"q": q.to(torch.bfloat16), "k": k.to(torch.bfloat16),
+                    "v": v.to(torch.bfloat16), "g": g.contiguous(),
+                    "beta": beta.to(torch.bfloat16), "cu_seqlens": cu})
+    return out
+
+
+def time_workloads(gdn, torch, steps, warmup):
+    """The exact forward on the pages' other workloads, timed like the headline (windows of
+    back-to-back calls; tokens/s at the median; the HBM roofline fraction on the algorithmic
+    bytes at the average launch time).  Algorithmic bytes: 1030 B per (token, head), plus 64 KiB
+    per (sequence, head) for the final state and again for an initial state.  Input sets rotate
+    where one set would fit in the 256 MB last-level cache."""
+    from gdn_inputs import workload_shape
+
+    res = {}
+
+    def one(name, desc, lengths, H, sets, h0=None):
+        N = len(lengths)
+        T = int(sum(lengths))
+        outs = [(torch.empty_like(s["v"]), torch.empty((N, H, 128, 128), device="cuda"))
+                for s in sets]
+        cu_host = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+
+        def step(i):
+            s = sets[i % len(sets)]
+            o, ht = outs[i % len(sets)]
+            gdn.chunk_fwd(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"], h0,
+                          mode="exact", cu_seqlens_host=cu_host, out=o, final_state=ht)
+
+        r = timed(torch, step, steps, warmup)
+        nbytes = BYTES_PER_TH * T * H + STATE_BYTES * H * N * (2 if h0 is not None else 1)
+        nflops = FLOP_PER_TH * T * H
+        res[name] = {"workload": desc, "mode": "exact", "tokens": T, "documents": N, "heads": H,
+                     "input_sets": len(sets), "ms_per_step": r["median_ms"],
+                     "tokens_per_s": T / (r["median_ms"] / 1e3),
+                     "roofline": {"bound": "hbm", "bytes_per_launch": nbytes,
+                                  "achieved_GBps": nbytes / (r["mean_ms"] / 1e3) / 1e9,
+                                  "frac": nbytes / (r["mean_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                                  "mfma_frac": nflops / (r["mean_ms"] / 1e3) / 1e12
+                                  / BF16_MFMA_PEAK_TFLOPS},
+                     "timing": r}
+        return outs[0]
+
+    w = workload_shape("packed")
+    sets = synth(torch, w["lengths"], w["H"], w["d"], 11, sets=4)
+    one("packed_8k", "8192 tokens packed from U{256..2048}-token documents, H=8, d=128, bf16 "
+        "(4 input sets rotated: one set is 72 MB)", w["lengths"], w["H"], sets)
+    w = workload_shape("train")
+    sets = synth(torch, w["lengths"], w["H"], w["d"], 12)
+    one("train_65k_forward", "65536 tokens packed from U{4096..16384}-token documents, H=8, "
+        "d=128, bf16 (the training batch's forward)", w["lengths"], w["H"], sets)
+    w = workload_shape("fork")
+    pre = synth(torch, [w["prefix_len"]], w["H"], w["d"], 13)
+    _, ht = one("fork_prefix_64k", "fork prefix: 1 x 65536 tokens, H=16, d=128, bf16",
+                [w["prefix_len"]], w["H"], pre)
+    del pre
+    shared = ht[0].contiguous()
+    br = synth(torch, w["lengths"], w["H"], w["d"], 14)
+    one("fork_branches", f"fork branches: {len(w['lengths'])} documents of U{{1024..4096}} "
+        f"tokens ({sum(w['lengths'])} in all) packed, every one starting from the prefix's "
+        "final state (broadcast), H=16, d=128, bf16", w["lengths"], w["H"], br, h0=shared)
+    return res
 
 
 def fractions(median_ms, nbytes, nflops, peaks):
@@ -357,29 +431,38 @@ def fractions(median_ms, nbytes, nflops, peaks):
     return out
 
 
-def time_decode(gdn, torch, steps, warmup):
+def time_decode(gdn, torch, steps, warmup, sets=3):
     """One decode step (gdn_decode_step) on the fork workload's serving shape: 80 sequences x
-    16 heads, d = 128, bf16 inputs, fp32 states updated in place.  Algorithmic bytes per step:
-    every state read and written once (2 x 64 KiB), q, k, v, o in bf16, g fp32, beta bf16."""
+    16 heads, d = 128, bf16 inputs, fp32 states updated in place.  ``sets`` independent state
+    sets (168 MB each) rotate between steps, so the working set (504 MB for three) exceeds the
+    256 MB last-level cache and each step reads its states from HBM.  Algorithmic bytes per
+    step: every state read and written once (2 x 64 KiB), q, k, v, o in bf16, g fp32, beta
+    bf16."""
     B, H, D = 80, 16, 128
     gen = torch.Generator(device="cuda").manual_seed(7)
-    q = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen), dim=-1)
-    k = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen), dim=-1)
-    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
-    v = torch.randn(B, H, D, device="cuda", generator=gen).to(torch.bfloat16)
-    g = -torch.nn.functional.softplus(torch.randn(B, H, device="cuda", generator=gen) - 3.0)
-    beta = torch.sigmoid(torch.randn(B, H, device="cuda", generator=gen)).to(torch.bfloat16)
-    state = 0.1 * torch.randn(B, H, D, D, device="cuda", generator=gen)
-    out = torch.empty_like(v)
+    data = []
+    for _ in range(sets):
+        q = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen),
+                                          dim=-1).to(torch.bfloat16)
+        k = torch.nn.functional.normalize(torch.randn(B, H, D, device="cuda", generator=gen),
+                                          dim=-1).to(torch.bfloat16)
+        v = torch.randn(B, H, D, device="cuda", generator=gen).to(torch.bfloat16)
+        g = -torch.nn.functional.softplus(torch.randn(B, H, device="cuda", generator=gen) - 3.0)
+        beta = torch.sigmoid(torch.randn(B, H, device="cuda", generator=gen)).to(torch.bfloat16)
+        state = 0.1 * torch.randn(B, H, D, D, device="cuda", generator=gen)
+        data.append((q, k, v, g, beta, state, torch.empty_like(v)))
 
-    r = timed(torch, lambda i: gdn.decode_step(q, k, v, g, beta, state, out=out), steps, warmup)
-    ms = r["mean_ms"]
+    def step(i):
+        q, k, v, g, beta, state, out = data[i % sets]
+        gdn.decode_step(q, k, v, g, beta, state, out=out)
+
+    r = timed(torch, step, steps, warmup)
     nbytes = B * H * (2 * D * D * 4 + 4 * D * 2 + 4 + 2)
-    achieved = nbytes / (ms / 1e3) / 1e9
-    return {"workload": f"{B} sequences x {H} heads, d_k=d_v={D}, bf16 inputs, fp32 state",
-            "us_per_step": ms * 1e3, "tokens_per_s": B / (ms / 1e3),
-            "median_us": r["median_ms"] * 1e3, "p10_us": r["p10_ms"] * 1e3,
-            "p90_us": r["p90_ms"] * 1e3,
+    achieved = nbytes / (r["mean_ms"] / 1e3) / 1e9
+    return {"workload": f"{B} sequences x {H} heads, d_k=d_v={D}, bf16 inputs, fp32 state "
+                        f"({sets} state sets rotated, {sets * B * H * D * D * 4 / 1e6:.0f} MB)",
+            "us_per_step": r["median_ms"] * 1e3, "tokens_per_s": B / (r["median_ms"] / 1e3),
+            "timing": r,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes}}
@@ -413,7 +496,7 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
         gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws)
 
     r = timed(torch, step, steps, warmup)
-    ms = r["mean_ms"]
+    ms = r["median_ms"]
     rn = None
     if with_l2norm:  # the same backward with q and k normalised inside the kernels
         pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact",
@@ -425,7 +508,7 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
                                                   cu, dev["dout"], workspace=wsn, qk_l2norm=True),
                    steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
-    achieved = nbytes_alg / (ms / 1e3) / 1e9
+    achieved = nbytes_alg / (r["mean_ms"] / 1e3) / 1e9
     traffic = None  # measured HBM bytes per call (rocprofv3), while the kernels are unchanged
     if os.path.exists(BWD_TRAFFIC_FILE):
         with open(BWD_TRAFFIC_FILE) as f:
@@ -435,7 +518,7 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
     return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
                         f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
             "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
-            "qk_l2norm_ms_per_step": rn["mean_ms"] if rn else None,
+            "qk_l2norm_ms_per_step": rn["median_ms"] if rn else None,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
                          "bytes_per_step": nbytes_alg, "traffic": traffic}}

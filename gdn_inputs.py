@@ -30,11 +30,17 @@ WORKLOAD_SEEDS = {"tiny": 1000, "packed": 1001, "long": 1002, "fork": 1003, "tra
 
 
 def bf16_round(x) -> np.ndarray:
-    """Round to the nearest bfloat16 (ties to even); returns float32 holding bf16 values."""
+    """Round to the nearest bfloat16 (ties to even); returns float32 holding bf16 values.
+
+    Works on the uint32 bit patterns in place: adding 0x7FFF plus the kept part's lowest bit
+    cannot carry out of 32 bits for finite values or infinities (the generated inputs are
+    finite)."""
     x32 = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    b = x32.view(np.uint32).astype(np.uint64)
-    lsb = (b >> 16) & 1
-    r = ((b + 0x7FFF + lsb) & 0xFFFF0000).astype(np.uint32)
+    b = x32.view(np.uint32)
+    r = (b >> 16) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += b
+    r &= np.uint32(0xFFFF0000)
     return r.view(np.float32).reshape(x32.shape)
 
 
@@ -114,32 +120,38 @@ def scale_qk_rows(inp, seed, lo=0.3, hi=3.0):
     return out
 
 
-def workload(name: str, **overrides):
-    """Inputs of one named workload (see the module docstring)."""
+def workload_shape(name: str):
+    """Document lengths and sizes of one named workload, without drawing any values: the same
+    lengths :func:`workload` uses.  Returns dict(lengths, H, d, dtype) and, for ``fork``,
+    prefix_len (the branches' lengths are ``lengths``)."""
     seed = WORKLOAD_SEEDS[name]
     rng = np.random.Generator(np.random.PCG64(seed + 7919))
     if name == "tiny":
-        spec = dict(lengths=[256], H=2, dk=64, dv=64, dtype="f32")
-    elif name == "packed":
-        spec = dict(lengths=lengths_until(rng, 256, 2048, 8192), H=8, dk=128, dv=128,
-                    dtype="bf16")
-    elif name == "long":
-        spec = dict(lengths=[32768], H=8, dk=128, dv=128, dtype="bf16")
-    elif name == "fork":
-        branches = [int(rng.integers(1024, 4097)) for _ in range(80)]
-        spec = dict(lengths=branches, H=16, dk=128, dv=128, dtype="bf16")
-        spec["prefix_len"] = 65536
-    elif name == "train":
-        spec = dict(lengths=lengths_until(rng, 4096, 16384, 65536), H=8, dk=128, dv=128,
-                    dtype="bf16", with_dout=True)
-    else:
-        raise KeyError(name)
+        return dict(lengths=[256], H=2, d=64, dtype="f32")
+    if name == "packed":
+        return dict(lengths=lengths_until(rng, 256, 2048, 8192), H=8, d=128, dtype="bf16")
+    if name == "long":
+        return dict(lengths=[32768], H=8, d=128, dtype="bf16")
+    if name == "fork":
+        return dict(lengths=[int(rng.integers(1024, 4097)) for _ in range(80)], H=16, d=128,
+                    dtype="bf16", prefix_len=65536)
+    if name == "train":
+        return dict(lengths=lengths_until(rng, 4096, 16384, 65536), H=8, d=128, dtype="bf16")
+    raise KeyError(name)
+
+
+def workload(name: str, **overrides):
+    """Inputs of one named workload (see the module docstring)."""
+    seed = WORKLOAD_SEEDS[name]
+    sh = workload_shape(name)
+    spec = dict(lengths=sh["lengths"], H=sh["H"], dk=sh["d"], dv=sh["d"], dtype=sh["dtype"])
+    if name == "train":
+        spec["with_dout"] = True
     spec.update(overrides)
-    prefix_len = spec.pop("prefix_len", None)
-    if prefix_len is not None:
+    if name == "fork":
         # the prefix and the branches are drawn as two documents sets with related seeds
-        prefix = make_inputs([prefix_len], spec["H"], spec["dk"], spec["dv"], spec["dtype"],
-                             seed)
+        prefix = make_inputs([sh["prefix_len"]], spec["H"], spec["dk"], spec["dv"],
+                             spec["dtype"], seed)
         branches = make_inputs(spec["lengths"], spec["H"], spec["dk"], spec["dv"],
                                spec["dtype"], seed + 1)
         return dict(prefix=prefix, branches=branches)

@@ -32,12 +32,21 @@
  *   Asynchrony: calls enqueue work on `stream` and return without a host synchronisation.
  *   Errors: arguments are validated before anything is enqueued; on an error nothing is written.
  *     A launch failure returns GDN_ERR_HIP.  gdn_last_error() gives a thread-local detail string.
- *     The contents of cu_seqlens are read on the device only: sequences must be as described
- *     above (not checked on the host).
+ *     The contents of cu_seqlens are read on the device only (the host checks
+ *     cu_seqlens_host when it is given).  On a malformed device table (cu[0] != 0, a descending
+ *     pair, or an offset past T) the kernels find no work for the sequences from the first bad
+ *     entry on and write nothing for them, so no access leaves the caller's buffers; the
+ *     outputs of such a call are undefined.  gdn_validate_cu_seqlens checks a table on the
+ *     device, and the debug mode (GDN_DEBUG=1 in the environment, or gdn_set_debug(1)) runs
+ *     that check inside every compute call before its first launch, returning
+ *     GDN_ERR_BAD_SHAPE with nothing launched, and after the launches synchronises the stream
+ *     and returns GDN_ERR_DEVICE_CHECK if a kernel set a fault flag (gdn_device_faults).
  *   Architecture: only gfx950 is supported; other devices return GDN_ERR_UNSUPPORTED_ARCH (the
  *     page's library likewise refuses hardware it was not built for, section "Using it, and the
  *     fine print").
- *   Threading: calls are re-entrant; the only global state is a per-device properties cache.
+ *   Threading: calls are re-entrant.  Global state: a per-device properties cache, the debug
+ *     switch, and per device four words of device memory (the debug mode's validation status and
+ *     the fault flags kernels set; a static device array, not an allocation).
  */
 #ifndef GDN_H_
 #define GDN_H_
@@ -60,7 +69,8 @@ typedef enum gdn_status {
   GDN_ERR_UNSUPPORTED_ARCH = 5,    /* the current device is not gfx950 */
   GDN_ERR_WORKSPACE_TOO_SMALL = 6, /* workspace_bytes below the *_workspace_size figure */
   GDN_ERR_BAD_ALIGNMENT = 7,       /* a tensor pointer is not 16-byte aligned */
-  GDN_ERR_HIP = 8                  /* a HIP runtime call or kernel launch failed */
+  GDN_ERR_HIP = 8,                 /* a HIP runtime call or kernel launch failed */
+  GDN_ERR_DEVICE_CHECK = 9         /* debug mode: a kernel set a fault flag (gdn_device_faults) */
 } gdn_status;
 
 /* Element type of q, k, v, beta, o (and of dout, dq, dk, dv, dbeta in the backward). */
@@ -119,14 +129,20 @@ typedef struct gdn_problem {
 } gdn_problem;
 
 /* Fills *p with defaults: chunk 64, dtype bf16, exact mode, threshold -10, scale 1, and the
- * given sizes. */
+ * given sizes.  The defaults follow "How to Speed Up GDN Kernels for Qwen Models": 64-token
+ * chunks and head size 128 (section "Using it, and the fine print"), the e^-10 truncation
+ * threshold (section "Lever 1"); the scale of 1 is the recurrence as written (section "What
+ * GDN actually computes").  No allocation; returns GDN_ERR_NULL_ARG for a NULL p. */
 gdn_status gdn_problem_init(gdn_problem *p, int64_t total_tokens, int32_t num_seqs,
                             int32_t num_heads, int32_t head_dim);
 
 /* Bytes of device workspace gdn_chunk_fwd needs for *p (zero except for the exact mode's
  * split).  cu_seqlens_host (optional, N + 1 host int32) lets a split mode size its segment plan
  * exactly (without it the unit count is an upper bound); pass the same pointer (or NULL) to
- * gdn_chunk_fwd. */
+ * gdn_chunk_fwd.  The operation is the forward described at the top of this file; the page
+ * names no workspace (its kernels are separate launches, "How to Speed Up GDN Kernels for Qwen
+ * Models", section "Lever 1"), so no passage applies to the figure itself.  Host only; the
+ * latency model may query the current device (num_slots = 0). */
 gdn_status gdn_chunk_fwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
                                         size_t *bytes);
 
@@ -167,7 +183,13 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
                                        float *hc, float *delta, void *workspace,
                                        size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of device workspace gdn_chunk_bwd needs for *p. */
+/* Bytes of device workspace gdn_chunk_bwd needs for *p: the recomputed per-chunk
+ * intermediates ("How to Speed Up GDN Kernels for Qwen Models", section "Lever 2": the hidden
+ * states are recomputed in one pass, not stored by the forward) and the reverse chain's
+ * per-chunk state gradients.  Sized on the chunk bound ceil(T / 64) + N rather than on a host
+ * copy of cu_seqlens: the bound exceeds the exact chunk count by fewer than N chunks, and it
+ * covers every chunk index a device table can produce, so the kernels' writes stay inside the
+ * workspace whatever the device table holds.  Host only. */
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes);
 
 /* Backward of the exact forward (mode must be GDN_MODE_EXACT): given dout (dtype, [T, H, d_v])
@@ -202,10 +224,38 @@ gdn_status gdn_decode_step(int32_t batch, int32_t num_heads, int32_t num_k_heads
                            const void *k, const void *v, const float *g, const void *beta,
                            float *state, void *o, hipStream_t stream);
 
-/* Static description of a status code. */
+/* Checks a cu_seqlens table on the device ("Step 10 · Making it fast": packed documents whose
+ * boundaries are wrong leak into each other; "How to Speed Up GDN Kernels for Qwen Models",
+ * section "Using it, and the fine print": misuse is refused).  Reads cu_seqlens[0..num_seqs]
+ * (device int32) and writes to *status (device int32, caller-owned) 0 when the table is valid,
+ * else a bit mask: 1 cu[0] != 0, 2 a descending pair, 4 cu[N] != total_tokens, 8 an offset
+ * outside [0, total_tokens].  Asynchronous on `stream`; read *status after the stream's work.
+ * Validates num_seqs >= 1, total_tokens in [0, 2^31) and the pointers before launching. */
+gdn_status gdn_validate_cu_seqlens(const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t *status, hipStream_t stream);
+
+/* Debug mode on (1) or off (0) for the whole process; its initial value comes from the
+ * environment variable GDN_DEBUG (unset or "0": off).  In debug mode gdn_chunk_fwd,
+ * gdn_chunk_fwd_intermediates, gdn_chunk_fwd_plan and gdn_chunk_bwd validate cu_seqlens on the
+ * device before their first launch and synchronise the stream (so they are not asynchronous,
+ * and calls that overlap on one device share its check words).  No passage applies: a
+ * diagnostic of this library. */
+gdn_status gdn_set_debug(int32_t on);
+int32_t gdn_get_debug(void);
+
+/* The current device's fault flags: bit 1 means a forward launch's bounded wait between its
+ * waves ran out (its results are not to be trusted).  Synchronises the device, then copies the
+ * flags to *flags (host) and clears them when clear != 0.  No passage applies: a diagnostic of
+ * this library's kernels. */
+gdn_status gdn_device_faults(uint32_t *flags, int32_t clear);
+
+/* Static description of a status code.  No passage applies (error reporting of this library;
+ * the page's library "raises" on what it cannot run, "How to Speed Up GDN Kernels for Qwen
+ * Models", section "Using it, and the fine print"). */
 const char *gdn_status_string(gdn_status s);
 
-/* Detail of the last error on the calling thread (empty string if none). */
+/* Detail of the last error on the calling thread (empty string if none).  No passage applies,
+ * as for gdn_status_string. */
 const char *gdn_last_error(void);
 
 #ifdef __cplusplus

@@ -2,7 +2,9 @@
 // plan's host-side parameters and kernel dispatch.  Declarations and conventions: include/gdn.h.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
+#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -29,6 +31,64 @@ gdn_status fail(gdn_status s, const char *fmt, ...) {
 
 gdn_status hip_fail(hipError_t e, const char *what) {
   return fail(GDN_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Debug mode (GDN_DEBUG=1 in the environment, or gdn_set_debug): every compute call first
+// validates cu_seqlens on the device and returns GDN_ERR_BAD_SHAPE before any compute launch if
+// it is malformed, and after its launches synchronises the stream and returns
+// GDN_ERR_DEVICE_CHECK if a kernel set a fault flag.
+std::atomic<int> g_debug{-1};
+
+bool debug_on() {
+  int d = g_debug.load(std::memory_order_relaxed);
+  if (d < 0) {
+    const char *e = std::getenv("GDN_DEBUG");
+    d = (e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0) ? 1 : 0;
+    int expected = -1;
+    g_debug.compare_exchange_strong(expected, d);
+    d = g_debug.load(std::memory_order_relaxed);
+  }
+  return d == 1;
+}
+
+gdn_status debug_validate(const int32_t *cu, int32_t N, int64_t T, hipStream_t stream) {
+  uint32_t *words = nullptr;
+  hipError_t e = gdn::device_check_words(&words);
+  if (e != hipSuccess) return hip_fail(e, "debug mode: check words");
+  e = gdn::launch_validate_cu(cu, N, T, reinterpret_cast<int32_t *>(words), words + 1, stream);
+  if (e != hipSuccess) return hip_fail(e, "debug mode: cu_seqlens validation launch");
+  uint32_t status = 0;
+  e = hipMemcpyAsync(&status, words, sizeof(status), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "debug mode: cu_seqlens validation");
+  if (status != 0)
+    return fail(GDN_ERR_BAD_SHAPE,
+                "cu_seqlens on the device is malformed (flags 0x%x:%s%s%s%s); nothing launched",
+                status, (status & gdn::kCuFirstNotZero) ? " cu[0] != 0" : "",
+                (status & gdn::kCuDescending) ? " descending offsets" : "",
+                (status & gdn::kCuLastNotTotal) ? " cu[N] != total_tokens" : "",
+                (status & gdn::kCuOutOfRange) ? " offsets outside [0, total_tokens]" : "");
+  return GDN_OK;
+}
+
+gdn_status debug_faults(hipStream_t stream) {
+  uint32_t *words = nullptr;
+  hipError_t e = gdn::device_check_words(&words);
+  if (e != hipSuccess) return hip_fail(e, "debug mode: check words");
+  uint32_t flags = 0;
+  e = hipMemcpyAsync(&flags, words + 1, sizeof(flags), hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) return hip_fail(e, "debug mode: fault flags");
+  if (flags != 0)
+    return fail(GDN_ERR_DEVICE_CHECK, "a kernel set fault flags 0x%x%s", flags,
+                (flags & gdn::kFaultDiagWait) ? " (the forward's wait for its diagonal blocks "
+                                                "ran out)" : "");
+  return GDN_OK;
+}
+
+uint32_t *fault_word() {
+  uint32_t *words = nullptr;
+  return gdn::device_check_words(&words) == hipSuccess ? words + 1 : nullptr;
 }
 
 // Per-device properties cache: is the device gfx950, and its CU count.
@@ -243,6 +303,9 @@ gdn_status check_tensors(const Tensors &t, int64_t T) {
   return GDN_OK;
 }
 
+gdn_status launch_fwd_passes(const gdn_problem *p, const Tensors &t, const FwdLayout &lay,
+                             bool dump, float *dbg[6], void *ws, hipStream_t stream);
+
 gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_host, bool dump,
                    float *dbg[6], void *ws, size_t ws_bytes, hipStream_t stream) {
   gdn_status s = check_problem(p);
@@ -265,6 +328,18 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   if (ws_bytes < lay.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
   if (lay.total > 0 && !aligned16(ws)) return fail(GDN_ERR_BAD_ALIGNMENT, "workspace alignment");
+  if (debug_on()) {
+    s = debug_validate(t.cu, p->num_seqs, p->total_tokens, stream);
+    if (s != GDN_OK) return s;
+    s = launch_fwd_passes(p, t, lay, dump, dbg, ws, stream);
+    return s != GDN_OK ? s : debug_faults(stream);
+  }
+  return launch_fwd_passes(p, t, lay, dump, dbg, ws, stream);
+}
+
+// The forward's launches for a checked problem: one kernel, or the exact split's three passes.
+gdn_status launch_fwd_passes(const gdn_problem *p, const Tensors &t, const FwdLayout &lay,
+                             bool dump, float *dbg[6], void *ws, hipStream_t stream) {
   gdn::FwdArgs a{};
   a.q = t.q;
   a.k = t.k;
@@ -293,6 +368,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
   a.log_thr = p->trunc_log_threshold;
   a.truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
   a.l2norm = p->qk_l2norm;
+  a.faults = fault_word();
   hipError_t e;
   if (lay.split) {
     char *base = static_cast<char *>(ws);
@@ -304,6 +380,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
     if (e != hipSuccess) return hip_fail(e, "exact split: first pass");
     gdn::SplitArgs sa{};
     sa.cu = t.cu;
+    sa.T = p->total_tokens;
     sa.N = p->num_seqs;
     sa.H = p->num_heads;
     sa.L = lay.L;
@@ -405,10 +482,14 @@ gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
   (void)workspace;
   if (plan_capacity < 2) return fail(GDN_ERR_BAD_SHAPE, "plan_capacity must be >= 2");
+  if (debug_on()) {
+    s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, stream);
+    if (s != GDN_OK) return s;
+  }
   const int truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
-  hipError_t e = gdn::launch_plan_export(cu_seqlens, p->num_seqs, g, p->num_heads, lay.L,
-                                         p->trunc_log_threshold, truncate, lay.units, plan_out,
-                                         plan_capacity, stream);
+  hipError_t e = gdn::launch_plan_export(cu_seqlens, p->num_seqs, p->total_tokens, g,
+                                         p->num_heads, lay.L, p->trunc_log_threshold, truncate,
+                                         lay.units, plan_out, plan_capacity, stream);
   if (e != hipSuccess) return hip_fail(e, "plan export launch");
   return GDN_OK;
 }
@@ -517,6 +598,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
   a.log_thr = p->trunc_log_threshold;
   a.truncate = 0;
   a.l2norm = p->qk_l2norm;
+  a.faults = fault_word();
   hipError_t e;
   int64_t units = p->num_seqs;
   if (L.L > 0) {
@@ -529,6 +611,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
     if (e != hipSuccess) return hip_fail(e, "backward recompute: first pass");
     gdn::SplitArgs sa{};
     sa.cu = t.cu;
+    sa.T = p->total_tokens;
     sa.N = p->num_seqs;
     sa.H = p->num_heads;
     sa.L = L.L;
@@ -599,6 +682,13 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   if (!workspace) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
   if (workspace_bytes < L.total)
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", L.total);
+  if (!cu_seqlens) return fail(GDN_ERR_NULL_ARG, "cu_seqlens is required");
+  const bool debug = debug_on();
+  if (debug) {
+    s = device_info(nullptr);
+    if (s == GDN_OK) s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, stream);
+    if (s != GDN_OK) return s;
+  }
   char *base = static_cast<char *>(workspace);
   float *gamma = reinterpret_cast<float *>(base + L.gamma);
   float *tmat = reinterpret_cast<float *>(base + L.tmat);
@@ -679,6 +769,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
       if (e != hipSuccess) return hip_fail(e, "backward chain: first pass");
       gdn::SplitArgs sa{};
       sa.cu = cu_seqlens;
+      sa.T = p->total_tokens;
       sa.N = p->num_seqs;
       sa.H = p->num_heads;
       sa.L = L.L;
@@ -722,7 +813,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     e = gdn::launch_sum_dh0(b.dh0_seq, p->num_seqs, p->num_heads, p->d_k, dh0, stream);
     if (e != hipSuccess) return hip_fail(e, "dh0 reduction launch");
   }
-  return GDN_OK;
+  return debug ? debug_faults(stream) : GDN_OK;
 }
 
 }  // extern "C"
@@ -792,6 +883,45 @@ gdn_status gdn_calib_mfma_bf16(float *out, int waves_per_cu, int iters, hipStrea
   return GDN_OK;
 }
 
+gdn_status gdn_validate_cu_seqlens(const int32_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t *status, hipStream_t stream) {
+  if (!cu_seqlens || !status) return fail(GDN_ERR_NULL_ARG, "cu_seqlens and status are required");
+  if (num_seqs < 1) return fail(GDN_ERR_BAD_SHAPE, "num_seqs must be >= 1");
+  if (total_tokens < 0 || total_tokens > INT32_MAX)
+    return fail(GDN_ERR_BAD_SHAPE, "total_tokens %lld out of range", (long long)total_tokens);
+  gdn_status s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  const hipError_t e = gdn::launch_validate_cu(cu_seqlens, num_seqs, total_tokens, status,
+                                               nullptr, stream);
+  if (e != hipSuccess) return hip_fail(e, "cu_seqlens validation launch");
+  return GDN_OK;
+}
+
+gdn_status gdn_set_debug(int32_t on) {
+  if (on != 0 && on != 1) return fail(GDN_ERR_BAD_MODE, "on must be 0 or 1");
+  g_debug.store(on, std::memory_order_relaxed);
+  return GDN_OK;
+}
+
+int32_t gdn_get_debug(void) { return debug_on() ? 1 : 0; }
+
+gdn_status gdn_device_faults(uint32_t *flags, int32_t clear) {
+  if (!flags) return fail(GDN_ERR_NULL_ARG, "flags is NULL");
+  gdn_status s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  uint32_t *words = nullptr;
+  hipError_t e = gdn::device_check_words(&words);
+  if (e != hipSuccess) return hip_fail(e, "check words");
+  e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(flags, words + 1, sizeof(uint32_t), hipMemcpyDeviceToHost);
+  if (e == hipSuccess && clear) {
+    const uint32_t zero = 0;
+    e = hipMemcpy(words + 1, &zero, sizeof(zero), hipMemcpyHostToDevice);
+  }
+  if (e != hipSuccess) return hip_fail(e, "fault flags");
+  return GDN_OK;
+}
+
 const char *gdn_status_string(gdn_status s) {
   switch (s) {
     case GDN_OK: return "ok";
@@ -803,6 +933,7 @@ const char *gdn_status_string(gdn_status s) {
     case GDN_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case GDN_ERR_BAD_ALIGNMENT: return "tensor pointer not 16-byte aligned";
     case GDN_ERR_HIP: return "HIP runtime error";
+    case GDN_ERR_DEVICE_CHECK: return "a device-side check failed";
   }
   return "unknown status";
 }

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void bwd_chain_kernel(BwdArgs b) {
   const int seq = blockIdx.x, h = blockIdx.y, H = b.H, hk = h / (H / b.HK);
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(b.cu, b.N, 0, seq, true, lane, un);
+    const bool ok = find_unit(b.cu, b.N, b.T, 0, seq, true, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? (int)un.chunk_base : -1;
       sm.imisc[1] = un.c1;

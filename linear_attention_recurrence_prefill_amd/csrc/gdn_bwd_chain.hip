@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M' half
   if (w == 0) {
     Unit un;
-    const bool ok = find_unit(b.cu, b.N, us.L, unit, true, lane, un);
+    const bool ok = find_unit(b.cu, b.N, b.T, us.L, unit, true, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;

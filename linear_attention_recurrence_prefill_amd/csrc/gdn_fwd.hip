@@ -40,16 +40,17 @@ namespace gdn {
 // still gets one (empty) unit so that its final state is written.
 
 __global__ __launch_bounds__(64) void plan_export_kernel(const int32_t *__restrict__ cu, int N,
-                                                         const float *__restrict__ g, int H,
+                                                         int64_t T, const float *__restrict__ g,
+                                                         int H,
                                                          int L, float thr, int truncate,
                                                          int32_t *__restrict__ out,
                                                          int64_t capacity) {
   const int u = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
   Unit un;
-  const bool ok = find_unit(cu, N, L, u, false, lane, un);
+  const bool ok = find_unit(cu, N, T, L, u, false, lane, un);
   // the last workgroup that finds a unit also writes the header
   Unit nx;
-  const bool next = find_unit(cu, N, L, u + 1, false, lane, nx);
+  const bool next = find_unit(cu, N, T, L, u + 1, false, lane, nx);
   if (ok && !next && h == 0 && lane == 0 && capacity >= 2) {
     out[0] = u + 1;
     out[1] = L;
@@ -69,11 +70,11 @@ __global__ __launch_bounds__(64) void plan_export_kernel(const int32_t *__restri
   }
 }
 
-hipError_t launch_plan_export(const int32_t *cu, int32_t N, const float *g, int32_t H,
+hipError_t launch_plan_export(const int32_t *cu, int32_t N, int64_t T, const float *g, int32_t H,
                               int32_t L, float log_thr, int32_t truncate, int64_t max_units,
                               int32_t *out, int64_t capacity, hipStream_t stream) {
   hipLaunchKernelGGL(plan_export_kernel, dim3((unsigned)max_units, H), dim3(64), 0, stream, cu,
-                     N, g, H, L, log_thr, truncate, out, capacity);
+                     N, T, g, H, L, log_thr, truncate, out, capacity);
   return hipGetLastError();
 }
 
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
   const int unit = blockIdx.x, h = blockIdx.y, H = a.H;
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(a.cu, a.N, a.L, unit, DUMP, lane, un);
+    const bool ok = find_unit(a.cu, a.N, a.T, a.L, unit, DUMP, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;

@@ -84,7 +84,7 @@ __global__ __launch_bounds__(64 * (D / 16)) void fwd_fast_kernel(FwdArgs a) {
   const int unit = blockIdx.x, h = blockIdx.y, H = a.H;
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(a.cu, a.N, a.L, unit, false, lane, un);
+    const bool ok = find_unit(a.cu, a.N, a.T, a.L, unit, false, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;

@@ -26,22 +26,29 @@ constexpr int kLS = kD + 4;  // fp32 row stride of the transposed column block i
 
 // Units of sequence n for segment length L (max(1, ceil(chunks / L)) each, in sequence order, as
 // the forward's unit lookup numbers them): the first unit's index and the count.  Called by one
-// full wave; every lane returns the same result.
-__device__ void seq_units(const int32_t *cu, int N, int L, int n, int lane, int64_t &first,
-                          int &count) {
+// full wave; every lane returns the same result.  Returns false when cu_seqlens is malformed up to
+// and including sequence n (cu[0] != 0, a descending pair or an offset past T), as the unit
+// lookup of the other passes does.
+__device__ bool seq_units(const int32_t *cu, int N, int64_t T, int L, int n, int lane,
+                          int64_t &first, int &count) {
+  if (cu[0] != 0) return false;
+  auto bad = [&](int m) { return cu[m + 1] < cu[m] || (int64_t)cu[m + 1] > T; };
   auto units_of = [&](int m) {
     const int ch = max(0, (cu[m + 1] - cu[m] + kChunk - 1) / kChunk);
     return max(1, (ch + L - 1) / L);
   };
   int64_t before = 0;
-  for (int base = 0; base < n; base += 64) {
-    int x = base + lane < n ? units_of(base + lane) : 0;
+  for (int base = 0; base <= n; base += 64) {
+    const int m = base + lane;
+    if (__ballot(m <= n && bad(m))) return false;
+    int x = m < n ? units_of(m) : 0;
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off, 64);
     before += x;
   }
   first = before;
   count = units_of(n);
+  return true;
 }
 
 }  // namespace
@@ -56,7 +63,11 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t first = 0;
   int count = 0;
-  seq_units(s.cu, s.N, s.L, n, lane, first, count);
+  if (!seq_units(s.cu, s.N, s.T, s.L, n, lane, first, count)) return;
+  // never past the units the buffers were sized for (a device table that disagrees with the
+  // host copy the caller planned with)
+  if (first >= s.units) return;
+  if (first + count > s.units) count = (int)(s.units - first);
   const int row0 = 16 * w + 4 * gq, col = 16 * cb + cl;  // this lane: rows row0 .. row0 + 3
   const int64_t dd = (int64_t)kD * kD;
 

@@ -187,7 +187,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M half
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(a.cu, a.N, a.L, unit, kDump, lane, un);
+    const bool ok = find_unit(a.cu, a.N, a.T, a.L, unit, kDump, lane, un);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;
@@ -708,11 +708,17 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           // ---- A's diagonal blocks 0 and 1 (wave 7 forms blocks 2 and 3 and publishes them
           //      through sm.ready; the bounded wait cannot hang)
           a_diag(Kt, vc, rn_s[kNorm ? c % 3 : 0][0], 0);
-          for (int it = 0; it < (1 << 22); ++it) {
+          int it = 0;
+          for (; it < (1 << 22); ++it) {
             const int r = __hip_atomic_load(&sm.ready, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
             if (__builtin_amdgcn_readfirstlane(r) >= c + 1) break;
             __builtin_amdgcn_s_sleep(1);
           }
+          // a wait that ran out leaves a flag the host can read (gdn_device_faults); the
+          // results of this launch are then not to be trusted
+          if (it == (1 << 22) && lane == 0 && a.faults != nullptr)
+            __hip_atomic_fetch_or(a.faults, kFaultDiagWait, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
           // ---- the four diagonal inverses by substitution: lane (block gq, column cl)
           {
             const float *ab = &sm.at[gq * AB];

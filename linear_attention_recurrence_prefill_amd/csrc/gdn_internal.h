@@ -10,6 +10,22 @@ constexpr int kChunk = 64;
 // eps of the optional q/k L2 normalisation: row / sqrt(|row|^2 + eps)
 constexpr float kL2NormEps = 1e-6f;
 
+// Status bits of the cu_seqlens validation (gdn_validate_cu_seqlens).
+constexpr uint32_t kCuFirstNotZero = 1u;  // cu[0] != 0
+constexpr uint32_t kCuDescending = 2u;    // cu[n + 1] < cu[n] for some n
+constexpr uint32_t kCuLastNotTotal = 4u;  // cu[N] != T
+constexpr uint32_t kCuOutOfRange = 8u;    // some cu[n + 1] outside [0, T]
+// Fault flags kernels set in the per-device check words (gdn_device_faults).
+constexpr uint32_t kFaultDiagWait = 1u;   // the forward's wait for its diagonal blocks ran out
+
+// The current device's check words ([0] validation status, [1] fault flags), from
+// hipGetSymbolAddress on first use per device.
+hipError_t device_check_words(uint32_t **words);
+// Validates cu [N + 1] against T on the device: writes the status bits to *status (0 = valid),
+// and clears *faults_to_clear when not null.
+hipError_t launch_validate_cu(const int32_t *cu, int32_t N, int64_t T, int32_t *status,
+                              uint32_t *faults_to_clear, hipStream_t stream);
+
 // Arguments of the fused forward kernel.  A "unit" is one (sequence, chunk range) pair: each
 // sequence is one unit (L == 0) or is split into units of L chunks; the kernel runs one
 // workgroup per (unit, head) and finds its unit from cu_seqlens itself.
@@ -36,11 +52,13 @@ struct FwdArgs {
   const float *unit_h0;
   float *unit_out;
   int64_t units;
+  uint32_t *faults;  // the device's fault flags (kFault*), or null
 };
 
 // Arguments of the exact split's middle pass (gdn_fwd_split.hip).
 struct SplitArgs {
   const int32_t *cu;
+  int64_t T;
   int32_t N, H, L;
   const float *h0;
   int64_t h0_stride;
@@ -102,7 +120,7 @@ int fwd_blocks_per_cu(int D, bool bf16);
 int fwd_fast_blocks_per_cu(int D);
 
 // Writes the plan with warmup windows to out (see gdn_chunk_fwd_plan).
-hipError_t launch_plan_export(const int32_t *cu, int32_t N, const float *g, int32_t H,
+hipError_t launch_plan_export(const int32_t *cu, int32_t N, int64_t T, const float *g, int32_t H,
                               int32_t L, float log_thr, int32_t truncate, int64_t max_units,
                               int32_t *out, int64_t capacity, hipStream_t stream);
 

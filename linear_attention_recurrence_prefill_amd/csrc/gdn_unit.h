@@ -7,25 +7,35 @@
 namespace gdn {
 
 // Finds unit u by scanning the sequence table 64 entries at a time.  Called by one full wave;
-// every lane returns the same result.  Returns false when u is past the last unit.
-__device__ inline bool find_unit(const int32_t *cu, int N, int L, int u, bool need_base, int lane,
-                          Unit &out) {
+// every lane returns the same result.  Returns false when u is past the last unit, and also when
+// the scanned part of cu_seqlens is malformed (cu[0] != 0, a descending pair, or an offset past
+// T): then no unit is found, so no workgroup indexes memory from a bad table.  Every sequence
+// before the one returned, and the returned one, have been checked, which bounds the chunk and
+// unit counts before it by the ones the host sized its buffers for.  With L == 0 and no chunk
+// base asked for, unit u is sequence u without a scan; the caller checks its range.
+__device__ inline bool find_unit(const int32_t *cu, int N, int64_t T, int L, int u,
+                                 bool need_base, int lane, Unit &out) {
   if (L == 0 && !need_base) {
     if (u >= N) return false;
     out.seq = u;
     out.c0 = 0;
-    out.c1 = (cu[u + 1] - cu[u] + kChunk - 1) / kChunk;
+    out.c1 = max(0, (cu[u + 1] - cu[u] + kChunk - 1) / kChunk);
     out.chunk_base = 0;
     return true;
   }
+  if (cu[0] != 0) return false;
   int64_t units_before = 0, chunks_before = 0;
   for (int base = 0; base < N; base += 64) {
     const int n = base + lane;
     int ch = 0, un = 0;
+    bool bad = false;
     if (n < N) {
-      ch = max(0, (cu[n + 1] - cu[n] + kChunk - 1) / kChunk);
+      const int a = cu[n], b = cu[n + 1];
+      bad = b < a || (int64_t)b > T;
+      ch = bad ? 0 : (b - a + kChunk - 1) / kChunk;
       un = L > 0 ? max(1, (ch + L - 1) / L) : 1;
     }
+    if (__ballot(bad)) return false;
     int sun = un, sch = ch;  // inclusive scans over the wave
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {

@@ -23,8 +23,12 @@ _MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
 # Every exported entry point of include/gdn.h.
 EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
            "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
-           "gdn_chunk_bwd", "gdn_decode_step", "gdn_status_string", "gdn_last_error",
+           "gdn_chunk_bwd", "gdn_decode_step", "gdn_validate_cu_seqlens", "gdn_set_debug",
+           "gdn_get_debug", "gdn_device_faults", "gdn_status_string", "gdn_last_error",
            "gdn_calib_copy", "gdn_calib_mfma_bf16")
+
+# Status bits of gdn_validate_cu_seqlens.
+CU_FIRST_NOT_ZERO, CU_DESCENDING, CU_LAST_NOT_TOTAL, CU_OUT_OF_RANGE = 1, 2, 4, 8
 
 
 class GdnError(RuntimeError):
@@ -85,6 +89,14 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_calib_copy.restype = st
     lib.gdn_calib_mfma_bf16.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
     lib.gdn_calib_mfma_bf16.restype = st
+    lib.gdn_validate_cu_seqlens.argtypes = [vp, ctypes.c_int32, ctypes.c_int64, vp, vp]
+    lib.gdn_validate_cu_seqlens.restype = st
+    lib.gdn_set_debug.argtypes = [ctypes.c_int32]
+    lib.gdn_set_debug.restype = st
+    lib.gdn_get_debug.argtypes = []
+    lib.gdn_get_debug.restype = ctypes.c_int32
+    lib.gdn_device_faults.argtypes = [ctypes.POINTER(ctypes.c_uint32), ctypes.c_int32]
+    lib.gdn_device_faults.restype = st
     lib.gdn_status_string.argtypes = [st]
     lib.gdn_status_string.restype = ctypes.c_char_p
     lib.gdn_last_error.argtypes = []
@@ -184,17 +196,43 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
-    if workspace is None or workspace.numel() < ws_bytes.value:
-        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, ws_bytes.value, q.device)
+    if out is not None:
+        _check_out("out", out, tuple(v.shape), v.dtype, q.device)
     o = out if out is not None else torch.empty_like(v)
     ht = None
     if output_final_state:
+        if final_state is not None:
+            _check_out("final_state", final_state, (N, H, D, D), torch.float32, q.device)
         ht = final_state if final_state is not None else torch.empty(
             (N, H, D, D), dtype=torch.float32, device=q.device)
     _check(lib.gdn_chunk_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                              _ptr(cu_seqlens), cu_h, _ptr(h0), _ptr(o), _ptr(ht),
-                             _ptr(workspace), workspace.numel(), _stream()))
+                             _ptr(workspace), _nbytes(workspace), _stream()))
     return o, ht
+
+
+def _check_out(name, t, shape, dtype, device):
+    """A caller-supplied output: the shape, dtype and device the call writes, contiguous."""
+    if tuple(t.shape) != tuple(shape) or t.dtype != dtype or t.device != device or \
+            not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {list(shape)} on "
+                         f"{device}")
+
+
+def _nbytes(t):
+    return t.numel() * t.element_size()
+
+
+def _workspace(workspace, nbytes, device):
+    """The caller's workspace if it is a contiguous device tensor of at least ``nbytes`` bytes
+    (any dtype), else a new uint8 one."""
+    if workspace is not None:
+        if workspace.device != device or not workspace.is_contiguous():
+            raise ValueError("workspace must be a contiguous tensor on the inputs' device")
+        if _nbytes(workspace) >= nbytes:
+            return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def fwd_workspace_bytes(q, cu_seqlens, H=None, *, mode="exact", seg_chunks=0, num_slots=0,
@@ -287,8 +325,7 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
                      qk_l2norm=qk_l2norm)
     ws_bytes = ctypes.c_size_t(0)
     _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
-    if workspace is None or workspace.numel() < ws_bytes.value:
-        workspace = torch.empty(max(ws_bytes.value, 1), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, ws_bytes.value, q.device)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dg=torch.empty_like(g), dbeta=torch.empty_like(beta), dh0=None)
     if need_dh0:
@@ -298,7 +335,7 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
                              _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(out["dq"]),
                              _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                              _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
-                             workspace.numel(), _stream()))
+                             _nbytes(workspace), _stream()))
     return out
 
 
@@ -333,6 +370,36 @@ def decode_step(q, k, v, g, beta, state, *, scale=1.0, out=None, qk_l2norm=False
     return out
 
 
+def validate_cu_seqlens(cu_seqlens, total_tokens):
+    """Checks a device cu_seqlens table on the device (gdn_validate_cu_seqlens) and returns its
+    status bits (0: valid; CU_* bits otherwise).  Synchronises torch's current stream."""
+    lib = load_library()
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or not cu_seqlens.is_cuda or \
+            not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 device tensor")
+    status = torch.full((1,), -1, dtype=torch.int32, device=cu_seqlens.device)
+    _check(lib.gdn_validate_cu_seqlens(_ptr(cu_seqlens), cu_seqlens.numel() - 1,
+                                       int(total_tokens), _ptr(status), _stream()))
+    return int(status.item())
+
+
+def set_debug(on):
+    """Debug mode (gdn_set_debug): compute calls validate cu_seqlens on the device first and
+    check the kernels' fault flags after their launches (synchronising the stream)."""
+    _check(load_library().gdn_set_debug(1 if on else 0))
+
+
+def get_debug():
+    return bool(load_library().gdn_get_debug())
+
+
+def device_faults(clear=False):
+    """The current device's fault flags (gdn_device_faults; synchronises the device)."""
+    flags = ctypes.c_uint32(0)
+    _check(load_library().gdn_device_faults(ctypes.byref(flags), 1 if clear else 0))
+    return int(flags.value)
+
+
 def calib_copy(src, dst):
     """Stream copy of ``src`` into ``dst`` (same byte size, a multiple of 16) by the library's
     calibration kernel (gdn_calib_copy): the HBM bandwidth a plain kernel reaches."""
@@ -360,5 +427,9 @@ gdn_chunk_fwd_plan = chunk_fwd_plan
 gdn_chunk_fwd_intermediates = chunk_fwd_intermediates
 gdn_chunk_bwd = chunk_bwd
 gdn_decode_step = decode_step
+gdn_validate_cu_seqlens = validate_cu_seqlens
+gdn_set_debug = set_debug
+gdn_get_debug = get_debug
+gdn_device_faults = device_faults
 gdn_calib_copy = calib_copy
 gdn_calib_mfma_bf16 = calib_mfma_bf16

@@ -237,3 +237,24 @@ def test_binding_has_every_compute_entry_point():
                           "gdn_chunk_bwd_workspace_size", "gdn_status_string", "gdn_last_error")]
     for n in names:
         assert callable(getattr(pkg, n)), n
+
+
+def test_validate_cu_seqlens_rejects_bad_arguments_on_the_host(lib):
+    status = ctypes.c_void_p(16)  # never dereferenced: every call below fails its host checks
+    assert lib.gdn_validate_cu_seqlens(None, 2, 10, status, None) == 1
+    assert lib.gdn_validate_cu_seqlens(status, 2, 10, None, None) == 1
+    assert lib.gdn_validate_cu_seqlens(status, 0, 10, status, None) == 2
+    assert lib.gdn_validate_cu_seqlens(status, 2, -1, status, None) == 2
+    assert lib.gdn_validate_cu_seqlens(status, 2, 1 << 31, status, None) == 2
+
+
+def test_debug_switch(lib):
+    before = lib.gdn_get_debug()
+    try:
+        assert lib.gdn_set_debug(1) == 0 and lib.gdn_get_debug() == 1
+        assert lib.gdn_set_debug(0) == 0 and lib.gdn_get_debug() == 0
+        assert lib.gdn_set_debug(2) == 4
+    finally:
+        lib.gdn_set_debug(before)
+    assert lib.gdn_device_faults(None, 0) == 1
+    assert lib.gdn_status_string(9) == b"a device-side check failed"

@@ -61,10 +61,11 @@ def _check_bwd(gdn, oracle_mod, inp, label, dht_scale=0.0, scale=1.0, heads=None
                          scale=scale)
     tol = tol_for(inp["dtype"])
     print(f"[{label}]", flush=True)
+    cu = inp["cu_seqlens"]
     for name in NAMES:
-        report(name, np64(gr[name])[:, sel], ref[name], tol)
+        report(name, np64(gr[name])[:, sel], ref[name], tol, cu=cu)
     if gr["dh0"] is not None:
-        report("dh0", np64(gr["dh0"])[:, sel], ref["dh0"], tol)
+        report("dh0", np64(gr["dh0"])[:, sel], ref["dh0"], tol, cu=cu, states=True)
     return gr, ref
 
 
@@ -85,11 +86,21 @@ def test_bwd_scale(gdn, oracle_mod):
     _check_bwd(gdn, oracle_mod, inp, "bwd scale", scale=0.0883883)
 
 
-def test_bwd_train_65k(gdn, oracle_mod):
-    """65536 tokens packed from documents of U{4096..16384} tokens, H=8, d=128, bf16,
-    dO ~ N(0, 1).  The oracle checks heads 0 and 5 (heads are independent)."""
+def test_train_65k_forward_and_backward(gdn, oracle_mod):
+    """The training workload: 65536 tokens packed from documents of U{4096..16384} tokens, H=8,
+    d=128, bf16, dO ~ N(0, 1) ("How to Speed Up GDN Kernels for Qwen Models", section "What it
+    adds up to": the backward at 16K-256K tokens).  The forward's o and final states, then every
+    gradient, on all 8 heads, per (document, head) and per 4096-token block."""
     inp = workload("train")
-    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K", heads=[0, 5])
+    d = to_dev(inp)
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = oracle_mod.fwd_recurrent(*_oargs(inp), inp["cu_seqlens"])
+    print("[train 65K forward]", flush=True)
+    report("o", np64(o), o_ref, 5e-3, cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_ref, 5e-3, cu=inp["cu_seqlens"], states=True)
+    del o, ht, o_ref, ht_ref
+    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K, all 8 heads")
 
 
 def test_bwd_shared_initial_state_sums_branches(gdn, oracle_mod):
@@ -109,7 +120,7 @@ def test_bwd_shared_initial_state_sums_branches(gdn, oracle_mod):
     ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], dout, h0=inp["h0"][0])
     report("dh0 (summed)", np64(gr["dh0"]), ref["dh0"].sum(axis=0), 5e-3)
     for name in NAMES:
-        report(name, np64(gr[name]), ref[name], 5e-3)
+        report(name, np64(gr[name]), ref[name], 5e-3, cu=inp["cu_seqlens"])
 
 
 def test_bwd_deterministic(gdn):
@@ -141,8 +152,8 @@ def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots):
     ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], dout, h0=inp["h0"], dht=dht)
     print(f"[bwd recompute seg={seg} slots={slots}]", flush=True)
     for name in NAMES:
-        report(name, np64(gr[name]), ref[name], 5e-3)
-    report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3)
+        report(name, np64(gr[name]), ref[name], 5e-3, cu=inp["cu_seqlens"])
+    report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3, cu=inp["cu_seqlens"], states=True)
 
 
 def test_fork_backward_through_shared_prefix(gdn, oracle_mod):
@@ -180,6 +191,6 @@ def test_fork_backward_through_shared_prefix(gdn, oracle_mod):
             ref_b[n][s0:s1] = r[n][P:]
     print("[fork backward]", flush=True)
     for n in NAMES:
-        report(f"prefix {n}", np64(gp[n]), ref_p[n], 5e-3)
+        report(f"prefix {n}", np64(gp[n]), ref_p[n], 5e-3, cu=pre["cu_seqlens"])
     for n in NAMES:
-        report(f"branch {n}", np64(gb[n]), ref_b[n], 5e-3)
+        report(f"branch {n}", np64(gb[n]), ref_b[n], 5e-3, cu=br["cu_seqlens"])

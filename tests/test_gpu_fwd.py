@@ -36,8 +36,8 @@ def _check_fwd(gdn, oracle_mod, inp, label, **kw):
                                              scale=kw.get("scale", 1.0))
     tol = tol_for(inp["dtype"])
     print(f"[{label}]", flush=True)
-    report("o", np64(o), o_ref, tol)
-    report("ht", np64(ht), ht_ref, tol)
+    report("o", np64(o), o_ref, tol, cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_ref, tol, cu=inp["cu_seqlens"], states=True)
     return o, ht
 
 
@@ -129,10 +129,11 @@ def test_long_32k_truncate(gdn, oracle_mod):
     o_e, ht_e = oracle_mod.fwd_recurrent(*_oracle_args(inp), inp["cu_seqlens"])
     print("[long 32K truncate]", flush=True)
     print(f"  oracle truncated vs exact: o {rel_l2(o_t, o_e):.2e}  ht {rel_l2(ht_t, ht_e):.2e}")
-    report("o vs oracle-trunc", np64(o), o_t, 5e-3)
-    report("ht vs oracle-trunc", np64(ht), ht_t, 5e-3)
-    report("o vs oracle-exact", np64(o), o_e, 5e-3)
-    report("ht vs oracle-exact", np64(ht), ht_e, 5e-3)
+    cu = inp["cu_seqlens"]
+    report("o vs oracle-trunc", np64(o), o_t, 5e-3, cu=cu)
+    report("ht vs oracle-trunc", np64(ht), ht_t, 5e-3, cu=cu, states=True)
+    report("o vs oracle-exact", np64(o), o_e, 5e-3, cu=cu)
+    report("ht vs oracle-exact", np64(ht), ht_e, 5e-3, cu=cu, states=True)
 
 
 def test_truncate_forced_segments_fp32(gdn, oracle_mod):
@@ -149,31 +150,75 @@ def test_truncate_forced_segments_fp32(gdn, oracle_mod):
                           seg_chunks=4, cu_seqlens_host=inp["cu_seqlens"])
     o_t, ht_t = oracle_mod.fwd_truncated(*_oracle_args(inp), inp["cu_seqlens"], ref_plan,
                                          h0=inp["h0"])
-    report("o vs oracle-trunc", np64(o), o_t, 1e-4)
-    report("ht vs oracle-trunc", np64(ht), ht_t, 1e-4)
+    cu = inp["cu_seqlens"]
+    report("o vs oracle-trunc", np64(o), o_t, 1e-4, cu=cu)
+    report("ht vs oracle-trunc", np64(ht), ht_t, 1e-4, cu=cu, states=True)
 
 
-def test_fork_shared_prefix(gdn, oracle_mod):
-    """A 65536-token prefix, then 80 branches of U{1024..4096} tokens whose initial state is the
-    prefix's final state broadcast (stride 0); H=16, d=128, bf16.  The oracle checks heads
-    0, 7 and 15 (heads are independent)."""
+@pytest.fixture(scope="module")
+def fork_case(oracle_mod):
+    """The shared-prefix fork workload ("Musings on long-context fine-tuning", section "Sharing
+    the repeated work"): a 65536-token prefix, then 80 branches of U{1024..4096} tokens whose
+    initial state is the prefix's final state; H=16, d=128, bf16.  With the oracle's prefix
+    state (all 16 heads)."""
     w = workload("fork")
+    pre = w["prefix"]
+    _, ht_pr = oracle_mod.fwd_recurrent(*_oracle_args(pre), pre["cu_seqlens"])
+    return w, ht_pr
+
+
+def test_fork_shared_prefix(gdn, oracle_mod, fork_case):
+    """The prefix runs once; its final state, broadcast (stride 0), starts all 80 branches in
+    one packed call.  Every head of the prefix's final state and of the branches' outputs and
+    final states against the oracle (which starts the branches from its own prefix state)."""
+    w, ht_pr = fork_case
     pre, br = w["prefix"], w["branches"]
     dp, db = to_dev(pre), to_dev(br)
     _, ht_p = gdn.chunk_fwd(*args_of(dp), dp["cu_seqlens"], None)
     o_b, ht_b = gdn.chunk_fwd(*args_of(db), db["cu_seqlens"], ht_p[0].contiguous())
     torch.cuda.synchronize()
-    heads = [0, 7, 15]
+    o_br, ht_br = oracle_mod.fwd_recurrent(*_oracle_args(br), br["cu_seqlens"], h0=ht_pr[0])
+    print("[fork, all 16 heads]", flush=True)
+    report("prefix ht", np64(ht_p), ht_pr, 5e-3, cu=pre["cu_seqlens"], states=True)
+    report("branch o", np64(o_b), o_br, 5e-3, cu=br["cu_seqlens"])
+    report("branch ht", np64(ht_b), ht_br, 5e-3, cu=br["cu_seqlens"], states=True)
 
-    def sub(inp):
-        return [np.ascontiguousarray(inp[x][:, heads]) for x in ("q", "k", "v", "g", "beta")]
 
-    _, ht_pr = oracle_mod.fwd_recurrent(*sub(pre), pre["cu_seqlens"])
-    o_br, ht_br = oracle_mod.fwd_recurrent(*sub(br), br["cu_seqlens"], h0=ht_pr[0])
-    print("[fork]", flush=True)
-    report("prefix ht", np64(ht_p)[:, heads], ht_pr, 5e-3)
-    report("branch o", np64(o_b)[:, heads], o_br, 5e-3)
-    report("branch ht", np64(ht_b)[:, heads], ht_br, 5e-3)
+def test_fork_backward_full_size(gdn, oracle_mod, fork_case):
+    """Backward of the fork workload at full size ("Musings on long-context fine-tuning",
+    section "Backward through P"), every head: the branches' backward from the shared prefix
+    state gives dh0 summed over the 80 branches; that sum is the prefix's dht, and the prefix's
+    backward with its own dO gives the prefix's gradients.  The oracle takes the same two steps
+    with its own backward (its per-branch dh0 summed in fp64); that a shared state's gradient is
+    the sum over the branches is pinned on the CPU against the oracle's backward of every
+    concatenated prefix + branch (test_oracle_pins), and on the GPU at small size
+    (test_fork_backward_through_shared_prefix)."""
+    from gdn_inputs import bf16_round
+
+    w, ht_pr = fork_case
+    pre, br = w["prefix"], w["branches"]
+    rng = np.random.Generator(np.random.PCG64(4003))
+    dout_p = bf16_round(rng.standard_normal(pre["v"].shape).astype(np.float32))
+    dout_b = bf16_round(rng.standard_normal(br["v"].shape).astype(np.float32))
+    dp, db = to_dev(pre), to_dev(br)
+    _, ht_p = gdn.chunk_fwd(*args_of(dp), dp["cu_seqlens"], None)
+    shared = ht_p[0].contiguous()
+    gb = gdn.chunk_bwd(*args_of(db), db["cu_seqlens"],
+                       torch.from_numpy(dout_b).cuda().to(torch.bfloat16), shared)
+    gp = gdn.chunk_bwd(*args_of(dp), dp["cu_seqlens"],
+                       torch.from_numpy(dout_p).cuda().to(torch.bfloat16), None,
+                       gb["dh0"].unsqueeze(0).contiguous())
+    torch.cuda.synchronize()
+    rb = oracle_mod.bwd(*_oracle_args(br), br["cu_seqlens"], dout_b, h0=ht_pr[0])
+    dht_ref = rb["dh0"].sum(axis=0)
+    rp = oracle_mod.bwd(*_oracle_args(pre), pre["cu_seqlens"], dout_p, dht=dht_ref[None])
+    print("[fork backward, all 16 heads]", flush=True)
+    report("dh0 summed over branches", np64(gb["dh0"]), dht_ref, 5e-3)
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        report(f"branch {n}", np64(gb[n]), rb[n], 5e-3, cu=br["cu_seqlens"])
+    for n in ("dq", "dk", "dv", "dg", "dbeta"):
+        report(f"prefix {n}", np64(gp[n]), rp[n], 5e-3, cu=pre["cu_seqlens"])
+    report("prefix dh0", np64(gp["dh0"]), rp["dh0"], 5e-3)
 
 
 def test_broadcast_h0_equals_explicit_copies(gdn):

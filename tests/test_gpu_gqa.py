@@ -64,8 +64,8 @@ def test_grouped_forward(gdn, oracle_mod, dtype, d, G, mode, seg):
         o_ref, ht_ref = oracle_mod.fwd_truncated(*[ref[x] for x in NAMES], inp["cu_seqlens"],
                                                  plan, h0=inp["h0"], scale=0.5)
     print(f"[grouped fwd {dtype} d={d} G={G} {mode} seg={seg}]", flush=True)
-    report("o", np64(o), o_ref, tol_for(dtype))
-    report("ht", np64(ht), ht_ref, tol_for(dtype))
+    report("o", np64(o), o_ref, tol_for(dtype), cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_ref, tol_for(dtype), cu=inp["cu_seqlens"], states=True)
 
 
 def test_grouped_forward_equals_repeated_heads(gdn):
@@ -98,9 +98,10 @@ def test_grouped_backward(gdn, oracle_mod, dtype, d, G):
     for n in ("dq", "dk"):
         summed = np.asarray(r[n]).reshape(T, H // G, G, d).sum(axis=2)
         assert tuple(gr[n].shape) == (T, H // G, d)
-        report(n, np64(gr[n]), summed, tol)
-    for n in ("dv", "dg", "dbeta", "dh0"):
-        report(n, np64(gr[n]), r[n], tol)
+        report(n, np64(gr[n]), summed, tol, cu=inp["cu_seqlens"])
+    for n in ("dv", "dg", "dbeta"):
+        report(n, np64(gr[n]), r[n], tol, cu=inp["cu_seqlens"])
+    report("dh0", np64(gr["dh0"]), r["dh0"], tol, cu=inp["cu_seqlens"], states=True)
 
 
 @pytest.mark.parametrize("mode", ["truncate", "exact"])
@@ -125,5 +126,5 @@ def test_grouped_many_heads_normalised(gdn, oracle_mod, mode):
         o_ref, ht_ref = oracle_mod.fwd_truncated(*[ref[x] for x in NAMES], inp["cu_seqlens"],
                                                  plan, h0=inp["h0"], qk_l2norm=True)
     print(f"[grouped 32/4 heads, normalised, {mode}]", flush=True)
-    report("o", np64(o), o_ref, 5e-3)
-    report("ht", np64(ht), ht_ref, 5e-3)
+    report("o", np64(o), o_ref, 5e-3, cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_ref, 5e-3, cu=inp["cu_seqlens"], states=True)

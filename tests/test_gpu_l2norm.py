@@ -59,8 +59,8 @@ def _run_fwd(gdn, oracle_mod, inp, label, mode="exact", seg=0, slots=256, scale=
         o_ref, ht_ref = oracle_mod.fwd_truncated(*oargs, inp["cu_seqlens"], plan, h0=inp["h0"],
                                                  scale=scale, qk_l2norm=True)
     tol = tol_for(inp["dtype"])
-    report("o", np64(o), o_ref, tol)
-    report("ht", np64(ht), ht_ref, tol)
+    report("o", np64(o), o_ref, tol, cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_ref, tol, cu=inp["cu_seqlens"], states=True)
     # without the normalisation the same inputs give a different result
     o_plain, _ = oracle_mod.fwd_recurrent(*oargs, inp["cu_seqlens"], h0=inp["h0"], scale=scale)
     assert np.linalg.norm(o_plain - o_ref) > 10 * tol * np.linalg.norm(o_ref)
@@ -99,8 +99,8 @@ def test_l2norm_long_32k_truncate(gdn, oracle_mod):
     o_t, ht_t = oracle_mod.fwd_truncated(*[inp[x] for x in NAMES], inp["cu_seqlens"], plan,
                                          qk_l2norm=True)
     print("[l2norm long 32K truncate]", flush=True)
-    report("o", np64(o), o_t, 5e-3)
-    report("ht", np64(ht), ht_t, 5e-3)
+    report("o", np64(o), o_t, 5e-3, cu=inp["cu_seqlens"])
+    report("ht", np64(ht), ht_t, 5e-3, cu=inp["cu_seqlens"], states=True)
 
 
 @pytest.mark.parametrize("mode,seg", [("exact", 0), ("truncate", 2)])
@@ -142,6 +142,7 @@ def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg):
     tol = tol_for(dtype)
     for n in ("dq", "dk"):
         summed = np.asarray(r[n]).reshape(T, 4 // G, G, d).sum(axis=2)
-        report(n, np64(gr[n]), summed, tol)
-    for n in ("dv", "dg", "dbeta", "dh0"):
-        report(n, np64(gr[n]), r[n], tol)
+        report(n, np64(gr[n]), summed, tol, cu=inp["cu_seqlens"])
+    for n in ("dv", "dg", "dbeta"):
+        report(n, np64(gr[n]), r[n], tol, cu=inp["cu_seqlens"])
+    report("dh0", np64(gr["dh0"]), r["dh0"], tol, cu=inp["cu_seqlens"], states=True)

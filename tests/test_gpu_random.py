@@ -81,8 +81,9 @@ def test_random_combination(gdn, oracle_mod, seed):
         o_ref, ht_ref = oracle_mod.fwd_truncated(*oargs, inp["cu_seqlens"], plan, h0=h0,
                                                  scale=c["scale"], qk_l2norm=c["norm"])
     tol = tol_for(c["dtype"])
-    report("o", np64(o), o_ref, tol)
-    report("ht", np64(ht), ht_ref, tol)
+    cu_h = inp["cu_seqlens"]
+    report("o", np64(o), o_ref, tol, cu=cu_h)
+    report("ht", np64(ht), ht_ref, tol, cu=cu_h, states=True)
     if c["mode"] != "exact":
         return
     gr = gdn.chunk_bwd(*args, cu, dev(inp["dout"], tdt), dev(h0), scale=c["scale"],
@@ -92,9 +93,12 @@ def test_random_combination(gdn, oracle_mod, seed):
                        qk_l2norm=c["norm"])
     T, d = inp["g"].shape[0], c["d"]
     for n in ("dq", "dk"):
-        report(n, np64(gr[n]), np.asarray(r[n]).reshape(T, c["H"] // G, G, d).sum(axis=2), tol)
+        report(n, np64(gr[n]), np.asarray(r[n]).reshape(T, c["H"] // G, G, d).sum(axis=2), tol,
+               cu=cu_h)
     for n in ("dv", "dg", "dbeta"):
-        report(n, np64(gr[n]), r[n], tol)
+        report(n, np64(gr[n]), r[n], tol, cu=cu_h)
     if h0 is not None:
-        dh0_ref = r["dh0"].sum(axis=0) if c["h0"] == "broadcast" else r["dh0"]
-        report("dh0", np64(gr["dh0"]), dh0_ref, tol)
+        if c["h0"] == "broadcast":
+            report("dh0", np64(gr["dh0"]), r["dh0"].sum(axis=0), tol)
+        else:
+            report("dh0", np64(gr["dh0"]), r["dh0"], tol, cu=cu_h, states=True)
