@@ -431,10 +431,10 @@ def fractions(median_ms, nbytes, nflops, peaks):
     return out
 
 
-def time_decode(gdn, torch, steps, warmup, sets=3):
+def time_decode(gdn, torch, steps, warmup, sets=6):
     """One decode step (gdn_decode_step) on the fork workload's serving shape: 80 sequences x
     16 heads, d = 128, bf16 inputs, fp32 states updated in place.  ``sets`` independent state
-    sets (168 MB each) rotate between steps, so the working set (504 MB for three) exceeds the
+    sets (84 MB each) rotate between steps, so the working set (504 MB for six) exceeds the
     256 MB last-level cache and each step reads its states from HBM.  Algorithmic bytes per
     step: every state read and written once (2 x 64 KiB), q, k, v, o in bf16, g fp32, beta
     bf16."""
