@@ -153,6 +153,21 @@ gdn_status gdn_chunk_fwd(const gdn_problem *p, const void *q, const void *k, con
                          const int32_t *cu_seqlens_host, const float *h0, void *o, float *ht,
                          void *workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* gdn_chunk_fwd for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same arguments without the
+ * workspace, which comes from a static device array of GDN_NOALLOC_SCRATCH_BYTES (128 MiB) that
+ * every GPU the library is loaded on holds until the process ends.  Calls nothing that
+ * allocates.  A problem whose workspace (gdn_chunk_fwd_workspace_size) exceeds that size is
+ * refused with GDN_ERR_WORKSPACE_TOO_SMALL before anything is enqueued (the exact mode's split
+ * needs 192 KiB per (segment, head): up to 682 of them; the truncate mode and unsplit runs need
+ * none).  All calls on one device share its array, so calls that overlap on one device race;
+ * nothing in the array needs to start at zero. */
+#define GDN_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem *p, const void *q, const void *k,
+                                 const void *v, const float *g, const void *beta,
+                                 const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                 const float *h0, void *o, float *ht, hipStream_t stream);
+
 /* The forward's segment plan, for inspection.  Runs the forward's own unit lookup and warmup
  * scan on the device and writes to plan_out (device int32, capacity plan_capacity entries):
  *   plan_out[0] = number of units U, plan_out[1] = segment length L (0 = unsplit),

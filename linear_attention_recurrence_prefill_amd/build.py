@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libgdn_mi355x.so")
 SOURCES = ["gdn_api.cpp", "gdn_fwd.hip", "gdn_fwd_fast.hip", "gdn_fwd_ws.hip",
            "gdn_fwd_split.hip", "gdn_bwd.hip", "gdn_bwd_chain.hip",
-           "gdn_bwd_grad.hip", "gdn_decode.hip", "gdn_calib.hip", "gdn_check.hip"]
+           "gdn_bwd_grad.hip", "gdn_decode.hip", "gdn_calib.hip", "gdn_check.hip",
+           "gdn_noalloc.hip"]
 ARCH = "gfx950"
 
 # Packed-fp32 instructions are not to be generated: they are turned off for the device code.

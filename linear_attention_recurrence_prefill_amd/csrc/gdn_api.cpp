@@ -17,6 +17,9 @@
 #include "gdn_decode.h"
 #include "gdn_internal.h"
 
+static_assert(GDN_NOALLOC_SCRATCH_BYTES == gdn::kStaticScratchBytes,
+              "the header's scratch size is the library's");
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -448,6 +451,34 @@ gdn_status gdn_chunk_fwd(const gdn_problem *p, const void *q, const void *k, con
                          void *workspace, size_t workspace_bytes, hipStream_t stream) {
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
   return run_fwd(p, t, cu_seqlens_host, false, nullptr, workspace, workspace_bytes, stream);
+}
+
+gdn_status gdn_chunk_fwd_noalloc(const gdn_problem *p, const void *q, const void *k,
+                                 const void *v, const float *g, const void *beta,
+                                 const int32_t *cu_seqlens, const int32_t *cu_seqlens_host,
+                                 const float *h0, void *o, float *ht, hipStream_t stream) {
+  Tensors t{q, k, v, g, beta, cu_seqlens, h0, o, ht};
+  gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  s = check_tensors(t, p->total_tokens);
+  if (s != GDN_OK) return s;
+  s = check_cu_host(p, cu_seqlens_host);
+  if (s != GDN_OK) return s;
+  FwdLayout lay;
+  s = fwd_layout(p, cu_seqlens_host, false, &lay);
+  if (s != GDN_OK) return s;
+  if (lay.total > gdn::kStaticScratchBytes)
+    return fail(GDN_ERR_WORKSPACE_TOO_SMALL,
+                "this problem needs %zu bytes of workspace; the static scratch of "
+                "gdn_chunk_fwd_noalloc holds %zu (use gdn_chunk_fwd with a workspace)",
+                lay.total, gdn::kStaticScratchBytes);
+  s = device_info(nullptr);
+  if (s != GDN_OK) return s;
+  void *scratch = nullptr;
+  const hipError_t e = gdn::static_scratch(&scratch);
+  if (e != hipSuccess) return hip_fail(e, "static scratch address");
+  return run_fwd(p, t, cu_seqlens_host, false, nullptr, scratch, gdn::kStaticScratchBytes,
+                 stream);
 }
 
 gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, const void *k,

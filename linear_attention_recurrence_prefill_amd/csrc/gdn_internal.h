@@ -18,6 +18,11 @@ constexpr uint32_t kCuOutOfRange = 8u;    // some cu[n + 1] outside [0, T]
 // Fault flags kernels set in the per-device check words (gdn_device_faults).
 constexpr uint32_t kFaultDiagWait = 1u;   // the forward's wait for its diagonal blocks ran out
 
+// Bytes of the static device scratch array behind gdn_chunk_fwd_noalloc (gdn_noalloc.hip).
+constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
+// The current device's address of that array (hipGetSymbolAddress on first use per device).
+hipError_t static_scratch(void **ptr);
+
 // The current device's check words ([0] validation status, [1] fault flags), from
 // hipGetSymbolAddress on first use per device.
 hipError_t device_check_words(uint32_t **words);

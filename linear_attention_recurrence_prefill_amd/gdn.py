@@ -22,7 +22,7 @@ _MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
 
 # Every exported entry point of include/gdn.h.
 EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
-           "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
+           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd", "gdn_decode_step", "gdn_validate_cu_seqlens", "gdn_set_debug",
            "gdn_get_debug", "gdn_device_faults", "gdn_status_string", "gdn_last_error",
            "gdn_calib_copy", "gdn_calib_mfma_bf16")
@@ -70,6 +70,8 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_workspace_size.restype = st
     lib.gdn_chunk_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, sz, vp]
     lib.gdn_chunk_fwd.restype = st
+    lib.gdn_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp]
+    lib.gdn_chunk_fwd_noalloc.restype = st
     lib.gdn_chunk_fwd_plan.argtypes = [P, vp, vp, i32p, vp, ctypes.c_int64, vp, sz, vp]
     lib.gdn_chunk_fwd_plan.restype = st
     lib.gdn_chunk_fwd_intermediates.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -210,6 +212,29 @@ def chunk_fwd(q, k, v, g, beta, cu_seqlens, h0=None, *, mode="exact", scale=1.0,
                              _ptr(cu_seqlens), cu_h, _ptr(h0), _ptr(o), _ptr(ht),
                              _ptr(workspace), _nbytes(workspace), _stream()))
     return o, ht
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # GDN_NOALLOC_SCRATCH_BYTES of include/gdn.h
+
+
+def chunk_fwd_noalloc(q, k, v, g, beta, cu_seqlens, h0=None, *, out, final_state=None,
+                      mode="exact", scale=1.0, seg_chunks=0, num_slots=0,
+                      trunc_log_threshold=-10.0, cu_seqlens_host=None, qk_l2norm=False):
+    """The forward through gdn_chunk_fwd_noalloc: the library allocates nothing (its workspace
+    is a static device array), and the caller passes the outputs (``out`` like v; optional
+    ``final_state`` [N, H, D, D] fp32).  Returns (out, final_state)."""
+    lib = load_library()
+    T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
+    p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks, num_slots,
+                     trunc_log_threshold, stride, num_k_heads=Hk, qk_l2norm=qk_l2norm)
+    _check_out("out", out, tuple(v.shape), v.dtype, q.device)
+    if final_state is not None:
+        _check_out("final_state", final_state, (N, H, D, D), torch.float32, q.device)
+    _check(lib.gdn_chunk_fwd_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                     _ptr(beta), _ptr(cu_seqlens),
+                                     _host_cu(cu_seqlens, cu_seqlens_host), _ptr(h0), _ptr(out),
+                                     _ptr(final_state), _stream()))
+    return out, final_state
 
 
 def _check_out(name, t, shape, dtype, device):
@@ -423,6 +448,7 @@ def calib_mfma_bf16(out, waves_per_cu, iters):
 
 # The C entry points' names (include/gdn.h, include/gdn_calib.h), one binding each.
 gdn_chunk_fwd = chunk_fwd
+gdn_chunk_fwd_noalloc = chunk_fwd_noalloc
 gdn_chunk_fwd_plan = chunk_fwd_plan
 gdn_chunk_fwd_intermediates = chunk_fwd_intermediates
 gdn_chunk_bwd = chunk_bwd

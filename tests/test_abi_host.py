@@ -258,3 +258,21 @@ def test_debug_switch(lib):
         lib.gdn_set_debug(before)
     assert lib.gdn_device_faults(None, 0) == 1
     assert lib.gdn_status_string(9) == b"a device-side check failed"
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch(lib):
+    """gdn_chunk_fwd_noalloc refuses, on the host and before any device call, a problem whose
+    workspace exceeds the static scratch (GDN_NOALLOC_SCRATCH_BYTES): here an exact split of
+    1 x 2^21 tokens over 32 heads (8192 units of 192 KiB)."""
+    from linear_attention_recurrence_prefill_amd.gdn import NOALLOC_SCRATCH_BYTES
+
+    p = _problem(total_tokens=1 << 21, num_seqs=1, num_heads=32, mode=0, seg_chunks=4,
+                 num_slots=256)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
+    assert n.value > NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced
+    rc = lib.gdn_chunk_fwd_noalloc(ctypes.byref(p), fake, fake, fake, fake, fake, fake, None,
+                                   None, fake, None, None)
+    assert rc == 6, lib.gdn_last_error()
+    assert b"static scratch" in lib.gdn_last_error()
