@@ -389,7 +389,8 @@ gdn_status launch_fwd_passes(const gdn_problem *p, const Tensors &t, const FwdLa
     sa.L = lay.L;
     sa.h0 = t.h0;
     sa.h0_stride = p->h0_seq_stride;
-    sa.unit_bm = bm;
+    sa.unit_b = bm;
+    sa.unit_m = bm + lay.units * p->num_heads * p->d_k * p->d_v;
     sa.unit_h0 = uh0;
     sa.units = lay.units;
     e = gdn::launch_affine_scan(sa, stream);
@@ -536,7 +537,7 @@ struct BwdLayout {
   int32_t L = 0;
   int64_t units = 0;
   size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
-  size_t unit_bm = 0, unit_h0 = 0;
+  size_t unit_bm = 0, unit_h0 = 0, unit_mt = 0;
   size_t dq_part = 0, dk_part = 0;  // grouped heads or qk_l2norm: per-value-head dq, dk (fp32)
   size_t rq = 0, rk = 0;            // qk_l2norm: inverse row norms of q and k (fp32 [T, Hk])
   size_t total = 0;
@@ -587,6 +588,7 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
     const size_t per = sizeof(float) * (size_t)L->units * H * D * D;
     L->unit_bm = take(2 * per);
     L->unit_h0 = take(per);
+    L->unit_mt = take(per);  // M^T of each unit, for the reverse walk
   }
   // partials: grouped heads (summed per key head), and the general kernels' normalised q, k
   // (finished by the normalisation's backward kernel; the bf16 d = 128 kernel finishes in place)
@@ -638,6 +640,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
     units = L.units;
     a.units = L.units;
     a.unit_out = bm;
+    a.unit_mt = reinterpret_cast<float *>(base + L.unit_mt);  // for the reverse walk
     e = gdn::launch_fwd_ws_transition(a, L.units, stream);
     if (e != hipSuccess) return hip_fail(e, "backward recompute: first pass");
     gdn::SplitArgs sa{};
@@ -648,12 +651,14 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
     sa.L = L.L;
     sa.h0 = t.h0;
     sa.h0_stride = p->h0_seq_stride;
-    sa.unit_bm = bm;
+    sa.unit_b = bm;
+    sa.unit_m = bm + L.units * p->num_heads * p->d_k * p->d_v;
     sa.unit_h0 = uh0;
     sa.units = L.units;
     e = gdn::launch_affine_scan(sa, stream);
     if (e != hipSuccess) return hip_fail(e, "backward recompute: start states");
     a.unit_out = nullptr;
+    a.unit_mt = nullptr;
     a.unit_h0 = uh0;
   }
   a.dbg_gamma = gamma;
@@ -787,8 +792,9 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   if (fast) {
     e = gdn::launch_bwd_tm(b, tmat, L.nc, stream);
     if (e != hipSuccess) return hip_fail(e, "backward: Tm");
-    // reverse chain, through the exact split when the recompute was split (same units; the
-    // recompute's per-unit buffers are free again)
+    // reverse chain, through the exact split when the recompute was split (same units): the
+    // transition pass writes B' over the recompute's B, and the reverse walk applies B' with the
+    // M^T the recompute's first pass stored
     gdn::BwdUnits u{};
     u.L = L.L;
     u.units = L.units;
@@ -806,7 +812,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
       sa.L = L.L;
       sa.h0 = dht;
       sa.h0_stride = (int64_t)p->num_heads * p->d_k * p->d_v;
-      sa.unit_bm = bm;
+      sa.unit_b = bm;
+      sa.unit_m = reinterpret_cast<const float *>(base + L.unit_mt);
       sa.unit_h0 = dend;
       sa.units = L.units;
       e = gdn::launch_affine_scan_reverse(sa, stream);

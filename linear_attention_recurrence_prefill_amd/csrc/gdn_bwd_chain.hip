@@ -29,10 +29,10 @@
 // the same order.
 //
 // Exact split (as in the forward): the map from a unit's end gradient to its start gradient is
-// affine, dh_start = M' dh_end + B'.  The transition pass runs each unit from a zero end
-// gradient (B') and, with dO = 0, from the identity (M', column by column); a reverse walk of the
-// affine scan composes them into every unit's true end gradient; the final pass reruns each unit
-// from it with the per-chunk outputs.
+// affine, dh_start = M^T dh_end + B', with M the forward map of the same unit (the derivative of
+// S_end = M S_start + B; the forward recompute computes M).  The transition pass runs each unit
+// from a zero end gradient (B'); a reverse walk of the affine scan composes M^T and B' into every
+// unit's true end gradient; the final pass reruns each unit from it with the per-chunk outputs.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 #include "gdn_unit.h"
@@ -92,7 +92,7 @@ struct ChainSmem {
   alignas(16) char pth[64 * 128];     // P^T = hi + lo (row i, column r)
   alignas(16) char ptl[64 * 128];
   alignas(16) float gam[64];  // gamma, rows past n hold gamma_last
-  alignas(16) float as[64];   // scale e^gamma, 0 past n (0 in the M' pass)
+  alignas(16) float as[64];   // scale e^gamma, 0 past n
   alignas(16) float c[64];    // e^{gamma_last - gamma}, 0 past n
   alignas(16) float ab[64];   // e^gamma beta, 0 past n
   alignas(16) float beta[64];
@@ -114,7 +114,6 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = blockIdx.x, h = blockIdx.y, H = b.H;
-  const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M' half
   if (w == 0) {
     Unit un;
     const bool ok = find_unit(b.cu, b.N, b.T, us.L, unit, true, lane, un);
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   const bf16 *__restrict__ gb = static_cast<const bf16 *>(b.beta);
   const int col0 = 16 * kNT * w + cl;  // this lane's column in tile nt: col0 + 16 nt
   const int64_t dd = (int64_t)kD * kD;
-  const float xs = is_m ? 0.f : b.scale;  // the M' half runs with dO = 0
+  const float xs = b.scale;
 
   f32x4 G[8][kNT];  // dh'
   {
@@ -168,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * md + 4 * gq + i, cc = col0 + 16 * nt;
-          G[md][nt][i] = src != nullptr ? src[r * kD + cc] : (is_m && r == cc ? 1.f : 0.f);
+          G[md][nt][i] = src != nullptr ? src[r * kD + cc] : 0.f;
         }
   }
 
@@ -220,10 +219,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const int u = ((lane & 15) ^ sw(r)) << 4;
       const int lo = ((64 / kWaves) * w + 4 * j) * kRowB;
       dma16(gk + t * tok_qk + u, sm.kqo[set][0] + lo);
-      if (!is_m) {  // the M' half runs with dO = 0 and reads neither Q nor dO
-        dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
-        dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
-      }
+      dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
+      dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
     }
     // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
     const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
@@ -268,9 +265,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     }
     if (c > c0) issue(c - 1, set ^ 1);
     __syncthreads();
-    // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo (the M' half
-    //      runs with dO = 0 and needs neither P nor the dO products below)
-    for (int t = w; t < (is_m ? 0 : 10); t += kWaves) {
+    // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo
+    for (int t = w; t < 10; t += kWaves) {
       const int mr = kPtR[t], mi = kPtI[t];
       f32x4 acc = zero4();
 #pragma unroll
@@ -330,7 +326,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
         }
       }
 #pragma unroll
-      for (int ks = 0; ks < 2 && !is_m; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
         bf16x8 of[kNT];  // dO over tokens, exact
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) of[nt] = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
@@ -412,12 +408,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 16 + 4 * gq]);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
-        if (!is_m) {
-          const bf16x8 o = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
-          const f32x4 o0 = to_f32x4(__builtin_shufflevector(o, o, 0, 1, 2, 3));
-          const f32x4 o1 = to_f32x4(__builtin_shufflevector(o, o, 4, 5, 6, 7));
-          split8(a0 * o0, a1 * o1, yh[ks][nt], yl[ks][nt]);
-        }
+        const bf16x8 o = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
+        const f32x4 o0 = to_f32x4(__builtin_shufflevector(o, o, 0, 1, 2, 3));
+        const f32x4 o1 = to_f32x4(__builtin_shufflevector(o, o, 4, 5, 6, 7));
+        split8(a0 * o0, a1 * o1, yh[ks][nt], yl[ks][nt]);
         split8(-(b0 * dR[2 * ks][nt]), -(b1 * dR[2 * ks + 1][nt]), nh[ks][nt], nl[ks][nt]);
       }
     }
@@ -429,13 +423,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         const bf16x8 ak = trfrag(Kt, ks, 4 * md);
-        if (!is_m) {
-          const bf16x8 aq = trfrag(Qt, ks, 4 * md);
+        const bf16x8 aq = trfrag(Qt, ks, 4 * md);
 #pragma unroll
-          for (int nt = 0; nt < kNT; ++nt) {
-            acc[nt] = mma_bf16(aq, yh[ks][nt], acc[nt]);
-            acc[nt] = mma_bf16(aq, yl[ks][nt], acc[nt]);
-          }
+        for (int nt = 0; nt < kNT; ++nt) {
+          acc[nt] = mma_bf16(aq, yh[ks][nt], acc[nt]);
+          acc[nt] = mma_bf16(aq, yl[ks][nt], acc[nt]);
         }
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
@@ -449,7 +441,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   }
   float *dst = nullptr;
   if (kTransition)
-    dst = us.unit_out + (((int64_t)blockIdx.z * us.units + unit) * H + h) * dd;
+    dst = us.unit_out + ((int64_t)unit * H + h) * dd;
   else if (c0 == 0 && b.dh0_seq != nullptr)
     dst = b.dh0_seq + ((int64_t)seq * H + h) * dd;
   if (dst != nullptr) {
@@ -593,7 +585,7 @@ hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream) {
   if (u.units <= 0) return hipSuccess;
-  hipLaunchKernelGGL(bwd_chain_bf16_kernel<true>, dim3((unsigned)u.units, b.H, 2), dim3(kThreads), 0,
+  hipLaunchKernelGGL(bwd_chain_bf16_kernel<true>, dim3((unsigned)u.units, b.H), dim3(kThreads), 0,
                      stream, b, u);
   return hipGetLastError();
 }

@@ -13,14 +13,14 @@ struct BwdUnits {
   int64_t units;
   // final pass: the state gradient at each unit's end [units, H, D, D] (null: dht, or zero)
   const float *unit_dend;
-  // transition pass: [2, units, H, D, D], the state gradient at each unit's start from a zero
-  // end gradient (B') and, column by column, from the identity with dO = 0 (the unit's map M')
+  // transition pass: [units, H, D, D], the state gradient at each unit's start from a zero end
+  // gradient (B'); the unit's map of end to start gradient is the forward's M transposed
   float *unit_out;
 };
 
 // The reverse state-gradient chain.  Final pass: grid (units, H); per chunk it writes dh' (dhn),
 // dR = Tm^T dDelta (into the ddelta slot, fp32 [T, H, D]) and dV.  Transition pass: grid
-// (units, H, 2), no per-chunk output, units that start a sequence are skipped.
+// (units, H), no per-chunk output, units that start a sequence are skipped.
 hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_t stream);
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream);
@@ -29,8 +29,9 @@ hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
 hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream);
 // Per-chunk gradients from the chain's dhn and dR (dV is the chain's).
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
-// The affine scan walked from each sequence's last unit to its first: S_end(u - 1) = M'_u
-// S_end(u) + B'_u from S_end(last) = s.h0 (dht, or zero), every unit's end state to s.unit_h0.
+// The affine scan walked from each sequence's last unit to its first: S_end(u - 1) = M_u^T
+// S_end(u) + B'_u from S_end(last) = s.h0 (dht, or zero), every unit's end state to s.unit_h0;
+// s.unit_b holds B'_u and s.unit_m the forward's M_u transposed.
 hipError_t launch_affine_scan_reverse(const SplitArgs &s, hipStream_t stream);
 
 }  // namespace gdn

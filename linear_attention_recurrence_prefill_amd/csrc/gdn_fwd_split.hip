@@ -1,5 +1,5 @@
 // Exact split of the forward: the middle pass, which turns every unit's pair (B, M) into the
-// true state at the unit's start.
+// true state at the unit's start; and the same walk in reverse for the backward.
 //
 // The recurrence over one unit's chunks is affine in the state it starts from: after the unit
 // the state is M S_start + B, with B the state reached from zero and M the state reached from
@@ -10,10 +10,19 @@
 // the sequence's initial state, and the last pass reruns every unit from its true start with
 // the output.  The result equals the unsplit recurrence up to rounding.
 //
-// One workgroup per (16-column block, head, sequence): the columns of the state are independent
-// under left multiplication by M, so the eight column blocks of a head walk the units without
-// talking to each other.  Eight waves, wave w owning state rows 16 w .. 16 w + 15 of the block,
-// products in fp32 (v_mfma_f32_16x16x4_f32).
+// The backward's state gradient obeys the transposed map: the gradient at a unit's start is
+// M_u^T times the gradient at its end plus B'_u (the unit's own contribution, from a zero end
+// gradient), so the reverse walk applies the forward's M transposed.
+//
+// One workgroup of eight waves per (16-column block, head, sequence): the columns of the state
+// are independent under left multiplication by M.  Wave w computes rows 16 w .. 16 w + 15 of the
+// block with v_mfma_f32_16x16x32_bf16 on split operands (x = hi + lo, two bf16 each; the product
+// hi hi' + hi lo' + lo hi', about 16 significant bits per operand), its rows of M (or M^T)
+// prefetched into registers kPre units ahead, so each step waits only for the state of the step
+// before: written to LDS as a bf16 head and remainder, column-major, in one of two buffers (one
+// barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids congruent
+// modulo 8, which round-robin dispatch places on one XCD, so their reads of the same M share its
+// L2.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -22,7 +31,8 @@ namespace gdn {
 namespace {
 
 constexpr int kD = 128;
-constexpr int kLS = kD + 4;  // fp32 row stride of the transposed column block in LDS
+constexpr int kPre = 4;           // units whose maps are in flight ahead of the one applied
+constexpr int kSR = 2 * kD + 16;  // bytes per column of the bf16 state block in LDS (padded)
 
 // Units of sequence n for segment length L (max(1, ceil(chunks / L)) each, in sequence order, as
 // the forward's unit lookup numbers them): the first unit's index and the count.  Called by one
@@ -51,70 +61,152 @@ __device__ bool seq_units(const int32_t *cu, int N, int64_t T, int L, int n, int
   return true;
 }
 
+__device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for 8 values (items 0..3 from x0).
+__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &lo) {
+  const bf16x4 h0 = to_bf16x4(x0), h1 = to_bf16x4(x1);
+  hi = cat8(h0, h1);
+  lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
+}
+
 }  // namespace
 
-// kReverse: the backward's walk, from each sequence's last unit to its first (the maps are the
-// reverse chain's, S the state gradient at a unit's end, s.h0 the gradient after the sequence).
+// kReverse: the backward's walk, from each sequence's last unit to its first, with the maps
+// M_u^T (the forward's M, stored transposed by the first pass of the backward's recompute) and
+// B'_u; S is the state gradient at a unit's end and s.h0 the gradient after the sequence.
 template <bool kReverse>
 __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
-  __shared__ __attribute__((aligned(16))) float st[16 * kLS];  // st[col * kLS + row]
-  const int cb = blockIdx.x, h = blockIdx.y, n = blockIdx.z, H = s.H;
+  __shared__ __attribute__((aligned(16))) char s_hi[2][16 * kSR];
+  __shared__ __attribute__((aligned(16))) char s_lo[2][16 * kSR];
+  const int id = blockIdx.x;
+  const int cb = (id >> 3) & 7;
+  const int64_t pair = (id & 7) + 8 * (int64_t)(id >> 6);
+  const int H = s.H;
+  if (pair >= (int64_t)H * s.N) return;
+  const int h = (int)(pair % H), n = (int)(pair / H);
   const int lane = threadIdx.x & 63, gq = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   int64_t first = 0;
   int count = 0;
   if (!seq_units(s.cu, s.N, s.T, s.L, n, lane, first, count)) return;
+  // the same in every lane: scalar registers, so the walk's branches are scalar
+  first = (int64_t)__builtin_amdgcn_readfirstlane((unsigned)(first & 0xffffffff)) |
+          ((int64_t)__builtin_amdgcn_readfirstlane((unsigned)(first >> 32)) << 32);
+  count = __builtin_amdgcn_readfirstlane(count);
   // never past the units the buffers were sized for (a device table that disagrees with the
   // host copy the caller planned with)
   if (first >= s.units) return;
   if (first + count > s.units) count = (int)(s.units - first);
-  const int row0 = 16 * w + 4 * gq, col = 16 * cb + cl;  // this lane: rows row0 .. row0 + 3
+  const int rowA = 16 * w + cl;      // the row of M (of M^T) this lane feeds to the MFMAs
+  const int rowC = 16 * w + 4 * gq;  // rows rowC .. rowC + 3 of the result in this lane
+  const int col = 16 * cb + cl;
   const int64_t dd = (int64_t)kD * kD;
 
   f32x4 S = zero4();
   if (s.h0 != nullptr) {
-    const float *hp = s.h0 + (int64_t)n * s.h0_stride + h * dd;
+    const float *hp = s.h0 + (int64_t)n * s.h0_stride + (int64_t)h * dd;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) S[i] = hp[(row0 + i) * kD + col];
+    for (int i = 0; i < 4; ++i) S[i] = hp[(rowC + i) * kD + col];
   }
-  for (int step = 0; step < count; ++step) {
-    const int64_t u = first + (kReverse ? count - 1 - step : step);
-    float *dst = s.unit_h0 + (u * H + h) * dd;
+  // the start state has landed before any map is fetched, so that no wait for it is left in the
+  // walk (where it would also hold back the maps in flight)
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // the walk's first unit, and the elements between the maps (states) of consecutive steps
+  const int64_t u0 = kReverse ? first + count - 1 : first;
+  const int64_t ustep = (kReverse ? -(int64_t)H : (int64_t)H) * dd;
+  const float *m0 = s.unit_m + (u0 * H + h) * dd + (int64_t)rowA * kD + 8 * gq;
+  const float *b0 = s.unit_b + (u0 * H + h) * dd + (int64_t)rowC * kD + col;
+  float *s0 = s.unit_h0 + (u0 * H + h) * dd + (int64_t)rowC * kD + col;
+  auto store = [&](int step) {
+    float *dst = s0 + step * ustep;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(row0 + i) * kD + col] = S[i];
-    if (step + 1 == count) break;
-    // S <- M_u S + B_u.  The contraction index of MFMA j of block b is 16 b + 4 gq + j on both
-    // operands, so that each lane reads 4 consecutive entries of M's row and of S's column.
-    *reinterpret_cast<f32x4 *>(&st[cl * kLS + row0]) = S;
-    __syncthreads();
-    const float *Mu = s.unit_bm + ((s.units + u) * H + h) * dd;
-    const float *Bu = s.unit_bm + (u * H + h) * dd;
-    f32x4 acc;
+    for (int i = 0; i < 4; ++i) dst[i * kD] = S[i];
+  };
+  store(0);
+  const int nmaps = count - 1;  // maps applied along the walk
+  if (nmaps <= 0) return;
+  // The maps of step m (m < nmaps): this lane's eight A-operand items of M (M^T) for each of the
+  // four 32-wide k-steps (k = 32 ks + 8 gq + 0..7), and its four entries of B.  Fetches past the
+  // last map reload the last one (unused), so the pipeline has no branches.
+  f32x4 am[kPre][8], bm[kPre];
+  auto fetch = [&](f32x4(&a)[8], f32x4 &b, int m) {
+    const int64_t off = min(m, nmaps - 1) * ustep;
+    const float *mr = m0 + off;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = Bu[(row0 + i) * kD + col];
-    const float *mrow = Mu + (int64_t)(16 * w + cl) * kD + 4 * gq;
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(mrow + 16 * b);
-      const f32x4 b4 = *reinterpret_cast<const f32x4 *>(&st[cl * kLS + 16 * b + 4 * gq]);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mma_f32(a4[j], b4[j], acc);
+    for (int ks = 0; ks < 4; ++ks) {
+      a[2 * ks] = *reinterpret_cast<const f32x4 *>(mr + 32 * ks);
+      a[2 * ks + 1] = *reinterpret_cast<const f32x4 *>(mr + 32 * ks + 4);
     }
-    __syncthreads();  // every wave has read the block before it is overwritten
-    S = acc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b[i] = b0[off + i * kD];
+  };
+  // S <- M S + B with the maps of slot j (M^T in the reverse walk); the state goes through LDS as
+  // a bf16 head and remainder, column-major, in the buffer of the step's parity
+  auto apply = [&](f32x4(&a)[8], f32x4 &b, int parity) {
+    char *bh = s_hi[parity], *bl = s_lo[parity];
+    {
+      const bf16x4 hi = to_bf16x4(S);
+      *reinterpret_cast<bf16x4 *>(bh + cl * kSR + rowC * 2) = hi;
+      *reinterpret_cast<bf16x4 *>(bl + cl * kSR + rowC * 2) = to_bf16x4(S - to_f32x4(hi));
+    }
+    __syncthreads();
+    f32x4 acc0 = b, acc1 = zero4(), acc2 = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 ahi, alo;
+      split8(a[2 * ks], a[2 * ks + 1], ahi, alo);
+      const int off = cl * kSR + (32 * ks + 8 * gq) * 2;
+      const bf16x8 bhi = *reinterpret_cast<const bf16x8 *>(bh + off);
+      const bf16x8 blo = *reinterpret_cast<const bf16x8 *>(bl + off);
+      acc0 = mma_bf16(ahi, bhi, acc0);
+      acc1 = mma_bf16(ahi, blo, acc1);
+      acc2 = mma_bf16(alo, bhi, acc2);
+    }
+    S = acc0 + (acc1 + acc2);
+  };
+#pragma unroll
+  for (int p = 0; p < kPre; ++p) fetch(am[p], bm[p], p);
+  int m = 0;
+  for (; m + kPre <= nmaps; m += kPre) {
+#pragma unroll
+    for (int j = 0; j < kPre; ++j) {
+      apply(am[j], bm[j], j & 1);
+      fetch(am[j], bm[j], m + j + kPre);
+      store(m + j + 1);
+    }
+  }
+  // the remaining maps (fewer than kPre) are in slots 0 .. nmaps - m - 1
+#pragma unroll
+  for (int j = 0; j < kPre - 1; ++j) {
+    if (m + j >= nmaps) break;
+    apply(am[j], bm[j], j & 1);
+    store(m + j + 1);
   }
 }
 
-hipError_t launch_affine_scan(const SplitArgs &s, hipStream_t stream) {
+static_assert(kPre % 2 == 0, "the LDS buffer of a step is chosen by the step's parity");
+
+namespace {
+hipError_t launch_scan(const SplitArgs &s, bool reverse, hipStream_t stream) {
   if (s.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(affine_scan_kernel<false>, dim3(kD / 16, s.H, s.N), dim3(512), 0, stream, s);
+  const int64_t groups = ((int64_t)s.H * s.N + 7) / 8;
+  if (groups * 64 > 0x7fffffff) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(groups * 64));
+  if (reverse)
+    hipLaunchKernelGGL(affine_scan_kernel<true>, grid, dim3(512), 0, stream, s);
+  else
+    hipLaunchKernelGGL(affine_scan_kernel<false>, grid, dim3(512), 0, stream, s);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_affine_scan(const SplitArgs &s, hipStream_t stream) {
+  return launch_scan(s, false, stream);
 }
 
 hipError_t launch_affine_scan_reverse(const SplitArgs &s, hipStream_t stream) {
-  if (s.N <= 0) return hipSuccess;
-  hipLaunchKernelGGL(affine_scan_kernel<true>, dim3(kD / 16, s.H, s.N), dim3(512), 0, stream, s);
-  return hipGetLastError();
+  return launch_scan(s, true, stream);
 }
 
 }  // namespace gdn

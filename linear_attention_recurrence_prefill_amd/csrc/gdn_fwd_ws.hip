@@ -204,7 +204,9 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const int64_t ts0 = a.cu[seq], ts1 = a.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > a.T) return;  // malformed cu_seqlens: touch nothing
   const int nchunks_seq = (int)((ts1 - ts0 + kChunk - 1) / kChunk);
-  if (kTransition && c1 == nchunks_seq) return;  // a sequence's last unit has no successor
+  // a sequence's last unit has no successor; its map M is still formed when asked (the reverse
+  // walk of the backward reads M transposed for every unit but a sequence's first)
+  if (kTransition && c1 == nchunks_seq && !(is_m && a.unit_mt != nullptr && c0 > 0)) return;
   const int64_t tok_bytes = (int64_t)H * kRowBytes;      // stride of one token in v, o
   const int64_t tok_qk = (int64_t)a.HK * kRowBytes;      // ... in q, k
   const int hk = h / (H / a.HK);                          // this value head's key head
@@ -580,6 +582,15 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             dst[(16 * mt + 4 * gq + i) * kD + ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)] = S[mt][nt][i];
+    }
+    if (kTransition && is_m && a.unit_mt != nullptr && c0 > 0) {  // M^T for the reverse walk
+      float *dt = a.unit_mt + ((int64_t)unit * H + h) * kD * kD;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          *reinterpret_cast<f32x4 *>(dt + (ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)) * kD +
+                                     16 * mt + 4 * gq) = S[mt][nt];
     }
   } else if (wave == 7) {
     // ================ wave 7: gate vectors, and K and Q from HBM into LDS, one chunk ahead ===========

@@ -58,6 +58,10 @@ struct FwdArgs {
   float *unit_out;
   int64_t units;
   uint32_t *faults;  // the device's fault flags (kFault*), or null
+  // exact split's first pass for the backward: when not null, M^T of every unit but a
+  // sequence's first goes here too ([units, H, D, D]; the reverse walk of the state gradient
+  // applies M^T), and M is then also formed for each sequence's last unit
+  float *unit_mt;
 };
 
 // Arguments of the exact split's middle pass (gdn_fwd_split.hip).
@@ -67,8 +71,9 @@ struct SplitArgs {
   int32_t N, H, L;
   const float *h0;
   int64_t h0_stride;
-  const float *unit_bm;  // [2, units, H, D, D]: B, then M
-  float *unit_h0;        // [units, H, D, D]: the true state at each unit's start
+  const float *unit_b;   // [units, H, D, D]: each unit's B (B' in the reverse walk)
+  const float *unit_m;   // [units, H, D, D]: each unit's M (M^T in the reverse walk)
+  float *unit_h0;        // [units, H, D, D]: the true state at each unit's start (end)
   int64_t units;
 };
 

@@ -160,7 +160,8 @@ def test_status_strings(lib):
 
 def test_bwd_recompute_split_workspace(lib):
     """bf16, d = 128 with num_seqs * H < P: the backward's forward recompute runs the exact split,
-    which adds per (unit, head) a pair (B, M) and a start state (3 fp32 states of 128 x 128).
+    which adds per (unit, head) a pair (B, M), a start state and M transposed for the reverse
+    walk (4 fp32 states of 128 x 128).
     Without the host cu_seqlens the unit count is bounded by ceil((ceil(T / 64) + N) / L) + N:
     T = 1024, N = 2, L = 4 (the forward's rule: 3 sqrt(8 * 16 / 256) rounds to 2, floored at 4)
     gives 7 units."""
@@ -169,7 +170,7 @@ def test_bwd_recompute_split_workspace(lib):
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
     p = _problem(num_slots=256)
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
-    assert n2.value - n1.value == 3 * 7 * 8 * 128 * 128 * 4
+    assert n2.value - n1.value == 4 * 7 * 8 * 128 * 128 * 4
     p = _problem(num_slots=256, dtype=0)  # fp32: the general kernel, never split
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
     assert n2.value < n1.value * 2
