@@ -440,10 +440,16 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     }
   }
   float *dst = nullptr;
-  if (kTransition)
-    dst = us.unit_out + ((int64_t)unit * H + h) * dd;
-  else if (c0 == 0 && b.dh0_seq != nullptr)
+  if (kTransition) {  // B' in the reverse walk's operand order (map_b_index)
+    float *bo = us.unit_out + ((int64_t)unit * H + h) * dd;
+#pragma unroll
+    for (int md = 0; md < 8; ++md)
+#pragma unroll
+      for (int nt = 0; nt < kNT; ++nt)
+        *reinterpret_cast<f32x4 *>(bo + map_b_index(16 * md + 4 * gq, col0 + 16 * nt)) = G[md][nt];
+  } else if (c0 == 0 && b.dh0_seq != nullptr) {
     dst = b.dh0_seq + ((int64_t)seq * H + h) * dd;
+  }
   if (dst != nullptr) {
 #pragma unroll
     for (int md = 0; md < 8; ++md)

@@ -18,9 +18,10 @@
 // are independent under left multiplication by M.  Wave w computes rows 16 w .. 16 w + 15 of the
 // block with v_mfma_f32_16x16x32_bf16 on split operands (x = hi + lo, two bf16 each; the product
 // hi hi' + hi lo' + lo hi', about 16 significant bits per operand), its rows of M (or M^T)
-// prefetched into registers kPre units ahead, so each step waits only for the state of the step
-// before: written to LDS as a bf16 head and remainder, column-major, in one of two buffers (one
-// barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids congruent
+// prefetched into registers kPre units ahead (the first passes store the maps in the order of
+// these MFMA operands, so each load instruction reads 1 KiB of consecutive bytes), so each step
+// waits only for the state of the step before: written to LDS as a bf16 head and remainder,
+// column-major, in one of two buffers (one barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids congruent
 // modulo 8, which round-robin dispatch places on one XCD, so their reads of the same M share its
 // L2.
 #include "gdn_bwd_internal.h"
@@ -98,7 +99,6 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   // host copy the caller planned with)
   if (first >= s.units) return;
   if (first + count > s.units) count = (int)(s.units - first);
-  const int rowA = 16 * w + cl;      // the row of M (of M^T) this lane feeds to the MFMAs
   const int rowC = 16 * w + 4 * gq;  // rows rowC .. rowC + 3 of the result in this lane
   const int col = 16 * cb + cl;
   const int64_t dd = (int64_t)kD * kD;
@@ -112,11 +112,14 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   // the start state has landed before any map is fetched, so that no wait for it is left in the
   // walk (where it would also hold back the maps in flight)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-  // the walk's first unit, and the elements between the maps (states) of consecutive steps
+  // the walk's first unit, and the elements between the maps (states) of consecutive steps;
+  // the maps are stored in this pass's operand order (map_m_index, map_b_index): this lane's
+  // items of M for k-step ks and half j are the 16 bytes at 256 (8 w + 2 ks + j) + 4 lane, its
+  // four entries of B the 16 bytes at 4 (64 (8 cb + w) + lane)
   const int64_t u0 = kReverse ? first + count - 1 : first;
   const int64_t ustep = (kReverse ? -(int64_t)H : (int64_t)H) * dd;
-  const float *m0 = s.unit_m + (u0 * H + h) * dd + (int64_t)rowA * kD + 8 * gq;
-  const float *b0 = s.unit_b + (u0 * H + h) * dd + (int64_t)rowC * kD + col;
+  const float *m0 = s.unit_m + (u0 * H + h) * dd + 256 * 8 * w + 4 * lane;
+  const float *b0 = s.unit_b + (u0 * H + h) * dd + 4 * (64 * (8 * cb + w) + lane);
   float *s0 = s.unit_h0 + (u0 * H + h) * dd + (int64_t)rowC * kD + col;
   auto store = [&](int step) {
     float *dst = s0 + step * ustep;
@@ -132,14 +135,9 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   f32x4 am[kPre][8], bm[kPre];
   auto fetch = [&](f32x4(&a)[8], f32x4 &b, int m) {
     const int64_t off = min(m, nmaps - 1) * ustep;
-    const float *mr = m0 + off;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      a[2 * ks] = *reinterpret_cast<const f32x4 *>(mr + 32 * ks);
-      a[2 * ks + 1] = *reinterpret_cast<const f32x4 *>(mr + 32 * ks + 4);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) b[i] = b0[off + i * kD];
+    for (int q = 0; q < 8; ++q) a[q] = *reinterpret_cast<const f32x4 *>(m0 + off + 256 * q);
+    b = *reinterpret_cast<const f32x4 *>(b0 + off);
   };
   // S <- M S + B with the maps of slot j (M^T in the reverse walk); the state goes through LDS as
   // a bf16 head and remainder, column-major, in the buffer of the step's parity

@@ -569,12 +569,29 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       lds_barrier();
     }
 
-    float *dst = nullptr;
-    if (kTransition)
-      dst = a.unit_out + (((int64_t)blockIdx.z * a.units + unit) * H + h) * kD * kD;
-    else if (a.ht != nullptr && c1 == nchunks_seq)
-      dst = a.ht + ((int64_t)seq * H + h) * kD * kD;
-    if (dst != nullptr) {
+    if (kTransition) {
+      // the unit's map in the middle pass's operand order: B (map_b_index), M (map_m_index) and,
+      // for the backward's reverse walk, M^T; this lane holds rows 16 mt + 4 gq + i of column c
+      float *dst = a.unit_out + (((int64_t)blockIdx.z * a.units + unit) * H + h) * kD * kD;
+      float *dt = (is_m && a.unit_mt != nullptr && c0 > 0)
+                      ? a.unit_mt + ((int64_t)unit * H + h) * kD * kD
+                      : nullptr;
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          const int c = ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3);
+          if (!is_m) {
+            *reinterpret_cast<f32x4 *>(dst + map_b_index(16 * mt + 4 * gq, c)) = S[mt][nt];
+          } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[map_m_index(16 * mt + 4 * gq + i, c)] = S[mt][nt][i];
+            if (dt != nullptr)  // M^T[c][r] = M[r][c]: the four rows are consecutive in k
+              *reinterpret_cast<f32x4 *>(dt + map_m_index(c, 16 * mt + 4 * gq)) = S[mt][nt];
+          }
+        }
+    } else if (a.ht != nullptr && c1 == nchunks_seq) {
+      float *dst = a.ht + ((int64_t)seq * H + h) * kD * kD;
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -582,15 +599,6 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             dst[(16 * mt + 4 * gq + i) * kD + ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)] = S[mt][nt][i];
-    }
-    if (kTransition && is_m && a.unit_mt != nullptr && c0 > 0) {  // M^T for the reverse walk
-      float *dt = a.unit_mt + ((int64_t)unit * H + h) * kD * kD;
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          *reinterpret_cast<f32x4 *>(dt + (ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3)) * kD +
-                                     16 * mt + 4 * gq) = S[mt][nt];
     }
   } else if (wave == 7) {
     // ================ wave 7: gate vectors, and K and Q from HBM into LDS, one chunk ahead ===========
