@@ -228,6 +228,21 @@ int64_t max_units(const gdn_problem *p, const int32_t *cu_host, int32_t L) {
   return ceil_div(ceil_div(p->total_tokens, gdn::kChunk) + p->num_seqs, L) + p->num_seqs;
 }
 
+// Segment length of the exact mode's split (a design of this library: the split is not on the
+// pages).  Its final pass runs one workgroup per (unit, head) as the truncate mode does, after a
+// first pass with two workgroups per (unit, head) and a walk along each sequence's units; one
+// workgroup fits per CU.  Starting from the latency model's length, the length doubles until the
+// final pass's workgroups fit in one round of the P slots: a second, partly filled round costs
+// a whole segment's time, while a round with fewer workgroups runs each chunk faster (measured on
+// the 8K packed, 32K x 8-head, 65K training and 64K x 16-head prefix workloads, where this picks
+// the fastest of L = 4 .. 64 every time).  The latency model's floor keeps the walk along a
+// sequence short when there are few heads.
+int32_t exact_segment_chunks(const gdn_problem *p, const int32_t *cu_host, int32_t L, int32_t P) {
+  if (L <= 0 || p->seg_chunks > 0) return L;
+  while (L < (1 << 24) && max_units(p, cu_host, L) * p->num_heads > P) L *= 2;
+  return L;
+}
+
 gdn_status check_cu_host(const gdn_problem *p, const int32_t *cu_host) {
   if (!cu_host) return GDN_OK;
   if (cu_host[0] != 0 || cu_host[p->num_seqs] != p->total_tokens)
@@ -266,6 +281,7 @@ gdn_status fwd_layout(const gdn_problem *p, const int32_t *cu_host, bool dump, F
   }
   const int64_t nc = count_chunks(p, cu_host);
   lay->L = segment_chunks(p, nc, slots, split_ok);
+  if (p->mode == GDN_MODE_EXACT) lay->L = exact_segment_chunks(p, cu_host, lay->L, slots);
   lay->units = max_units(p, cu_host, lay->L);
   // an exact-mode split in which every sequence stays one unit is no split
   if (p->mode == GDN_MODE_EXACT && lay->L > 0 && cu_host && lay->units == p->num_seqs) {
