@@ -418,7 +418,13 @@ gdn_status launch_fwd_passes(const gdn_problem *p, const Tensors &t, const FwdLa
     return GDN_OK;
   }
   switch (fwd_kernel_for(p, dump)) {
-    case FwdKernel::kPipelined: e = gdn::launch_fwd_ws(a, lay.units, stream); break;
+    case FwdKernel::kPipelined:
+      // one workgroup per (sequence, head): the longest sequences first, so that no long one
+      // starts late and stretches the tail of the launch
+      a.longest_first = (lay.L == 0 && p->num_seqs >= 2 && p->num_seqs <= gdn::kMaxLongestFirst &&
+                         lay.units <= 65535) ? 1 : 0;
+      e = gdn::launch_fwd_ws(a, lay.units, stream);
+      break;
     case FwdKernel::kFast: e = gdn::launch_fwd_fast(a, p->d_k, lay.units, stream); break;
     default: e = gdn::launch_fwd(a, p->d_k, p->dtype == GDN_DTYPE_BF16, dump, lay.units, stream);
   }

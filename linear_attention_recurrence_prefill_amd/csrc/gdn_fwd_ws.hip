@@ -183,11 +183,12 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   // wave-uniform role (scalar branches: a wave never steps through the other role's barriers)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int unit = blockIdx.x, h = blockIdx.y, H = a.H;
+  const int unit = a.longest_first ? blockIdx.y : blockIdx.x;
+  const int h = a.longest_first ? blockIdx.x : blockIdx.y, H = a.H;
   const bool is_m = kTransition && blockIdx.z == 1;  // transition pass: the M half
   if (wave == 0) {
     Unit un;
-    const bool ok = find_unit(a.cu, a.N, a.T, a.L, unit, kDump, lane, un);
+    const bool ok = find_unit(a.cu, a.N, a.T, a.L, unit, kDump, lane, un, a.longest_first != 0);
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;
@@ -846,11 +847,11 @@ int fwd_ws_blocks_per_cu() {
 
 hipError_t launch_fwd_ws(const FwdArgs &a, int64_t max_units, hipStream_t stream) {
   if (max_units <= 0) return hipSuccess;
+  const dim3 grid = a.longest_first ? dim3(a.H, (unsigned)max_units) : dim3((unsigned)max_units, a.H);
   if (a.l2norm)
-    hipLaunchKernelGGL((fwd_ws_kernel<false, false, true>), dim3((unsigned)max_units, a.H),
-                       dim3(512), 0, stream, a);
+    hipLaunchKernelGGL((fwd_ws_kernel<false, false, true>), grid, dim3(512), 0, stream, a);
   else
-    hipLaunchKernelGGL(fwd_ws_kernel<false>, dim3((unsigned)max_units, a.H), dim3(512), 0, stream, a);
+    hipLaunchKernelGGL(fwd_ws_kernel<false>, grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

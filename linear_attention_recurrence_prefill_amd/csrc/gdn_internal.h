@@ -10,6 +10,10 @@ constexpr int kChunk = 64;
 // eps of the optional q/k L2 normalisation: row / sqrt(|row|^2 + eps)
 constexpr float kL2NormEps = 1e-6f;
 
+// Most sequences an unsplit forward takes longest first (the ranking runs in one wave per
+// workgroup, four sequences per lane).
+constexpr int kMaxLongestFirst = 256;
+
 // Status bits of the cu_seqlens validation (gdn_validate_cu_seqlens).
 constexpr uint32_t kCuFirstNotZero = 1u;  // cu[0] != 0
 constexpr uint32_t kCuDescending = 2u;    // cu[n + 1] < cu[n] for some n
@@ -63,6 +67,9 @@ struct FwdArgs {
   // sequence's first goes here too ([units, H, D * D] in map_m_index order; the reverse walk of
   // the state gradient applies M^T), and M is then also formed for each sequence's last unit
   float *unit_mt;
+  // unsplit runs of the pipelined kernel: 1 = workgroups take the sequences longest first, with
+  // the grid transposed to (H, N) so that every head of the longest sequence starts first
+  int32_t longest_first;
 };
 
 // Layouts of a unit's maps (B and M, 128 x 128 fp32 each) as the exact split's first passes write

@@ -6,20 +6,53 @@
 
 namespace gdn {
 
+// The sequence with the u-th most chunks, ties in sequence order (u < N <= kMaxLongestFirst).
+// Called by one full wave; every lane returns the same result.  Lane l holds the chunk counts of
+// sequences l, l + 64, .., and ranks them against every count, broadcast by shuffles.
+__device__ inline int seq_by_length(const int32_t *cu, int N, int u, int lane) {
+  int len[4], rank[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int n = lane + 64 * j;
+    len[j] = n < N ? max(0, (cu[n + 1] - cu[n] + kChunk - 1) / kChunk) : -1;
+    rank[j] = 0;
+  }
+#pragma unroll
+  for (int j2 = 0; j2 < 4; ++j2) {
+    if (64 * j2 >= N) break;
+    for (int m2 = 0; m2 < 64; ++m2) {
+      const int m = 64 * j2 + m2;
+      const int lm = __shfl(len[j2], m2, 64);  // -1 past N: ranks no valid sequence
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        rank[j] += (lm > len[j] || (lm == len[j] && m < lane + 64 * j)) ? 1 : 0;
+    }
+  }
+  int seq = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint64_t hit = __ballot(lane + 64 * j < N && rank[j] == u);
+    if (hit) seq = 64 * j + __builtin_ctzll(hit);
+  }
+  return seq;
+}
+
 // Finds unit u by scanning the sequence table 64 entries at a time.  Called by one full wave;
 // every lane returns the same result.  Returns false when u is past the last unit, and also when
 // the scanned part of cu_seqlens is malformed (cu[0] != 0, a descending pair, or an offset past
 // T): then no unit is found, so no workgroup indexes memory from a bad table.  Every sequence
 // before the one returned, and the returned one, have been checked, which bounds the chunk and
 // unit counts before it by the ones the host sized its buffers for.  With L == 0 and no chunk
-// base asked for, unit u is sequence u without a scan; the caller checks its range.
+// base asked for, unit u is sequence u without a scan (with longest_first, the sequence with the
+// u-th most chunks, N <= kMaxLongestFirst); the caller checks its range.
 __device__ inline bool find_unit(const int32_t *cu, int N, int64_t T, int L, int u,
-                                 bool need_base, int lane, Unit &out) {
+                                 bool need_base, int lane, Unit &out, bool longest_first = false) {
   if (L == 0 && !need_base) {
     if (u >= N) return false;
-    out.seq = u;
+    const int seq = longest_first ? seq_by_length(cu, N, u, lane) : u;
+    out.seq = seq;
     out.c0 = 0;
-    out.c1 = max(0, (cu[u + 1] - cu[u] + kChunk - 1) / kChunk);
+    out.c1 = max(0, (cu[seq + 1] - cu[seq] + kChunk - 1) / kChunk);
     out.chunk_base = 0;
     return true;
   }
