@@ -490,12 +490,16 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
     from linear_attention_recurrence_prefill_amd.gdn import make_problem
 
     p = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact")
+    cu_host = inp["cu_seqlens"]
+    cu_arr = (ctypes.c_int32 * len(cu_host))(*[int(x) for x in cu_host])
     nbytes = ctypes.c_size_t(0)
-    assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(nbytes)) == 0
+    assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(p), cu_arr,
+                                                           ctypes.byref(nbytes)) == 0
     ws = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")  # allocated once, outside
 
     def step(i):
-        gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws)
+        gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws,
+                      cu_seqlens_host=cu_host)
 
     r = timed(torch, step, steps, warmup)
     ms = r["median_ms"]
@@ -503,11 +507,12 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
     if with_l2norm:  # the same backward with q and k normalised inside the kernels
         pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact",
                           qk_l2norm=True)
-        assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pn),
+        assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pn), cu_arr,
                                                                ctypes.byref(nbytes)) == 0
         wsn = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")
         rn = timed(torch, lambda i: gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"],
-                                                  cu, dev["dout"], workspace=wsn, qk_l2norm=True),
+                                                  cu, dev["dout"], workspace=wsn, qk_l2norm=True,
+                                                  cu_seqlens_host=cu_host),
                    steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
     achieved = nbytes_alg / (r["mean_ms"] / 1e3) / 1e9

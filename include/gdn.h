@@ -200,12 +200,15 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
 
 /* Bytes of device workspace gdn_chunk_bwd needs for *p: the recomputed per-chunk
  * intermediates ("How to Speed Up GDN Kernels for Qwen Models", section "Lever 2": the hidden
- * states are recomputed in one pass, not stored by the forward) and the reverse chain's
- * per-chunk state gradients.  Sized on the chunk bound ceil(T / 64) + N rather than on a host
- * copy of cu_seqlens: the bound exceeds the exact chunk count by fewer than N chunks, and it
- * covers every chunk index a device table can produce, so the kernels' writes stay inside the
- * workspace whatever the device table holds.  Host only. */
-gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes);
+ * states are recomputed in one pass, not stored by the forward), the reverse chain's per-chunk
+ * state gradients and, when the exact split runs, its per-unit maps.  The per-chunk arrays are
+ * sized on the chunk bound ceil(T / 64) + N (fewer than N chunks above the exact count), which
+ * covers every chunk index a device table can produce.  cu_seqlens_host (optional, N + 1 host
+ * int32, checked like the forward's) sets the split's segment length and unit count exactly
+ * (without it the unit bound is used); pass the same pointer (or NULL) to gdn_chunk_bwd.
+ * Host only. */
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
+                                        size_t *bytes);
 
 /* Backward of the exact forward (mode must be GDN_MODE_EXACT): given dout (dtype, [T, H, d_v])
  * and optionally dht ([N, H, d_k, d_v] fp32, NULL = zero), writes dq, dk (dtype, [T, Hk, d_k];
@@ -215,12 +218,12 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes);
  * summed over all sequences when h0_seq_stride is 0 (a state shared by every sequence collects
  * the sum of their gradients, "Musings on long-context fine-tuning", section "Backward
  * through P").  Hidden states are recomputed, not stored ("How to Speed Up GDN Kernels for
- * Qwen Models", section "Lever 2"). */
+ * Qwen Models", section "Lever 2").  cu_seqlens_host is optional, as for the workspace query. */
 gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
                          const float *g, const void *beta, const int32_t *cu_seqlens,
-                         const float *h0, const void *dout, const float *dht, void *dq, void *dk,
-                         void *dv, float *dg, void *dbeta, float *dh0, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream);
+                         const int32_t *cu_seqlens_host, const float *h0, const void *dout,
+                         const float *dht, void *dq, void *dk, void *dv, float *dg, void *dbeta,
+                         float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* One decode step ("How to Speed Up GDN Kernels for Qwen Models", section "FAQ": decode is the
  * recurrent step on one token): every (sequence b, head h) state advances by one token of the

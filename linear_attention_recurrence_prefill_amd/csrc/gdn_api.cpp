@@ -2,11 +2,12 @@
 // plan's host-side parameters and kernel dispatch.  Declarations and conventions: include/gdn.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
-#include <cstdlib>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 
@@ -228,19 +229,31 @@ int64_t max_units(const gdn_problem *p, const int32_t *cu_host, int32_t L) {
   return ceil_div(ceil_div(p->total_tokens, gdn::kChunk) + p->num_seqs, L) + p->num_seqs;
 }
 
-// Segment length of the exact mode's split (a design of this library: the split is not on the
-// pages).  Its final pass runs one workgroup per (unit, head) as the truncate mode does, after a
-// first pass with two workgroups per (unit, head) and a walk along each sequence's units; one
-// workgroup fits per CU.  Starting from the latency model's length, the length doubles until the
-// final pass's workgroups fit in one round of the P slots: a second, partly filled round costs
-// a whole segment's time, while a round with fewer workgroups runs each chunk faster (measured on
-// the 8K packed, 32K x 8-head, 65K training and 64K x 16-head prefix workloads, where this picks
-// the fastest of L = 4 .. 64 every time).  The latency model's floor keeps the walk along a
-// sequence short when there are few heads.
+// Segment length of the exact split, forward and backward (a design of this library: the split
+// is not on the pages).  The split's last pass runs one workgroup per (unit, head), as the
+// truncate mode does, after a first pass with one or two workgroups per (unit, head) and a walk
+// along each sequence's units; one workgroup fits per CU.  The length is the smallest one, not
+// below the latency model's, for which the last pass's workgroups fit in one round of the P
+// slots: a second, partly filled round costs a whole segment's time, while a round with fewer
+// workgroups runs each chunk faster.  Measured on the 65K-token training batch (six documents,
+// 8 heads): forward 0.365 ms at 16 chunks, 0.276 ms at 35 (this rule), 0.320 ms at 64; backward
+// 2.21 ms at 16, 1.95 ms at 36.  The latency model's floor keeps the walk along a sequence short
+// when there are few heads.  Exact unit counts need the host copy of cu_seqlens; without it the
+// unit bound makes the length somewhat longer.
 int32_t exact_segment_chunks(const gdn_problem *p, const int32_t *cu_host, int32_t L, int32_t P) {
   if (L <= 0 || p->seg_chunks > 0) return L;
-  while (L < (1 << 24) && max_units(p, cu_host, L) * p->num_heads > P) L *= 2;
-  return L;
+  const auto fits = [&](int64_t len) { return max_units(p, cu_host, (int32_t)len) * p->num_heads <= P; };
+  if (fits(L)) return L;
+  // the units fall as the length grows: the smallest fitting length by bisection, at most the
+  // total chunk count (where every sequence is one unit)
+  int64_t hi = std::max<int64_t>(L, ceil_div(p->total_tokens, gdn::kChunk) + 1);
+  if (!fits(hi)) return (int32_t)std::min<int64_t>(hi, INT32_MAX);
+  int64_t lo = L;  // lo does not fit, hi fits
+  while (hi - lo > 1) {
+    const int64_t mid = lo + (hi - lo) / 2;
+    (fits(mid) ? hi : lo) = mid;
+  }
+  return (int32_t)hi;
 }
 
 gdn_status check_cu_host(const gdn_problem *p, const int32_t *cu_host) {
@@ -572,8 +585,10 @@ bool bwd_bf16_path(const gdn_problem *p) { return p->dtype == GDN_DTYPE_BF16 && 
 // The recompute's (and the reverse chain's) segment length: the forward's exact-split rule
 // (measured on the 65K-token training workload: 2.42 ms per call at 16 chunks, 2.50 at 8, 2.54 at
 // 32, 2.89 at 4); 0 (unsplit) where the forward would not split.
-gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
+gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L) {
   const int64_t T = p->total_tokens, H = p->num_heads, D = p->d_k;
+  // per-chunk arrays on the chunk bound, whatever the host copy says: chunk indices come from
+  // the device table
   L->nc = ceil_div(T, gdn::kChunk) + p->num_seqs;
   L->L = 0;
   L->units = 0;
@@ -585,9 +600,13 @@ gdn_status bwd_layout(const gdn_problem *p, BwdLayout *L) {
     }
     gdn_problem pe = *p;
     pe.mode = GDN_MODE_EXACT;  // the backward is defined for the exact forward
-    const int32_t Lf = segment_chunks(&pe, count_chunks(p, nullptr), slots, true);
-    L->L = Lf;
-    if (L->L > 0) L->units = max_units(p, nullptr, L->L);
+    const int32_t Lf = segment_chunks(&pe, count_chunks(p, cu_host), slots, true);
+    L->L = exact_segment_chunks(&pe, cu_host, Lf, slots);
+    if (L->L > 0) L->units = max_units(p, cu_host, L->L);
+    if (L->L > 0 && cu_host && L->units == p->num_seqs) {  // every sequence is one unit: no split
+      L->L = 0;
+      L->units = 0;
+    }
     if (L->units > INT32_MAX) return fail(GDN_ERR_BAD_SHAPE, "too many work units");
   }
   const size_t esz = p->dtype == GDN_DTYPE_BF16 ? 2 : 4;
@@ -695,12 +714,15 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
 
 extern "C" {
 
-gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes) {
+gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
+                                        size_t *bytes) {
   gdn_status s = check_problem(p);
   if (s != GDN_OK) return s;
   if (!bytes) return fail(GDN_ERR_NULL_ARG, "bytes is NULL");
+  s = check_cu_host(p, cu_seqlens_host);
+  if (s != GDN_OK) return s;
   BwdLayout L;
-  s = bwd_layout(p, &L);
+  s = bwd_layout(p, cu_seqlens_host, &L);
   if (s != GDN_OK) return s;
   *bytes = L.total;
   return GDN_OK;
@@ -708,10 +730,12 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, size_t *bytes) {
 
 gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
                          const float *g, const void *beta, const int32_t *cu_seqlens,
-                         const float *h0, const void *dout, const float *dht, void *dq, void *dk,
-                         void *dv, float *dg, void *dbeta, float *dh0, void *workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+                         const int32_t *cu_seqlens_host, const float *h0, const void *dout,
+                         const float *dht, void *dq, void *dk, void *dv, float *dg, void *dbeta,
+                         float *dh0, void *workspace, size_t workspace_bytes, hipStream_t stream) {
   gdn_status s = check_problem(p);
+  if (s != GDN_OK) return s;
+  s = check_cu_host(p, cu_seqlens_host);
   if (s != GDN_OK) return s;
   if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
   if (p->total_tokens > 0 && (!dout || !dq || !dk || !dv || !dg || !dbeta))
@@ -735,7 +759,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     return e == hipSuccess ? GDN_OK : hip_fail(e, "dh0 of empty sequences");
   }
   BwdLayout L;
-  s = bwd_layout(p, &L);
+  s = bwd_layout(p, cu_seqlens_host, &L);
   if (s != GDN_OK) return s;
   if (!workspace) return fail(GDN_ERR_NULL_ARG, "workspace is NULL");
   if (workspace_bytes < L.total)

@@ -22,7 +22,8 @@ _MODES = {"exact": GDN_MODE_EXACT, "truncate": GDN_MODE_TRUNCATE}
 
 # Every exported entry point of include/gdn.h.
 EXPORTS = ("gdn_problem_init", "gdn_chunk_fwd_workspace_size", "gdn_chunk_fwd",
-           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates", "gdn_chunk_bwd_workspace_size",
+           "gdn_chunk_fwd_noalloc", "gdn_chunk_fwd_plan", "gdn_chunk_fwd_intermediates",
+           "gdn_chunk_bwd_workspace_size",
            "gdn_chunk_bwd", "gdn_decode_step", "gdn_validate_cu_seqlens", "gdn_set_debug",
            "gdn_get_debug", "gdn_device_faults", "gdn_status_string", "gdn_last_error",
            "gdn_calib_copy", "gdn_calib_mfma_bf16")
@@ -77,10 +78,10 @@ def load_library() -> ctypes.CDLL:
     lib.gdn_chunk_fwd_intermediates.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 vp, vp, vp, vp, vp, sz, vp]
     lib.gdn_chunk_fwd_intermediates.restype = st
-    lib.gdn_chunk_bwd_workspace_size.argtypes = [P, ctypes.POINTER(sz)]
+    lib.gdn_chunk_bwd_workspace_size.argtypes = [P, i32p, ctypes.POINTER(sz)]
     lib.gdn_chunk_bwd_workspace_size.restype = st
-    lib.gdn_chunk_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                  vp, vp, sz, vp]
+    lib.gdn_chunk_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, i32p, vp, vp, vp, vp, vp, vp, vp,
+                                  vp, vp, vp, sz, vp]
     lib.gdn_chunk_bwd.restype = st
     lib.gdn_decode_step.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32,
@@ -332,12 +333,14 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
 
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.0,
-              need_dh0=True, workspace=None, seg_chunks=0, num_slots=0, qk_l2norm=False):
+              need_dh0=True, workspace=None, seg_chunks=0, num_slots=0, qk_l2norm=False,
+              cu_seqlens_host=None):
     """Backward of the exact forward.  Returns dict(dq, dk, dv, dg, dbeta, dh0).  dh0 is
     [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D]).
     seg_chunks / num_slots set the segment length of the forward recompute's split and the
     workgroup slots it is planned for (0: chosen by the library).  qk_l2norm: backward of the
-    forward with q and k normalised inside the kernels (dq, dk are the raw inputs' gradients)."""
+    forward with q and k normalised inside the kernels (dq, dk are the raw inputs' gradients).
+    cu_seqlens_host: an optional host copy of cu_seqlens (sets the recompute split exactly)."""
     lib = load_library()
     T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
@@ -348,8 +351,9 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
                      num_slots=num_slots,
                      h0_seq_stride=stride if stride is not None else H * D * D, num_k_heads=Hk,
                      qk_l2norm=qk_l2norm)
+    cu_h = _host_cu(cu_seqlens, cu_seqlens_host)
     ws_bytes = ctypes.c_size_t(0)
-    _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(ws_bytes)))
+    _check(lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), cu_h, ctypes.byref(ws_bytes)))
     workspace = _workspace(workspace, ws_bytes.value, q.device)
     out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
                dg=torch.empty_like(g), dbeta=torch.empty_like(beta), dh0=None)
@@ -357,8 +361,8 @@ def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.
         shape = (H, D, D) if stride == 0 else (N, H, D, D)
         out["dh0"] = torch.empty(shape, dtype=torch.float32, device=q.device)
     _check(lib.gdn_chunk_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                             _ptr(cu_seqlens), _ptr(h0), _ptr(dout), _ptr(dht), _ptr(out["dq"]),
-                             _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
+                             _ptr(cu_seqlens), cu_h, _ptr(h0), _ptr(dout), _ptr(dht),
+                             _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]), _ptr(out["dg"]),
                              _ptr(out["dbeta"]), _ptr(out["dh0"]), _ptr(workspace),
                              _nbytes(workspace), _stream()))
     return out

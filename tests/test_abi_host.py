@@ -76,7 +76,7 @@ def test_bad_problem_rejected_on_host(lib, field, value, status):
     p = _problem(**{field: value})
     n = ctypes.c_size_t(0)
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == status
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == status
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == status
     assert lib.gdn_last_error()
 
 
@@ -94,8 +94,8 @@ def test_null_pointers_rejected_before_launch(lib):
     st = lib.gdn_chunk_fwd(ctypes.byref(p), None, ptr, ptr, ptr, ptr, ptr, None, None, ptr, None,
                            None, 0, None)
     assert st == 1
-    st = lib.gdn_chunk_bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, ptr,
-                           ptr, ptr, ptr, ptr, None, None, 0, None)
+    st = lib.gdn_chunk_bwd(ctypes.byref(p), ptr, ptr, ptr, ptr, ptr, ptr, None, None, None, None,
+                           ptr, ptr, ptr, ptr, ptr, None, None, 0, None)
     assert st == 1
 
 
@@ -129,7 +129,7 @@ def test_workspace_sizes(lib):
     p = _problem(num_slots=256, mode=1)  # truncate mode: no scratch
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
     assert n.value == 0
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
     assert n.value > 1024 * 8 * 128 * 4
 
 
@@ -167,12 +167,12 @@ def test_bwd_recompute_split_workspace(lib):
     gives 7 units."""
     n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
     p = _problem(num_slots=1)  # num_seqs * H >= P: the recompute is not split
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n1)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n1)) == 0
     p = _problem(num_slots=256)
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n2)) == 0
     assert n2.value - n1.value == 4 * 7 * 8 * 128 * 128 * 4
     p = _problem(num_slots=256, dtype=0)  # fp32: the general kernel, never split
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n2)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n2)) == 0
     assert n2.value < n1.value * 2
 
 
@@ -226,7 +226,7 @@ def test_qk_l2norm_accepted_for_every_dtype_and_size(lib, dtype, d):
     n = ctypes.c_size_t(0)
     p = _problem(qk_l2norm=1, d_k=d, d_v=d, dtype=dtype, num_slots=256)
     assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
-    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), ctypes.byref(n)) == 0
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n)) == 0
 
 
 def test_binding_has_every_compute_entry_point():
@@ -277,3 +277,32 @@ def test_noalloc_refuses_problems_beyond_its_scratch(lib):
                                    None, fake, None, None)
     assert rc == 6, lib.gdn_last_error()
     assert b"static scratch" in lib.gdn_last_error()
+
+
+def test_exact_split_segment_length_fills_one_round(lib):
+    """The exact split's segment length: the shortest (not below the latency model's) whose last
+    pass fits in one round of P workgroups, so a non-power of two when the documents ask for it.
+    65536 tokens in documents of 191, 231, 83, 209, 245 and 68 chunks, 8 heads, P = 256: the
+    latency model gives 16 (68 units, 544 workgroups); 35 gives 6 + 7 + 3 + 6 + 7 + 2 = 31 units
+    (248 workgroups) and 34 gives 33.  The forward's workspace holds 3 states per (unit, head),
+    the backward's 4 per (unit, head) on top of its per-chunk arrays."""
+    chunks = [191, 231, 83, 209, 245, 68]
+    lens = [64 * c for c in chunks]
+    lens[-1] -= 64 * sum(chunks) - 65536 if sum(lens) > 65536 else 0
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    T = cu[-1]
+    arr = (ctypes.c_int32 * len(cu))(*cu)
+    p = _problem(total_tokens=T, num_seqs=6, num_heads=8, mode=0, num_slots=256)
+    n = ctypes.c_size_t(0)
+    assert lib.gdn_chunk_fwd_workspace_size(ctypes.byref(p), arr, ctypes.byref(n)) == 0
+    state = 128 * 128 * 4
+    units = sum((c + 34) // 35 for c in chunks)
+    assert units == 31
+    assert n.value == 3 * units * 8 * state
+    nb1, nb2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), arr, ctypes.byref(nb1)) == 0
+    p1 = _problem(total_tokens=T, num_seqs=6, num_heads=8, mode=0, num_slots=6 * 8)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p1), arr, ctypes.byref(nb2)) == 0
+    assert nb1.value - nb2.value == 4 * units * 8 * state  # num_seqs * H >= P: no split

@@ -32,7 +32,7 @@ def _oargs(inp, heads=None):
     return out
 
 
-def _check_bwd(gdn, oracle_mod, inp, label, dht_scale=0.0, scale=1.0, heads=None):
+def _check_bwd(gdn, oracle_mod, inp, label, dht_scale=0.0, scale=1.0, heads=None, **kw):
     d = to_dev(inp)
     rng = np.random.default_rng(123)
     dout = inp.get("dout")
@@ -50,7 +50,7 @@ def _check_bwd(gdn, oracle_mod, inp, label, dht_scale=0.0, scale=1.0, heads=None
     if dht_scale:
         dht = (dht_scale * rng.standard_normal((N, H, D, D))).astype(np.float32)
         dht_d = torch.from_numpy(dht).cuda()
-    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], dout_d, d["h0"], dht_d, scale=scale)
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], dout_d, d["h0"], dht_d, scale=scale, **kw)
     torch.cuda.synchronize()
     sel = heads if heads is not None else slice(None)
     h0 = inp["h0"]
@@ -90,17 +90,26 @@ def test_train_65k_forward_and_backward(gdn, oracle_mod):
     """The training workload: 65536 tokens packed from documents of U{4096..16384} tokens, H=8,
     d=128, bf16, dO ~ N(0, 1) ("How to Speed Up GDN Kernels for Qwen Models", section "What it
     adds up to": the backward at 16K-256K tokens).  The forward's o and final states, then every
-    gradient, on all 8 heads, per (document, head) and per 4096-token block."""
+    gradient, on all 8 heads, per (document, head) and per 4096-token block.  Both calls get the
+    host copy of cu_seqlens, as the benchmark's do: the exact split then takes the shortest
+    segment length (not below the latency model's 16) whose last pass fits one round of 256
+    workgroups, 35 chunks for these documents."""
     inp = workload("train")
     d = to_dev(inp)
-    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None)
+    cu_h = inp["cu_seqlens"]
+    plan = gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], 8, 128, torch.bfloat16, mode="exact",
+                              num_slots=256, cu_seqlens_host=cu_h)
+    chunks = (np.diff(cu_h) + 63) // 64
+    assert plan["L"] == 35 and len(plan["seq"]) == int(((chunks + 34) // 35).sum()) <= 32
+    o, ht = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None, num_slots=256, cu_seqlens_host=cu_h)
     torch.cuda.synchronize()
     o_ref, ht_ref = oracle_mod.fwd_recurrent(*_oargs(inp), inp["cu_seqlens"])
     print("[train 65K forward]", flush=True)
     report("o", np64(o), o_ref, 5e-3, cu=inp["cu_seqlens"])
     report("ht", np64(ht), ht_ref, 5e-3, cu=inp["cu_seqlens"], states=True)
     del o, ht, o_ref, ht_ref
-    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K, all 8 heads")
+    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K, all 8 heads", num_slots=256,
+               cu_seqlens_host=cu_h)
 
 
 def test_bwd_shared_initial_state_sums_branches(gdn, oracle_mod):
