@@ -83,6 +83,10 @@ def parse():
                          "forward")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the forward on the pages' other workloads")
+    ap.add_argument("--only", choices=["truncate", "exact", "workloads", "backward", "decode"],
+                    default=None,
+                    help="profiling aid: run only this path (after the same warmup) and print its "
+                         "object alone, not the benchmark line")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run 5 device copies of MIB MiB each (reads and writes MIB MiB per "
                          "launch): the reference for scaling HBM traffic counters, then exit")
@@ -231,6 +235,8 @@ def main():
               "not supported; heads and documents shard across GPUs without communication).",
               file=sys.stderr)
         return 2
+    if args.only:
+        return only_path(args)
     import torch
 
     from gdn_inputs import workload
@@ -333,6 +339,35 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(inp)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def only_path(args):
+    """One path alone, for profiling runs (rocprofv3 attributes every kernel of the run to it)."""
+    import torch
+
+    from gdn_inputs import workload
+    import linear_attention_recurrence_prefill_amd as gdn
+
+    gdn.load_library()
+    out = {"only": args.only}
+    if args.only in ("truncate", "exact"):
+        inp = workload("long")
+        base = {n: torch.from_numpy(np.ascontiguousarray(inp[n])).cuda().to(torch.bfloat16)
+                for n in ("q", "k", "v", "beta")}
+        base["g"] = torch.from_numpy(inp["g"]).cuda()
+        base["cu_seqlens"] = torch.from_numpy(inp["cu_seqlens"]).cuda()
+        sets = [base] + [{n: (torch.roll(t, shifts=4096 * j, dims=0).contiguous()
+                              if n != "cu_seqlens" else t) for n, t in base.items()}
+                         for j in range(1, args.sets)]
+        out["timing"] = time_steps(gdn, torch, sets, args.only, args.steps, args.warmup)
+    elif args.only == "workloads":
+        out["workloads"] = time_workloads(gdn, torch, args.steps, args.warmup)
+    elif args.only == "backward":
+        out["backward"] = time_backward(gdn, torch, args.steps, args.warmup, with_l2norm=False)
+    else:
+        out["decode"] = time_decode(gdn, torch, args.steps, args.warmup)
+    print(json.dumps(out), flush=True)
     return 0
 
 
