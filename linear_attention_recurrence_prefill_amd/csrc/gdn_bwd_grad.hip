@@ -59,10 +59,17 @@ __device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &l
   hi = cat8(h0, h1);
   lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
 }
-__device__ __forceinline__ void dma16(const char *g, char *l) {
-  __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
+// the four rows' totals of a value that row16_sum_dpp made uniform within each row, added in
+// row order (a wave-uniform result).  Call it where every lane is active: it reads lanes 16, 32
+// and 48 whatever the branch, and the compiler may sink the row sums' last adds into a branch
+// taken by lane 0 alone.
+__device__ __forceinline__ float wave_sum_rows(float x) {
+  const int b = __float_as_int(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(b, 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(b, 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(b, 48)));
 }
-__device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void st_split(char *hi, char *lo, int off, float x) {
   const bf16 h = (bf16)x;
   *reinterpret_cast<bf16 *>(hi + off) = h;
@@ -148,10 +155,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
   const float *dhn = b.dhn + ((int64_t)cg * H + h) * dd;
 
-  // ---- stage.  Every load is issued before any is waited for: dO, Q, K, V go straight into LDS
-  //      (direct loads; rows past n repeat the chunk's last token, which every use masks), Delta
-  //      and dR through registers (split; rows past n zero), and each wave's rows of h and dh'
-  //      into registers for its B operands.
+  // ---- stage.  Every load is issued before any is waited for, h and dh' last: dO, Q, K, V into
+  //      LDS through registers (rows past n repeat the chunk's last token, which every use
+  //      masks), Delta and dR split into LDS (rows past n zero), and each wave's rows of h and
+  //      dh' into registers for its B operands, where they stay in flight through the tile phase.
   const int fcol = 16 * kNT * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
   f32x4 hv[kNT][4][2], gv[kNT][4][2];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
   {
@@ -159,16 +166,19 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
                           static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
     char *dst[4] = {sm.dout, sm.q, sm.k, sm.v};
     // wave w fills rows 8 w .. 8 w + 7; lane l of load j writes physical unit l % 16 of row
-    // 8 w + 4 j + l / 16, which holds logical unit (l % 16) ^ sw(row)
+    // 8 w + 4 j + l / 16, which holds logical unit (l % 16) ^ sw(row).  Staged through registers,
+    // not by direct global->LDS loads: with those outstanding the compiler waits for every load
+    // before the first use of any, which would hold h and dh' (issued last) up at the barrier.
+    f32x4 tv[4][16 / kWaves];
 #pragma unroll
     for (int s = 0; s < 4; ++s)
 #pragma unroll
       for (int j = 0; j < 16 / kWaves; ++j) {
         const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
         const bool qk = s == 1 || s == 2;  // q and k: the key head's rows
-        dma16(src[s] + (t0 + min(r, n - 1)) * (qk ? tok_qk : tok_bytes) +
-                  (int64_t)(qk ? hk : h) * kRowB + (((lane & 15) ^ sw(r)) << 4),
-              dst[s] + ((64 / kWaves) * w + 4 * j) * kRowB);
+        tv[s][j] = *reinterpret_cast<const f32x4 *>(
+            src[s] + (t0 + min(r, n - 1)) * (qk ? tok_qk : tok_bytes) +
+            (int64_t)(qk ? hk : h) * kRowB + (((lane & 15) ^ sw(r)) << 4));
       }
     f32x4 xr[2][8 * 4 / kWaves];
 #pragma unroll
@@ -176,20 +186,44 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       const float *g = s == 0 ? b.delta : b.ddelta;  // Delta, dR
 #pragma unroll
       for (int m = 0; m < 8 * 4 / kWaves; ++m) {
+        // branch-free: rows past n load the last row and are zeroed once they land (a load
+        // under a branch would make the compiler wait for every load at the join)
         const int u = tid + kThreads * m, r = u >> 5, c4 = u & 31;
-        xr[s][m] = r < n ? *reinterpret_cast<const f32x4 *>(g + ((t0 + r) * H + h) * kD + 4 * c4)
-                         : zero4();
+        xr[s][m] = *reinterpret_cast<const f32x4 *>(g + ((t0 + min(r, n - 1)) * H + h) * kD + 4 * c4);
       }
     }
-    float gmv = 0.f, bev = 0.f, rqv = 1.f, rkv = 1.f;
-    if (w == 0 && lane < n) {
-      gmv = b.gamma[(t0 + lane) * H + h];
-      bev = (float)static_cast<const bf16 *>(b.beta)[(t0 + lane) * H + h];
-      if (kNorm) {
-        rqv = b.rq[(t0 + lane) * b.HK + hk];
-        rkv = b.rk[(t0 + lane) * b.HK + hk];
-      }
+    // the gates (every wave loads them, so that no load sits under a branch; wave 0 stores
+    // them); lanes past n read the last token and are replaced below
+    float rqv = 1.f, rkv = 1.f;
+    const int64_t tl = t0 + min(lane, n - 1);
+    const float gmv = b.gamma[tl * H + h];
+    const unsigned short bbits = static_cast<const unsigned short *>(b.beta)[tl * H + h];
+    if (kNorm) {
+      rqv = b.rq[tl * b.HK + hk];
+      rkv = b.rk[tl * b.HK + hk];
     }
+    // h and dh' rows of this wave into registers, issued after every other load so that the
+    // wait before the barrier below leaves them in flight: first used after the tile phase
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    sched_fence();
+#pragma unroll
+    for (int nt = 0; nt < kNT; ++nt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
+        hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
+        hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
+        gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
+        gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+      }
+    sched_fence();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 16 / kWaves; ++j)
+        *reinterpret_cast<f32x4 *>(dst[s] + ((64 / kWaves) * w + 4 * j) * kRowB + 16 * lane) =
+            tv[s][j];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       char *hi = s == 0 ? sm.dh : sm.eh;
@@ -197,35 +231,24 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
       for (int m = 0; m < 8 * 4 / kWaves; ++m) {
         const int u = tid + kThreads * m, r = u >> 5, c4 = u & 31;
-        const bf16x4 xh = to_bf16x4(xr[s][m]);
+        const f32x4 x = r < n ? xr[s][m] : zero4();
+        const bf16x4 xh = to_bf16x4(x);
         *reinterpret_cast<bf16x4 *>(hi + toff(r, c4)) = xh;
-        *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(xr[s][m] - to_f32x4(xh));
+        *reinterpret_cast<bf16x4 *>(lo + toff(r, c4)) = to_bf16x4(x - to_f32x4(xh));
       }
     }
-    if (w == 0) {
+    if (w == 0) {  // lane n - 1 holds gamma_last
       const float glast = __shfl(gmv, n - 1, 64);
-      sm.gam[lane] = lane < n ? gmv : glast;
-      sm.a[lane] = lane < n ? __expf(gmv) : 0.f;
-      sm.c[lane] = lane < n ? __expf(glast - gmv) : 0.f;
-      sm.beta[lane] = bev;
-      sm.rq[lane] = rqv;
-      sm.rk[lane] = rkv;
+      const bool in = lane < n;
+      sm.gam[lane] = in ? gmv : glast;
+      sm.a[lane] = in ? __expf(gmv) : 0.f;
+      sm.c[lane] = in ? __expf(glast - gmv) : 0.f;
+      sm.beta[lane] = in ? __uint_as_float((unsigned)bbits << 16) : 0.f;
+      sm.rq[lane] = in ? rqv : 1.f;
+      sm.rk[lane] = in ? rkv : 1.f;
     }
   }
-  wait_vm0();  // this wave's direct loads have landed
-  __syncthreads();
-  // h and dh' rows of this wave into registers: first used after the tile phase, so the loads
-  // run while it computes
-#pragma unroll
-  for (int nt = 0; nt < kNT; ++nt)
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
-      hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
-      hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
-      gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
-      gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
-    }
+  __syncthreads();  // the loads of h and dh' may still be in flight
 
   // fragment readers
   // A or B operand over features, natural order: row r, elements 32 ks + 8 gq .. + 7
@@ -329,12 +352,10 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       csc += tg;
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        rg4[j] += __shfl_xor(rg4[j], off, 64);
-        rb4[j] += __shfl_xor(rb4[j], off, 64);
-      }
+    for (int j = 0; j < 4; ++j) {
+      rg4[j] = row16_sum_dpp(rg4[j]);
+      rb4[j] = row16_sum_dpp(rb4[j]);
+    }
     csc += __shfl_xor(csc, 16, 64);
     csc += __shfl_xor(csc, 32, 64);
     if (cl == 0) {
@@ -383,8 +404,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       }
     }
   }
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) hdot += __shfl_xor(hdot, off, 64);
+  hdot = wave_sum_rows(row16_sum_dpp(hdot));  // at full exec: every lane's partial is formed
   if (lane == 0) sm.hd[w] = hdot;
 
   // ---- Rh = dR h^T over this wave's columns (d)
@@ -506,18 +526,12 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int off = 8; off > 0; off >>= 1) {
-        rg[mt][i] += __shfl_xor(rg[mt][i], off, 64);
-        rb[mt][i] += __shfl_xor(rb[mt][i], off, 64);
-        rc[mt][i] += __shfl_xor(rc[mt][i], off, 64);
-      }
+      rg[mt][i] = row16_sum_dpp(rg[mt][i]);
+      rb[mt][i] = row16_sum_dpp(rb[mt][i]);
+      rc[mt][i] = row16_sum_dpp(rc[mt][i]);
       if constexpr (norm) {
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) {
-          pq[mt][i] += __shfl_xor(pq[mt][i], off, 64);
-          pk[mt][i] += __shfl_xor(pk[mt][i], off, 64);
-        }
+        pq[mt][i] = row16_sum_dpp(pq[mt][i]);
+        pk[mt][i] = row16_sum_dpp(pk[mt][i]);
       }
       if (cl == 0) {
         const int r = 16 * mt + 4 * gq + i;
@@ -574,8 +588,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       dgam = 0.f;
       csum = 0.f;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) csum += __shfl_xor(csum, off, 64);
+    csum = wave_sum_rows(row16_sum_dpp(csum));
     float hdot = 0.f;
 #pragma unroll
     for (int x = 0; x < kWaves; ++x) hdot += sm.hd[x];

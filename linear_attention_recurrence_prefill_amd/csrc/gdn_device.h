@@ -125,6 +125,18 @@ __device__ __forceinline__ float wave_inclusive_scan_dpp(float x) {
   return x;
 }
 
+// Sum over each row of 16 lanes (lanes 16 j .. 16 j + 15) with DPP lane moves only: pairs
+// (quad_perm 1,0,3,2), quads (quad_perm 2,3,0,1), half-rows (row_half_mirror), rows (row_mirror).
+// Every lane of a row receives the same bits (each step adds two equal partial sums in either
+// order), and the order is fixed, so the result is reproducible.
+__device__ __forceinline__ float row16_sum_dpp(float x) {
+  x += dpp_moved<0xB1, 0xf>(x);
+  x += dpp_moved<0x4E, 0xf>(x);
+  x += dpp_moved<0x141, 0xf>(x);
+  x += dpp_moved<0x140, 0xf>(x);
+  return x;
+}
+
 // Wave-wide sum in fp64 (64 lanes); every lane receives the total.
 __device__ __forceinline__ double wave_sum_f64(double x) {
 #pragma unroll
