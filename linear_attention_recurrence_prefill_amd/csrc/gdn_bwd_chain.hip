@@ -81,9 +81,8 @@ __device__ __forceinline__ void st_split(char *hi, char *lo, int off, float x) {
   *reinterpret_cast<bf16 *>(lo + off) = (bf16)(x - (float)h);
 }
 
-__device__ __forceinline__ void dma16(const char *g, char *l) {
-  __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
-}
+// next-chunk loads: untracked, waited for by wait_vm0 at the chunk turn
+__device__ __forceinline__ void dma16(const char *g, char *l) { dma16_untracked(g, l); }
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 struct ChainSmem {
@@ -264,7 +263,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       sm.rk[lane] = rk_r;
     }
     if (c > c0) issue(c - 1, set ^ 1);
-    __syncthreads();
+    lds_barrier();  // the gate vectors; the next chunk's loads stay in flight
     // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo
     for (int t = w; t < 10; t += kWaves) {
       const int mr = kPtR[t], mi = kPtI[t];
@@ -285,7 +284,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       *reinterpret_cast<bf16x4 *>(&sm.pth[off]) = hi;
       *reinterpret_cast<bf16x4 *>(&sm.ptl[off]) = to_bf16x4(p - to_f32x4(hi));
     }
-    __syncthreads();
+    lds_barrier();  // P^T
     const float lam = __expf(sm.gam[63]);
 
     // ---- dh' of this chunk to the workspace

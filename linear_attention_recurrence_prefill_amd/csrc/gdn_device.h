@@ -97,6 +97,30 @@ __device__ __forceinline__ bf16 from_f32<bf16>(float x) {
   return (bf16)x;
 }
 
+// A workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes are complete
+// before it (lgkmcnt(0)); its global loads and stores may still be in flight.  The signal fences
+// keep the compiler from moving memory accesses across it.  (__syncthreads() would also wait
+// for every outstanding global load, direct global->LDS loads of a next tile included.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// A direct global->LDS load of 16 bytes per lane (lane l writes l_base + 16 l) that the
+// compiler does not track.  With the builtin, the compiler makes any later LDS read that it cannot
+// prove disjoint (a transposing read, for one) wait until the load has landed, which serialises a
+// next-tile prefetch with the current tile's work.  The caller must wait for these loads itself
+// (s_waitcnt vmcnt(0)) before the data is read, and must not read or write the destination
+// until then.  The compiler's own vmcnt waits stay correct: loads retire in order, so an extra
+// load in flight only makes a wait stricter.
+__device__ __forceinline__ void dma16_untracked(const void *g, const void *l_base) {
+  const unsigned la = __builtin_amdgcn_readfirstlane(
+      (unsigned)(unsigned long)(__attribute__((address_space(3))) const void *)l_base);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(la) : "memory");
+}
+
 // Wave-wide inclusive prefix sum (64 lanes).
 __device__ __forceinline__ float wave_inclusive_scan(float x, int lane) {
 #pragma unroll

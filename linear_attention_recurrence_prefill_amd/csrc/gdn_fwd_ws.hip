@@ -120,15 +120,6 @@ __device__ __forceinline__ int pin(int x) {
 }
 
 __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-// A workgroup barrier that orders LDS accesses only: this wave's LDS reads and writes are complete
-// before it (lgkmcnt(0)); its global loads and stores may still be in flight.  The signal fences
-// keep the compiler from moving memory accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_barrier();
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // The 16x16 tiles waves 5 and 6 form per chunk: tile t is K's row block bj[t] times the row block
 // bi[t] of K (q[t] == 0: A's blocks below the diagonal) or of Q (q[t] == 1: P).  Each wave's list
