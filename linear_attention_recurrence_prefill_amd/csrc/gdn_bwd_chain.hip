@@ -42,7 +42,13 @@ namespace {
 
 constexpr int kD = 128;
 constexpr int kRowB = kD * 2;  // bytes per row of a 64 x 128 bf16 tile
-constexpr int kTile = 64 * kRowB;
+// The 16-row blocks of every LDS tile sit 16 bytes further apart than their size: two reads at
+// the same lane offset a whole number of 512-byte steps apart would otherwise be fused by the
+// compiler into one ds_read2st64_b64, which the hardware serves as two passes over the same banks.
+constexpr int kBlk = 16 * kRowB + 16;  // 64 x 128 tiles (K, Q, dO)
+constexpr int kTile = 4 * kBlk;
+constexpr int pBlk = 16 * 128 + 16;    // 64 x 64 tiles (P^T, Tm^T)
+constexpr int pTile = 4 * pBlk;
 // Eight waves of 16 state-gradient columns each (kNT = 1 column tile of 16 per wave): two waves
 // per SIMD, so that one wave's MFMA, LDS and store latencies overlap the other's work.
 constexpr int kWaves = 8;
@@ -55,12 +61,13 @@ constexpr int kThreads = 64 * kWaves;
 __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
 // byte offset of the 8-byte unit u (elements 4 u .. 4 u + 3) of row r
 __device__ __forceinline__ int toff(int r, int u) {
-  return r * kRowB + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
+  return (r >> 4) * kBlk + (r & 15) * kRowB + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
 }
 // 64 x 64 bf16 (P^T, Tm^T): rows of 128 bytes, the 8-byte unit u of row r at u ^ 2 ((r / 2) % 8)
-__device__ __forceinline__ int poff(int r, int u) {
+__device__ __forceinline__ int poff0(int r, int u) {  // unpadded: Tm^T as bwd_tm_kernel stores it
   return r * 128 + ((u ^ (((r >> 1) & 7) << 1)) << 3);
 }
+__device__ __forceinline__ int poff(int r, int u) { return (r >> 4) * pBlk + poff0(r & 15, u); }
 
 __device__ __forceinline__ bf16x4 ld8(const char *p) { return *reinterpret_cast<const bf16x4 *>(p); }
 __device__ __forceinline__ bf16x4 ldtr(const char *p) {
@@ -87,9 +94,9 @@ __device__ __forceinline__ void wait_vm0() { __builtin_amdgcn_s_waitcnt(0x0F70);
 
 struct ChainSmem {
   alignas(16) char kqo[2][3][kTile];  // [set][K, Q, dO]: this chunk's and the next chunk's
-  alignas(16) char tt[2][2][64 * 128];  // [set][hi, lo]: Tm^T = hi + lo (row r, column i)
-  alignas(16) char pth[64 * 128];     // P^T = hi + lo (row i, column r)
-  alignas(16) char ptl[64 * 128];
+  alignas(16) char tt[2][2][pTile];  // [set][hi, lo]: Tm^T = hi + lo (row r, column i)
+  alignas(16) char pth[pTile];       // P^T = hi + lo (row i, column r)
+  alignas(16) char ptl[pTile];
   alignas(16) float gam[64];  // gamma, rows past n hold gamma_last
   alignas(16) float as[64];   // scale e^gamma, 0 past n
   alignas(16) float c[64];    // e^{gamma_last - gamma}, 0 past n
@@ -177,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) o_kf[ks][hf] = toff(cl, 8 * ks + 4 * hf + gq);
   auto kfrag = [&](const char *t, int m, int ks) {
-    return cat8(ld8(t + m * 16 * kRowB + o_kf[ks][0]), ld8(t + m * 16 * kRowB + o_kf[ks][1]));
+    return cat8(ld8(t + m * kBlk + o_kf[ks][0]), ld8(t + m * kBlk + o_kf[ks][1]));
   };
   auto pfrag = [&](const char *t, int m, int ks) {
     const int r = 16 * m + cl;
@@ -216,17 +223,20 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       const int r = (64 / kWaves) * w + 4 * j + (lane >> 4);
       const int64_t t = t0 + min(r, n - 1);
       const int u = ((lane & 15) ^ sw(r)) << 4;
-      const int lo = ((64 / kWaves) * w + 4 * j) * kRowB;
+      const int row0 = (64 / kWaves) * w + 4 * j;  // 4 rows, within one 16-row block
+      const int lo = (row0 >> 4) * kBlk + (row0 & 15) * kRowB;
       dma16(gk + t * tok_qk + u, sm.kqo[set][0] + lo);
       dma16(gqp + t * tok_qk + u, sm.kqo[set][1] + lo);
       dma16(gdo + t * tok_bytes + u, sm.kqo[set][2] + lo);
     }
-    // Tm^T hi and lo: 16 KiB laid out as in LDS (bwd_tm_kernel), copied as they are
+    // Tm^T hi and lo: 16 KiB in the tiles' layout without the block padding (bwd_tm_kernel),
+    // copied 1 KiB (half a 16-row block) at a time to its padded place
     const char *tm = reinterpret_cast<const char *>(b.tmat) + ((chunk_base + c) * H + h) * 16384;
 #pragma unroll
-    for (int j = 0; j < 16 / kWaves; ++j)
-      dma16(tm + ((16 / kWaves) * w + j) * 1024 + 16 * lane,
-            &sm.tt[set][0][0] + ((16 / kWaves) * w + j) * 1024);
+    for (int j = 0; j < 16 / kWaves; ++j) {
+      const int q = (16 / kWaves) * w + j;
+      dma16(tm + q * 1024 + 16 * lane, &sm.tt[set][q >> 3][0] + ((q & 7) >> 1) * pBlk + (q & 1) * 1024);
+    }
     if (w == 0) {
       const int64_t t = t0 + min(lane, n - 1);
       g_r = b.gamma[t * H + h];
@@ -464,7 +474,8 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 // outside [0, n)^2.  One wave per (chunk, head): K K^T on bf16 MFMA (exact products of the bf16
 // inputs), A into LDS, then forward substitution column by column, lane j holding column j of
 // Tm: Tm[r][j] = [r == j] - sum_{j <= i < r} A[r][i] Tm[i][j].  Written for the reverse chain as
-// Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles (poff), 16 KiB per
+// Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles without their block padding
+// (poff0), 16 KiB per
 // (chunk, head) of tmat.
 __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict__ tmat) {
   __shared__ __attribute__((aligned(16))) float am[64][68];  // A^T, then the output tiles
@@ -562,8 +573,8 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = (col_in && 4 * u + e < n) ? x[4 * u + e] : 0.f;
     const bf16x4 hi = to_bf16x4(v);
-    *reinterpret_cast<bf16x4 *>(stage + poff(lane, u)) = hi;
-    *reinterpret_cast<bf16x4 *>(stage + 8192 + poff(lane, u)) = to_bf16x4(v - to_f32x4(hi));
+    *reinterpret_cast<bf16x4 *>(stage + poff0(lane, u)) = hi;
+    *reinterpret_cast<bf16x4 *>(stage + 8192 + poff0(lane, u)) = to_bf16x4(v - to_f32x4(hi));
   }
   __syncthreads();
   char *dst = reinterpret_cast<char *>(tmat) + ((int64_t)cg * H + h) * 16384;

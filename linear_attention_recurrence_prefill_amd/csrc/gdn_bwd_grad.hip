@@ -80,7 +80,9 @@ struct GradSmem {
   alignas(16) char dout[64 * kRowB];
   alignas(16) char q[64 * kRowB];
   alignas(16) char k[64 * kRowB];
-  alignas(16) char v[64 * kRowB];   // V; from the tile phase on, E hi and lo
+  // V; from the tile phase on, E hi and lo (lo 16 bytes past hi's end, so that reads of the two
+  // at the same lane offset are not fused into one two-address read over the same banks)
+  alignas(16) char v[64 * kRowB + 16];
   alignas(16) char dh[64 * kRowB];  // Delta = hi + lo
   alignas(16) char dl[64 * kRowB];
   alignas(16) char eh[64 * kRowB];  // dR = hi + lo
@@ -288,6 +290,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
     }
   }
   __syncthreads();  // every wave is done with V
+  char *eth = sm.v, *etl = sm.v + 64 * 128 + 16;  // E = hi + lo
   // zero the tiles above the diagonal of dPm (tth, ttl) and E (v region)
   for (int i = tid; i < 6 * 64; i += kThreads) {
     const int t = i >> 6, rr = (i >> 2) & 15, u = i & 3;
@@ -298,12 +301,11 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
     *reinterpret_cast<uint2 *>(&sm.tth[off]) = uint2{0u, 0u};
     *reinterpret_cast<uint2 *>(&sm.ttl[off]) = uint2{0u, 0u};
     *reinterpret_cast<uint2 *>(&sm.v[off]) = uint2{0u, 0u};
-    *reinterpret_cast<uint2 *>(&sm.v[64 * 128 + off]) = uint2{0u, 0u};
+    *reinterpret_cast<uint2 *>(&etl[off]) = uint2{0u, 0u};
   }
   __syncthreads();
 
   // ---- 64 x 64 tiles on and below the diagonal: dP, dR Delta^T, Q K^T, K K^T
-  char *eth = sm.v, *etl = sm.v + 64 * 128;  // E = hi + lo
   for (int t = w; t < 10; t += kWaves) {
     const int tr = kTR[t], ti = kTI[t];
     f32x4 dp = zero4(), da = zero4(), qk = zero4(), kk = zero4();
@@ -427,6 +429,34 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 
   __syncthreads();
 
+  // dq, dk of row r (this lane's rows 4 gq + r - r % 16 .. , column fcol) through buffer
+  // resources whose range ends at the chunk's last token: rows at or past n are dropped by the
+  // hardware, the row offset is a scalar operand and the lane's offset is one register.  Grouped
+  // heads write fp32 partials, summed per key head afterwards.
+  const bool part = b.dq_part != nullptr;
+  const int64_t row0 = (t0 * H + h) * kD;
+  const int es = part ? 4 : 2;
+  const int rb_bytes = H * kD * es;  // one token
+  const __amdgpu_buffer_rsrc_t rq_ = __builtin_amdgcn_make_buffer_rsrc(
+      part ? (void *)(b.dq_part + row0) : (void *)(static_cast<bf16 *>(b.dq) + row0), (short)0,
+      n * rb_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rk_ = __builtin_amdgcn_make_buffer_rsrc(
+      part ? (void *)(b.dk_part + row0) : (void *)(static_cast<bf16 *>(b.dk) + row0), (short)0,
+      n * rb_bytes, 0x00020000);
+  const int vo = 4 * gq * rb_bytes + fcol * es;
+  auto store_qk = [&](int r16, float dqv, float dkv) {  // r16 = 16 mt + i: the row less 4 gq
+    const int so = r16 * rb_bytes;
+    if (part) {
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dqv), rq_, vo, so, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dkv), rk_, vo, so, 0);
+    } else {
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)dqv), rq_, vo,
+                                            so, 0);
+      __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, (bf16)dkv), rk_, vo,
+                                            so, 0);
+    }
+  };
+
   // ---- dQ = diag(a) Y1 + dPm K;  dK = dPm^T Q + (E + E^T) K + diag(c) Y2 - diag(beta a) Rh
   float rg[4][4], rc[4][4];
   // normalised q, k: Z = rq dQ and W = rk dK of the normalised rows, held until the row dots
@@ -493,7 +523,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
         const f32x4 y1 = scale * Y1[mt][nt];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * mt + 4 * gq + i;
           const float dqv = aq[i] * y1[i] + dq[nt][i];
           const float dkv = dk[nt][i] + cr[i] * Y2[mt][nt][i] - br[i] * ak[i] * Rh[mt][nt][i];
           if constexpr (norm) {
@@ -501,15 +530,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
             zk[mt][i] = dkv;
             pq[mt][i] += qv[i] * dqv;
             pk[mt][i] += kv[i] * dkv;
-          } else if (r < n) {
-            const int64_t gi = ((t0 + r) * H + h) * kD + fcol + 16 * nt;
-            if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
-              b.dq_part[gi] = dqv;
-              b.dk_part[gi] = dkv;
-            } else {
-              static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
-              static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
-            }
+          } else {
+            store_qk(16 * mt + i, dqv, dkv);
           }
           rg[mt][i] += aq[i] * y1[i] * qv[i] - br[i] * ak[i] * Rh[mt][nt][i] * kv[i] -
                        cr[i] * Y2[mt][nt][i] * kv[i];
@@ -559,19 +581,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       const f32x4 rkr = *reinterpret_cast<const f32x4 *>(&sm.rk[16 * mt + 4 * gq]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * mt + 4 * gq + i;
-        if (r < n) {
-          const float dqv = zq[mt][i] - rqr[i] * rqr[i] * qv[i] * tq[i];
-          const float dkv = zk[mt][i] - rkr[i] * rkr[i] * kv[i] * tk[i];
-          const int64_t gi = ((t0 + r) * H + h) * kD + fcol;
-          if (b.dq_part != nullptr) {  // grouped heads: summed per key head afterwards
-            b.dq_part[gi] = dqv;
-            b.dk_part[gi] = dkv;
-          } else {
-            static_cast<bf16 *>(b.dq)[gi] = (bf16)dqv;
-            static_cast<bf16 *>(b.dk)[gi] = (bf16)dkv;
-          }
-        }
+        store_qk(16 * mt + i, zq[mt][i] - rqr[i] * rqr[i] * qv[i] * tq[i],
+                 zk[mt][i] - rkr[i] * rkr[i] * kv[i] * tk[i]);
       }
     }
   }

@@ -25,7 +25,8 @@ hipError_t launch_bwd_chain_bf16(const BwdArgs &b, const BwdUnits &u, hipStream_
 hipError_t launch_bwd_chain_bf16_transition(const BwdArgs &b, const BwdUnits &u,
                                             hipStream_t stream);
 // Tm = (I + A)^-1 of every chunk from k, beta and the recompute's gamma, stored for the reverse
-// chain as Tm^T = hi + lo: two bf16 64 x 64 tiles in its LDS layout, 16 KiB per (chunk, head).
+// chain as Tm^T = hi + lo: two bf16 64 x 64 tiles in its LDS layout (without the LDS copy's block
+// padding), 16 KiB per (chunk, head).
 hipError_t launch_bwd_tm(const BwdArgs &b, float *tmat, int64_t max_chunks, hipStream_t stream);
 // Per-chunk gradients from the chain's dhn and dR (dV is the chain's).
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream);
