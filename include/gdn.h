@@ -210,7 +210,7 @@ gdn_status gdn_chunk_fwd_intermediates(const gdn_problem *p, const void *q, cons
 gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, const int32_t *cu_seqlens_host,
                                         size_t *bytes);
 
-/* Backward of the exact forward (mode must be GDN_MODE_EXACT): given dout (dtype, [T, H, d_v])
+/* Backward of the forward: given dout (dtype, [T, H, d_v])
  * and optionally dht ([N, H, d_k, d_v] fp32, NULL = zero), writes dq, dk (dtype, [T, Hk, d_k];
  * with grouped heads, the sums over each key head's value heads),
  * dv (dtype, [T, H, d_v]), dg (fp32, [T, H]) and dbeta (dtype, [T, H]).  dh0 (optional, fp32)
@@ -218,7 +218,13 @@ gdn_status gdn_chunk_bwd_workspace_size(const gdn_problem *p, const int32_t *cu_
  * summed over all sequences when h0_seq_stride is 0 (a state shared by every sequence collects
  * the sum of their gradients, "Musings on long-context fine-tuning", section "Backward
  * through P").  Hidden states are recomputed, not stored ("How to Speed Up GDN Kernels for
- * Qwen Models", section "Lever 2").  cu_seqlens_host is optional, as for the workspace query. */
+ * Qwen Models", section "Lever 2").  cu_seqlens_host is optional, as for the workspace query.
+ * Mode: the exact backward (GDN_MODE_EXACT), split along the sequences for bf16 with d = 128
+ * as the exact forward is.  GDN_MODE_TRUNCATE, where that split applies, gives each segment
+ * warmup windows instead of the split's extra passes ("Lever 1"): the recompute's start state
+ * from the chunks before the segment whose summed g reaches trunc_log_threshold, and the state
+ * gradient at the segment's end from the chunks after it, by the same rule (the reverse chain's
+ * maps are the forward maps transposed and decay alike); elsewhere it is the exact backward. */
 gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, const void *v,
                          const float *g, const void *beta, const int32_t *cu_seqlens,
                          const int32_t *cu_seqlens_host, const float *h0, const void *dout,

@@ -568,9 +568,11 @@ namespace {
 
 struct BwdLayout {
   int64_t nc = 0;  // chunk-count bound: ceil(T / 64) + N
-  // forward recompute through the exact split (bf16, d = 128): segment length and unit bound
+  // the recompute and the reverse chain split into units (bf16, d = 128): segment length and
+  // unit bound; through the exact split, or (truncate mode) with warmup windows
   int32_t L = 0;
   int64_t units = 0;
+  bool truncate = false;
   size_t gamma = 0, tmat = 0, w = 0, hc = 0, delta = 0, o = 0, dhn = 0, ddelta = 0, dh0 = 0;
   size_t unit_bm = 0, unit_h0 = 0, unit_mt = 0;
   size_t dq_part = 0, dk_part = 0;  // grouped heads or qk_l2norm: per-value-head dq, dk (fp32)
@@ -584,7 +586,9 @@ bool bwd_bf16_path(const gdn_problem *p) { return p->dtype == GDN_DTYPE_BF16 && 
 
 // The recompute's (and the reverse chain's) segment length: the forward's exact-split rule
 // (measured on the 65K-token training workload: 2.42 ms per call at 16 chunks, 2.50 at 8, 2.54 at
-// 32, 2.89 at 4); 0 (unsplit) where the forward would not split.
+// 32, 2.89 at 4); 0 (unsplit) where the forward would not split.  The truncate mode takes the
+// same length: a unit then costs its own chunks plus a warmup window whose length does not
+// depend on L, so the shortest length that fits one round is again the fastest.
 gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L) {
   const int64_t T = p->total_tokens, H = p->num_heads, D = p->d_k;
   // per-chunk arrays on the chunk bound, whatever the host copy says: chunk indices come from
@@ -625,7 +629,8 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
   L->dhn = take(sizeof(float) * L->nc * H * D * D);
   L->ddelta = take(sizeof(float) * T * H * D);
   L->dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
-  if (L->L > 0) {
+  L->truncate = L->L > 0 && p->mode == GDN_MODE_TRUNCATE;
+  if (L->L > 0 && !L->truncate) {
     const size_t per = sizeof(float) * (size_t)L->units * H * D * D;
     L->unit_bm = take(2 * per);
     L->unit_h0 = take(per);
@@ -648,7 +653,8 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
 // Forward recompute of the backward for bf16 inputs with d = 128, on the pipelined forward kernel:
 // the per-chunk start states, Delta and gamma, from all units in parallel when the recompute is
 // split (every unit's affine map (B, M), then the maps composed along each sequence into true
-// start states, as in the forward's exact split).
+// start states, as in the forward's exact split; or, in the truncate mode, each unit from the
+// warmup window before it, as the truncate-mode forward runs).
 gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float *gamma, float *hc,
                                   float *delta, const BwdLayout &L, char *base,
                                   hipStream_t stream) {
@@ -670,12 +676,15 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
   a.L = L.L;
   a.scale = p->scale;
   a.log_thr = p->trunc_log_threshold;
-  a.truncate = 0;
+  a.truncate = L.truncate ? 1 : 0;
   a.l2norm = p->qk_l2norm;
   a.faults = fault_word();
   hipError_t e;
   int64_t units = p->num_seqs;
-  if (L.L > 0) {
+  if (L.truncate) {
+    units = L.units;
+    a.units = L.units;
+  } else if (L.L > 0) {
     float *bm = reinterpret_cast<float *>(base + L.unit_bm);
     float *uh0 = reinterpret_cast<float *>(base + L.unit_h0);
     units = L.units;
@@ -737,7 +746,6 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   if (s != GDN_OK) return s;
   s = check_cu_host(p, cu_seqlens_host);
   if (s != GDN_OK) return s;
-  if (p->mode != GDN_MODE_EXACT) return fail(GDN_ERR_BAD_MODE, "the backward is exact-mode only");
   if (p->total_tokens > 0 && (!dout || !dq || !dk || !dv || !dg || !dbeta))
     return fail(GDN_ERR_NULL_ARG, "dout, dq, dk, dv, dg and dbeta are required");
   const void *ptrs[] = {dout, dq, dk, dv, dg, dbeta};
@@ -785,8 +793,9 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     s = check_tensors(t, p->total_tokens);
     if (s == GDN_OK) s = device_info(nullptr);
     if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc, delta, L, base, stream);
-  } else {
+  } else {  // the general kernels' backward is unsplit: the exact one, whatever the mode
     gdn_problem pe = *p;
+    pe.mode = GDN_MODE_EXACT;
     s = run_fwd(&pe, t, nullptr, true, dbg, nullptr, 0, stream);
   }
   if (s != GDN_OK) return s;
@@ -840,11 +849,14 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
     if (e != hipSuccess) return hip_fail(e, "backward: Tm");
     // reverse chain, through the exact split when the recompute was split (same units): the
     // transition pass writes B' over the recompute's B, and the reverse walk applies B' with the
-    // M^T the recompute's first pass stored
+    // M^T the recompute's first pass stored; in the truncate mode each unit's chain starts after
+    // a warmup window instead
     gdn::BwdUnits u{};
     u.L = L.L;
     u.units = L.units;
-    if (L.L > 0) {
+    u.truncate = L.truncate ? 1 : 0;
+    u.log_thr = p->trunc_log_threshold;
+    if (L.L > 0 && !L.truncate) {
       float *bm = reinterpret_cast<float *>(base + L.unit_bm);
       float *dend = reinterpret_cast<float *>(base + L.unit_h0);
       u.unit_out = bm;

@@ -35,6 +35,7 @@
 // unit's true end gradient; the final pass reruns each unit from it with the per-chunk outputs.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
+#include "gdn_tiles.h"
 #include "gdn_unit.h"
 
 namespace gdn {
@@ -103,7 +104,7 @@ struct ChainSmem {
   alignas(16) float ab[64];   // e^gamma beta, 0 past n
   alignas(16) float beta[64];
   alignas(16) float rq[64], rk[64];  // q/k L2 normalisation: inverse row norms (1 without)
-  alignas(16) int imisc[4];
+  alignas(16) int imisc[8];
 };
 static_assert(sizeof(ChainSmem) <= 160 * 1024, "LDS budget");
 
@@ -123,11 +124,20 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   if (w == 0) {
     Unit un;
     const bool ok = find_unit(b.cu, b.N, b.T, us.L, unit, true, lane, un);
+    // the chain starts at chunk ce - 1: the unit's last chunk, or (truncate mode) the last of
+    // its warmup window after it
+    int ce = un.c1;
+    if (!kTransition && us.truncate && ok) {
+      const int64_t s0 = b.cu[un.seq], s1 = b.cu[un.seq + 1];  // checked by find_unit
+      const int nc = (int)((s1 - s0 + kChunk - 1) / kChunk);
+      if (un.c1 < nc) ce = warm_window_rev(b.g, s0, s1, un.c1, nc, h, H, us.log_thr, lane);
+    }
     if (lane == 0) {
       sm.imisc[0] = ok ? un.seq : -1;
       sm.imisc[1] = un.c0;
       sm.imisc[2] = un.c1;
       sm.imisc[3] = (int)un.chunk_base;
+      sm.imisc[4] = ce;
     }
   }
   // P^T's tiles below the diagonal (row block > column block) are read but never written: zero
@@ -144,6 +154,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   if (seq < 0) return;
   const int c0 = __builtin_amdgcn_readfirstlane(sm.imisc[1]);
   const int c1 = __builtin_amdgcn_readfirstlane(sm.imisc[2]);
+  const int ce = __builtin_amdgcn_readfirstlane(sm.imisc[4]);
   const int64_t chunk_base = sm.imisc[3];
   const int64_t ts0 = b.cu[seq], ts1 = b.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;  // malformed cu_seqlens: touch nothing
@@ -162,10 +173,11 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   f32x4 G[8][kNT];  // dh'
   {
     const float *src = nullptr;
-    if (!kTransition)
-      src = us.unit_dend != nullptr ? us.unit_dend + ((int64_t)unit * H + h) * dd
-            : b.dht != nullptr      ? b.dht + ((int64_t)seq * H + h) * dd
-                                    : nullptr;
+    const int ncs = (int)((ts1 - ts0 + kChunk - 1) / kChunk);  // the sequence's chunks
+    if (!kTransition)  // dht where the chain starts at the sequence's end
+      src = us.unit_dend != nullptr            ? us.unit_dend + ((int64_t)unit * H + h) * dd
+            : (b.dht != nullptr && ce == ncs) ? b.dht + ((int64_t)seq * H + h) * dd
+                                              : nullptr;
 #pragma unroll
     for (int md = 0; md < 8; ++md)
 #pragma unroll
@@ -248,8 +260,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     }
   };
 
-  if (c1 > c0) issue(c1 - 1, 0);
-  for (int c = c1 - 1, it = 0; c >= c0; --c, ++it) {
+  if (ce > c0) issue(ce - 1, 0);
+  for (int c = ce - 1, it = 0; c >= c0; --c, ++it) {
+    const bool emit = !kTransition && c < c1;  // the unit's own chunks (not a warmup's)
     const int set = it & 1;
     const char *Kt = sm.kqo[set][0], *Qt = sm.kqo[set][1], *Ot = sm.kqo[set][2];
     const int64_t t0 = chunk_t0(c);
@@ -298,7 +311,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     const float lam = __expf(sm.gam[63]);
 
     // ---- dh' of this chunk to the workspace
-    if (!kTransition) {  // row offsets as scalar operands
+    if (emit) {  // row offsets as scalar operands
       const __amdgpu_buffer_rsrc_t hr =
           __builtin_amdgcn_make_buffer_rsrc(b.dhn + (cg * H + h) * dd, (short)0, (int)dd * 4, 0x00020000);
 #pragma unroll
@@ -383,7 +396,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
         }
       }
     }
-    if (!kTransition) {  // rows at or past the chunk's end fall outside the buffer ranges
+    if (emit) {  // rows at or past the chunk's end fall outside the buffer ranges
       const int64_t base = (t0 * H + h) * kD;
       const __amdgpu_buffer_rsrc_t rr =
           __builtin_amdgcn_make_buffer_rsrc(b.ddelta + base, (short)0, n * H * kD * 4, 0x00020000);

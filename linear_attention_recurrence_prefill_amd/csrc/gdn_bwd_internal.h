@@ -16,6 +16,11 @@ struct BwdUnits {
   // transition pass: [units, H, D, D], the state gradient at each unit's start from a zero end
   // gradient (B'); the unit's map of end to start gradient is the forward's M transposed
   float *unit_out;
+  // truncate mode (final pass, L > 0): each unit's chain starts after its end, over the chunks
+  // whose summed g reaches log_thr (warm_window_rev), from a zero gradient or dht at the
+  // sequence's end; per-chunk outputs only for the unit's own chunks
+  int32_t truncate;
+  float log_thr;
 };
 
 // The reverse state-gradient chain.  Final pass: grid (units, H); per chunk it writes dh' (dhn),

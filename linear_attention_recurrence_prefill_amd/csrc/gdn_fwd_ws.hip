@@ -149,7 +149,8 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 
 // kDump: the pass of the backward's forward recompute.  No output; per chunk it writes the state
 // at the chunk's start (a.dbg_hc [chunks, H, D, D]), Delta (a.dbg_delta [T, H, D]) and gamma
-// (a.dbg_gamma [T, H]), all fp32, chunks numbered across sequences.
+// (a.dbg_gamma [T, H]), all fp32, chunks numbered across sequences; in the truncate mode, for
+// the unit's own chunks only (the warmup's belong to the unit before).
 // kTransition: the first pass of the exact split.  Workgroup (unit, head, z) runs the unit's
 // chunks from a fixed start without output and writes its final state to a.unit_out[z]: z = 0
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
@@ -390,8 +391,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         const int64_t t0 = chunk_t0(cc);
         const int n = chunk_n(cc);
         const bool emit = !kTransition && !kDump && cc >= c0;
-        if constexpr (kDump) {  // the state at the chunk's start (all rows in range; row offsets
-                                // as scalar operands)
+        if (kDump && cc >= c0) {  // the state at the chunk's start (all rows in range; row
+                                  // offsets as scalar operands); none for a warmup's chunks
           const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
               a.dbg_hc + ((chunk_base + cc) * H + h) * kD * kD, (short)0, kD * kD * 4, 0x00020000);
 #pragma unroll
@@ -465,8 +466,8 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
               R[2 * hb + 1][nt] = mma_bf16_k16(nf, to_bf16x4(Dl0[nt]), R[2 * hb + 1][nt]);
 #pragma unroll
             for (int nt = 0; nt < 2; ++nt) Dl1[nt] = mma_bf16_k16(t1, to_bf16x4(R[2 * hb + 1][nt]), zero4());
-            if constexpr (kDump) {  // Delta rows 32 hb + 4 gq + i and 32 hb + 16 + 4 gq + i; rows
-                                    // at or past the chunk's end fall outside the range
+            if (kDump && cc >= c0) {  // Delta rows 32 hb + 4 gq + i and 32 hb + 16 + 4 gq + i;
+                                      // rows at or past the chunk's end fall outside the range
               const __amdgpu_buffer_rsrc_t dr = __builtin_amdgcn_make_buffer_rsrc(
                   a.dbg_delta + (tok0 * H + h) * kD, (short)0, n * H * kD * 4, 0x00020000);
 #pragma unroll
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       vc.edt[lane] = __expf(gl - gam);
       vc.gam[lane] = gam;
       if (lane == 0) vc.egl[0] = __expf(gl);
-      if (kDump && lane < n) a.dbg_gamma[(chunk_t0(c) + lane) * H + h] = gam;
+      if (kDump && c >= c0 && lane < n) a.dbg_gamma[(chunk_t0(c) + lane) * H + h] = gam;
     };
     // kNorm: inverse norms of the rows of chunk c's K (and Q) tiles, once they are in LDS.  Lane r
     // sums row r, reading its 16-byte units in an order rotated by r (no two lanes of a 16-row

@@ -34,6 +34,35 @@ __device__ inline int warm_window(const float *__restrict__ g, int64_t ts0, int 
   return w;
 }
 
+// The same window on the other side, for the truncate mode's reverse chain: the gradient of the
+// state after a segment that ends before chunk c1 < nc of its sequence takes the contributions of
+// later chunks through the chunk maps transposed, which decay as the forward maps do.  Whole
+// following chunks are added one at a time (c1, c1 + 1, ...) until their summed g is below thr;
+// returns the window's end (exclusive; nc when it reaches the sequence end).  Tokens past ts1
+// (the sequence's ragged last chunk) add nothing.  One full wave calls it.
+__device__ inline int warm_window_rev(const float *__restrict__ g, int64_t ts0, int64_t ts1, int c1,
+                                      int nc, int h, int H, float thr, int lane) {
+  double acc = 0.0;
+  int e = c1;
+  while (e < nc && !(acc < (double)thr)) {
+    float x[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {  // chunks e .. e + 3 (those at or past nc are not used)
+      const int64_t t = ts0 + (int64_t)min(e + j, nc - 1) * kChunk + lane;
+      x[j] = t < ts1 ? g[t * H + h] : 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const double sj = wave_sum_f64((double)x[j]);
+      if (e < nc && !(acc < (double)thr)) {
+        ++e;
+        acc += sj;
+      }
+    }
+  }
+  return e;
+}
+
 // Lower-triangular 16x16 tiles (bi, bj), bj <= bi, of a 64x64 matrix, numbered row by row:
 // tau = bi (bi + 1) / 2 + bj, 0 <= tau < 10.
 __device__ __forceinline__ int tile_bi(int tau) {

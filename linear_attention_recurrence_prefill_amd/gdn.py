@@ -334,21 +334,24 @@ def chunk_fwd_intermediates(q, k, v, g, beta, cu_seqlens, h0=None, *, scale=1.0,
 
 def chunk_bwd(q, k, v, g, beta, cu_seqlens, dout, h0=None, dht=None, *, scale=1.0,
               need_dh0=True, workspace=None, seg_chunks=0, num_slots=0, qk_l2norm=False,
-              cu_seqlens_host=None):
+              cu_seqlens_host=None, mode="exact", trunc_log_threshold=-10.0):
     """Backward of the exact forward.  Returns dict(dq, dk, dv, dg, dbeta, dh0).  dh0 is
     [N, H, D, D], or [H, D, D] summed over sequences when h0 is shared ([H, D, D]).
-    seg_chunks / num_slots set the segment length of the forward recompute's split and the
-    workgroup slots it is planned for (0: chosen by the library).  qk_l2norm: backward of the
-    forward with q and k normalised inside the kernels (dq, dk are the raw inputs' gradients).
-    cu_seqlens_host: an optional host copy of cu_seqlens (sets the recompute split exactly)."""
+    seg_chunks / num_slots set the segment length of the split (the forward recompute and the
+    reverse chain) and the workgroup slots it is planned for (0: chosen by the library).
+    mode "truncate": where the backward splits (bf16, d = 128), each unit starts from a warmup
+    window (summed g below trunc_log_threshold) instead of the exact split's extra passes.
+    qk_l2norm: backward of the forward with q and k normalised inside the kernels (dq, dk are
+    the raw inputs' gradients).  cu_seqlens_host: an optional host copy of cu_seqlens (sets the
+    split exactly)."""
     lib = load_library()
     T, H, D, N, stride, Hk = _validate(q, k, v, g, beta, cu_seqlens, h0)
     if dout.shape != v.shape or dout.dtype != q.dtype or not dout.is_contiguous():
         raise ValueError("dout must be contiguous with v's shape and q's dtype")
     if dht is not None and (dht.shape != (N, H, D, D) or dht.dtype != torch.float32):
         raise ValueError("dht must be float32 [N, H, D, D]")
-    p = make_problem(T, N, H, D, q.dtype, "exact", scale, seg_chunks=seg_chunks,
-                     num_slots=num_slots,
+    p = make_problem(T, N, H, D, q.dtype, mode, scale, seg_chunks=seg_chunks,
+                     num_slots=num_slots, trunc_log_threshold=trunc_log_threshold,
                      h0_seq_stride=stride if stride is not None else H * D * D, num_k_heads=Hk,
                      qk_l2norm=qk_l2norm)
     cu_h = _host_cu(cu_seqlens, cu_seqlens_host)

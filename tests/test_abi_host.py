@@ -174,6 +174,11 @@ def test_bwd_recompute_split_workspace(lib):
     p = _problem(num_slots=256, dtype=0)  # fp32: the general kernel, never split
     assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n2)) == 0
     assert n2.value < n1.value * 2
+    # truncate mode: the same split with warmup windows, no per-unit maps or states
+    n3 = ctypes.c_size_t(0)
+    p = _problem(num_slots=256, mode=1)
+    assert lib.gdn_chunk_bwd_workspace_size(ctypes.byref(p), None, ctypes.byref(n3)) == 0
+    assert n3.value == n1.value
 
 
 @pytest.mark.parametrize("args,status", [

@@ -86,7 +86,24 @@ def test_bwd_scale(gdn, oracle_mod):
     _check_bwd(gdn, oracle_mod, inp, "bwd scale", scale=0.0883883)
 
 
-def test_train_65k_forward_and_backward(gdn, oracle_mod):
+@pytest.fixture(scope="module")
+def train65k(oracle_mod):
+    """The training workload on the GPU and the oracle's gradients for all 8 heads (computed once
+    for the tests below)."""
+    inp = workload("train")
+    ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], inp["dout"])
+    return inp, ref
+
+
+def _report_train(gr, inp, ref, label):
+    print(f"[{label}]", flush=True)
+    cu = inp["cu_seqlens"]
+    for name in NAMES:
+        report(name, np64(gr[name]), ref[name], 5e-3, cu=cu)
+    report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3, cu=cu, states=True)
+
+
+def test_train_65k_forward_and_backward(gdn, oracle_mod, train65k):
     """The training workload: 65536 tokens packed from documents of U{4096..16384} tokens, H=8,
     d=128, bf16, dO ~ N(0, 1) ("How to Speed Up GDN Kernels for Qwen Models", section "What it
     adds up to": the backward at 16K-256K tokens).  The forward's o and final states, then every
@@ -94,7 +111,7 @@ def test_train_65k_forward_and_backward(gdn, oracle_mod):
     host copy of cu_seqlens, as the benchmark's do: the exact split then takes the shortest
     segment length (not below the latency model's 16) whose last pass fits one round of 256
     workgroups, 35 chunks for these documents."""
-    inp = workload("train")
+    inp, ref = train65k
     d = to_dev(inp)
     cu_h = inp["cu_seqlens"]
     plan = gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], 8, 128, torch.bfloat16, mode="exact",
@@ -108,8 +125,22 @@ def test_train_65k_forward_and_backward(gdn, oracle_mod):
     report("o", np64(o), o_ref, 5e-3, cu=inp["cu_seqlens"])
     report("ht", np64(ht), ht_ref, 5e-3, cu=inp["cu_seqlens"], states=True)
     del o, ht, o_ref, ht_ref
-    _check_bwd(gdn, oracle_mod, inp, "bwd train 65K, all 8 heads", num_slots=256,
-               cu_seqlens_host=cu_h)
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], num_slots=256,
+                       cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    _report_train(gr, inp, ref, "bwd train 65K, all 8 heads")
+
+
+def test_train_65k_backward_truncate(gdn, train65k):
+    """The truncate mode's backward on the training workload (warmup windows of e^-10 on both
+    passes instead of the exact split's extra passes), against the oracle's exact gradients on all
+    8 heads: the dropped terms are below the bf16 tolerance."""
+    inp, ref = train65k
+    d = to_dev(inp)
+    gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], num_slots=256,
+                       cu_seqlens_host=inp["cu_seqlens"], mode="truncate")
+    torch.cuda.synchronize()
+    _report_train(gr, inp, ref, "bwd train 65K truncate, all 8 heads")
 
 
 def test_bwd_shared_initial_state_sums_branches(gdn, oracle_mod):
@@ -143,10 +174,12 @@ def test_bwd_deterministic(gdn):
             assert torch.equal(g1[name], g2[name]), name
 
 
-@pytest.mark.parametrize("seg,slots", [(2, 0), (0, 1)])
-def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots):
-    """The forward recompute split into 2-chunk segments (several units per sequence, h0 and a
-    nonzero dht) and run unsplit (one workgroup slot: num_seqs * H >= P) both match the oracle."""
+@pytest.mark.parametrize("seg,slots,mode", [(2, 0, "exact"), (0, 1, "exact"), (2, 0, "truncate")])
+def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots, mode):
+    """The backward split into 2-chunk segments (several units per sequence, h0 and a nonzero
+    dht), through the exact split or with the truncate mode's warmup windows (about three chunks
+    here, so windows that stop inside a sequence and windows that reach its start or end), and
+    run unsplit (one workgroup slot: num_seqs * H >= P): all match the oracle."""
     inp = make_inputs([700, 333, 0, 1000, 64], H=2, dk=128, dv=128, dtype="bf16", seed=95,
                       h0_scale=0.5)
     d = to_dev(inp)
@@ -156,13 +189,32 @@ def test_bwd_recompute_split_and_unsplit(gdn, oracle_mod, seg, slots):
     N, H, D = 5, 2, 128
     dht = (0.3 * rng.standard_normal((N, H, D, D))).astype(np.float32)
     gr = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], torch.from_numpy(dout).cuda().to(torch.bfloat16),
-                       d["h0"], torch.from_numpy(dht).cuda(), seg_chunks=seg, num_slots=slots)
+                       d["h0"], torch.from_numpy(dht).cuda(), seg_chunks=seg, num_slots=slots,
+                       mode=mode)
     torch.cuda.synchronize()
     ref = oracle_mod.bwd(*_oargs(inp), inp["cu_seqlens"], dout, h0=inp["h0"], dht=dht)
-    print(f"[bwd recompute seg={seg} slots={slots}]", flush=True)
+    print(f"[bwd recompute seg={seg} slots={slots} {mode}]", flush=True)
     for name in NAMES:
         report(name, np64(gr[name]), ref[name], 5e-3, cu=inp["cu_seqlens"])
     report("dh0", np64(gr["dh0"]), ref["dh0"], 5e-3, cu=inp["cu_seqlens"], states=True)
+
+
+def test_bwd_truncate_unbounded_windows_equal_unsplit(gdn):
+    """With a threshold no window reaches, every unit's recompute starts at its sequence's start
+    (from h0) and its reverse chain at the sequence's end (from dht): each unit then repeats the
+    unsplit backward's arithmetic on its chunks, so the gradients are bitwise those of the exact
+    backward run unsplit."""
+    inp = make_inputs([700, 333, 0, 1000, 64], H=2, dk=128, dv=128, dtype="bf16", seed=96,
+                      h0_scale=0.5, with_dout=True)
+    d = to_dev(inp)
+    rng = np.random.default_rng(12)
+    dht = torch.from_numpy((0.3 * rng.standard_normal((5, 2, 128, 128))).astype(np.float32)).cuda()
+    a = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], d["h0"], dht, num_slots=1)
+    b = gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], d["h0"], dht, seg_chunks=2,
+                      num_slots=0, mode="truncate", trunc_log_threshold=-1e30)
+    torch.cuda.synchronize()
+    for name in NAMES + ("dh0",):
+        assert torch.equal(a[name], b[name]), name
 
 
 def test_fork_backward_through_shared_prefix(gdn, oracle_mod):
