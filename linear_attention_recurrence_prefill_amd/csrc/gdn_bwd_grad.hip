@@ -18,7 +18,7 @@
 // chunked form of "How to Speed Up GDN Kernels for Qwen Models" (section "What GDN actually
 // computes"), with the hidden states recomputed ("Lever 2").
 //
-// One workgroup of eight waves per (chunk, head).  Products run on v_mfma_f32_16x16x32_bf16 with
+// One workgroup of eight waves per (chunk, head), the heads of a chunk in consecutive workgroups.  Products run on v_mfma_f32_16x16x32_bf16 with
 // fp32 accumulation; q, k, v and dO enter exactly, every other operand as a bf16 head plus a bf16
 // remainder (see the reverse chain).  Wave w owns feature columns [16 w, 16 w + 16) of every
 // 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go straight from HBM into
@@ -113,7 +113,9 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   __shared__ GradSmem sm;
   const int tid = threadIdx.x, lane = tid & 63, gq = lane >> 4, cl = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
+  // workgroup x = cg * H + h: the heads of a chunk are consecutive (their rows of the [T, H, d]
+  // tensors interleave in memory and are read close together)
+  const int H = b.H, h = (int)(blockIdx.x % (unsigned)H), cg = (int)(blockIdx.x / (unsigned)H);
   // locate the chunk: its sequence and its index within that sequence
   if (w == 0) {
     int64_t before = 0;
@@ -620,12 +622,14 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 
 hipError_t launch_bwd_grad_bf16(const BwdArgs &b, int64_t max_chunks, hipStream_t stream) {
   if (max_chunks <= 0) return hipSuccess;
+  const int64_t wgs = max_chunks * b.H;
+  if (wgs > (int64_t)UINT32_MAX) return hipErrorInvalidConfiguration;
   if (b.rq != nullptr)
-    hipLaunchKernelGGL(bwd_grad_bf16_kernel<true>, dim3((unsigned)max_chunks, b.H), dim3(kThreads),
-                       0, stream, b);
+    hipLaunchKernelGGL(bwd_grad_bf16_kernel<true>, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                       b);
   else
-    hipLaunchKernelGGL(bwd_grad_bf16_kernel<false>, dim3((unsigned)max_chunks, b.H), dim3(kThreads),
-                       0, stream, b);
+    hipLaunchKernelGGL(bwd_grad_bf16_kernel<false>, dim3((unsigned)wgs), dim3(kThreads), 0, stream,
+                       b);
   return hipGetLastError();
 }
 
