@@ -83,7 +83,8 @@ def parse():
                          "forward")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the forward on the pages' other workloads")
-    ap.add_argument("--only", choices=["truncate", "exact", "workloads", "backward", "decode"],
+    ap.add_argument("--only", choices=["truncate", "exact", "workloads", "backward",
+                                       "backward_truncate", "decode"],
                     default=None,
                     help="profiling aid: run only this path (after the same warmup) and print its "
                          "object alone, not the benchmark line")
@@ -364,7 +365,11 @@ def only_path(args):
     elif args.only == "workloads":
         out["workloads"] = time_workloads(gdn, torch, args.steps, args.warmup)
     elif args.only == "backward":
-        out["backward"] = time_backward(gdn, torch, args.steps, args.warmup, with_l2norm=False)
+        out["backward"] = time_backward(gdn, torch, args.steps, args.warmup, with_l2norm=False,
+                                        with_truncate=False)
+    elif args.only == "backward_truncate":
+        out["backward"] = time_backward(gdn, torch, args.steps, args.warmup, with_l2norm=False,
+                                        with_exact=False)
     else:
         out["decode"] = time_decode(gdn, torch, args.steps, args.warmup)
     print(json.dumps(out), flush=True)
@@ -505,10 +510,11 @@ def time_decode(gdn, torch, steps, warmup, sets=6):
                          "bytes_per_step": nbytes}}
 
 
-def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
+def time_backward(gdn, torch, steps, warmup, with_l2norm=True, with_exact=True,
+                  with_truncate=True):
     """The training step's backward (gdn_chunk_bwd: forward recompute, reverse chain, per-chunk
     gradients) on the packed 65536-token workload of 4096..16384-token documents, H = 8, d = 128,
-    bf16, dO ~ N(0, 1), timed like the forward.  Algorithmic bytes: q, k, v, dO read and dq, dk,
+    bf16, dO ~ N(0, 1), timed like the forward: the exact mode, and beside it the truncate mode.  Algorithmic bytes: q, k, v, dO read and dq, dk,
     dv written in bf16, g read and dg written in fp32, beta read and dbeta written in bf16."""
     from gdn_inputs import workload
 
@@ -536,8 +542,18 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
         gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu, dev["dout"], workspace=ws,
                       cu_seqlens_host=cu_host)
 
-    r = timed(torch, step, steps, warmup)
-    ms = r["median_ms"]
+    r = timed(torch, step, steps, warmup) if with_exact else None
+    ms = r["median_ms"] if r else None
+    rt = None
+    if with_truncate:  # the truncate mode's backward (warmup windows instead of the extra passes)
+        pt = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "truncate")
+        assert gdn.load_library().gdn_chunk_bwd_workspace_size(ctypes.byref(pt), cu_arr,
+                                                               ctypes.byref(nbytes)) == 0
+        wst = torch.empty(nbytes.value, dtype=torch.uint8, device="cuda")
+        rt = timed(torch, lambda i: gdn.chunk_bwd(dev["q"], dev["k"], dev["v"], g, dev["beta"], cu,
+                                                  dev["dout"], workspace=wst, mode="truncate",
+                                                  cu_seqlens_host=cu_host),
+                   steps, warmup)
     rn = None
     if with_l2norm:  # the same backward with q and k normalised inside the kernels
         pn = make_problem(T, len(inp["cu_seqlens"]) - 1, H, D, torch.bfloat16, "exact",
@@ -550,20 +566,27 @@ def time_backward(gdn, torch, steps, warmup, with_l2norm=True):
                                                   cu_seqlens_host=cu_host),
                    steps, warmup)
     nbytes_alg = BWD_BYTES_PER_TH * T * H
-    achieved = nbytes_alg / (r["mean_ms"] / 1e3) / 1e9
-    traffic = None  # measured HBM bytes per call (rocprofv3), while the kernels are unchanged
-    if os.path.exists(BWD_TRAFFIC_FILE):
-        with open(BWD_TRAFFIC_FILE) as f:
-            rec = json.load(f)
-        if rec.get("kernel_source_sha") == kernel_source_sha(BWD_SOURCES):
-            traffic = rec.get("bytes_per_call")
-    return {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
-                        f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
-            "ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
-            "qk_l2norm_ms_per_step": rn["median_ms"] if rn else None,
-            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                         "bytes_per_step": nbytes_alg, "traffic": traffic}}
+    out = {"workload": f"packed {T} tokens ({len(inp['cu_seqlens']) - 1} documents of "
+                       f"4096..16384), H={H}, d_k=d_v={D}, bf16, dO ~ N(0,1)",
+           "qk_l2norm_ms_per_step": rn["median_ms"] if rn else None}
+    if r:
+        achieved = nbytes_alg / (r["mean_ms"] / 1e3) / 1e9
+        traffic = None  # measured HBM bytes per call (rocprofv3), while the kernels are unchanged
+        if os.path.exists(BWD_TRAFFIC_FILE):
+            with open(BWD_TRAFFIC_FILE) as f:
+                rec = json.load(f)
+            if rec.get("kernel_source_sha") == kernel_source_sha(BWD_SOURCES):
+                traffic = rec.get("bytes_per_call")
+        out.update({"ms_per_step": ms, "tokens_per_s": T / (ms / 1e3), "timing": r,
+                    "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                                 "bytes_per_step": nbytes_alg, "traffic": traffic}})
+    if rt:
+        out["truncate"] = {"ms_per_step": rt["median_ms"],
+                           "tokens_per_s": T / (rt["median_ms"] / 1e3), "timing": rt,
+                           "roofline_frac": nbytes_alg / (rt["median_ms"] / 1e3) / 1e9
+                           / HBM_PEAK_GBS}
+    return out
 
 
 def kernel_source_sha(sources=("gdn_fwd_ws.hip",)):

@@ -43,9 +43,17 @@ __device__ __forceinline__ int sw(int r) { return ((r & 7) << 1) | ((r >> 3) & 1
 __device__ __forceinline__ int toff(int r, int u) {
   return r * kRowB + (((u >> 1) ^ sw(r)) << 4) + ((u & 1) << 3);
 }
-// 64 x 64 bf16 tiles: rows of 128 bytes, 8-byte unit u of row r at u ^ 2 ((r / 2) % 8)
+// 64 x 64 bf16 tiles (dPm, E): rows of 128 bytes, 8-byte unit u of row r at u ^ f(x), x =
+// (r / 2) % 8 = (b2 b1 b0), f = 8 b1 + 4 (b0 ^ b2) + 2 b2.  Two rows of 128 bytes fill the 64
+// banks.  Each access below then touches every bank pair once per half-wave: the row reads (16
+// consecutive rows, one unit each: f's bits 3..1 differ over the 8 rows of one parity), the
+// transposing reads (4 rows, 4 consecutive units each: f's bits 3..2 differ over the 4 rows of one
+// parity, b2 being 0 there) and the 2-byte stores of a 16 x 16 block (4 rows two apart: bits 3..2
+// differ over (b2, b1) with b0 fixed).
 __device__ __forceinline__ int poff(int r, int u) {
-  return r * 128 + ((u ^ (((r >> 1) & 7) << 1)) << 3);
+  const int x = (r >> 1) & 7;
+  const int f = ((x & 2) << 2) | (((x ^ (x >> 2)) & 1) << 2) | ((x >> 2) << 1);
+  return r * 128 + ((u ^ f) << 3);
 }
 
 __device__ __forceinline__ bf16x4 ld8(const char *p) { return *reinterpret_cast<const bf16x4 *>(p); }
