@@ -38,8 +38,9 @@
  *     entry on and write nothing for them, so no access leaves the caller's buffers; the
  *     outputs of such a call are undefined.  gdn_validate_cu_seqlens checks a table on the
  *     device, and the debug mode (GDN_DEBUG=1 in the environment, or gdn_set_debug(1)) runs
- *     that check inside every compute call before its first launch, returning
- *     GDN_ERR_BAD_SHAPE with nothing launched, and after the launches synchronises the stream
+ *     that check inside every compute call before its first launch, and also checks that
+ *     cu_seqlens_host, when given, equals the device table (read back); either failure returns
+ *     GDN_ERR_BAD_SHAPE with nothing launched.  After the launches it synchronises the stream
  *     and returns GDN_ERR_DEVICE_CHECK if a kernel set a fault flag (gdn_device_faults).
  *   Architecture: only gfx950 is supported; other devices return GDN_ERR_UNSUPPORTED_ARCH (the
  *     page's library likewise refuses hardware it was not built for, section "Using it, and the
@@ -261,7 +262,8 @@ gdn_status gdn_validate_cu_seqlens(const int32_t *cu_seqlens, int32_t num_seqs,
 /* Debug mode on (1) or off (0) for the whole process; its initial value comes from the
  * environment variable GDN_DEBUG (unset or "0": off).  In debug mode gdn_chunk_fwd,
  * gdn_chunk_fwd_intermediates, gdn_chunk_fwd_plan and gdn_chunk_bwd validate cu_seqlens on the
- * device before their first launch and synchronise the stream (so they are not asynchronous,
+ * device (and compare it with cu_seqlens_host when one is given) before their first launch and
+ * synchronise the stream (so they are not asynchronous,
  * and calls that overlap on one device share its check words).  No passage applies: a
  * diagnostic of this library. */
 gdn_status gdn_set_debug(int32_t on);

@@ -39,8 +39,8 @@ gdn_status hip_fail(hipError_t e, const char *what) {
 
 // Debug mode (GDN_DEBUG=1 in the environment, or gdn_set_debug): every compute call first
 // validates cu_seqlens on the device and returns GDN_ERR_BAD_SHAPE before any compute launch if
-// it is malformed, and after its launches synchronises the stream and returns
-// GDN_ERR_DEVICE_CHECK if a kernel set a fault flag.
+// it is malformed or differs from the host copy the call was given, and after its launches
+// synchronises the stream and returns GDN_ERR_DEVICE_CHECK if a kernel set a fault flag.
 std::atomic<int> g_debug{-1};
 
 bool debug_on() {
@@ -55,7 +55,8 @@ bool debug_on() {
   return d == 1;
 }
 
-gdn_status debug_validate(const int32_t *cu, int32_t N, int64_t T, hipStream_t stream) {
+gdn_status debug_validate(const int32_t *cu, int32_t N, int64_t T, const int32_t *cu_host,
+                          hipStream_t stream) {
   uint32_t *words = nullptr;
   hipError_t e = gdn::device_check_words(&words);
   if (e != hipSuccess) return hip_fail(e, "debug mode: check words");
@@ -72,6 +73,21 @@ gdn_status debug_validate(const int32_t *cu, int32_t N, int64_t T, hipStream_t s
                 (status & gdn::kCuDescending) ? " descending offsets" : "",
                 (status & gdn::kCuLastNotTotal) ? " cu[N] != total_tokens" : "",
                 (status & gdn::kCuOutOfRange) ? " offsets outside [0, total_tokens]" : "");
+  if (cu_host != nullptr) {  // the host copy plans the split: it must be the device table
+    int32_t part[1024];      // read back in pieces, with no allocation
+    for (int64_t i0 = 0; i0 <= N; i0 += 1024) {
+      const int64_t cnt = std::min<int64_t>(1024, (int64_t)N + 1 - i0);
+      e = hipMemcpyAsync(part, cu + i0, sizeof(int32_t) * cnt, hipMemcpyDeviceToHost, stream);
+      if (e == hipSuccess) e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "debug mode: cu_seqlens read-back");
+      for (int64_t i = 0; i < cnt; ++i)
+        if (part[i] != cu_host[i0 + i])
+          return fail(GDN_ERR_BAD_SHAPE,
+                      "cu_seqlens_host[%lld] = %d differs from the device cu_seqlens (%d); "
+                      "nothing launched",
+                      (long long)(i0 + i), cu_host[i0 + i], part[i]);
+    }
+  }
   return GDN_OK;
 }
 
@@ -361,7 +377,7 @@ gdn_status run_fwd(const gdn_problem *p, const Tensors &t, const int32_t *cu_hos
     return fail(GDN_ERR_WORKSPACE_TOO_SMALL, "workspace needs %zu bytes", lay.total);
   if (lay.total > 0 && !aligned16(ws)) return fail(GDN_ERR_BAD_ALIGNMENT, "workspace alignment");
   if (debug_on()) {
-    s = debug_validate(t.cu, p->num_seqs, p->total_tokens, stream);
+    s = debug_validate(t.cu, p->num_seqs, p->total_tokens, cu_host, stream);
     if (s != GDN_OK) return s;
     s = launch_fwd_passes(p, t, lay, dump, dbg, ws, stream);
     return s != GDN_OK ? s : debug_faults(stream);
@@ -550,7 +566,7 @@ gdn_status gdn_chunk_fwd_plan(const gdn_problem *p, const float *g, const int32_
   (void)workspace;
   if (plan_capacity < 2) return fail(GDN_ERR_BAD_SHAPE, "plan_capacity must be >= 2");
   if (debug_on()) {
-    s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, stream);
+    s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, cu_seqlens_host, stream);
     if (s != GDN_OK) return s;
   }
   const int truncate = (p->mode == GDN_MODE_TRUNCATE && lay.L > 0) ? 1 : 0;
@@ -776,7 +792,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   const bool debug = debug_on();
   if (debug) {
     s = device_info(nullptr);
-    if (s == GDN_OK) s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, stream);
+    if (s == GDN_OK)
+      s = debug_validate(cu_seqlens, p->num_seqs, p->total_tokens, cu_seqlens_host, stream);
     if (s != GDN_OK) return s;
   }
   char *base = static_cast<char *>(workspace);

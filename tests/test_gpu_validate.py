@@ -82,6 +82,38 @@ def test_debug_mode_refuses_a_malformed_table_before_launching(gdn):
     assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
 
 
+def test_debug_mode_refuses_a_host_copy_that_differs(gdn):
+    """The host copy of cu_seqlens plans the split; in debug mode a copy that differs from the
+    device table (both well formed) is refused with nothing launched, and a matching copy runs."""
+    inp = make_inputs([100, 200], H=2, dk=128, dv=128, dtype="bf16", seed=14, with_dout=True)
+    d = to_dev(inp)
+    other = np.array([0, 150, 300], dtype=np.int32)  # well formed, not the device's [0, 100, 300]
+    o = torch.full_like(d["v"], 7.0)
+    before = gdn.get_debug()
+    gdn.set_debug(True)
+    try:
+        for mode in ("exact", "truncate"):
+            with pytest.raises(gdn.GdnError) as ei:
+                gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None, mode=mode, out=o,
+                              cu_seqlens_host=other)
+            assert ei.value.status == 2 and "differs" in str(ei.value)
+        with pytest.raises(gdn.GdnError) as ei:
+            gdn.chunk_fwd_plan(d["g"], d["cu_seqlens"], 2, 128, torch.bfloat16, mode="truncate",
+                               cu_seqlens_host=other)
+        assert ei.value.status == 2
+        with pytest.raises(gdn.GdnError) as ei:
+            gdn.chunk_bwd(*args_of(d), d["cu_seqlens"], d["dout"], cu_seqlens_host=other)
+        assert ei.value.status == 2
+        torch.cuda.synchronize()
+        assert bool((o == 7.0).all())
+        o1, _ = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None,
+                              cu_seqlens_host=inp["cu_seqlens"])
+    finally:
+        gdn.set_debug(before)
+    o2, _ = gdn.chunk_fwd(*args_of(d), d["cu_seqlens"], None)
+    assert torch.equal(o1, o2)
+
+
 def test_no_fault_flags_after_normal_runs(gdn):
     inp = make_inputs([3000], H=8, dk=128, dv=128, dtype="bf16", seed=12)
     d = to_dev(inp)
