@@ -111,12 +111,15 @@ def test_l2norm_bf16_d64(gdn, oracle_mod, mode, seg):
     _run_fwd(gdn, oracle_mod, inp, f"l2norm bf16 d=64 {mode}", mode=mode, seg=seg, scale=0.7)
 
 
-@pytest.mark.parametrize("dtype,d,G,seg", [("bf16", 128, 1, 0), ("bf16", 128, 2, 2),
-                                           ("bf16", 64, 1, 0), ("bf16", 64, 2, 0),
-                                           ("f32", 64, 1, 0), ("f32", 128, 2, 0)])
-def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg):
+@pytest.mark.parametrize("dtype,d,G,seg,mode", [
+    ("bf16", 128, 1, 0, "exact"), ("bf16", 128, 2, 2, "exact"), ("bf16", 64, 1, 0, "exact"),
+    ("bf16", 64, 2, 0, "exact"), ("f32", 64, 1, 0, "exact"), ("f32", 128, 2, 0, "exact"),
+    ("bf16", 128, 1, 2, "truncate"), ("bf16", 128, 2, 2, "truncate")])
+def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg, mode):
     """Gradients of the raw q, k (through the normalisation) and of v, g, beta, h0 against the
-    oracle's backward with the normalisation; grouped heads sum dq, dk over each group."""
+    oracle's backward with the normalisation; grouped heads sum dq, dk over each group.  The
+    truncate mode's backward (2-chunk segments: warmup windows that stop inside a document and
+    ones that reach its start or end) against the same exact gradients."""
     inp = make_inputs([300, 65, 0, 260], H=4, dk=d, dv=d, dtype=dtype, seed=521, h0_scale=0.5,
                       with_dout=True)
     inp = scale_qk_rows(inp, seed=522)
@@ -131,10 +134,10 @@ def test_l2norm_backward(gdn, oracle_mod, dtype, d, G, seg):
     N = len(inp["cu_seqlens"]) - 1
     dht = (0.3 * rng.standard_normal((N, 4, d, d))).astype(np.float32)
     args = [_dev(gi[x], tdt if x != "g" else None) for x in NAMES]
-    print(f"[l2norm bwd {dtype} d={d} G={G} seg={seg}]", flush=True)
+    print(f"[l2norm bwd {dtype} d={d} G={G} seg={seg} {mode}]", flush=True)
     gr = gdn.chunk_bwd(*args, _dev(inp["cu_seqlens"]), _dev(inp["dout"], tdt), _dev(inp["h0"]),
                        _dev(dht), scale=0.7, seg_chunks=seg, num_slots=256 if seg else 0,
-                       qk_l2norm=True)
+                       qk_l2norm=True, mode=mode)
     torch.cuda.synchronize()
     r = oracle_mod.bwd(*[ref[x] for x in NAMES], inp["cu_seqlens"], inp["dout"], h0=inp["h0"],
                        dht=dht, scale=0.7, qk_l2norm=True)
