@@ -639,10 +639,12 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
   L->gamma = take(sizeof(float) * T * H);
   L->tmat = take(sizeof(float) * L->nc * H * 64 * 64);
   if (!bwd_bf16_path(p)) L->w = take(sizeof(float) * L->nc * H * 64 * D);  // W: general kernels only
-  L->hc = take(sizeof(float) * L->nc * H * D * D);
+  // per-chunk states h and dh': bf16 on the bf16 d = 128 kernels, fp32 on the general ones
+  const size_t ssz = bwd_bf16_path(p) ? 2 : 4;
+  L->hc = take(ssz * L->nc * H * D * D);
   L->delta = take(sizeof(float) * T * H * D);
   L->o = take(esz * T * H * D);
-  L->dhn = take(sizeof(float) * L->nc * H * D * D);
+  L->dhn = take(ssz * L->nc * H * D * D);
   L->ddelta = take(sizeof(float) * T * H * D);
   L->dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
   L->truncate = L->L > 0 && p->mode == GDN_MODE_TRUNCATE;
@@ -671,8 +673,8 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
 // split (every unit's affine map (B, M), then the maps composed along each sequence into true
 // start states, as in the forward's exact split; or, in the truncate mode, each unit from the
 // warmup window before it, as the truncate-mode forward runs).
-gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float *gamma, float *hc,
-                                  float *delta, const BwdLayout &L, char *base,
+gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float *gamma,
+                                  uint16_t *hc, float *delta, const BwdLayout &L, char *base,
                                   hipStream_t stream) {
   gdn::FwdArgs a{};
   a.q = t.q;
@@ -728,7 +730,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
     a.unit_h0 = uh0;
   }
   a.dbg_gamma = gamma;
-  a.dbg_hc = hc;
+  a.dump_hc = hc;
   a.dbg_delta = delta;
   e = gdn::launch_fwd_ws_dump(a, units, stream);
   if (e != hipSuccess) return hip_fail(e, "backward recompute: intermediates");
@@ -801,7 +803,8 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   float *tmat = reinterpret_cast<float *>(base + L.tmat);
   const bool fast = bwd_bf16_path(p);
   float *w = fast ? nullptr : reinterpret_cast<float *>(base + L.w);
-  float *hc = reinterpret_cast<float *>(base + L.hc);
+  float *hc = fast ? nullptr : reinterpret_cast<float *>(base + L.hc);
+  uint16_t *hc_b16 = fast ? reinterpret_cast<uint16_t *>(base + L.hc) : nullptr;
   float *delta = reinterpret_cast<float *>(base + L.delta);
   // forward recompute with the per-chunk intermediates (o goes to scratch)
   Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
@@ -809,7 +812,7 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   if (fast) {
     s = check_tensors(t, p->total_tokens);
     if (s == GDN_OK) s = device_info(nullptr);
-    if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc, delta, L, base, stream);
+    if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc_b16, delta, L, base, stream);
   } else {  // the general kernels' backward is unsplit: the exact one, whatever the mode
     gdn_problem pe = *p;
     pe.mode = GDN_MODE_EXACT;
@@ -837,8 +840,10 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.tmat = tmat;
   b.w = w;
   b.hc = hc;
+  b.hc_b16 = hc_b16;
   b.delta = delta;
-  b.dhn = reinterpret_cast<float *>(base + L.dhn);
+  b.dhn = fast ? nullptr : reinterpret_cast<float *>(base + L.dhn);
+  b.dhn_b16 = fast ? reinterpret_cast<uint16_t *>(base + L.dhn) : nullptr;
   const bool grouped = k_heads(p) < p->num_heads;
   const bool part = grouped || (p->qk_l2norm && !fast);
   b.dq_part = part ? reinterpret_cast<float *>(base + L.dq_part) : nullptr;

@@ -9,7 +9,8 @@
 // (the last term is W^T dDelta with W = Tm diag(beta a) K), the reverse-mode derivative of the
 // chunked form of "How to Speed Up GDN Kernels for Qwen Models" (section "What GDN actually
 // computes"); the hidden states themselves are recomputed by a forward pass ("Lever 2").  dh' of
-// every chunk, dR and dV go out for the per-chunk gradient kernel.
+// every chunk (in bf16: the gradient kernel's products take it as a bf16 operand), dR and dV go
+// out for the per-chunk gradient kernel.
 //
 // Products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation.  q, k and dO are bf16 inputs
 // and enter exactly.  Every other operand (dh', dDelta, dR, Tm, P, a dO) is split into a bf16
@@ -209,12 +210,12 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     return cat8(ldtr(t + toff(r, u)), ldtr(t + toff(r + 16, u)));
   };
 
-  // store offsets (bytes): row 4 gq of a 128 x 128 fp32 matrix and token 4 gq of a [T, H, 128]
+  // store offsets (bytes): row 4 gq of a 128 x 128 bf16 matrix and token 4 gq of a [T, H, 128]
   // fp32 tensor, at this lane's column of tile nt
   int o_st[kNT], o_tk[kNT];
 #pragma unroll
   for (int nt = 0; nt < kNT; ++nt) {
-    o_st[nt] = (4 * gq * kD + col0 + 16 * nt) * 4;
+    o_st[nt] = (4 * gq * kD + col0 + 16 * nt) * 2;
     o_tk[nt] = (4 * gq * H * kD + col0 + 16 * nt) * 4;
   }
 
@@ -310,18 +311,19 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     lds_barrier();  // P^T
     const float lam = __expf(sm.gam[63]);
 
-    // ---- dh' of this chunk to the workspace
+    // ---- dh' of this chunk to the workspace, in bf16 (the precision of the products that use it)
     if (emit) {  // row offsets as scalar operands
-      const __amdgpu_buffer_rsrc_t hr =
-          __builtin_amdgcn_make_buffer_rsrc(b.dhn + (cg * H + h) * dd, (short)0, (int)dd * 4, 0x00020000);
+      const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
+          b.dhn_b16 + (cg * H + h) * dd, (short)0, (int)dd * 2, 0x00020000);
 #pragma unroll
       for (int md = 0; md < 8; ++md)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int nt = 0; nt < kNT; ++nt)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(G[md][nt][i]), hr, o_st[nt],
-                                                  (16 * md + i) * kD * 4, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(
+                __builtin_bit_cast(unsigned short, (bf16)G[md][nt][i]), hr, o_st[nt],
+                (16 * md + i) * kD * 2, 0);
     }
 
     // ---- dDelta = P^T dO_s + diag(c) K dh'

@@ -18,11 +18,12 @@
 // chunked form of "How to Speed Up GDN Kernels for Qwen Models" (section "What GDN actually
 // computes"), with the hidden states recomputed ("Lever 2").
 //
-// One workgroup of eight waves per (chunk, head), the heads of a chunk in consecutive workgroups.  Products run on v_mfma_f32_16x16x32_bf16 with
-// fp32 accumulation; q, k, v and dO enter exactly, every other operand as a bf16 head plus a bf16
-// remainder (see the reverse chain).  Wave w owns feature columns [16 w, 16 w + 16) of every
-// 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go straight from HBM into
-// the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
+// One workgroup of eight waves per (chunk, head), the heads of a chunk in consecutive
+// workgroups.  Products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; q, k, v and dO
+// enter exactly, h and dh' as stored (bf16, as the forward takes h in its products), every other
+// operand as a bf16 head plus a bf16 remainder (see the reverse chain).  Wave w owns feature
+// columns [16 w, 16 w + 16) of every 64 x 128 result and takes its share of the 64 x 64 tiles;
+// h and dh' go straight from HBM into the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
 // so results are bitwise reproducible.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
@@ -62,11 +63,6 @@ __device__ __forceinline__ bf16x4 ldtr(const char *p) {
   return lds_tr16(reinterpret_cast<const bf16 *>(p));
 }
 __device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
-__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &lo) {
-  const bf16x4 h0 = to_bf16x4(x0), h1 = to_bf16x4(x1);
-  hi = cat8(h0, h1);
-  lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
-}
 // the four rows' totals of a value that row16_sum_dpp made uniform within each row, added in
 // row order (a wave-uniform result).  Call it where every lane is active: it reads lanes 16, 32
 // and 48 whatever the branch, and the compiler may sink the row sums' last adds into a branch
@@ -164,15 +160,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   const int64_t tok_qk = (int64_t)b.HK * kRowB;   // stride of one token in q, k
   const int64_t dd = (int64_t)kD * kD;
   const float scale = b.scale;
-  const float *hS = b.hc + ((int64_t)cg * H + h) * dd;
-  const float *dhn = b.dhn + ((int64_t)cg * H + h) * dd;
+  const bf16 *hS = reinterpret_cast<const bf16 *>(b.hc_b16) + ((int64_t)cg * H + h) * dd;
+  const bf16 *dhn = reinterpret_cast<const bf16 *>(b.dhn_b16) + ((int64_t)cg * H + h) * dd;
 
   // ---- stage.  Every load is issued before any is waited for, h and dh' last: dO, Q, K, V into
   //      LDS through registers (rows past n repeat the chunk's last token, which every use
   //      masks), Delta and dR split into LDS (rows past n zero), and each wave's rows of h and
   //      dh' into registers for its B operands, where they stay in flight through the tile phase.
   const int fcol = 16 * kNT * w + cl;  // this lane's feature column in tile nt: fcol + 16 nt
-  f32x4 hv[kNT][4][2], gv[kNT][4][2];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
+  bf16x8 hh[kNT][4], gh[kNT][4];  // h and dh' rows fcol + 16 nt, elements 32 ks + 8 gq .. + 7
   {
     const char *src[4] = {static_cast<const char *>(b.dout), static_cast<const char *>(b.q),
                           static_cast<const char *>(b.k), static_cast<const char *>(b.v)};
@@ -223,10 +219,8 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
         const int64_t off = (int64_t)(fcol + 16 * nt) * kD + 32 * ks + 8 * gq;
-        hv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(hS + off);
-        hv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(hS + off + 4);
-        gv[nt][ks][0] = *reinterpret_cast<const f32x4 *>(dhn + off);
-        gv[nt][ks][1] = *reinterpret_cast<const f32x4 *>(dhn + off + 4);
+        hh[nt][ks] = *reinterpret_cast<const bf16x8 *>(hS + off);
+        gh[nt][ks] = *reinterpret_cast<const bf16x8 *>(dhn + off);
       }
     sched_fence();
     __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -379,20 +373,16 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
     }
     if (gq == 0) sm.pcg[w][i] = csc;
   }
-  // ---- h and dh' rows of this wave (B operands over features, split), <dh', h>
-  bf16x8 hh[kNT][4], hl[kNT][4];
+  // ---- h and dh' rows of this wave (bf16 B operands over features), <dh', h>
   f32x4 Y1[4][kNT], Y2[4][kNT];
   float hdot = 0.f;
   {
-    bf16x8 gh[kNT][4], gl[kNT][4];
 #pragma unroll
     for (int nt = 0; nt < kNT; ++nt)
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const f32x4 h0 = hv[nt][ks][0], h1 = hv[nt][ks][1];
-        const f32x4 d0 = gv[nt][ks][0], d1 = gv[nt][ks][1];
-        split8(h0, h1, hh[nt][ks], hl[nt][ks]);
-        split8(d0, d1, gh[nt][ks], gl[nt][ks]);
+        const f32x4 h0 = to_f32x4(lo4(hh[nt][ks])), h1 = to_f32x4(hi4(hh[nt][ks]));
+        const f32x4 d0 = to_f32x4(lo4(gh[nt][ks])), d1 = to_f32x4(hi4(gh[nt][ks]));
 #pragma unroll
         for (int j = 0; j < 4; ++j) hdot += h0[j] * d0[j] + h1[j] * d1[j];
       }
@@ -408,9 +398,7 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) {
           Y1[mt][nt] = mma_bf16(ao, hh[nt][ks], Y1[mt][nt]);
-          Y1[mt][nt] = mma_bf16(ao, hl[nt][ks], Y1[mt][nt]);
           Y2[mt][nt] = mma_bf16(ah, gh[nt][ks], Y2[mt][nt]);
-          Y2[mt][nt] = mma_bf16(ah, gl[nt][ks], Y2[mt][nt]);
           Y2[mt][nt] = mma_bf16(al, gh[nt][ks], Y2[mt][nt]);
         }
       }
@@ -431,7 +419,6 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         Rh[mt][nt] = mma_bf16(ah, hh[nt][ks], Rh[mt][nt]);
-        Rh[mt][nt] = mma_bf16(ah, hl[nt][ks], Rh[mt][nt]);
         Rh[mt][nt] = mma_bf16(al, hh[nt][ks], Rh[mt][nt]);
       }
     }

@@ -148,9 +148,10 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 }  // namespace
 
 // kDump: the pass of the backward's forward recompute.  No output; per chunk it writes the state
-// at the chunk's start (a.dbg_hc [chunks, H, D, D]), Delta (a.dbg_delta [T, H, D]) and gamma
-// (a.dbg_gamma [T, H]), all fp32, chunks numbered across sequences; in the truncate mode, for
-// the unit's own chunks only (the warmup's belong to the unit before).
+// at the chunk's start in bf16 (a.dump_hc [chunks, H, D, D], the precision of the products that
+// use it), Delta (a.dbg_delta [T, H, D]) and gamma (a.dbg_gamma [T, H]) in fp32, chunks numbered
+// across sequences; in the truncate mode, for the unit's own chunks only (the warmup's belong
+// to the unit before).
 // kTransition: the first pass of the exact split.  Workgroup (unit, head, z) runs the unit's
 // chunks from a fixed start without output and writes its final state to a.unit_out[z]: z = 0
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
@@ -303,14 +304,14 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     const int vu = 4 * w + ((lane & 3) ^ (((lane >> 4) & 1) << 1));
     const int o_gv = pin((int)((lane >> 2) * tok_bytes) + vu * 16);
     const int o_go = pin((int)(cl * tok_bytes) + (ncol + 8 * gq) * 2);      // O stores
-    // dump stores (fp32): the state (row 4 gq of a 128 x 128 matrix) and Delta (token 4 gq), at
-    // this lane's column of tile nt
+    // dump stores: the state (bf16, row 4 gq of a 128 x 128 matrix) and Delta (fp32, token 4 gq),
+    // at this lane's column of tile nt
     int o_dh[2] = {0, 0}, o_dd[2] = {0, 0};
     if constexpr (kDump) {
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) {
         const int col = ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3);
-        o_dh[nt] = pin((4 * gq * kD + col) * 4);
+        o_dh[nt] = pin((4 * gq * kD + col) * 2);
         o_dd[nt] = pin((4 * gq * H * kD + col) * 4);
       }
     }
@@ -394,15 +395,16 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         if (kDump && cc >= c0) {  // the state at the chunk's start (all rows in range; row
                                   // offsets as scalar operands); none for a warmup's chunks
           const __amdgpu_buffer_rsrc_t hr = __builtin_amdgcn_make_buffer_rsrc(
-              a.dbg_hc + ((chunk_base + cc) * H + h) * kD * kD, (short)0, kD * kD * 4, 0x00020000);
+              a.dump_hc + ((chunk_base + cc) * H + h) * kD * kD, (short)0, kD * kD * 2, 0x00020000);
 #pragma unroll
           for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
               for (int nt = 0; nt < 2; ++nt)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(S[mt][nt][i]), hr,
-                                                      o_dh[nt], (16 * mt + i) * kD * 4, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(
+                    __builtin_bit_cast(unsigned short, (bf16)S[mt][nt][i]), hr, o_dh[nt],
+                    (16 * mt + i) * kD * 2, 0);
         }
         const int Y = cc & 1;
         const char *Kt = sm.kq[cc % 3][0], *Qt = sm.kq[cc % 3][1];

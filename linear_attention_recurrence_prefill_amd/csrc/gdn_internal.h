@@ -48,6 +48,7 @@ struct FwdArgs {
   void *o;
   float *ht;
   float *dbg_gamma, *dbg_tmat, *dbg_w, *dbg_u, *dbg_hc, *dbg_delta;  // intermediates (or null)
+  uint16_t *dump_hc;  // the pipelined kernel's recompute pass: start states in bf16 [Nc, H, D, D]
   int64_t T;
   int32_t N, H;
   int32_t HK;  // heads of q and k (H / HK value heads share one)
@@ -104,7 +105,9 @@ struct SplitArgs {
 // Arguments of the backward kernels (see gdn_bwd.hip).  Workspace arrays (fp32):
 //   gamma [T, H], tmat [Nc, H, 64, 64], w [Nc, H, 64, D], hc [Nc, H, D, D], delta [T, H, D]
 //   from the forward recompute; dhn [Nc, H, D, D] (state gradient after each chunk) and
-//   ddelta [T, H, D] from the reverse chain.
+//   ddelta [T, H, D] from the reverse chain.  bf16 inputs with d = 128 keep the per-chunk states
+//   in bf16 instead (hc_b16, dhn_b16; hc and dhn null): the products that use them take bf16
+//   operands, as the forward's do.
 struct BwdArgs {
   const void *q, *k, *v, *beta, *dout;
   const float *g, *dht;
@@ -113,6 +116,8 @@ struct BwdArgs {
   float *dg, *dh0_seq;
   const float *gamma, *tmat, *w, *hc, *delta;
   float *dhn, *ddelta;
+  const uint16_t *hc_b16;  // bf16 bit patterns
+  uint16_t *dhn_b16;
   // grouped heads (HK < H): dq and dk of every value head, fp32 [T, H, D], summed per key head
   // afterwards (null when HK == H: dq and dk are written directly)
   float *dq_part, *dk_part;

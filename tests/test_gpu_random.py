@@ -6,11 +6,12 @@ and the backward in the case's mode against the oracle's exact gradients (the tr
 backward approximates them within the same bound as its forward; gfx950 only; marked
 ``gpu``).
 
-With bf16 inputs and the normalisation, the kernels round the normalised rows to bf16 before
-using them, as an unfused normalise-then-cast would.  On a short document with d = 64 that
-rounding alone moves a (document, head) slice of dg by more than the bf16 bound, so those cases
-check each (document, head) against the oracle run on the rounded rows and the whole tensors
-against the exact oracle."""
+With bf16 inputs, d = 64 and the normalisation, the kernels round the normalised rows to bf16
+before using them, as an unfused normalise-then-cast would (with d = 128 they fold the norms into
+fp32 factors instead and round nothing).  On a short document that rounding alone moves a
+(document, head) slice of dg by more than the bf16 bound, so those cases check each (document,
+head) against the oracle run on the rounded rows and the whole tensors against the exact
+oracle."""
 import numpy as np
 import pytest
 
@@ -91,7 +92,7 @@ def test_random_combination(gdn, oracle_mod, seed):
                           scale=c["scale"], qk_l2norm=c["norm"])
     torch.cuda.synchronize()
     oargs = [ref[x] for x in NAMES]
-    rounded = c["norm"] and c["dtype"] == "bf16"
+    rounded = c["norm"] and c["dtype"] == "bf16" and c["d"] == 64
     uargs = None
     if rounded:
         used = dict(ref)
