@@ -340,8 +340,9 @@ struct Tensors {
 };
 
 // The per-token arrays may be NULL only when there are no tokens.
-gdn_status check_tensors(const Tensors &t, int64_t T) {
-  if (!t.cu || (T > 0 && (!t.q || !t.k || !t.v || !t.g || !t.beta || !t.o)))
+// need_o: false for the backward's recompute on the pipelined kernel, which writes no output
+gdn_status check_tensors(const Tensors &t, int64_t T, bool need_o = true) {
+  if (!t.cu || (T > 0 && (!t.q || !t.k || !t.v || !t.g || !t.beta || (need_o && !t.o))))
     return fail(GDN_ERR_NULL_ARG, "q, k, v, g, beta, cu_seqlens and o are required");
   const void *ptrs[] = {t.q, t.k, t.v, t.g, t.beta, t.o};
   for (const void *x : ptrs)
@@ -643,7 +644,7 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
   const size_t ssz = bwd_bf16_path(p) ? 2 : 4;
   L->hc = take(ssz * L->nc * H * D * D);
   L->delta = take(sizeof(float) * T * H * D);
-  L->o = take(esz * T * H * D);
+  if (!bwd_bf16_path(p)) L->o = take(esz * T * H * D);  // the general recompute's output (unused)
   L->dhn = take(ssz * L->nc * H * D * D);
   L->ddelta = take(sizeof(float) * T * H * D);
   L->dh0 = take(sizeof(float) * p->num_seqs * H * D * D);
@@ -806,11 +807,12 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   float *hc = fast ? nullptr : reinterpret_cast<float *>(base + L.hc);
   uint16_t *hc_b16 = fast ? reinterpret_cast<uint16_t *>(base + L.hc) : nullptr;
   float *delta = reinterpret_cast<float *>(base + L.delta);
-  // forward recompute with the per-chunk intermediates (o goes to scratch)
-  Tensors t{q, k, v, g, beta, cu_seqlens, h0, base + L.o, nullptr};
+  // forward recompute with the per-chunk intermediates (the general kernels' o goes to scratch;
+  // the pipelined kernel's recompute pass writes none)
+  Tensors t{q, k, v, g, beta, cu_seqlens, h0, fast ? nullptr : base + L.o, nullptr};
   float *dbg[6] = {gamma, tmat, w, nullptr, hc, delta};
   if (fast) {
-    s = check_tensors(t, p->total_tokens);
+    s = check_tensors(t, p->total_tokens, false);
     if (s == GDN_OK) s = device_info(nullptr);
     if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc_b16, delta, L, base, stream);
   } else {  // the general kernels' backward is unsplit: the exact one, whatever the mode

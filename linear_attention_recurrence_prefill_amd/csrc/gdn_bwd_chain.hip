@@ -156,7 +156,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
   const int c0 = __builtin_amdgcn_readfirstlane(sm.imisc[1]);
   const int c1 = __builtin_amdgcn_readfirstlane(sm.imisc[2]);
   const int ce = __builtin_amdgcn_readfirstlane(sm.imisc[4]);
-  const int64_t chunk_base = sm.imisc[3];
+  const int64_t chunk_base = __builtin_amdgcn_readfirstlane(sm.imisc[3]);
   const int64_t ts0 = b.cu[seq], ts1 = b.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;  // malformed cu_seqlens: touch nothing
   if (kTransition && c0 == 0) return;  // a sequence's first unit has no predecessor
@@ -486,14 +486,39 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 
 // Tm = (I + A)^-1 of every chunk, A_ri = beta_r e^{gamma_r - gamma_i} k_r . k_i for i < r < n
 // ("How to Speed Up GDN Kernels for Qwen Models", section "What GDN actually computes"), zero
-// outside [0, n)^2.  One wave per (chunk, head): K K^T on bf16 MFMA (exact products of the bf16
-// inputs), A into LDS, then forward substitution column by column, lane j holding column j of
-// Tm: Tm[r][j] = [r == j] - sum_{j <= i < r} A[r][i] Tm[i][j].  Written for the reverse chain as
-// Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles without their block padding
-// (poff0), 16 KiB per
-// (chunk, head) of tmat.
+// outside [0, n)^2, by 16 x 16 blocks (block row and column indices below): the four diagonal
+// blocks D_k = (I + A_kk)^-1 by forward substitution, lane 16 k + c holding column c of D_k;
+// then the blocks below the diagonal in order of their distance from it,
+//     T_ij = -D_i sum_{j <= k < i} A_ik T_kj,
+// each 16 x 16 x 16 product on v_mfma_f32_16x16x16_bf16 with both operands split, x = hi + lo
+// (hi hi' + hi lo' + lo hi': about 16 significant bits, the precision Tm is stored in).  One wave
+// per (chunk, head).  K K^T on bf16 MFMA (exact products of the bf16 inputs): the blocks below
+// the diagonal straight into A-operand registers, the diagonal ones into LDS.  Written for the
+// reverse chain as Tm^T = hi + lo in two bf16 64 x 64 tiles laid out as the chain's LDS tiles
+// without their block padding (poff0), 16 KiB per (chunk, head) of tmat.
+namespace {
+constexpr int kTb = 16 * 20;  // one 16 x 16 fp32 block in LDS, rows padded to 20 floats
+// T's block (i, j), i >= j, at index i (i + 1) / 2 + j
+__host__ __device__ constexpr int tblk(int i, int j) { return i * (i + 1) / 2 + j; }
+__device__ __forceinline__ void split4(f32x4 x, bf16x4 &hi, bf16x4 &lo) {
+  hi = to_bf16x4(x);
+  lo = to_bf16x4(x - to_f32x4(hi));
+}
+__device__ __forceinline__ f32x4 mma3(bf16x4 ah, bf16x4 al, bf16x4 bh, bf16x4 bl, f32x4 c) {
+  c = mma_bf16_k16(ah, bh, c);
+  c = mma_bf16_k16(ah, bl, c);
+  return mma_bf16_k16(al, bh, c);
+}
+}  // namespace
+
 __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict__ tmat) {
-  __shared__ __attribute__((aligned(16))) float am[64][68];  // A^T, then the output tiles
+  // tb: T's ten blocks on and below the diagonal, each transposed (tb[blk][c][r] = T_blk[r][c]);
+  // dt: A's diagonal blocks transposed (dt[k][c][r] = A_kk[r][c]), then, in the same space (one
+  // wave: its LDS accesses take effect in program order), dr: D_k row by row.  The output tiles
+  // (16 KiB) take the whole space once every block has been read.
+  __shared__ __attribute__((aligned(16))) float smem[14 * kTb];
+  float *const tb = smem, *const dt = smem + 10 * kTb, *const dr = dt;
+  static_assert(14 * kTb * 4 >= 16384, "output tiles fit");
   const int lane = threadIdx.x, gq = lane >> 4, cl = lane & 15;
   const int cg = blockIdx.x, h = blockIdx.y, H = b.H;
   // the chunk's sequence and index within it
@@ -540,53 +565,111 @@ __global__ __launch_bounds__(64) void bwd_tm_kernel(BwdArgs b, float *__restrict
       kf[m][ks] = *reinterpret_cast<const bf16x8 *>(gk + t * b.HK * kD + 32 * ks + 8 * gq);
   }
   __syncthreads();
-  // A transposed: am[i][r] = A[r][i]
+  // A_rc for rows r = 16 bi + cl and columns c = 16 bk + 4 gq + e: the MFMA with K's block bk as
+  // its A operand and block bi as its B operand leaves k_c . k_r at this lane, which is the
+  // k16 A-operand layout of block (bi, bk) (row cl, items 4 gq .. 4 gq + 3)
+  auto ablock = [&](int bi, int bk) {
+    f32x4 acc = zero4();
 #pragma unroll
-  for (int mr = 0; mr < 4; ++mr)
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      f32x4 acc = zero4();
-      if (mi <= mr) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kf[mr][ks], kf[mi][ks], acc);
-      }
-      // acc[e] = k_r . k_i for r = 16 mr + 4 gq + e, i = 16 mi + cl
-      const int i = 16 * mi + cl, r0 = 16 * mr + 4 * gq;
-      const float gi = sg[i], ki = srk[i];
-      f32x4 v;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = r0 + e;
-        v[e] = (i < r && r < n) ? sb[r] * (srk[r] * ki) * __expf(sg[r] - gi) * acc[e] : 0.f;
-      }
-      *reinterpret_cast<f32x4 *>(&am[i][r0]) = v;
-    }
-  __syncthreads();
-  // column `lane` of Tm, right-looking: once row r is final, it is taken out of every later row,
-  // so the chain from row r to row r + 1 is one multiply-add
-  float x[64];
-#pragma unroll
-  for (int r = 0; r < 64; ++r) x[r] = r == lane ? 1.f : 0.f;
-#pragma unroll
-  for (int r = 0; r < 63; ++r) {
-#pragma unroll
-    for (int s4 = (r + 1) / 4 * 4; s4 < 64; s4 += 4) {
-      const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&am[r][s4]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (s4 + e > r) x[s4 + e] -= a4[e] * x[r];
-    }
-  }
-  __syncthreads();  // every read of A is done: its space takes the output tiles
-  // row `lane` of Tm^T (column lane of Tm) = hi + lo, in the chain's LDS layout, then out with
-  // contiguous 16-byte stores
-  char *stage = reinterpret_cast<char *>(&am[0][0]);
-  const bool col_in = lane < n;
-#pragma unroll
-  for (int u = 0; u < 16; ++u) {
+    for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kf[bk][ks], kf[bi][ks], acc);
+    const int r = 16 * bi + cl;
+    const float gr = sg[r], br = sb[r] * srk[r];
     f32x4 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = (col_in && 4 * u + e < n) ? x[4 * u + e] : 0.f;
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * bk + 4 * gq + e;
+      v[e] = (c < r && r < n) ? br * srk[c] * __expf(gr - sg[c]) * acc[e] : 0.f;
+    }
+    return v;
+  };
+  // the diagonal blocks, transposed into LDS: ablock(k, k) holds A_kk[cl][4 gq + e], which goes
+  // to dt[k][4 gq + e][cl] (row c of dt[k] is column c of A_kk)
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f32x4 v = ablock(k, k);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) dt[k * kTb + (4 * gq + e) * 20 + cl] = v[e];
+  }
+  // the blocks below the diagonal, split, in registers: a[i][k] for i > k
+  bf16x4 ah[4][3], al[4][3];
+#pragma unroll
+  for (int i = 1; i < 4; ++i)
+#pragma unroll
+    for (int k = 0; k < i; ++k) split4(ablock(i, k), ah[i][k], al[i][k]);
+  __syncthreads();
+  // D_k = (I + A_kk)^-1, lane 16 k + c: column c, right-looking (row r final, then taken out of
+  // every later row: x_s -= A_kk[s][r] x_r, A_kk[s][r] = dt[k][r][s])
+  {
+    const int k = gq, c = cl;
+    float x[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) x[s] = s == c ? 1.f : 0.f;
+#pragma unroll
+    for (int r = 0; r < 15; ++r) {
+#pragma unroll
+      for (int s4 = r / 4 * 4; s4 < 16; s4 += 4) {
+        const f32x4 a4 = *reinterpret_cast<const f32x4 *>(&dt[k * kTb + r * 20 + s4]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (s4 + e > r) x[s4 + e] -= a4[e] * x[r];
+      }
+    }
+    // T_kk = D_k: tb (transposed: row c of the block is column c of D_k) and dr (row by row)
+#pragma unroll
+    for (int s4 = 0; s4 < 16; s4 += 4)
+      *reinterpret_cast<f32x4 *>(&tb[tblk(k, k) * kTb + c * 20 + s4]) =
+          f32x4{x[s4], x[s4 + 1], x[s4 + 2], x[s4 + 3]};
+#pragma unroll
+    for (int s = 0; s < 16; ++s) dr[k * kTb + s * 20 + c] = x[s];
+  }
+  __syncthreads();
+  // T_ij = -D_i sum_{j <= k < i} A_ik T_kj: Y = sum A_ik T_kj with T_kj as the B operand (column
+  // cl, rows 4 gq ..: row cl of tb's block), then D_i Y with Y, a D-layout accumulator, as the B
+  // operand as it stands; T_ij (column cl, rows 4 gq + e) to row cl of its tb block
+  auto tblock = [&](int i, int j) {
+    f32x4 y = zero4();
+#pragma unroll
+    for (int k = j; k < i; ++k) {
+      bf16x4 th, tl;
+      split4(*reinterpret_cast<const f32x4 *>(&tb[tblk(k, j) * kTb + cl * 20 + 4 * gq]), th, tl);
+      y = mma3(ah[i][k], al[i][k], th, tl, y);
+    }
+    bf16x4 dh, dl, yh, yl;
+    split4(*reinterpret_cast<const f32x4 *>(&dr[i * kTb + cl * 20 + 4 * gq]), dh, dl);
+    split4(y, yh, yl);
+    const f32x4 t = mma3(dh, dl, yh, yl, zero4());
+    *reinterpret_cast<f32x4 *>(&tb[tblk(i, j) * kTb + cl * 20 + 4 * gq]) = -t;
+  };
+  tblock(1, 0);
+  tblock(2, 1);
+  tblock(3, 2);
+  __syncthreads();
+  tblock(2, 0);
+  tblock(3, 1);
+  __syncthreads();
+  tblock(3, 0);
+  __syncthreads();
+  // column `lane` of Tm (row lane of Tm^T): rows 16 i .. 16 i + 15 from row lane % 16 of block
+  // (i, lane / 16), zero above the diagonal blocks and outside [0, n)
+  const int jb = lane >> 4, jc = lane & 15;
+  const bool col_in = lane < n;
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int s4 = 0; s4 < 16; s4 += 4) {
+      f32x4 v = zero4();
+      if (i >= jb) v = *reinterpret_cast<const f32x4 *>(&tb[tblk(i, jb) * kTb + jc * 20 + s4]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[16 * i + s4 + e] = (col_in && 16 * i + s4 + e < n) ? v[e] : 0.f;
+    }
+  __syncthreads();  // every block is read: the output tiles take the space
+  // row `lane` of Tm^T = hi + lo, in the chain's LDS layout, then out with contiguous 16-byte
+  // stores
+  char *stage = reinterpret_cast<char *>(smem);
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const f32x4 v{x[4 * u], x[4 * u + 1], x[4 * u + 2], x[4 * u + 3]};
     const bf16x4 hi = to_bf16x4(v);
     *reinterpret_cast<bf16x4 *>(stage + poff0(lane, u)) = hi;
     *reinterpret_cast<bf16x4 *>(stage + 8192 + poff0(lane, u)) = to_bf16x4(v - to_f32x4(hi));

@@ -149,11 +149,13 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
   }
   for (int i = tid; i < 6 * kWaves * 64; i += kThreads) (&sm.prg[0][0])[i] = 0.f;
   __syncthreads();
-  const int seq = sm.imisc[0];
+  // wave-uniform (read from LDS, which the compiler cannot tell): the addresses built from them
+  // stay scalar, and the buffer resources of the stores below need no per-lane loop
+  const int seq = __builtin_amdgcn_readfirstlane(sm.imisc[0]);
   if (seq < 0) return;
   const int64_t ts0 = b.cu[seq], ts1 = b.cu[seq + 1];
   if (ts0 < 0 || ts1 < ts0 || ts1 > b.T) return;
-  const int64_t t0 = ts0 + (int64_t)sm.imisc[1] * kChunk;
+  const int64_t t0 = ts0 + (int64_t)__builtin_amdgcn_readfirstlane(sm.imisc[1]) * kChunk;
   const int n = (int)min<int64_t>(kChunk, ts1 - t0);
   const int64_t tok_bytes = (int64_t)H * kRowB;
   const int hk = h / (H / b.HK);                  // this value head's key head
