@@ -99,20 +99,17 @@ struct ChainSmem {
   alignas(16) char tt[2][2][pTile];  // [set][hi, lo]: Tm^T = hi + lo (row r, column i)
   alignas(16) char pth[pTile];       // P^T = hi + lo (row i, column r)
   alignas(16) char ptl[pTile];
-  alignas(16) float gam[64];  // gamma, rows past n hold gamma_last
-  alignas(16) float as[64];   // scale e^gamma, 0 past n
-  alignas(16) float c[64];    // e^{gamma_last - gamma}, 0 past n
-  alignas(16) float ab[64];   // e^gamma beta, 0 past n
-  alignas(16) float beta[64];
-  alignas(16) float rq[64], rk[64];  // q/k L2 normalisation: inverse row norms (1 without)
+  // per-token gate vectors, [set] as the tiles: the next chunk's are written at the end of a step
+  alignas(16) float gam[2][64];  // gamma, rows past n hold gamma_last
+  alignas(16) float as[2][64];   // scale e^gamma, 0 past n
+  alignas(16) float c[2][64];    // e^{gamma_last - gamma}, 0 past n
+  alignas(16) float ab[2][64];   // e^gamma beta, 0 past n
+  alignas(16) float beta[2][64];
+  alignas(16) float rq[2][64], rk[2][64];  // q/k L2 normalisation: inverse row norms (1 without)
   alignas(16) int imisc[8];
 };
 static_assert(sizeof(ChainSmem) <= 160 * 1024, "LDS budget");
 
-// P's 16 x 16 tiles on or below the diagonal: tile t is rows 16 kPtR[t] .. (tokens r), columns
-// 16 kPtI[t] .. (tokens i)
-__constant__ int kPtR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kPtI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 }  // namespace
 
@@ -261,7 +258,27 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     }
   };
 
-  if (ce > c0) issue(ce - 1, 0);
+  // wave 0: chunk c's gate vectors (its loads, from issue) into set gs
+  auto put_gates = [&](int c, int gs) {
+    const int n = chunk_n(c);
+    const float glast = __shfl(g_r, n - 1, 64);
+    const bool in = lane < n;
+    const float ea = __expf(g_r);
+    const float bt = __uint_as_float((unsigned)b_r << 16);
+    // normalised q, k: the rows' inverse norms fold into the factors of Q and K below
+    sm.gam[gs][lane] = in ? g_r : glast;
+    sm.as[gs][lane] = in ? xs * ea * rq_r : 0.f;
+    sm.c[gs][lane] = in ? __expf(glast - g_r) * rk_r : 0.f;
+    sm.ab[gs][lane] = in ? ea * bt * rk_r : 0.f;
+    sm.beta[gs][lane] = in ? bt : 0.f;
+    sm.rq[gs][lane] = rq_r;
+    sm.rk[gs][lane] = rk_r;
+  };
+
+  if (ce > c0) {
+    issue(ce - 1, 0);
+    if (w == 0) put_gates(ce - 1, 0);
+  }
   for (int c = ce - 1, it = 0; c >= c0; --c, ++it) {
     const bool emit = !kTransition && c < c1;  // the unit's own chunks (not a warmup's)
     const int set = it & 1;
@@ -270,38 +287,36 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     const int n = chunk_n(c);
     const int64_t cg = chunk_base + c;
     wait_vm0();       // this chunk's loads have landed (and this wave's stores are done)
-    __syncthreads();  // ... for every wave; every wave is done with the previous chunk's LDS
-    // ---- the gate vectors of this chunk into LDS, then the next chunk's loads
-    if (w == 0) {
-      const float glast = __shfl(g_r, n - 1, 64);
-      const bool in = lane < n;
-      const float ea = __expf(g_r);
-      const float bt = __uint_as_float((unsigned)b_r << 16);
-      // normalised q, k: the rows' inverse norms fold into the factors of Q and K below
-      sm.gam[lane] = in ? g_r : glast;
-      sm.as[lane] = in ? xs * ea * rq_r : 0.f;
-      sm.c[lane] = in ? __expf(glast - g_r) * rk_r : 0.f;
-      sm.ab[lane] = in ? ea * bt * rk_r : 0.f;
-      sm.beta[lane] = in ? bt : 0.f;
-      sm.rq[lane] = rq_r;
-      sm.rk[lane] = rk_r;
-    }
+    __syncthreads();  // ... for every wave, and its gate vectors; every wave is done with the
+                      // previous chunk's LDS
+    // ---- the next chunk's loads (in flight through this chunk)
     if (c > c0) issue(c - 1, set ^ 1);
-    lds_barrier();  // the gate vectors; the next chunk's loads stay in flight
     // ---- P^T = ((Q K^T) o decay)^T on and below the diagonal, split into hi + lo
     for (int t = w; t < 10; t += kWaves) {
-      const int mr = kPtR[t], mi = kPtI[t];
+      int mr, mi;
+      tri_tile(t, mr, mi);
+      // the gates first, so that their LDS reads overlap the products
+      const int i = 16 * mi + cl;
+      const float gi = sm.gam[set][i], ki = sm.rk[set][i];
+      const f32x4 gr = *reinterpret_cast<const f32x4 *>(&sm.gam[set][16 * mr + 4 * gq]);
+      const f32x4 rr = *reinterpret_cast<const f32x4 *>(&sm.rq[set][16 * mr + 4 * gq]);
+      bf16x8 fq[4], fk[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        fq[ks] = kfrag(Qt, mr, ks);
+        fk[ks] = kfrag(Kt, mi, ks);
+      }
       f32x4 acc = zero4();
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(kfrag(Qt, mr, ks), kfrag(Kt, mi, ks), acc);
-      // acc[j] = q_r . k_i for r = 16 mr + 4 gq + j, i = 16 mi + cl
-      const int i = 16 * mi + cl;
-      const float gi = sm.gam[i], ki = sm.rk[i];
+      for (int ks = 0; ks < 4; ++ks) acc = mma_bf16(fq[ks], fk[ks], acc);
+      // acc[j] = q_r . k_i for r = 16 mr + 4 gq + j, i = 16 mi + cl; branch-free (above the
+      // diagonal the exponential may overflow: the select drops it)
       f32x4 p;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int r = 16 * mr + 4 * gq + j;
-        p[j] = (i <= r && r < n) ? (sm.rq[r] * ki) * __expf(sm.gam[r] - gi) * acc[j] : 0.f;
+        const float v = (rr[j] * ki) * __expf(gr[j] - gi) * acc[j];
+        p[j] = (i <= r && r < n) ? v : 0.f;
       }
       const bf16x4 hi = to_bf16x4(p);
       const int off = poff(i, 4 * mr + gq);
@@ -309,7 +324,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       *reinterpret_cast<bf16x4 *>(&sm.ptl[off]) = to_bf16x4(p - to_f32x4(hi));
     }
     lds_barrier();  // P^T
-    const float lam = __expf(sm.gam[63]);
+    const float lam = __expf(sm.gam[set][63]);
 
     // ---- dh' of this chunk to the workspace, in bf16 (the precision of the products that use it)
     if (emit) {  // row offsets as scalar operands
@@ -367,7 +382,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[16 * mt + 4 * gq]);
+        const f32x4 cr = *reinterpret_cast<const f32x4 *>(&sm.c[set][16 * mt + 4 * gq]);
 #pragma unroll
         for (int nt = 0; nt < kNT; ++nt) dD[mt][nt] = xs * x[mt][nt] + cr * kd[mt][nt];
       }
@@ -406,7 +421,7 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
           static_cast<bf16 *>(b.dv) + base, (short)0, n * H * kD * 2, 0x00020000);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * mt + 4 * gq]);
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(&sm.beta[set][16 * mt + 4 * gq]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int row = (16 * mt + i) * H * kD;  // + 4 gq rows in the lane-constant part
@@ -426,10 +441,10 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
     bf16x8 yh[2][kNT], yl[2][kNT], nh[2][kNT], nl[2][kNT];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sm.as[32 * ks + 4 * gq]);
-      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sm.as[32 * ks + 16 + 4 * gq]);
-      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 4 * gq]);
-      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.ab[32 * ks + 16 + 4 * gq]);
+      const f32x4 a0 = *reinterpret_cast<const f32x4 *>(&sm.as[set][32 * ks + 4 * gq]);
+      const f32x4 a1 = *reinterpret_cast<const f32x4 *>(&sm.as[set][32 * ks + 16 + 4 * gq]);
+      const f32x4 b0 = *reinterpret_cast<const f32x4 *>(&sm.ab[set][32 * ks + 4 * gq]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4 *>(&sm.ab[set][32 * ks + 16 + 4 * gq]);
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) {
         const bf16x8 o = trfrag(Ot, ks, 4 * kNT * w + 4 * nt);
@@ -462,6 +477,9 @@ __global__ __launch_bounds__(kThreads) void bwd_chain_bf16_kernel(BwdArgs b, Bwd
 #pragma unroll
       for (int nt = 0; nt < kNT; ++nt) G[md][nt] = acc[nt];
     }
+    // the next chunk's gate vectors (its loads have had the whole chunk to land), visible after
+    // the barrier that opens the next step
+    if (w == 0 && c > c0) put_gates(c - 1, set ^ 1);
   }
   float *dst = nullptr;
   if (kTransition) {  // B' in the reverse walk's operand order (map_b_index)

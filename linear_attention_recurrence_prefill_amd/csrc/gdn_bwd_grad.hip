@@ -106,8 +106,6 @@ struct GradSmem {
 };
 static_assert(sizeof(GradSmem) <= 160 * 1024, "LDS budget");
 
-__constant__ int kTR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int kTI[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
 
 }  // namespace
 
@@ -313,7 +311,15 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
 
   // ---- 64 x 64 tiles on and below the diagonal: dP, dR Delta^T, Q K^T, K K^T
   for (int t = w; t < 10; t += kWaves) {
-    const int tr = kTR[t], ti = kTI[t];
+    int tr, ti;
+    tri_tile(t, tr, ti);
+    // the gates first, so that their LDS reads overlap the products
+    const int i = 16 * ti + cl;
+    const float gi = sm.gam[i], ki = sm.rk[i];
+    const f32x4 gr = *reinterpret_cast<const f32x4 *>(&sm.gam[16 * tr + 4 * gq]);
+    const f32x4 rqr = *reinterpret_cast<const f32x4 *>(&sm.rq[16 * tr + 4 * gq]);
+    const f32x4 rkr = *reinterpret_cast<const f32x4 *>(&sm.rk[16 * tr + 4 * gq]);
+    const f32x4 btr = *reinterpret_cast<const f32x4 *>(&sm.beta[16 * tr + 4 * gq]);
     f32x4 dp = zero4(), da = zero4(), qk = zero4(), kk = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -329,29 +335,25 @@ __global__ __launch_bounds__(kThreads) void bwd_grad_bf16_kernel(BwdArgs b) {
       qk = mma_bf16(aq, bk, qk);
       kk = mma_bf16(ak, bk, kk);
     }
-    const int i = 16 * ti + cl;
-    const float gi = sm.gam[i], ki = sm.rk[i];
     float rg4[4], rb4[4], csc = 0.f;  // csc: this column's sum
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int r = 16 * tr + 4 * gq + j;
-      float pm = 0.f, e = 0.f, tg = 0.f, tb = 0.f;
       // normalised q, k (factors 1 without): qk and kk of the normalised rows are rq_r rk_i qk
       // and rk_r rk_i kk; the stored tiles carry rq_r dPm rk_i and rk_r E rk_i, so that the
       // products below give rq dQ and rk dK of the normalised rows
-      const float qs = sm.rq[r] * ki, ks2 = sm.rk[r] * ki;
-      if (i <= r && r < n) {
-        const float gm = __expf(sm.gam[r] - gi);
-        pm = scale * dp[j] * gm;
-        tg = pm * (qs * qk[j]);
-        if (i < r) {
-          const float dA = -da[j];
-          const float gk = gm * (ks2 * kk[j]);
-          e = dA * gm * sm.beta[r];
-          tb = dA * gk;
-          tg += dA * sm.beta[r] * gk;
-        }
-      }
+      const float qs = rqr[j] * ki, ks2 = rkr[j] * ki;
+      // branch-free: every term is formed and the masks select (above the diagonal the
+      // exponential may overflow; the selects drop it)
+      const bool on = i <= r && r < n, below = on && i < r;
+      const float gm = __expf(gr[j] - gi);
+      const float pm0 = scale * dp[j] * gm;
+      const float dA = -da[j];
+      const float gk = gm * (ks2 * kk[j]);
+      const float pm = on ? pm0 : 0.f;
+      const float e = below ? dA * gm * btr[j] : 0.f;
+      const float tb = below ? dA * gk : 0.f;
+      const float tg = (on ? pm0 * (qs * qk[j]) : 0.f) + (below ? dA * btr[j] * gk : 0.f);
       const int off = poff(r, i >> 2) + 2 * (i & 3);
       st_split(sm.tth, sm.ttl, off, qs * pm);
       st_split(eth, etl, off, ks2 * e);

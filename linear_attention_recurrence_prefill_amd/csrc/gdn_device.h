@@ -48,6 +48,13 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 __device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
 }
+// Tile t of the ten 16 x 16 tiles on and below the diagonal of a 64 x 64 matrix, numbered row by
+// row (t = r (r + 1) / 2 + i): its block row r and block column i <= r.  Scalar arithmetic, for
+// a wave-uniform t.
+__device__ __forceinline__ void tri_tile(int t, int &r, int &i) {
+  r = (t >= 1) + (t >= 3) + (t >= 6);
+  i = t - r * (r + 1) / 2;
+}
 __device__ __forceinline__ bf16x4 lo4(bf16x8 x) { return __builtin_shufflevector(x, x, 0, 1, 2, 3); }
 __device__ __forceinline__ bf16x4 hi4(bf16x8 x) { return __builtin_shufflevector(x, x, 4, 5, 6, 7); }
 
