@@ -67,8 +67,10 @@ BWD_SOURCES = ("gdn_bwd_chain.hip", "gdn_bwd_grad.hip", "gdn_fwd_split.hip", "gd
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=20,
+    # 200 timed steps (40 windows of 5, about 15 ms on the headline): the median window is then
+    # taken over the card's sustained clock rather than a few milliseconds of it
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200,
                     help="untimed steps before the timed ones (after the on-device peak "
                          "measurements, which bring the card to its sustained clock)")
     ap.add_argument("--sets", type=int, default=3, help="input sets rotated between steps")
