@@ -1,8 +1,11 @@
 """Degenerate inputs of the method on the GPU against the fp64 oracle: beta = 0 (pure decay),
 g = 0 (no decay: the truncation window never closes, so truncate mode must reach back to each
 document's start), very negative g (the state forgets everything between tokens), and all-zero
-q and k rows under the L2 normalisation (they stay zero).  bf16 with d = 128 on the pipelined
-kernel, and fp32 with d = 64 on the general kernel (gfx950 only; marked ``gpu``)."""
+q and k rows under the L2 normalisation (they stay zero).  The forward of each, and the backward
+of the first three (every gradient against the oracle's exact backward, per (document, head);
+with g = -30 the decay factors above the diagonal of a chunk overflow and must be masked, not
+multiplied).  bf16 with d = 128 on the pipelined kernels, and fp32 with d = 64 on the general
+kernels (gfx950 only; marked ``gpu``)."""
 import numpy as np
 import pytest
 
@@ -47,6 +50,29 @@ def _run(gdn, oracle_mod, inp, label, mode, norm=False, seg=2):
     report("o", np64(o), o_ref, tol)
     report("ht", np64(ht), ht_ref, tol)
     return o, ht, o_ref, ht_ref
+
+
+def _run_bwd(gdn, oracle_mod, inp, label, mode, seg=2, rel=("dq", "dk", "dv", "dg", "dbeta")):
+    """The backward in ``mode`` against the oracle's exact gradients, per (document, head), for
+    the gradients named in ``rel``."""
+    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    dev = lambda a, t=None: torch.from_numpy(np.ascontiguousarray(a)).cuda().to(
+        t if t is not None else torch.float32)
+    args = [dev(inp[x], tdt if x != "g" else None) for x in NAMES]
+    cu = torch.from_numpy(inp["cu_seqlens"]).cuda()
+    h0 = None if inp["h0"] is None else dev(inp["h0"])
+    print(f"[{label} {mode} backward]", flush=True)
+    gr = gdn.chunk_bwd(*args, cu, dev(inp["dout"], tdt), h0, seg_chunks=seg, num_slots=256,
+                       mode=mode)
+    torch.cuda.synchronize()
+    r = oracle_mod.bwd(*[inp[x] for x in NAMES], inp["cu_seqlens"], inp["dout"], h0=inp["h0"])
+    tol = tol_for(inp["dtype"])
+    cu_h = inp["cu_seqlens"]
+    for n in rel:
+        report(n, np64(gr[n]), r[n], tol, cu=cu_h)
+    if h0 is not None:
+        report("dh0", np64(gr["dh0"]), r["dh0"], tol, cu=cu_h, states=True)
+    return gr, r
 
 
 CASES = [("bf16", 128), ("f32", 64)]
@@ -121,3 +147,44 @@ def test_all_documents_empty(gdn, dtype, d):
     torch.cuda.synchronize()
     assert gr["dq"].shape == (0, H, d)
     assert torch.equal(gr["dh0"], dht)
+
+
+@pytest.mark.parametrize("dtype,d", CASES)
+@pytest.mark.parametrize("mode", ["exact", "truncate"])
+def test_beta_zero_backward(gdn, oracle_mod, dtype, d, mode):
+    """beta = 0: dv is zero, dbeta is not (the gradient at beta = 0)."""
+    inp = make_inputs([300, 130], H=2, dk=d, dv=d, dtype=dtype, seed=601, h0_scale=0.5,
+                      with_dout=True)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    gr, _ = _run_bwd(gdn, oracle_mod, inp, f"beta=0 {dtype} d={d}", mode)
+    assert np.all(np64(gr["dv"]) == 0.0)
+
+
+@pytest.mark.parametrize("dtype,d", CASES)
+@pytest.mark.parametrize("mode", ["exact", "truncate"])
+def test_no_decay_backward(gdn, oracle_mod, dtype, d, mode):
+    """g = 0: the truncate mode's windows reach every document's ends, as exact mode."""
+    inp = make_inputs([600, 200], H=2, dk=d, dv=d, dtype=dtype, seed=602, with_dout=True)
+    inp["g"] = np.zeros_like(inp["g"])
+    _run_bwd(gdn, oracle_mod, inp, f"g=0 {dtype} d={d}", mode)
+
+
+@pytest.mark.parametrize("dtype,d", CASES)
+@pytest.mark.parametrize("mode", ["exact", "truncate"])
+def test_total_forgetting_backward(gdn, oracle_mod, dtype, d, mode):
+    """g = -30: every gradient is local to its token and the chunk maps vanish.  dg itself is
+    then of order e^-30 (the oracle's is about 1e-13): the chunked form obtains it as the row
+    minus the column sums of a chunk's products, whose diagonal terms are of order one and
+    cancel, so the e^-30 remainder lies below fp32 resolution of those sums.  dg is held to the
+    tolerance absolutely, on the scale of those per-row products (dbeta is formed from the same
+    kind), and the other gradients relatively as everywhere."""
+    inp = make_inputs([257, 64], H=2, dk=d, dv=d, dtype=dtype, seed=603, h0_scale=0.5,
+                      with_dout=True)
+    inp["g"] = np.full_like(inp["g"], -30.0)
+    gr, r = _run_bwd(gdn, oracle_mod, inp, f"g=-30 {dtype} d={d}", mode,
+                     rel=("dq", "dk", "dv", "dbeta"))
+    dg = np64(gr["dg"])
+    assert np.all(np.isfinite(dg))
+    err = np.linalg.norm(dg - r["dg"]) / np.linalg.norm(r["dbeta"])
+    print(f"  dg: |error| / |dbeta| = {err:.3e}", flush=True)
+    assert err <= tol_for(dtype)
