@@ -704,7 +704,13 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         if (c + 2 < c1) gbx = gb_load(c + 2);
       }
       wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
-      if (kNorm && c + 1 < c1) row_norms(c + 1, !kTransition && !kDump && c + 1 >= c0);
+      if (kNorm && c + 1 < c1) {
+        // the step's barrier waits for these norms: this wave goes before the chain wave that
+        // shares its SIMD while it forms them
+        __builtin_amdgcn_s_setprio(3);
+        row_norms(c + 1, !kTransition && !kDump && c + 1 >= c0);
+        __builtin_amdgcn_s_setprio(0);
+      }
       __syncthreads();
     }
   } else {
