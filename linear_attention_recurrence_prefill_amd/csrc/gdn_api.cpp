@@ -101,8 +101,8 @@ gdn_status debug_faults(hipStream_t stream) {
   if (e != hipSuccess) return hip_fail(e, "debug mode: fault flags");
   if (flags != 0)
     return fail(GDN_ERR_DEVICE_CHECK, "a kernel set fault flags 0x%x%s", flags,
-                (flags & gdn::kFaultDiagWait) ? " (the forward's wait for its diagonal blocks "
-                                                "ran out)" : "");
+                (flags & gdn::kFaultDiagWait) ? " (a bounded wait between the forward "
+                                                "kernel's waves ran out)" : "");
   return GDN_OK;
 }
 

@@ -98,7 +98,8 @@ struct WsSmem {
   alignas(16) float at[4 * AB];  // A_bb transposed (row i = column i of A_bb), wave 4 only
   alignas(16) float tt[4 * AB];  // T_bb row-major, wave 4 only
   alignas(16) int imisc[4];
-  int ready;  // chunk index + 1 whose A_22, A_33 (wave 7's part) are in at
+  int ready;   // chunk index + 1 whose A_22, A_33 (wave 7's part) are in at
+  int landed;  // kNorm: chunk index + 1 whose K and Q tiles and gate vectors wave 7 has put in
 };
 static_assert(sizeof(WsSmem) <= 160 * 1024, "LDS budget");
 
@@ -157,11 +158,12 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
 // with V = 0 (the unit's transition matrix M, so that the state after the unit is
 // M S_start + B for any start state).
-// kNorm: q and k are L2-normalised per row.  The tiles stay as loaded; wave 7 computes each row's
-// inverse norm 1 / sqrt(|row|^2 + eps) once the chunk's K and Q have landed in LDS and folds it
+// kNorm: q and k are L2-normalised per row.  The tiles stay as loaded; waves 5 (K) and 6 (Q)
+// compute each row's inverse norm 1 / sqrt(|row|^2 + eps) once wave 7 has the chunk's K and Q in
+// LDS, a step before prep uses them (wave 7 itself for the first chunk), and fold it
 // into the per-token factors: in place into the chain's gate vectors (e^gamma of R', scale
-// e^gamma of the output, e^{gamma_last - gamma} of the update; no other wave touches that chunk's
-// vectors at that point), and through rn_s into A and P, whose prep applies it by rows and
+// e^gamma of the output, e^{gamma_last - gamma} of the update; no other wave reads that chunk's
+// vectors at that point, and waves 5 and 6 scale different ones), and through rn_s into A and P, whose prep applies it by rows and
 // columns.  The normalised rows are never rounded to bf16, and the chain's code is the same as
 // without the normalisation.
 template <bool kTransition, bool kDump = false, bool kNorm = false>
@@ -216,7 +218,10 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     *reinterpret_cast<uint2 *>(&sm.p[set][poff(r, u)]) = uint2{0u, 0u};
   }
 
-  if (tid == 0) sm.ready = 0;
+  if (tid == 0) {
+    sm.ready = 0;
+    if (kNorm) sm.landed = 0;
+  }
   int cw = c0;
   if (a.truncate && c0 > 0) {
     __syncthreads();  // every wave has read the unit
@@ -274,6 +279,38 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     *reinterpret_cast<float2 *>(t1p) = float2{a11[0], a11[1]};
     *reinterpret_cast<float2 *>(t1p + 2) = float2{a11[2], a11[3]};
   };
+
+  // kNorm: inverse norms 1 / sqrt(|row|^2 + eps) of the rows of chunk c's K (which = 0) or Q
+  // (which = 1) tile, once it is in LDS, into rn_s and folded into the chunk's gate vectors (K:
+  // e^gamma of R' and e^{gamma_last - gamma} of the update; Q: the output's scale e^gamma), which
+  // gate_vectors wrote earlier.  Lane r sums row r, reading its 16-byte units in an order rotated
+  // by r (no two lanes of a 16-row block on one bank group).
+  auto row_norms = [&](int c, int which) __attribute__((always_inline)) {  // three call sites
+    const int base = (lane >> 4) * kBlk + (lane & 15) * kRowBytes;
+    const char *t = sm.kq[c % 3][which];
+    float s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const bf16x8 x = *reinterpret_cast<const bf16x8 *>(t + base + (((u + lane) & 15) << 4));
+      const bf16x2 p0 = __builtin_shufflevector(x, x, 0, 1), p1 = __builtin_shufflevector(x, x, 2, 3);
+      const bf16x2 p2 = __builtin_shufflevector(x, x, 4, 5), p3 = __builtin_shufflevector(x, x, 6, 7);
+      s = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, s, false);
+      s = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, s, false);
+    }
+    const float r = 1.f / sqrtf(s + kL2NormEps);
+    rn_s[c % 3][which][lane] = r;
+    WsSmem::Vec &vc = sm.vec[c % 3];
+    if (which == 0) {
+      vc.eg[lane] *= r;
+      vc.edt[lane] *= r;
+    } else {
+      vc.ego[lane] *= r;
+    }
+  };
+  // the Q tile of chunk c carries output rows (it is loaded and normalised only then)
+  auto emits = [&](int c) { return !kTransition && !kDump && c >= c0; };
 
   const int w = wave & 3;
 
@@ -652,34 +689,6 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (lane == 0) vc.egl[0] = __expf(gl);
       if (kDump && c >= c0 && lane < n) a.dbg_gamma[(chunk_t0(c) + lane) * H + h] = gam;
     };
-    // kNorm: inverse norms of the rows of chunk c's K (and Q) tiles, once they are in LDS.  Lane r
-    // sums row r, reading its 16-byte units in an order rotated by r (no two lanes of a 16-row
-    // block on one bank group).
-    auto row_norms = [&](int c, bool with_q) {
-      const int base = (lane >> 4) * kBlk + (lane & 15) * kRowBytes;
-      auto inv_norm = [&](const char *t) {
-        float s = 0.f;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const bf16x8 x = *reinterpret_cast<const bf16x8 *>(t + base + (((u + lane) & 15) << 4));
-          const bf16x2 p0 = __builtin_shufflevector(x, x, 0, 1), p1 = __builtin_shufflevector(x, x, 2, 3);
-          const bf16x2 p2 = __builtin_shufflevector(x, x, 4, 5), p3 = __builtin_shufflevector(x, x, 6, 7);
-          s = __builtin_amdgcn_fdot2_f32_bf16(p0, p0, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(p1, p1, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, s, false);
-          s = __builtin_amdgcn_fdot2_f32_bf16(p3, p3, s, false);
-        }
-        return 1.f / sqrtf(s + kL2NormEps);
-      };
-      const float rk = inv_norm(sm.kq[c % 3][0]);
-      const float rq = with_q ? inv_norm(sm.kq[c % 3][1]) : 1.f;
-      rn_s[c % 3][0][lane] = rk;
-      rn_s[c % 3][1][lane] = rq;
-      WsSmem::Vec &vc = sm.vec[c % 3];  // written by gate_vectors earlier in this step
-      vc.eg[lane] *= rk;
-      vc.edt[lane] *= rk;
-      vc.ego[lane] *= rq;
-    };
     GB gbx{0.f, 0};
     if (cw < c1) {
       gbx = gb_load(cw);
@@ -690,7 +699,13 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
       if (cw + 1 < c1) gbx = gb_load(cw + 1);
     }
     wait_vm0();
-    if (kNorm && cw < c1) row_norms(cw, !kTransition && !kDump && cw >= c0);
+    if (kNorm && cw < c1) {  // the first chunk's norms; waves 5 and 6 form the later chunks'
+      row_norms(cw, 0);
+      if (emits(cw))
+        row_norms(cw, 1);
+      else
+        rn_s[cw % 3][1][lane] = 1.f;
+    }
     __syncthreads();
     for (int c = cw; c <= c1; ++c) {
       if (c < c1) {  // A's diagonal blocks 2 and 3 of the chunk prep works on
@@ -704,13 +719,9 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
         if (c + 2 < c1) gbx = gb_load(c + 2);
       }
       wait_vm0();  // chunk c + 1's K and Q are in LDS before the barrier that hands them over
-      if (kNorm && c + 1 < c1) {
-        // the step's barrier waits for these norms: this wave goes before the chain wave that
-        // shares its SIMD while it forms them
-        __builtin_amdgcn_s_setprio(3);
-        row_norms(c + 1, !kTransition && !kDump && c + 1 >= c0);
-        __builtin_amdgcn_s_setprio(0);
-      }
+      // kNorm: waves 5 and 6 form chunk c + 1's row norms from them before the same barrier
+      if (kNorm && c + 1 < c1)
+        __hip_atomic_store(&sm.landed, c + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       __syncthreads();
     }
   } else {
@@ -833,6 +844,28 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           else
             run(PrepTiles<6>{});
         }
+      }
+      // kNorm: chunk c + 1's row norms, K by wave 5 and Q by wave 6, once wave 7 has put in its
+      // tiles and gate vectors (it does so in every step that has a chunk c + 1, before the
+      // step's barrier; the wait is bounded all the same, as wave 4's).  The barrier waits for
+      // these norms, so the two waves go before the chain waves on their SIMDs meanwhile.
+      if (kNorm && c + 1 < c1 && wave != 4) {
+        int it = 0;
+        for (; it < (1 << 22); ++it) {
+          const int r = __hip_atomic_load(&sm.landed, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP);
+          if (__builtin_amdgcn_readfirstlane(r) >= c + 1) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (it == (1 << 22) && lane == 0 && a.faults != nullptr)
+          __hip_atomic_fetch_or(a.faults, kFaultDiagWait, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_setprio(3);
+        if (wave == 5)
+          row_norms(c + 1, 0);
+        else if (emits(c + 1))
+          row_norms(c + 1, 1);
+        else
+          rn_s[(c + 1) % 3][1][lane] = 1.f;
+        __builtin_amdgcn_s_setprio(0);
       }
       __syncthreads();
     }

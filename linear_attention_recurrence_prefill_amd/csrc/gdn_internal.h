@@ -20,7 +20,7 @@ constexpr uint32_t kCuDescending = 2u;    // cu[n + 1] < cu[n] for some n
 constexpr uint32_t kCuLastNotTotal = 4u;  // cu[N] != T
 constexpr uint32_t kCuOutOfRange = 8u;    // some cu[n + 1] outside [0, T]
 // Fault flags kernels set in the per-device check words (gdn_device_faults).
-constexpr uint32_t kFaultDiagWait = 1u;   // the forward's wait for its diagonal blocks ran out
+constexpr uint32_t kFaultDiagWait = 1u;   // a bounded wait between the forward's waves ran out
 
 // Bytes of the static device scratch array behind gdn_chunk_fwd_noalloc (gdn_noalloc.hip).
 constexpr size_t kStaticScratchBytes = (size_t)128 << 20;
