@@ -19,12 +19,12 @@
 // computes"), with the hidden states recomputed ("Lever 2").
 //
 // One workgroup of eight waves per (chunk, head), the heads of a chunk in consecutive
-// workgroups.  Products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; q, k, v and dO
-// enter exactly, h and dh' as stored (bf16, as the forward takes h in its products), every other
-// operand as a bf16 head plus a bf16 remainder (see the reverse chain).  Wave w owns feature
-// columns [16 w, 16 w + 16) of every 64 x 128 result and takes its share of the 64 x 64 tiles;
-// h and dh' go straight from HBM into the B operands of the wave that owns their rows.  Every reduction has a fixed owner and order,
-// so results are bitwise reproducible.
+// workgroups.  Products run on v_mfma_f32_16x16x32_bf16 with fp32 accumulation; q, k, v and dO enter
+// exactly, h and dh' as stored (bf16, as the forward takes h in its products), every other operand
+// as a bf16 head plus a bf16 remainder (see the reverse chain).  Wave w owns feature columns [16 w,
+// 16 w + 16) of every 64 x 128 result and takes its share of the 64 x 64 tiles; h and dh' go
+// straight from HBM into the B operands of the wave that owns their rows.  Every reduction has a
+// fixed owner and order, so results are bitwise reproducible.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 

@@ -12,10 +12,10 @@
 
 namespace gdn {
 
-// Per-device words: [0] the last validation status written by the debug mode, [1] fault flags
-// set by kernels (kFaultDiagWait: one of the forward kernel's bounded waits between its waves,
-// for the diagonal blocks or for the normalised tiles, ran out), [2], [3] unused.  Each device holds its own copy; the host reaches it only through the
-// address hipGetSymbolAddress returns on that device.
+// Per-device words: [0] the last validation status written by the debug mode, [1] fault flags set
+// by kernels (kFaultDiagWait: one of the forward kernel's bounded waits between its waves, for the
+// diagonal blocks or for the normalised tiles, ran out), [2], [3] unused.  Each device holds its own
+// copy; the host reaches it only through the address hipGetSymbolAddress returns on that device.
 __device__ __attribute__((aligned(16))) uint32_t check_words[4];
 
 namespace {

@@ -14,16 +14,16 @@
 // M_u^T times the gradient at its end plus B'_u (the unit's own contribution, from a zero end
 // gradient), so the reverse walk applies the forward's M transposed.
 //
-// One workgroup of eight waves per (16-column block, head, sequence): the columns of the state
-// are independent under left multiplication by M.  Wave w computes rows 16 w .. 16 w + 15 of the
-// block with v_mfma_f32_16x16x32_bf16 on split operands (x = hi + lo, two bf16 each; the product
-// hi hi' + hi lo' + lo hi', about 16 significant bits per operand), its rows of M (or M^T)
-// prefetched into registers kPre units ahead (the first passes store the maps in the order of
-// these MFMA operands, so each load instruction reads 1 KiB of consecutive bytes), so each step
-// waits only for the state of the step before: written to LDS as a bf16 head and remainder,
-// column-major, in one of two buffers (one barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids congruent
-// modulo 8, which round-robin dispatch places on one XCD, so their reads of the same M share its
-// L2.
+// One workgroup of eight waves per (16-column block, head, sequence): the columns of the state are
+// independent under left multiplication by M.  Wave w computes rows 16 w .. 16 w + 15 of the block
+// with v_mfma_f32_16x16x32_bf16 on split operands (x = hi + lo, two bf16 each; the product hi hi' +
+// hi lo' + lo hi', about 16 significant bits per operand), its rows of M (or M^T) prefetched into
+// registers kPre units ahead (the first passes store the maps in the order of these MFMA operands,
+// so each load instruction reads 1 KiB of consecutive bytes), so each step waits only for the state
+// of the step before: written to LDS as a bf16 head and remainder, column-major, in one of two
+// buffers (one barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids
+// congruent modulo 8, which round-robin dispatch places on one XCD, so their reads of the same M
+// share its L2.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"

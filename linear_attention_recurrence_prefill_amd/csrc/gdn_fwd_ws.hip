@@ -11,7 +11,8 @@
 // P = (Q K^T) o decay o mask) is "prep"; the rest (K h, Delta, the output, the state update) is
 // the "chain".  A workgroup has eight waves: waves 0-3 run the chain, wave w owning state columns
 // [32 w, 32 w + 32); waves 4-6 prep chunk c + 1 while the chain runs chunk c; wave 7 forms chunk
-// c + 2's gate vectors and streams its K and Q from HBM into LDS with direct global->LDS loads.
+// c + 2's gate vectors and streams its K and Q from HBM into LDS with direct global->LDS loads
+// (with the in-kernel q/k normalisation, waves 5 and 6 also form the next chunk's row norms).
 // Each chain wave streams its own columns of the next chunk's V the same way, into a tile only it
 // reads.  One barrier per chunk hands the prepared chunk over; chain waves never wait for each
 // other (each owns its columns of the state, of V and of the output), and their barrier waits for
@@ -160,12 +161,12 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 // M S_start + B for any start state).
 // kNorm: q and k are L2-normalised per row.  The tiles stay as loaded; waves 5 (K) and 6 (Q)
 // compute each row's inverse norm 1 / sqrt(|row|^2 + eps) once wave 7 has the chunk's K and Q in
-// LDS, a step before prep uses them (wave 7 itself for the first chunk), and fold it
-// into the per-token factors: in place into the chain's gate vectors (e^gamma of R', scale
-// e^gamma of the output, e^{gamma_last - gamma} of the update; no other wave reads that chunk's
-// vectors at that point, and waves 5 and 6 scale different ones), and through rn_s into A and P, whose prep applies it by rows and
-// columns.  The normalised rows are never rounded to bf16, and the chain's code is the same as
-// without the normalisation.
+// LDS, a step before prep uses them (wave 7 itself for the first chunk), and fold it into the
+// per-token factors: in place into the chain's gate vectors (e^gamma of R', scale e^gamma of the
+// output, e^{gamma_last - gamma} of the update; no other wave reads that chunk's vectors at that
+// point, and waves 5 and 6 scale different ones), and through rn_s into A and P, whose prep
+// applies it by rows and columns.  The normalised rows are never rounded to bf16, and the chain's
+// code is the same as without the normalisation.
 template <bool kTransition, bool kDump = false, bool kNorm = false>
 __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
   __shared__ WsSmem sm;
