@@ -675,8 +675,8 @@ gdn_status bwd_layout(const gdn_problem *p, const int32_t *cu_host, BwdLayout *L
 // start states, as in the forward's exact split; or, in the truncate mode, each unit from the
 // warmup window before it, as the truncate-mode forward runs).
 gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float *gamma,
-                                  uint16_t *hc, float *delta, const BwdLayout &L, char *base,
-                                  hipStream_t stream) {
+                                  uint16_t *hc, float *delta, float *rk, const BwdLayout &L,
+                                  char *base, hipStream_t stream) {
   gdn::FwdArgs a{};
   a.q = t.q;
   a.k = t.k;
@@ -733,6 +733,7 @@ gdn_status run_fwd_recompute_bf16(const gdn_problem *p, const Tensors &t, float 
   a.dbg_gamma = gamma;
   a.dump_hc = hc;
   a.dbg_delta = delta;
+  a.dump_rk = rk;  // with l2norm: K's inverse row norms, as the recompute forms them
   e = gdn::launch_fwd_ws_dump(a, units, stream);
   if (e != hipSuccess) return hip_fail(e, "backward recompute: intermediates");
   return GDN_OK;
@@ -814,7 +815,10 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   if (fast) {
     s = check_tensors(t, p->total_tokens, false);
     if (s == GDN_OK) s = device_info(nullptr);
-    if (s == GDN_OK) s = run_fwd_recompute_bf16(p, t, gamma, hc_b16, delta, L, base, stream);
+    if (s == GDN_OK)
+      s = run_fwd_recompute_bf16(p, t, gamma, hc_b16, delta,
+                                 p->qk_l2norm ? reinterpret_cast<float *>(base + L.rk) : nullptr,
+                                 L, base, stream);
   } else {  // the general kernels' backward is unsplit: the exact one, whatever the mode
     gdn_problem pe = *p;
     pe.mode = GDN_MODE_EXACT;
@@ -862,9 +866,10 @@ gdn_status gdn_chunk_bwd(const gdn_problem *p, const void *q, const void *k, con
   b.scale = p->scale;
   hipError_t e;
   const bool bf = p->dtype == GDN_DTYPE_BF16;
-  if (p->qk_l2norm) {  // the rows' inverse norms, folded in by the kernels below
+  if (p->qk_l2norm) {  // the rows' inverse norms, folded in by the kernels below (K's come from
+                       // the pipelined recompute, which forms them anyway)
     e = gdn::launch_row_rnorm(q, p->total_tokens * k_heads(p), p->d_k, bf, rq, stream);
-    if (e == hipSuccess)
+    if (e == hipSuccess && !fast)
       e = gdn::launch_row_rnorm(k, p->total_tokens * k_heads(p), p->d_k, bf, rk, stream);
     if (e != hipSuccess) return hip_fail(e, "q/k inverse norms");
   }

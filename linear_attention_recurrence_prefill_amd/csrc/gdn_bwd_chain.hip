@@ -84,11 +84,6 @@ __device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &l
   hi = cat8(h0, h1);
   lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
 }
-__device__ __forceinline__ void st_split(char *hi, char *lo, int off, float x) {
-  const bf16 h = (bf16)x;
-  *reinterpret_cast<bf16 *>(hi + off) = h;
-  *reinterpret_cast<bf16 *>(lo + off) = (bf16)(x - (float)h);
-}
 
 // next-chunk loads: untracked, waited for by wait_vm0 at the chunk turn
 __device__ __forceinline__ void dma16(const char *g, char *l) { dma16_untracked(g, l); }

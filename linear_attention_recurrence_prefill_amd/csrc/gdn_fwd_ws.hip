@@ -153,7 +153,8 @@ __device__ __forceinline__ void dma16(const char *g, char *l) {
 // at the chunk's start in bf16 (a.dump_hc [chunks, H, D, D], the precision of the products that
 // use it), Delta (a.dbg_delta [T, H, D]) and gamma (a.dbg_gamma [T, H]) in fp32, chunks numbered
 // across sequences; in the truncate mode, for the unit's own chunks only (the warmup's belong
-// to the unit before).
+// to the unit before).  With kNorm it also writes the inverse norms of K's rows of those chunks
+// to a.dump_rk [T, HK] when given (by the first value head of each key head).
 // kTransition: the first pass of the exact split.  Workgroup (unit, head, z) runs the unit's
 // chunks from a fixed start without output and writes its final state to a.unit_out[z]: z = 0
 // from the zero state with the real V (the unit's own contribution B), z = 1 from the identity
@@ -302,6 +303,10 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     }
     const float r = 1.f / sqrtf(s + kL2NormEps);
     rn_s[c % 3][which][lane] = r;
+    if constexpr (kDump) {  // K's of the unit's own chunks, once per key head, for the backward
+      if (which == 0 && a.dump_rk != nullptr && c >= c0 && h % (H / a.HK) == 0 && lane < chunk_n(c))
+        a.dump_rk[(chunk_t0(c) + lane) * a.HK + h / (H / a.HK)] = r;
+    }
     WsSmem::Vec &vc = sm.vec[c % 3];
     if (which == 0) {
       vc.eg[lane] *= r;

@@ -49,6 +49,7 @@ struct FwdArgs {
   float *ht;
   float *dbg_gamma, *dbg_tmat, *dbg_w, *dbg_u, *dbg_hc, *dbg_delta;  // intermediates (or null)
   uint16_t *dump_hc;  // the pipelined kernel's recompute pass: start states in bf16 [Nc, H, D, D]
+  float *dump_rk;     // ... with l2norm: the inverse norms of K's rows [T, HK] (or null)
   int64_t T;
   int32_t N, H;
   int32_t HK;  // heads of q and k (H / HK value heads share one)
