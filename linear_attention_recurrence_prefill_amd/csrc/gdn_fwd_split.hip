@@ -19,11 +19,11 @@
 // with v_mfma_f32_16x16x32_bf16 on split operands (x = hi + lo, two bf16 each; the product hi hi' +
 // hi lo' + lo hi', about 16 significant bits per operand), its rows of M (or M^T) prefetched into
 // registers kPre units ahead (the first passes store the maps in the order of these MFMA operands,
-// so each load instruction reads 1 KiB of consecutive bytes), so each step waits only for the state
-// of the step before: written to LDS as a bf16 head and remainder, column-major, in one of two
-// buffers (one barrier per step).  The eight column blocks of one (head, sequence) get workgroup ids
-// congruent modulo 8, which round-robin dispatch places on one XCD, so their reads of the same M
-// share its L2.
+// M already split, so each load instruction reads 1 KiB of consecutive bytes and the walk converts
+// none of them), so each step waits only for the state of the step before: written to LDS as a bf16
+// head and remainder, column-major, in one of two buffers (one barrier per step).  The eight column
+// blocks of one (head, sequence) get workgroup ids congruent modulo 8, which round-robin dispatch
+// places on one XCD, so their reads of the same M share its L2.
 #include "gdn_bwd_internal.h"
 #include "gdn_device.h"
 #include "gdn_internal.h"
@@ -63,13 +63,6 @@ __device__ bool seq_units(const int32_t *cu, int N, int64_t T, int L, int n, int
 }
 
 __device__ __forceinline__ f32x4 to_f32x4(bf16x4 x) { return __builtin_convertvector(x, f32x4); }
-
-// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), for 8 values (items 0..3 from x0).
-__device__ __forceinline__ void split8(f32x4 x0, f32x4 x1, bf16x8 &hi, bf16x8 &lo) {
-  const bf16x4 h0 = to_bf16x4(x0), h1 = to_bf16x4(x1);
-  hi = cat8(h0, h1);
-  lo = cat8(to_bf16x4(x0 - to_f32x4(h0)), to_bf16x4(x1 - to_f32x4(h1)));
-}
 
 }  // namespace
 
@@ -113,9 +106,10 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
   // walk (where it would also hold back the maps in flight)
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   // the walk's first unit, and the elements between the maps (states) of consecutive steps;
-  // the maps are stored in this pass's operand order (map_m_index, map_b_index): this lane's
-  // items of M for k-step ks and half j are the 16 bytes at 256 (8 w + 2 ks + j) + 4 lane, its
-  // four entries of B the 16 bytes at 4 (64 (8 cb + w) + lane)
+  // the maps are stored in this pass's operand order (map_m_hi_byte, map_b_index): this lane's
+  // eight bf16 heads of M for k-step ks are the 16 bytes at float 256 (8 w + 2 ks) + 4 lane and
+  // their remainders the 16 bytes at 256 (8 w + 2 ks + 1) + 4 lane, its four entries of B the
+  // 16 bytes at 4 (64 (8 cb + w) + lane)
   const int64_t u0 = kReverse ? first + count - 1 : first;
   const int64_t ustep = (kReverse ? -(int64_t)H : (int64_t)H) * dd;
   const float *m0 = s.unit_m + (u0 * H + h) * dd + 256 * 8 * w + 4 * lane;
@@ -152,8 +146,9 @@ __global__ __launch_bounds__(512) void affine_scan_kernel(SplitArgs s) {
     f32x4 acc0 = b, acc1 = zero4(), acc2 = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 ahi, alo;
-      split8(a[2 * ks], a[2 * ks + 1], ahi, alo);
+      // M as stored: the k-step's eight bf16 heads, then its eight remainders
+      const bf16x8 ahi = __builtin_bit_cast(bf16x8, a[2 * ks]);
+      const bf16x8 alo = __builtin_bit_cast(bf16x8, a[2 * ks + 1]);
       const int off = cl * kSR + (32 * ks + 8 * gq) * 2;
       const bf16x8 bhi = *reinterpret_cast<const bf16x8 *>(bh + off);
       const bf16x8 blo = *reinterpret_cast<const bf16x8 *>(bl + off);

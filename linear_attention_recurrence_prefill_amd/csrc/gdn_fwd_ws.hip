@@ -608,8 +608,9 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
     }
 
     if (kTransition) {
-      // the unit's map in the middle pass's operand order: B (map_b_index), M (map_m_index) and,
-      // for the backward's reverse walk, M^T; this lane holds rows 16 mt + 4 gq + i of column c
+      // the unit's map in the middle pass's operand order: B (map_b_index), M (split,
+      // map_m_hi_byte) and, for the backward's reverse walk, M^T; this lane holds rows
+      // 16 mt + 4 gq + i of column c
       float *dst = a.unit_out + (((int64_t)blockIdx.z * a.units + unit) * H + h) * kD * kD;
       float *dt = (is_m && a.unit_mt != nullptr && c0 > 0)
                       ? a.unit_mt + ((int64_t)unit * H + h) * kD * kD
@@ -621,11 +622,21 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           const int c = ncol + 8 * (cl >> 2) + 4 * nt + (cl & 3);
           if (!is_m) {
             *reinterpret_cast<f32x4 *>(dst + map_b_index(16 * mt + 4 * gq, c)) = S[mt][nt];
-          } else {
+          } else {  // split into bf16 head and remainder (map_m_hi_byte)
+            const bf16x4 hi = to_bf16x4(S[mt][nt]);
+            const bf16x4 lo = to_bf16x4(S[mt][nt] - __builtin_convertvector(hi, f32x4));
+            char *dm = reinterpret_cast<char *>(dst);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[map_m_index(16 * mt + 4 * gq + i, c)] = S[mt][nt][i];
-            if (dt != nullptr)  // M^T[c][r] = M[r][c]: the four rows are consecutive in k
-              *reinterpret_cast<f32x4 *>(dt + map_m_index(c, 16 * mt + 4 * gq)) = S[mt][nt];
+            for (int i = 0; i < 4; ++i) {
+              const int64_t o = map_m_hi_byte(16 * mt + 4 * gq + i, c);
+              *reinterpret_cast<bf16 *>(dm + o) = hi[i];
+              *reinterpret_cast<bf16 *>(dm + o + 1024) = lo[i];
+            }
+            if (dt != nullptr) {  // M^T[c][r] = M[r][c]: the four rows are consecutive in k
+              char *dmt = reinterpret_cast<char *>(dt) + map_m_hi_byte(c, 16 * mt + 4 * gq);
+              *reinterpret_cast<bf16x4 *>(dmt) = hi;
+              *reinterpret_cast<bf16x4 *>(dmt + 1024) = lo;
+            }
           }
         }
     } else if (a.ht != nullptr && c1 == nchunks_seq) {

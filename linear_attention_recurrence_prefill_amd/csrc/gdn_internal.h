@@ -60,13 +60,13 @@ struct FwdArgs {
   int32_t l2norm;  // q and k rows divided by sqrt(|row|^2 + kL2NormEps) inside the kernel
   // exact split (pipelined kernel only): per-unit start states [units, H, D, D] for the final
   // pass, or the first pass's outputs [2, units, H, D * D] (B from zero in map_b_index order, M
-  // from the identity in map_m_index order)
+  // from the identity split into bf16 head and remainder, map_m_hi_byte)
   const float *unit_h0;
   float *unit_out;
   int64_t units;
   uint32_t *faults;  // the device's fault flags (kFault*), or null
   // exact split's first pass for the backward: when not null, M^T of every unit but a
-  // sequence's first goes here too ([units, H, D * D] in map_m_index order; the reverse walk of
+  // sequence's first goes here too ([units, H, D * D], split as M; the reverse walk of
   // the state gradient applies M^T), and M is then also formed for each sequence's last unit
   float *unit_mt;
   // unsplit runs of the pipelined kernel: 1 = workgroups take the sequences longest first, with
@@ -74,16 +74,20 @@ struct FwdArgs {
   int32_t longest_first;
 };
 
-// Layouts of a unit's maps (B and M, 128 x 128 fp32 each) as the exact split's first passes write
-// them and its middle pass reads them: in the order of that pass's MFMA operands, so that each of
-// its load instructions reads 1 KiB of consecutive bytes.  The middle pass computes, per 16-column
-// block cb of the state and per wave w (rows 16 w .. 16 w + 15), B + M S with
-// v_mfma_f32_16x16x32_bf16; lane l = 16 gq + cl holds, of M, row 16 w + cl at k = 32 ks + 8 gq +
-// 4 half + e (e < 4) for the four k-steps ks, and of B, rows 16 w + 4 gq + i (i < 4) of column
-// 16 cb + cl.
-__host__ __device__ inline int64_t map_m_index(int r, int k) {  // element M[r][k]
+// Layouts of a unit's maps (B and M, 128 x 128 each, 64 KiB) as the exact split's first passes
+// write them and its middle pass reads them: in the order of that pass's MFMA operands, so that
+// each of its load instructions reads 1 KiB of consecutive bytes.  The middle pass computes, per
+// 16-column block cb of the state and per wave w (rows 16 w .. 16 w + 15), B + M S with
+// v_mfma_f32_16x16x32_bf16; lane l = 16 gq + cl takes, of M, row 16 w + cl at k = 32 ks + 8 gq +
+// j (j < 8) for the four k-steps ks, and of B, rows 16 w + 4 gq + i (i < 4) of column 16 cb + cl.
+// B is fp32.  M is stored split, as the middle pass multiplies it: M = hi + lo with hi = bf16(M)
+// and lo = bf16(M - hi); lane l's 32 bytes of k-step ks are the eight heads (item j at bytes 2 j)
+// and then the eight remainders, and the k-steps of a wave's rows follow one another in 2 KiB
+// units (1 KiB of heads, then 1 KiB of remainders, over the 64 lanes).
+// Byte offset of M[r][k]'s head within the map; its remainder is 1 KiB further on.
+__host__ __device__ inline int64_t map_m_hi_byte(int r, int k) {
   const int w = r >> 4, cl = r & 15, ks = k >> 5, gq = (k >> 3) & 3, half = (k >> 2) & 1;
-  return ((((int64_t)(w * 4 + ks) * 2 + half) * 64 + 16 * gq + cl) * 4) + (k & 3);
+  return (((int64_t)(w * 4 + ks) * 2) * 64 + 16 * gq + cl) * 16 + 2 * (4 * half + (k & 3));
 }
 __host__ __device__ inline int64_t map_b_index(int r, int c) {  // element B[r][c]
   const int cb = c >> 4, w = r >> 4, gq = (r >> 2) & 3;
@@ -98,7 +102,7 @@ struct SplitArgs {
   const float *h0;
   int64_t h0_stride;
   const float *unit_b;   // [units, H, D * D]: each unit's B (B' in the reverse walk), map_b_index
-  const float *unit_m;   // [units, H, D * D]: each unit's M (M^T in the reverse walk), map_m_index
+  const float *unit_m;   // [units, H, D * D]: each unit's M (M^T in the reverse walk), split (map_m_hi_byte)
   float *unit_h0;        // [units, H, D, D]: the true state at each unit's start (end)
   int64_t units;
 };
