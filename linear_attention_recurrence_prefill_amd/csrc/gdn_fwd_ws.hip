@@ -143,6 +143,20 @@ struct PrepTiles<6> {
   static constexpr int q[8] = {0, 0, 0, 1, 1, 1, 1, 1};
 };
 
+// A 4 x 4 block of 16-bit values over the four lanes of a quad, lane q holding column q (item i
+// = row i, two to a dword, low half first): returns row q in lane q (item j = column j).  Two
+// exchange stages: 2 x 2 blocks transposed between lanes q and q ^ 1 (byte permutes), then the
+// off-diagonal 2 x 2 blocks swapped between lanes q and q ^ 2.
+__device__ __forceinline__ uint2 quad_transpose16(uint2 d, int lane) {
+  const unsigned p0 = __builtin_amdgcn_update_dpp(0u, d.x, 0xB1, 0xF, 0xF, true);  // lane ^ 1
+  const unsigned p1 = __builtin_amdgcn_update_dpp(0u, d.y, 0xB1, 0xF, 0xF, true);
+  const unsigned sel = (lane & 1) ? 0x03020706u : 0x05040100u;
+  const unsigned a0 = __builtin_amdgcn_perm(p0, d.x, sel), a1 = __builtin_amdgcn_perm(p1, d.y, sel);
+  const bool upper = (lane & 2) != 0;
+  const unsigned y = __builtin_amdgcn_update_dpp(0u, upper ? a0 : a1, 0x4E, 0xF, 0xF, true);  // lane ^ 2
+  return upper ? uint2{y, a1} : uint2{a0, y};
+}
+
 __device__ __forceinline__ void dma16(const char *g, char *l) {
   __builtin_amdgcn_global_load_lds(g, (GDN_LDS void *)l, 16, 0, 0);
 }
@@ -625,13 +639,14 @@ __global__ __launch_bounds__(512) void fwd_ws_kernel(FwdArgs a) {
           } else {  // split into bf16 head and remainder (map_m_hi_byte)
             const bf16x4 hi = to_bf16x4(S[mt][nt]);
             const bf16x4 lo = to_bf16x4(S[mt][nt] - __builtin_convertvector(hi, f32x4));
-            char *dm = reinterpret_cast<char *>(dst);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int64_t o = map_m_hi_byte(16 * mt + 4 * gq + i, c);
-              *reinterpret_cast<bf16 *>(dm + o) = hi[i];
-              *reinterpret_cast<bf16 *>(dm + o + 1024) = lo[i];
-            }
+            // the quad's lanes hold four consecutive columns (c % 4 = lane % 4): transposed, lane
+            // q holds row 16 mt + 4 gq + q at those columns, 8 consecutive bytes of the map
+            const uint2 th = quad_transpose16(__builtin_bit_cast(uint2, hi), lane);
+            const uint2 tl = quad_transpose16(__builtin_bit_cast(uint2, lo), lane);
+            char *dm = reinterpret_cast<char *>(dst) +
+                       map_m_hi_byte(16 * mt + 4 * gq + (lane & 3), c - (lane & 3));
+            *reinterpret_cast<uint2 *>(dm) = th;
+            *reinterpret_cast<uint2 *>(dm + 1024) = tl;
             if (dt != nullptr) {  // M^T[c][r] = M[r][c]: the four rows are consecutive in k
               char *dmt = reinterpret_cast<char *>(dt) + map_m_hi_byte(c, 16 * mt + 4 * gq);
               *reinterpret_cast<bf16x4 *>(dmt) = hi;
